@@ -1,0 +1,9 @@
+"""CPU oracle for the CfC K-loop -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke entry point and the benchmark's CPU-baseline leg may
+import this package.  The GPU library never does, and this package imports
+nothing from it.
+"""
+from .oracle import (  # noqa: F401
+    fwd_step, bwd_step, forward, train, reduce_axis0_f64, sum_axis0, lib_path,
+)

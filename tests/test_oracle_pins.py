@@ -1,0 +1,216 @@
+"""Pins of the CPU oracle to things other than itself (CPU only, no GPU).
+
+The pages print no worked numeric example of the cell, so the oracle is pinned by:
+  * central finite differences of its own loss (backward vs forward: every
+    weight, bias, h0 entry and a sample of u entries);
+  * a library routine: with W_f = 0 and W_g = W_h the cell is an Elman tanh
+    RNN, which torch.nn.RNN computes (forward, and autograd gradients);
+    with the gate driven to 0 or 1 by a large f-bias the cell follows one
+    head alone, which pins the gate's sign and the head order;
+  * exact special cases (gate = 0.5 exactly when a_f = 0; gW_f = 0 exactly
+    when the g and h heads coincide), invariants (gate in (0,1), |h_t| <= 1),
+    descent of the loss along -grad, linearity over the batch;
+  * the fp32 instantiation against the fp64 one within the fp32 bounds.
+A plausible slip -- a dropped term, a flipped sign, swapped heads, a transposed
+W, u and h swapped in z, a missing BPTT carry -- fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from recurrent_cell_amd.inputs import CONFIGS, cfc_inputs
+from tests.tolerances import assert_ok, check_act, check_grad, grad_mass
+
+
+def _loss(oracle_mod, u, y, h0, W, bias):
+    return oracle_mod.forward(u, y, h0, W, bias, "f64")[0]
+
+
+def test_finite_differences_tiny(oracle_mod):
+    """Central differences on the tiny configuration (B=4, C=16, n_x=8, K=4),
+    with non-zero biases, all 3*16*24 weights, 48 biases and 64 h0 entries."""
+    x = cfc_inputs(**CONFIGS["tiny"], seed=3, bias_scale=0.5)
+    u, y, h0 = (a.astype(np.float64) for a in (x.u, x.y, x.h0))
+    W, bias = x.W.astype(np.float64), x.bias.astype(np.float64)
+    r = oracle_mod.train(u, y, h0, W, bias, "f64", want_du=True)
+    eps = 1e-6
+
+    def fd(arr, idx):
+        old = arr[idx]
+        arr[idx] = old + eps
+        lp = _loss(oracle_mod, u, y, h0, W, bias)
+        arr[idx] = old - eps
+        lm = _loss(oracle_mod, u, y, h0, W, bias)
+        arr[idx] = old
+        return (lp - lm) / (2 * eps)
+
+    for arr, grad in ((W, r["gW"]), (bias, r["gb"]), (h0, r["dh0"])):
+        num = np.array([fd(arr, idx) for idx in np.ndindex(arr.shape)]).reshape(arr.shape)
+        err = np.abs(num - grad)
+        assert np.all(err <= 1e-6 * np.maximum(1.0, np.abs(grad))), err.max()
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        idx = tuple(int(rng.integers(0, s)) for s in u.shape)
+        assert abs(fd(u, idx) - r["du"][idx]) <= 1e-6 * max(1.0, abs(r["du"][idx]))
+
+
+def _rnn(Wq, bq, n_x, u, h0, y):
+    """torch.nn.RNN (tanh) with W_ih = Wq[:, :n_x], W_hh = Wq[:, n_x:], b_ih = bq,
+    b_hh = 0; loss 0.5 * sum (h_t - y_t)^2.  Returns outputs and gradients."""
+    C = Wq.shape[0]
+    rnn = torch.nn.RNN(n_x, C, nonlinearity="tanh", bias=True, dtype=torch.float64)
+    with torch.no_grad():
+        rnn.weight_ih_l0.copy_(torch.from_numpy(Wq[:, :n_x]))
+        rnn.weight_hh_l0.copy_(torch.from_numpy(Wq[:, n_x:]))
+        rnn.bias_ih_l0.copy_(torch.from_numpy(bq))
+        rnn.bias_hh_l0.zero_()
+    h0t = torch.from_numpy(h0.copy())[None].requires_grad_(True)
+    out, _ = rnn(torch.from_numpy(u), h0t)
+    loss = 0.5 * ((out - torch.from_numpy(y)) ** 2).sum()
+    loss.backward()
+    gw = torch.cat([rnn.weight_ih_l0.grad, rnn.weight_hh_l0.grad], dim=1).numpy()
+    return dict(h=out.detach().numpy(), loss=loss.item(), gW=gw,
+                gb=rnn.bias_ih_l0.grad.numpy(), dh0=h0t.grad[0].numpy())
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "pages"])
+def test_tied_heads_reduce_to_torch_rnn(oracle_mod, cfg):
+    """W_f = 0, W_g = W_h, b_g = b_h: h_t = tanh(W_g z + b_g) whatever the gate,
+    so the cell is torch.nn.RNN; the gradient of the tied weight is gW_g + gW_h
+    and gW_f, gb_f are exactly zero."""
+    d = dict(CONFIGS[cfg])
+    if cfg == "pages":
+        d.update(B=4, K=8)
+    x = cfc_inputs(**d, seed=5, bias_scale=0.3)
+    n_x = d["n_x"]
+    W = x.W.astype(np.float64)
+    bias = x.bias.astype(np.float64)
+    W[0] = 0.0
+    W[2] = W[1]
+    bias[2] = bias[1]
+    u, y, h0 = (a.astype(np.float64) for a in (x.u, x.y, x.h0))
+    r = oracle_mod.train(u, y, h0, W, bias, "f64")
+    t = _rnn(W[1], bias[1], n_x, u, h0, y)
+    np.testing.assert_allclose(r["h_hist"][1:], t["h"], rtol=0, atol=1e-13)
+    assert abs(r["loss"] - t["loss"]) <= 1e-11 * abs(t["loss"])
+    np.testing.assert_allclose(r["gW"][1] + r["gW"][2], t["gW"], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["gb"][1] + r["gb"][2], t["gb"], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["dh0"], t["dh0"], rtol=1e-11, atol=1e-11)
+    assert np.all(r["gW"][0] == 0.0) and np.all(r["gb"][0] == 0.0)
+
+
+@pytest.mark.parametrize("beta,head", [(40.0, 2), (-40.0, 1)])
+def test_gate_limits_follow_one_head(oracle_mod, beta, head):
+    """b_f = +40 drives gate = 1/(1+e^40) ~ 4e-18, so h_t = hh (head h);
+    b_f = -40 drives gate to 1 (exactly, in fp64), so h_t = g (head g).
+    With W_g != W_h this pins the sign of the gate and the head order."""
+    d = CONFIGS["tiny"]
+    x = cfc_inputs(**d, seed=7, bias_scale=0.3)
+    W = x.W.astype(np.float64)
+    bias = x.bias.astype(np.float64)
+    W[0] = 0.0
+    bias[0] = beta
+    u, y, h0 = (a.astype(np.float64) for a in (x.u, x.y, x.h0))
+    r = oracle_mod.train(u, y, h0, W, bias, "f64")
+    t = _rnn(W[head], bias[head], d["n_x"], u, h0, y)
+    np.testing.assert_allclose(r["h_hist"][1:], t["h"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["gW"][head], t["gW"], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(r["gb"][head], t["gb"], rtol=1e-9, atol=1e-12)
+    other = 1 if head == 2 else 2
+    assert np.abs(r["gW"][other]).max() < 1e-12
+
+
+def test_gate_is_exactly_half_when_f_preactivation_is_zero(oracle_mod):
+    x = cfc_inputs(**CONFIGS["tiny"], seed=2)
+    W = x.W.astype(np.float64)
+    W[0] = 0.0
+    _, h_hist, act = oracle_mod.forward(x.u, x.y, x.h0, W, x.bias, "f64")
+    assert np.all(act[:, 0] == 0.5)
+    np.testing.assert_array_equal(h_hist[1:], 0.5 * act[:, 1] + 0.5 * act[:, 2])
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "pages"])
+def test_invariants_gate_open_interval_and_convex_h(oracle_mod, cfg):
+    x = cfc_inputs(**CONFIGS[cfg], seed=0)
+    for prec in ("f64", "f32"):
+        _, h_hist, act = oracle_mod.forward(x.u, x.y, x.h0, x.W, x.bias, prec)
+        gate = act[:, 0]
+        assert np.all(gate > 0) and np.all(gate < 1)
+        assert np.all(np.abs(h_hist[1:]) <= 1.0)
+        assert np.all(np.abs(act[:, 1:]) <= 1.0)
+        # h_t lies between g and hh (a convex combination)
+        lo = np.minimum(act[:, 1], act[:, 2])
+        hi = np.maximum(act[:, 1], act[:, 2])
+        tol = 4 * np.finfo(h_hist.dtype).eps
+        assert np.all(h_hist[1:] >= lo - tol) and np.all(h_hist[1:] <= hi + tol)
+
+
+def test_descent_along_negative_gradient(oracle_mod):
+    x = cfc_inputs(**CONFIGS["tiny"], seed=11, bias_scale=0.2)
+    W, bias = x.W.astype(np.float64), x.bias.astype(np.float64)
+    r = oracle_mod.train(x.u, x.y, x.h0, W, bias, "f64")
+    gnorm = math.sqrt((r["gW"] ** 2).sum() + (r["gb"] ** 2).sum())
+    for scale in (1e-3, 1e-2):
+        eta = scale / gnorm
+        l1 = _loss(oracle_mod, x.u, x.y, x.h0, W - eta * r["gW"], bias - eta * r["gb"])
+        assert l1 < r["loss"]
+        # first-order prediction of the decrease holds to second order
+        pred = eta * gnorm ** 2
+        assert abs((r["loss"] - l1) - pred) <= 0.05 * pred
+
+
+def test_batch_linearity_and_per_sample_scratch(oracle_mod):
+    """S[b] depends on sample b only (bitwise), and gW = sum_b gW(sample b alone)."""
+    x = cfc_inputs(**CONFIGS["tiny"], seed=4, bias_scale=0.1)
+    full = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64")
+    acc_W = np.zeros_like(full["gW"])
+    acc_b = np.zeros_like(full["gb"])
+    for b in range(x.h0.shape[0]):
+        one = oracle_mod.train(x.u[:, b:b + 1], x.y[:, b:b + 1], x.h0[b:b + 1], x.W, x.bias, "f64")
+        np.testing.assert_array_equal(one["S"][0], full["S"][b])
+        np.testing.assert_array_equal(one["Sb"][0], full["Sb"][b])
+        np.testing.assert_array_equal(one["h_hist"][:, 0], full["h_hist"][:, b])
+        np.testing.assert_array_equal(one["gW"], one["S"][0])
+        acc_W += one["gW"]
+        acc_b += one["gb"]
+    np.testing.assert_allclose(acc_W, full["gW"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(acc_b, full["gb"], rtol=1e-13, atol=1e-13)
+
+
+def test_steps_compose_to_train(oracle_mod):
+    """The per-step functions chained by hand give the train function's results."""
+    x = cfc_inputs(**CONFIGS["tiny"], seed=9, bias_scale=0.2)
+    K, B, n_x = x.u.shape
+    C = x.h0.shape[1]
+    full = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64", want_du=True)
+    hs = [x.h0.astype(np.float64)]
+    acts = []
+    for t in range(K):
+        h, a = oracle_mod.fwd_step(x.u[t], hs[-1], x.W, x.bias, "f64")
+        hs.append(h)
+        acts.append(a)
+    np.testing.assert_array_equal(np.stack(hs), full["h_hist"])
+    S = np.zeros((B, 3, C, n_x + C))
+    Sb = np.zeros((B, 3, C))
+    carry = np.zeros((B, C))
+    for t in range(K, 0, -1):
+        carry, du, S, Sb, _ = oracle_mod.bwd_step(x.u[t - 1], hs[t - 1], hs[t], x.y[t - 1], x.W,
+                                                  acts[t - 1], carry, S, Sb, "f64")
+        np.testing.assert_array_equal(du, full["du"][t - 1])
+    np.testing.assert_array_equal(S, full["S"])
+    np.testing.assert_array_equal(carry, full["dh0"])
+    np.testing.assert_array_equal(oracle_mod.sum_axis0(S.reshape(B, -1), "f64").reshape(3, C, -1), full["gW"])
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "pages"])
+def test_fp32_instantiation_within_fp32_bounds(oracle_mod, cfg):
+    x = cfc_inputs(**CONFIGS[cfg], seed=1)
+    r64 = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64", want_dp=True)
+    r32 = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f32")
+    m = grad_mass(x.u, r64["h_hist"], r64["dp"])
+    assert_ok(check_act("h_hist", r32["h_hist"], r64["h_hist"]))
+    assert_ok(check_act("act", r32["act"], r64["act"]))
+    for k in ("S", "Sb", "gW", "gb"):
+        assert_ok(check_grad(k, r32[k], r64[k], m[k]))
