@@ -1,0 +1,148 @@
+/*
+ * cfc.h -- C ABI of libcfc.so: a closed-form continuous-time (CfC) recurrent
+ * cell trained over a K-step loop (forward, then full backpropagation through
+ * time) on AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  "K-loop Parallelization -- Block-per-Batch Kernel Refactor"
+ * (design spec of the foxhunt project):
+ *   - section Problem: the CfC forward and backward step kernels run once per
+ *     K-iteration (64 calls each per training step) and are parallel across
+ *     the batch;
+ *   - section Architecture Choice, "Param-grad writes": every (sample,
+ *     channel) pair is the sole writer of its row of a per-sample weight
+ *     gradient scratch [B, C, n_in], accumulated with +=;
+ *   - same section, "reduce_axis0": one parameterised reducer [B, N] -> [N]
+ *     that OVERWRITES its output, sums over the batch axis without atomics;
+ *   - subsection "Per-K-iteration accumulation invariant": scratch is zeroed
+ *     once at step start, every K-iteration adds into it, the reducer runs
+ *     once after the K-loop;
+ *   - subsection "AdamW-after-reducer invariant": the final gradient buffers
+ *     hold this step's values only after the reducer has run;
+ *   - section Trainer Wiring: the whole step, reducers included, is one
+ *     captured graph.
+ * The pages do not write the cell equations.  This library fixes them, with
+ * dt = 1, heads ordered f, g, h:
+ *     z    = [u_t ; h_{t-1}]            n_in = n_x + C
+ *     a_q  = W_q z + b_q
+ *     gate = 1 / (1 + exp(a_f))          (= sigmoid(-a_f * dt))
+ *     g    = tanh(a_g),  hh = tanh(a_h)
+ *     h_t  = gate * g + (1 - gate) * hh
+ *     L    = 0.5 * sum over b, t = 1..K, c of (h_t - y_t)^2
+ *
+ * Conventions for every entry point.
+ *   - All float* are DEVICE pointers to contiguous row-major fp32 arrays,
+ *     owned by the caller.  The library never allocates, frees or keeps them,
+ *     except that cfc_train_kloop remembers pointer VALUES as a graph-cache key.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and never synchronise the host; device
+ *     faults surface at the caller's next synchronisation.
+ *   - Return value: CFC_OK (0) or a negative cfc_status.  Nothing throws
+ *     across the ABI.  cfc_last_error() describes the last failure on the
+ *     calling thread.
+ *   - Sizes: B >= 0, C >= 1, n_x >= 0, K >= 0; C <= CFC_MAX_C and
+ *     n_in <= CFC_MAX_N_IN.  Index arithmetic is 64-bit.
+ *   - Outputs must not overlap the inputs of the same call (CFC_EINVAL).
+ *   - Results are deterministic: no atomics; every sum has an order fixed by
+ *     the sizes, so repeated calls give identical bits, and row b of a batched
+ *     call equals a B = 1 call on sample b bit for bit.
+ */
+#ifndef CFC_H
+#define CFC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum cfc_status {
+    CFC_OK = 0,
+    CFC_EINVAL = -1, /* null pointer, size out of range, forbidden overlap */
+    CFC_EHIP = -2    /* a HIP runtime call failed (launch, capture, instantiate) */
+};
+
+#define CFC_MAX_C 2048
+#define CFC_MAX_N_IN 8192
+
+/* One forward step for all B samples ("K-loop Parallelization", section
+ * Problem: the forward step kernel; the equations in the header comment).
+ *   u_t    [B, n_x]      input at step t
+ *   h_prev [B, C]        h_{t-1}
+ *   W      [3, C, n_in]  weights, heads f, g, h; column k < n_x multiplies
+ *                        u_t, column n_x + j multiplies h_{t-1}[j]
+ *   bias   [3, C]
+ *   h_t    [B, C]        out, overwritten; must not overlap any input
+ *   act_t  [3, B, C]     out, overwritten: (gate, g, hh) saved for backward
+ */
+int cfc_fwd_step(const float* u_t, const float* h_prev, const float* W,
+                 const float* bias, float* h_t, float* act_t,
+                 int B, int C, int n_x, void* stream);
+
+/* One backward (BPTT) step for all B samples ("K-loop Parallelization",
+ * section Architecture Choice, "Param-grad writes"):
+ *   dh    = (h_t - y_t) + dh_in
+ *   dp_f  = dh * (g - hh) * (-gate * (1 - gate))
+ *   dp_g  = dh * gate * (1 - g^2),   dp_h = dh * (1 - gate) * (1 - hh^2)
+ *   gW_scratch[b, q, c, :] += dp_q[b, c] * z_b     (sole writer per (b, c))
+ *   gb_scratch[b, q, c]    += dp_q[b, c]
+ *   dz_b = sum_q W_q^T dp_q[b, :];  dh_out = dz[n_x:],  du_t = dz[:n_x]
+ * Arguments:
+ *   u_t, h_prev, h_t, y_t, act_t  as in the forward step ([B,n_x], [B,C],
+ *                        [B,C], [B,C] targets, [3,B,C])
+ *   dh_in  [B, C]        carry from step t+1, or NULL for a zero carry (t = K)
+ *   dh_out [B, C]        out, overwritten: carry to step t-1; != dh_in
+ *   du_t   [B, n_x]      out, overwritten, or NULL to skip
+ *   gW_scratch [B, 3, C, n_in], gb_scratch [B, 3, C]   accumulated (+=)
+ */
+int cfc_bwd_step(const float* u_t, const float* h_prev, const float* h_t,
+                 const float* y_t, const float* W, const float* act_t,
+                 const float* dh_in, float* dh_out, float* du_t,
+                 float* gW_scratch, float* gb_scratch,
+                 int B, int C, int n_x, void* stream);
+
+/* Batch-axis reduction ("K-loop Parallelization", section Architecture
+ * Choice, reduce_axis0; section Risks + Mitigations: deterministic order).
+ *   out[n] = sum_{b < n_batch} per_batch[b, n]      for n < n_tail
+ * per_batch [n_batch, n_tail] fp32, out [n_tail] fp32, OVERWRITTEN.
+ * Sums are carried in fp64 in an order fixed by n_batch alone and rounded to
+ * fp32 once.  n_batch == 0 writes zeros; n_tail == 0 is a no-op; n_batch == 1
+ * is an exact copy.  out must not overlap per_batch.  Negative sizes: EINVAL.
+ */
+int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
+                 float* out, void* stream);
+
+/* One whole training step of the K-loop, replayed as one HIP graph
+ * ("K-loop Parallelization", sections Trainer Wiring and Architecture
+ * Choice): forward t = 1..K, backward t = K..1 into the per-sample scratch
+ * (zeroed at step start: the t = K backward step writes where later steps
+ * add), then reduce_axis0 over the batch overwrites gW and gb.
+ *   u [K, B, n_x], y [K, B, C], h0 [B, C], W [3, C, n_in], bias [3, C]
+ *   h_hist [K+1, B, C]   out: h_hist[0] = h0, h_hist[t] = h_t
+ *   act    [K, 3, B, C]  out: saved (gate, g, hh) of every step
+ *   dh_ws  [2, B, C]     workspace for the BPTT carry
+ *   gW_scratch [B, 3, C, n_in], gb_scratch [B, 3, C]   out: per-sample sums
+ *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
+ *                        call's work on `stream` has completed
+ * The graph is built on the first call for a given (device, pointers, sizes)
+ * and cached; later calls with the same key replay it.  Calls sharing a key
+ * must be issued on one stream at a time.  K == 0 writes h_hist[0] = h0 and
+ * zeros to the scratch and gradients.
+ */
+int cfc_train_kloop(const float* u, const float* y, const float* h0,
+                    const float* W, const float* bias,
+                    float* h_hist, float* act, float* dh_ws,
+                    float* gW_scratch, float* gb_scratch,
+                    float* gW, float* gb,
+                    int B, int C, int n_x, int K, void* stream);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* cfc_last_error(void);
+
+/* Drop every cached graph (waits for their last replay to finish). */
+int cfc_clear_graph_cache(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFC_H */

@@ -1,0 +1,166 @@
+"""Python binding of libcfc.so (include/cfc.h), same names as the C ABI.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libcfc.so.  PyTorch provides device memory (CUDA/HIP tensors) and
+the current stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcfc.so")
+
+CFC_OK = 0
+CFC_EINVAL = -1
+CFC_EHIP = -2
+
+_LIB = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+
+
+class CfcError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__("%s failed (%d): %s" % (fn, code, msg))
+        self.code = code
+
+
+def lib():
+    """The loaded libcfc.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libcfc.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.cfc_fwd_step.argtypes = [_P] * 6 + [_I, _I, _I, _P]
+        L.cfc_bwd_step.argtypes = [_P] * 11 + [_I, _I, _I, _P]
+        L.reduce_axis0.argtypes = [_P, _I64, _I64, _P, _P]
+        L.cfc_train_kloop.argtypes = [_P] * 12 + [_I, _I, _I, _I, _P]
+        L.cfc_last_error.argtypes = []
+        L.cfc_last_error.restype = ctypes.c_char_p
+        L.cfc_clear_graph_cache.argtypes = []
+        for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
+                  L.cfc_clear_graph_cache):
+            f.restype = _I
+        _LIB = L
+    return _LIB
+
+
+def last_error() -> str:
+    return lib().cfc_last_error().decode()
+
+
+def _check(fn, rc):
+    if rc != CFC_OK:
+        raise CfcError(fn, rc, last_error())
+
+
+def _dev(t, name, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError("%s must be contiguous float32" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def cfc_fwd_step(u_t, h_prev, W, bias, h_t=None, act_t=None):
+    """One forward step; returns (h_t [B,C], act_t [3,B,C])."""
+    B, n_x = u_t.shape
+    C = h_prev.shape[1]
+    if h_t is None:
+        h_t = torch.empty((B, C), dtype=torch.float32, device=h_prev.device)
+    if act_t is None:
+        act_t = torch.empty((3, B, C), dtype=torch.float32, device=h_prev.device)
+    args = (_dev(u_t, "u_t", (B, n_x)), _dev(h_prev, "h_prev", (B, C)),
+            _dev(W, "W", (3, C, n_x + C)), _dev(bias, "bias", (3, C)),
+            _dev(h_t, "h_t", (B, C)), _dev(act_t, "act_t", (3, B, C)))
+    _check("cfc_fwd_step", lib().cfc_fwd_step(*args, B, C, n_x, _stream(h_prev)))
+    return h_t, act_t
+
+
+def cfc_bwd_step(u_t, h_prev, h_t, y_t, W, act_t, dh_in, gW_scratch, gb_scratch,
+                 dh_out=None, du_t=None, want_du=False):
+    """One backward step.  dh_in may be None (zero carry).  gW_scratch and
+    gb_scratch are accumulated in place.  Returns (dh_out, du_t or None)."""
+    B, n_x = u_t.shape
+    C = h_prev.shape[1]
+    n_in = n_x + C
+    dev = h_prev.device
+    if dh_out is None:
+        dh_out = torch.empty((B, C), dtype=torch.float32, device=dev)
+    if want_du and du_t is None:
+        du_t = torch.empty((B, n_x), dtype=torch.float32, device=dev)
+    args = (_dev(u_t, "u_t", (B, n_x)), _dev(h_prev, "h_prev", (B, C)), _dev(h_t, "h_t", (B, C)),
+            _dev(y_t, "y_t", (B, C)), _dev(W, "W", (3, C, n_in)), _dev(act_t, "act_t", (3, B, C)),
+            _dev(dh_in, "dh_in", (B, C)), _dev(dh_out, "dh_out", (B, C)),
+            _dev(du_t, "du_t", (B, n_x)), _dev(gW_scratch, "gW_scratch", (B, 3, C, n_in)),
+            _dev(gb_scratch, "gb_scratch", (B, 3, C)))
+    _check("cfc_bwd_step", lib().cfc_bwd_step(*args, B, C, n_x, _stream(h_prev)))
+    return dh_out, du_t
+
+
+def reduce_axis0(per_batch, out=None):
+    """out[n] = sum_b per_batch[b, n] (overwrites out); per_batch is [B, N]."""
+    B, N = per_batch.shape
+    if out is None:
+        out = torch.empty((N,), dtype=torch.float32, device=per_batch.device)
+    p_in = _dev(per_batch, "per_batch", (B, N))
+    p_out = _dev(out, "out", (N,))
+    _check("reduce_axis0", lib().reduce_axis0(p_in, B, N, p_out, _stream(out)))
+    return out
+
+
+@dataclass
+class KloopBuffers:
+    """Outputs and workspaces of cfc_train_kloop.  Reuse one instance across
+    steps: the library caches its graph per set of pointers."""
+    h_hist: torch.Tensor      # [K+1, B, C]
+    act: torch.Tensor         # [K, 3, B, C]
+    dh_ws: torch.Tensor       # [2, B, C]
+    gW_scratch: torch.Tensor  # [B, 3, C, n_in]
+    gb_scratch: torch.Tensor  # [B, 3, C]
+    gW: torch.Tensor          # [3, C, n_in]
+    gb: torch.Tensor          # [3, C]
+
+    @staticmethod
+    def allocate(B, C, n_x, K, device):
+        n_in = n_x + C
+        e = lambda *s: torch.empty(s, dtype=torch.float32, device=device)  # noqa: E731
+        return KloopBuffers(h_hist=e(K + 1, B, C), act=e(K, 3, B, C), dh_ws=e(2, B, C),
+                            gW_scratch=e(B, 3, C, n_in), gb_scratch=e(B, 3, C),
+                            gW=e(3, C, n_in), gb=e(3, C))
+
+
+def cfc_train_kloop(u, y, h0, W, bias, out=None):
+    """One training step of the K-loop (forward, BPTT, reduce) as one graph
+    replay.  Returns the KloopBuffers holding h_hist, act, scratch, gW, gb."""
+    K, B, n_x = u.shape
+    C = h0.shape[1]
+    n_in = n_x + C
+    if out is None:
+        out = KloopBuffers.allocate(B, C, n_x, K, h0.device)
+    args = (_dev(u, "u", (K, B, n_x)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
+            _dev(W, "W", (3, C, n_in)), _dev(bias, "bias", (3, C)),
+            _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
+            _dev(out.dh_ws, "dh_ws", (2, B, C)), _dev(out.gW_scratch, "gW_scratch", (B, 3, C, n_in)),
+            _dev(out.gb_scratch, "gb_scratch", (B, 3, C)), _dev(out.gW, "gW", (3, C, n_in)),
+            _dev(out.gb, "gb", (3, C)))
+    _check("cfc_train_kloop", lib().cfc_train_kloop(*args, B, C, n_x, K, _stream(h0)))
+    return out
+
+
+def clear_graph_cache():
+    _check("cfc_clear_graph_cache", lib().cfc_clear_graph_cache())

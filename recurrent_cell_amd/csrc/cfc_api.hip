@@ -1,0 +1,400 @@
+// C ABI of libcfc.so (declared in include/cfc.h): argument checks, tiling
+// plans, the eager step launches and the cached HIP graph of the whole
+// K-loop training step.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "../../include/cfc.h"
+#include "cfc_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(CFC_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define CFC_HIP(call, what)                              \
+    do {                                                 \
+        hipError_t e_ = (call);                          \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+constexpr int64_t kMaxB = int64_t(1) << 24;
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b)
+{
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+Span span(const float* p, int64_t n) { return Span{p, (size_t)(n > 0 ? n : 0) * sizeof(float)}; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(int B, int C, int n_x)
+{
+    if (B < 0 || B > kMaxB) return fail(CFC_EINVAL, "B=%d out of range [0, %lld]", B, (long long)kMaxB);
+    if (C < 1 || C > CFC_MAX_C) return fail(CFC_EINVAL, "C=%d out of range [1, %d]", C, CFC_MAX_C);
+    if (n_x < 0 || n_x + C > CFC_MAX_N_IN)
+        return fail(CFC_EINVAL, "n_x=%d out of range (n_in = n_x + C must be <= %d)", n_x, CFC_MAX_N_IN);
+    return CFC_OK;
+}
+
+// Tiling: channel tiles of 16 (one XCD per tile index mod 8); several samples
+// per workgroup once the batch is large enough that W re-reads from L2, not
+// the number of workgroups, limit the step.  None of these choices changes
+// the arithmetic of any output.
+cfc::StepPlan make_plan(int B, int C, int n_x, const float* W, const float* scratch)
+{
+    cfc::StepPlan p{};
+    const int n_in = n_x + C;
+    p.CT = 16;
+    p.n_ctiles = (C + p.CT - 1) / p.CT;
+    p.BT = B >= 128 ? 4 : 1;
+    p.ldz = (n_in + 3) & ~3;
+    auto smem = [&](int bt) {
+        const size_t fwd = sizeof(float) * ((size_t)bt * p.ldz + (size_t)bt * 3 * p.CT);
+        const size_t bwd = sizeof(float) * ((size_t)bt * p.ldz + (size_t)bt * 3 * C +
+                                            (size_t)cfc::kSlices * bt * cfc::kCols);
+        return std::make_pair(fwd, bwd);
+    };
+    while (p.BT > 1 && smem(p.BT).second > 64 * 1024) p.BT /= 2;
+    p.fwd_smem = smem(p.BT).first;
+    p.bwd_smem = smem(p.BT).second;
+    p.n_btiles = B > 0 ? (B + p.BT - 1) / p.BT : 0;
+    // The forward's dot-product order follows Vf, so Vf depends on W alone;
+    // the backward's vector width changes no arithmetic.
+    p.Vf = (n_in % 4 == 0 && aligned16(W)) ? 4 : 1;
+    p.Vb = (n_in % 4 == 0 && scratch != nullptr && aligned16(scratch)) ? 4 : 1;
+    return p;
+}
+
+int check_plan(const cfc::StepPlan& p)
+{
+    if (p.bwd_smem > 64 * 1024 || p.fwd_smem > 64 * 1024)
+        return fail(CFC_EINVAL, "sizes need %zu bytes of LDS per workgroup (limit 65536)", p.bwd_smem);
+    if ((int64_t)p.n_btiles * p.n_ctiles > 0x7fffffffLL) return fail(CFC_EINVAL, "grid too large");
+    return CFC_OK;
+}
+
+int enqueue_fwd(const float* u_t, const float* h_prev, const float* W, const float* bias, float* h_t,
+                float* act_t, float* h_prev_copy, int B, int C, int n_x, const cfc::StepPlan& p,
+                hipStream_t s)
+{
+    if (B == 0) return CFC_OK;
+    cfc::FwdArgs a{u_t, h_prev, W, bias, h_t, act_t, h_prev_copy, B, C, n_x, p.CT, p.n_ctiles, p.ldz};
+    CFC_HIP(cfc::launch_fwd(a, p, s), "forward step launch");
+    return CFC_OK;
+}
+
+int enqueue_bwd(const float* u_t, const float* h_prev, const float* h_t, const float* y_t,
+                const float* W, const float* act_t, const float* dh_in, float* dh_out, float* du_t,
+                float* gW_s, float* gb_s, int B, int C, int n_x, int accumulate,
+                const cfc::StepPlan& p, hipStream_t s)
+{
+    if (B == 0) return CFC_OK;
+    cfc::BwdArgs a{u_t, h_prev, h_t, y_t, W, act_t, dh_in, dh_out, du_t, gW_s, gb_s,
+                   B, C, n_x, p.CT, p.n_ctiles, p.ldz, accumulate};
+    CFC_HIP(cfc::launch_bwd(a, p, s), "backward step launch");
+    return CFC_OK;
+}
+
+int enqueue_reduce(const cfc::ReduceSeg* segs_in, int nseg, int64_t B, hipStream_t s)
+{
+    cfc::ReduceSeg segs[cfc::kMaxReduceSegs];
+    int n = 0;
+    bool vec = true;
+    for (int i = 0; i < nseg; ++i) {
+        if (segs_in[i].N == 0) continue;
+        if (B == 0) {
+            CFC_HIP(cfc::launch_fill_zero(segs_in[i].out, segs_in[i].N, s), "reduce (zero fill) launch");
+            continue;
+        }
+        segs[n++] = segs_in[i];
+        vec = vec && segs_in[i].N % 4 == 0 && aligned16(segs_in[i].in) && aligned16(segs_in[i].out);
+    }
+    if (n == 0) return CFC_OK;
+    const int V = vec ? 4 : 1;
+    for (int i = 0; i < n; ++i) segs[i].groups = (segs[i].N + V - 1) / V;
+    CFC_HIP(cfc::launch_reduce(segs, n, B, V, s), "reduce_axis0 launch");
+    return CFC_OK;
+}
+
+struct KloopArgs {
+    const float *u, *y, *h0, *W, *bias;
+    float *h_hist, *act, *dh_ws, *gW_s, *gb_s, *gW, *gb;
+    int B, C, n_x, K;
+};
+
+// The whole K-loop step as a sequence of launches on one stream: K forward
+// steps (the first also copies h0 into h_hist[0]), K backward steps (the
+// t = K step writes the scratch, later steps add to it: the scratch holds
+// only this step's contributions), then one reduction launch over both
+// scratch tensors.
+int enqueue_kloop(const KloopArgs& k, const cfc::StepPlan& p, hipStream_t s)
+{
+    const int64_t BC = (int64_t)k.B * k.C;
+    const int64_t BX = (int64_t)k.B * k.n_x;
+    const int n_in = k.n_x + k.C;
+    int rc;
+    for (int t = 1; t <= k.K; ++t) {
+        const float* h_prev = (t == 1) ? k.h0 : k.h_hist + (t - 1) * BC;
+        rc = enqueue_fwd(k.u + (t - 1) * BX, h_prev, k.W, k.bias, k.h_hist + t * BC,
+                         k.act + (int64_t)(t - 1) * 3 * BC, t == 1 ? k.h_hist : nullptr, k.B, k.C,
+                         k.n_x, p, s);
+        if (rc) return rc;
+    }
+    for (int t = k.K; t >= 1; --t) {
+        const int step = k.K - t;  // 0 for t = K
+        const float* dh_in = (t == k.K) ? nullptr : k.dh_ws + ((step - 1) % 2) * BC;
+        float* dh_out = k.dh_ws + (step % 2) * BC;
+        rc = enqueue_bwd(k.u + (t - 1) * BX, k.h_hist + (t - 1) * BC, k.h_hist + t * BC,
+                         k.y + (t - 1) * BC, k.W, k.act + (int64_t)(t - 1) * 3 * BC, dh_in, dh_out,
+                         nullptr, k.gW_s, k.gb_s, k.B, k.C, k.n_x, t == k.K ? 0 : 1, p, s);
+        if (rc) return rc;
+    }
+    cfc::ReduceSeg segs[2] = {
+        {k.gW_s, k.gW, (int64_t)3 * k.C * n_in, 0},
+        {k.gb_s, k.gb, (int64_t)3 * k.C, 0},
+    };
+    return enqueue_reduce(segs, 2, k.B, s);
+}
+
+// ---------------------------------------------------------------------------
+// Graph cache of the K-loop step, keyed on device, pointer values and sizes.
+// ---------------------------------------------------------------------------
+using GraphKey = std::tuple<int, const void*, const void*, const void*, const void*, const void*,
+                            void*, void*, void*, void*, void*, void*, void*, int, int, int, int>;
+
+struct GraphEntry {
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;
+    uint64_t last_use = 0;
+};
+
+constexpr size_t kMaxGraphs = 64;
+
+std::mutex g_mu;
+std::map<GraphKey, GraphEntry> g_graphs;
+std::map<int, hipStream_t> g_capture_streams;
+uint64_t g_clock = 0;
+
+void destroy_entry(GraphEntry& e)
+{
+    if (e.done) {
+        (void)hipEventSynchronize(e.done);
+        (void)hipEventDestroy(e.done);
+    }
+    if (e.exec) (void)hipGraphExecDestroy(e.exec);
+    e = GraphEntry{};
+}
+
+int build_graph(const KloopArgs& k, const cfc::StepPlan& p, int dev, GraphEntry& out)
+{
+    hipStream_t cap;
+    auto it = g_capture_streams.find(dev);
+    if (it == g_capture_streams.end()) {
+        CFC_HIP(hipStreamCreateWithFlags(&cap, hipStreamNonBlocking), "capture stream create");
+        g_capture_streams[dev] = cap;
+    } else {
+        cap = it->second;
+    }
+    CFC_HIP(hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal), "graph capture begin");
+    const int rc = enqueue_kloop(k, p, cap);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(cap, &graph);
+    if (rc != CFC_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (ec != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return hip_fail(ec, "graph capture end");
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return hip_fail(ei, "graph instantiate");
+    hipEvent_t done;
+    const hipError_t ee = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (ee != hipSuccess) {
+        (void)hipGraphExecDestroy(exec);
+        return hip_fail(ee, "event create");
+    }
+    out.exec = exec;
+    out.done = done;
+    return CFC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cfc_last_error(void) { return g_last_error.c_str(); }
+
+int cfc_fwd_step(const float* u_t, const float* h_prev, const float* W, const float* bias, float* h_t,
+                 float* act_t, int B, int C, int n_x, void* stream)
+{
+    g_last_error.clear();
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (B == 0) return CFC_OK;
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    if (!h_prev || !W || !bias || !h_t || !act_t || (n_x > 0 && !u_t))
+        return fail(CFC_EINVAL, "cfc_fwd_step: null pointer");
+    const Span outs[] = {span(h_t, BC), span(act_t, 3 * BC)};
+    const Span ins[] = {span(u_t, (int64_t)B * n_x), span(h_prev, BC), span(W, 3 * C * n_in),
+                        span(bias, 3 * C)};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return fail(CFC_EINVAL, "cfc_fwd_step: an output overlaps an input");
+    if (overlap(outs[0], outs[1])) return fail(CFC_EINVAL, "cfc_fwd_step: h_t overlaps act_t");
+    const cfc::StepPlan p = make_plan(B, C, n_x, W, nullptr);
+    if (int rc = check_plan(p)) return rc;
+    return enqueue_fwd(u_t, h_prev, W, bias, h_t, act_t, nullptr, B, C, n_x, p, (hipStream_t)stream);
+}
+
+int cfc_bwd_step(const float* u_t, const float* h_prev, const float* h_t, const float* y_t,
+                 const float* W, const float* act_t, const float* dh_in, float* dh_out, float* du_t,
+                 float* gW_scratch, float* gb_scratch, int B, int C, int n_x, void* stream)
+{
+    g_last_error.clear();
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (B == 0) return CFC_OK;
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    if (!h_prev || !h_t || !y_t || !W || !act_t || !dh_out || !gW_scratch || !gb_scratch ||
+        (n_x > 0 && !u_t))
+        return fail(CFC_EINVAL, "cfc_bwd_step: null pointer");
+    if (n_x == 0) du_t = nullptr;
+    const Span outs[] = {span(dh_out, BC), span(du_t, (int64_t)B * n_x),
+                         span(gW_scratch, BC * 3 * n_in), span(gb_scratch, 3 * BC)};
+    const Span ins[] = {span(u_t, (int64_t)B * n_x), span(h_prev, BC), span(h_t, BC), span(y_t, BC),
+                        span(W, 3 * C * n_in), span(act_t, 3 * BC), span(dh_in, BC)};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return fail(CFC_EINVAL, "cfc_bwd_step: an output overlaps an input");
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "cfc_bwd_step: outputs overlap");
+    const cfc::StepPlan p = make_plan(B, C, n_x, W, gW_scratch);
+    if (int rc = check_plan(p)) return rc;
+    return enqueue_bwd(u_t, h_prev, h_t, y_t, W, act_t, dh_in, dh_out, du_t, gW_scratch, gb_scratch, B,
+                       C, n_x, 1, p, (hipStream_t)stream);
+}
+
+int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail, float* out, void* stream)
+{
+    g_last_error.clear();
+    if (n_batch < 0 || n_tail < 0) return fail(CFC_EINVAL, "reduce_axis0: negative size");
+    if (n_tail == 0) return CFC_OK;
+    if (!out || (n_batch > 0 && !per_batch)) return fail(CFC_EINVAL, "reduce_axis0: null pointer");
+    if (n_batch > 0 && n_tail > INT64_MAX / 4 / n_batch) return fail(CFC_EINVAL, "reduce_axis0: size overflow");
+    if (overlap(Span{per_batch, (size_t)(n_batch * n_tail) * 4}, Span{out, (size_t)n_tail * 4}))
+        return fail(CFC_EINVAL, "reduce_axis0: out overlaps per_batch");
+    const cfc::ReduceSeg seg{per_batch, out, n_tail, 0};
+    return enqueue_reduce(&seg, 1, n_batch, (hipStream_t)stream);
+}
+
+int cfc_train_kloop(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                    float* h_hist, float* act, float* dh_ws, float* gW_scratch, float* gb_scratch,
+                    float* gW, float* gb, int B, int C, int n_x, int K, void* stream)
+{
+    g_last_error.clear();
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "K=%d out of range", K);
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    // a pointer may be null only when its array is empty
+    const struct {
+        const void* p;
+        int64_t n;
+    } need[] = {{u, (int64_t)K * B * n_x}, {y, (int64_t)K * BC}, {h0, BC}, {W, 3 * C * n_in},
+                {bias, 3 * C}, {h_hist, (K + 1) * BC}, {act, (int64_t)K * 3 * BC}, {dh_ws, 2 * BC},
+                {gW_scratch, BC * 3 * n_in}, {gb_scratch, 3 * BC}, {gW, 3 * C * n_in}, {gb, 3 * C}};
+    for (const auto& q : need)
+        if (q.n > 0 && q.p == nullptr) return fail(CFC_EINVAL, "cfc_train_kloop: null pointer");
+    const Span outs[] = {span(h_hist, (K + 1) * BC), span(act, (int64_t)K * 3 * BC), span(dh_ws, 2 * BC),
+                         span(gW_scratch, BC * 3 * n_in), span(gb_scratch, 3 * BC),
+                         span(gW, 3 * C * n_in), span(gb, 3 * C)};
+    const Span ins[] = {span(u, (int64_t)K * B * n_x), span(y, (int64_t)K * BC), span(h0, BC),
+                        span(W, 3 * C * n_in), span(bias, 3 * C)};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return fail(CFC_EINVAL, "cfc_train_kloop: an output overlaps an input");
+    for (int i = 0; i < 7; ++i)
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "cfc_train_kloop: outputs overlap");
+    const cfc::StepPlan p = make_plan(B, C, n_x, W, gW_scratch);
+    if (int rc = check_plan(p)) return rc;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (K == 0 || B == 0) {
+        // Nothing to replay: h_hist[0] = h0, scratch and gradients zero.
+        if (BC > 0) CFC_HIP(hipMemcpyAsync(h_hist, h0, BC * 4, hipMemcpyDeviceToDevice, s), "h0 copy");
+        CFC_HIP(cfc::launch_fill_zero(gW_scratch, BC * 3 * n_in, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gb_scratch, 3 * BC, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gW, 3 * C * n_in, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gb, 3 * C, s), "zero fill");
+        return CFC_OK;
+    }
+
+    int dev = 0;
+    CFC_HIP(hipGetDevice(&dev), "hipGetDevice");
+    const KloopArgs k{u, y, h0, W, bias, h_hist, act, dh_ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
+    const GraphKey key{dev, u, y, h0, W, bias, h_hist, act, dh_ws, gW_scratch, gb_scratch, gW, gb,
+                       B, C, n_x, K};
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_graphs.find(key);
+    if (it == g_graphs.end()) {
+        if (g_graphs.size() >= kMaxGraphs) {
+            auto victim = g_graphs.begin();
+            for (auto j = g_graphs.begin(); j != g_graphs.end(); ++j)
+                if (j->second.last_use < victim->second.last_use) victim = j;
+            destroy_entry(victim->second);
+            g_graphs.erase(victim);
+        }
+        GraphEntry e;
+        if (int rc = build_graph(k, p, dev, e)) return rc;
+        it = g_graphs.emplace(key, e).first;
+    }
+    GraphEntry& e = it->second;
+    e.last_use = ++g_clock;
+    CFC_HIP(hipGraphLaunch(e.exec, s), "graph launch");
+    CFC_HIP(hipEventRecord(e.done, s), "event record");
+    return CFC_OK;
+}
+
+int cfc_clear_graph_cache(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto& kv : g_graphs) destroy_entry(kv.second);
+    g_graphs.clear();
+    return CFC_OK;
+}
+
+}  // extern "C"

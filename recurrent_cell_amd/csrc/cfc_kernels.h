@@ -1,0 +1,79 @@
+// Internal interface between the C-ABI layer (cfc_api.hip) and the gfx950
+// kernels (cfc_kernels.hip).  Not installed; include/cfc.h is the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cfc {
+
+constexpr int kThreads = 256;          // every kernel runs 256-lane workgroups (4 wave64)
+constexpr int kGroup = 16;             // lanes that share one forward dot product
+constexpr int kGroups = kThreads / kGroup;
+constexpr int kSlices = 16;            // row slices of the backward W^T dp reduction
+constexpr int kCols = kThreads / kSlices;
+constexpr int kMaxReduceSegs = 2;
+
+struct FwdArgs {
+    const float* u_t;     // [B, n_x]
+    const float* h_prev;  // [B, C]
+    const float* W;       // [3, C, n_in]
+    const float* bias;    // [3, C]
+    float* h_t;           // [B, C]
+    float* act_t;         // [3, B, C]
+    float* h_prev_copy;   // nullable [B, C]: receives h_prev (h_hist[0] = h0 in the K-loop)
+    int B, C, n_x, CT, n_ctiles, ldz;
+};
+
+struct BwdArgs {
+    const float* u_t;
+    const float* h_prev;
+    const float* h_t;
+    const float* y_t;
+    const float* W;
+    const float* act_t;
+    const float* dh_in;   // nullable: zero carry
+    float* dh_out;
+    float* du_t;          // nullable
+    float* gW_s;          // [B, 3, C, n_in]
+    float* gb_s;          // [B, 3, C]
+    int B, C, n_x, CT, n_ctiles, ldz;
+    int accumulate;       // 0: write dp*z (the scratch is treated as zero), 1: add
+};
+
+struct ReduceSeg {
+    const float* in;      // [B, N]
+    float* out;           // [N]
+    int64_t N;
+    int64_t groups;       // column groups of V columns: ceil(N / V)
+};
+
+struct ReduceArgs {
+    ReduceSeg seg[kMaxReduceSegs];
+    int nseg;
+    int64_t B;
+    int R;                // row slices per column (a function of B only)
+    int64_t rows_per_slice;
+};
+
+// Tiling chosen on the host; every choice leaves each output's arithmetic
+// unchanged (see DESIGN notes in cfc_kernels.hip).
+struct StepPlan {
+    int BT;        // samples per workgroup
+    int CT;        // channels per workgroup
+    int n_ctiles;  // ceil(C / CT)
+    int n_btiles;  // ceil(B / BT)
+    int Vf;        // forward: 4 = float4 reads of W rows (n_in % 4 == 0, W 16-byte aligned), else 1
+    int Vb;        // backward: 4 = float4 scratch updates (n_in % 4 == 0, scratch aligned), else 1
+    int ldz;       // LDS row pitch of z (n_in rounded up to 4)
+    size_t fwd_smem, bwd_smem;
+};
+
+int reduce_slices(int64_t B);
+
+hipError_t launch_fwd(const FwdArgs& a, const StepPlan& p, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, const StepPlan& p, hipStream_t s);
+hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+}  // namespace cfc

@@ -63,6 +63,12 @@ def reduce_rows(B: int, N: int, seed: int = 0) -> np.ndarray:
     return out
 
 
+def normal(shape, seed: int, stream: int = 0) -> np.ndarray:
+    """N(0, 1) fp32 array from stream [seed, stream] (extra operands of the
+    single-step cases: incoming carry, pre-existing scratch)."""
+    return np.random.default_rng([seed, 0x5EED, stream]).standard_normal(shape).astype(np.float32)
+
+
 def small_int_rows(B: int, N: int, seed: int = 0, lo: int = -8, hi: int = 8) -> np.ndarray:
     """Integers in [lo, hi] stored as fp32: every partial sum of at most 2^20 such
     rows is an integer below 2^24 in magnitude, so fp32 sums of them are exact."""

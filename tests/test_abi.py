@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches a kernel).
+
+* libcfc.so loads and exports every function include/cfc.h declares;
+* argument validation rejects bad sizes, null pointers and overlapping
+  buffers before anything is enqueued (fake addresses are safe here because
+  every call below is refused by the checks that run first);
+* the kernel sources contain no atomics, and the product package never
+  touches the oracle.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cfc.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from recurrent_cell_amd import build as hbuild
+    hbuild.build(force=False)
+    from recurrent_cell_amd import cfc
+    return cfc.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for n in ("cfc_fwd_step", "cfc_bwd_step", "reduce_axis0", "cfc_train_kloop"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+FAKE = 1 << 40  # never dereferenced: every call below fails validation first
+
+
+def test_reduce_axis0_argument_errors(L):
+    assert L.reduce_axis0(FAKE, -1, 4, FAKE + 4096, None) == -1
+    assert L.reduce_axis0(FAKE, 4, -1, FAKE + 4096, None) == -1
+    assert L.reduce_axis0(FAKE, 4, 8, None, None) == -1
+    assert L.reduce_axis0(None, 4, 8, FAKE, None) == -1
+    # out inside per_batch
+    assert L.reduce_axis0(FAKE, 4, 8, FAKE + 16, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    # n_tail == 0 is a no-op that succeeds without touching memory
+    assert L.reduce_axis0(None, 4, 0, None, None) == 0
+
+
+def test_step_argument_errors(L):
+    B, C, n_x = 4, 16, 8
+    n_in = n_x + C
+    u, h, W, b = FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20)
+    ht, act = FAKE + (4 << 20), FAKE + (5 << 20)
+    assert L.cfc_fwd_step(u, h, W, b, ht, act, -1, C, n_x, None) == -1
+    assert L.cfc_fwd_step(u, h, W, b, ht, act, B, 0, n_x, None) == -1
+    assert L.cfc_fwd_step(u, h, W, b, ht, act, B, 4097, n_x, None) == -1
+    assert L.cfc_fwd_step(u, h, W, b, ht, act, B, C, -1, None) == -1
+    assert L.cfc_fwd_step(u, h, W, b, ht, act, B, 2048, 8000, None) == -1
+    assert L.cfc_fwd_step(u, None, W, b, ht, act, B, C, n_x, None) == -1
+    # h_t aliasing h_prev is a race: refused
+    assert L.cfc_fwd_step(u, h, W, b, h, act, B, C, n_x, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    # act_t overlapping W
+    assert L.cfc_fwd_step(u, h, W, b, ht, W + 4 * 3 * C * n_in - 8, B, C, n_x, None) == -1
+    # backward: dh_out == dh_in, scratch overlapping W, missing scratch
+    y, dhi, dho = FAKE + (6 << 20), FAKE + (7 << 20), FAKE + (8 << 20)
+    S, Sb = FAKE + (9 << 20), FAKE + (10 << 20)
+    assert L.cfc_bwd_step(u, h, ht, y, W, act, dhi, dhi, None, S, Sb, B, C, n_x, None) == -1
+    assert L.cfc_bwd_step(u, h, ht, y, W, act, dhi, dho, None, W, Sb, B, C, n_x, None) == -1
+    assert L.cfc_bwd_step(u, h, ht, y, W, act, dhi, dho, None, None, Sb, B, C, n_x, None) == -1
+    assert L.cfc_bwd_step(u, h, ht, y, W, act, dhi, dho, None, S, Sb, B, C, n_x + 9000, None) == -1
+
+
+def test_kloop_argument_errors(L):
+    B, C, n_x, K = 4, 16, 8, 3
+    a = [FAKE + (i << 24) for i in range(12)]
+    assert L.cfc_train_kloop(*a, B, C, n_x, -1, None) == -1
+    assert L.cfc_train_kloop(*a, -2, C, n_x, K, None) == -1
+    bad = list(a)
+    bad[5] = None  # h_hist
+    assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
+    bad = list(a)
+    bad[10] = bad[9]  # gW == gb_scratch
+    assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    bad = list(a)
+    bad[6] = a[0]  # act over u
+    assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
+
+
+def test_no_atomics_in_kernel_sources():
+    csrc = os.path.join(ROOT, "recurrent_cell_amd", "csrc")
+    for fn in os.listdir(csrc):
+        text = open(os.path.join(csrc, fn)).read()
+        assert not re.search(r"\batomic\w*\s*\(|__hip_atomic|__atomic_|std::atomic", text), fn
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "recurrent_cell_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), fn
+                assert "liboracle" not in text, fn

@@ -1,0 +1,350 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Every case prints its name before touching the GPU.  Floating-point criteria
+are in tests/tolerances.py; structural properties (determinism, graph ==
+eager, batched row == single-sample run, scratch cleared between steps,
+overwrite semantics, exact special cases) are checked bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from recurrent_cell_amd.inputs import CONFIGS, cfc_inputs, normal, reduce_rows, small_int_rows
+from tests.tolerances import (assert_ok, check_act, check_grad, check_reduce, grad_mass)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": CONFIGS["tiny"],
+    "pages": CONFIGS["pages"],
+    "wide": CONFIGS["wide"],
+    "ragged_scalar": dict(B=3, C=20, n_x=5, K=3),     # n_in = 25: scalar path, partial tile
+    "three_tiles": dict(B=5, C=40, n_x=12, K=5),       # 3 channel tiles, last one partial
+    "sample_tiles": dict(B=130, C=24, n_x=8, K=3),     # 4 samples per workgroup, ragged last
+    "no_input": dict(B=2, C=16, n_x=0, K=3),           # n_x = 0: autonomous recurrence
+}
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def cfc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from recurrent_cell_amd import cfc as mod
+    mod.lib()
+    return mod
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def kloop_dev(cfc, x, out=None):
+    t = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    return cfc.cfc_train_kloop(*t, out=out), t
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+# ---------------------------------------------------------------- K-loop parity
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_kloop_matches_oracle(cfc, oracle_mod, case):
+    d = CASES[case]
+    say("kloop parity", case, d)
+    x = cfc_inputs(**d, seed=1, bias_scale=0.2)
+    out, _ = kloop_dev(cfc, x)
+    g = {k: host(getattr(out, k)) for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
+    r = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64", want_dp=True)
+    m = grad_mass(x.u, r["h_hist"], r["dp"])
+    reps = [check_act("h_hist", g["h_hist"], r["h_hist"]),
+            check_act("act", g["act"], r["act"]),
+            check_grad("S", g["gW_scratch"], r["S"], m["S"]),
+            check_grad("Sb", g["gb_scratch"], r["Sb"], m["Sb"]),
+            check_grad("gW", g["gW"], r["gW"], m["gW"]),
+            check_grad("gb", g["gb"], r["gb"], m["gb"])]
+    for rep in reps:
+        say("  ", rep["name"], "worst", "%.3g" % rep["worst_ratio"], "normwise", "%.3g" % rep["normwise"])
+    for rep in reps:
+        assert_ok(rep)
+
+
+# ---------------------------------------------------------------- single steps
+
+@pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input"])
+def test_fwd_step_matches_oracle(cfc, oracle_mod, case):
+    d = CASES[case]
+    say("fwd step parity", case)
+    x = cfc_inputs(**d, seed=2, bias_scale=0.5)
+    h_t, act_t = cfc.cfc_fwd_step(dev(x.u[0]), dev(x.h0), dev(x.W), dev(x.bias))
+    rh, ra = oracle_mod.fwd_step(x.u[0], x.h0, x.W, x.bias, "f64")
+    assert_ok(check_act("h_t", host(h_t), rh))
+    assert_ok(check_act("act_t", host(act_t), ra))
+
+
+@pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input"])
+@pytest.mark.parametrize("carry", [True, False])
+def test_bwd_step_matches_oracle(cfc, oracle_mod, case, carry):
+    d = CASES[case]
+    say("bwd step parity", case, "carry" if carry else "zero carry")
+    B, C, n_x = d["B"], d["C"], d["n_x"]
+    n_in = n_x + C
+    x = cfc_inputs(**d, seed=3, bias_scale=0.3)
+    h_t, act_t = oracle_mod.fwd_step(x.u[0], x.h0, x.W, x.bias, "f32")
+    dh_in = normal((B, C), 3, 1) if carry else None
+    S0 = normal((B, 3, C, n_in), 3, 2)
+    Sb0 = normal((B, 3, C), 3, 3)
+    S_dev, Sb_dev = dev(S0), dev(Sb0)
+    dh_out, du = cfc.cfc_bwd_step(dev(x.u[0]), dev(x.h0), dev(h_t), dev(x.y[0]), dev(x.W), dev(act_t),
+                                  dev(dh_in) if carry else None, S_dev, Sb_dev, want_du=n_x > 0)
+    zero = np.zeros((B, C), np.float32)
+    r_dh, r_du, r_S, r_Sb, r_dp = oracle_mod.bwd_step(x.u[0], x.h0, h_t, x.y[0], x.W, act_t,
+                                                      dh_in if carry else zero, S0, Sb0, "f64")
+    adp = np.abs(r_dp)                                     # [3,B,C]
+    z = np.concatenate([x.u[0], x.h0], axis=1).astype(np.float64)
+    mdz = np.einsum("qbc,qck->bk", adp, np.abs(x.W.astype(np.float64)))
+    mS = np.abs(S0) + adp.transpose(1, 0, 2)[..., None] * np.abs(z)[:, None, None, :]
+    mSb = np.abs(Sb0) + adp.transpose(1, 0, 2)
+    assert_ok(check_grad("dh_out", host(dh_out), r_dh, mdz[:, n_x:]))
+    if n_x > 0:
+        assert_ok(check_grad("du_t", host(du), r_du, mdz[:, :n_x]))
+    assert_ok(check_grad("S", host(S_dev), r_S, mS))
+    assert_ok(check_grad("Sb", host(Sb_dev), r_Sb, mSb))
+
+
+def test_bwd_carry_bits_do_not_depend_on_du_request(cfc):
+    d = CASES["pages"]
+    say("bwd du request independence")
+    x = cfc_inputs(**d, seed=4)
+    h_t, act_t = cfc.cfc_fwd_step(dev(x.u[0]), dev(x.h0), dev(x.W), dev(x.bias))
+    outs = []
+    for want in (False, True):
+        S = torch.zeros((d["B"], 3, d["C"], d["n_x"] + d["C"]), device="cuda")
+        Sb = torch.zeros((d["B"], 3, d["C"]), device="cuda")
+        dh, _ = cfc.cfc_bwd_step(dev(x.u[0]), dev(x.h0), h_t, dev(x.y[0]), dev(x.W), act_t, None, S, Sb,
+                                 want_du=want)
+        outs.append((host(dh), host(S)))
+    np.testing.assert_array_equal(bits(outs[0][0]), bits(outs[1][0]))
+    np.testing.assert_array_equal(bits(outs[0][1]), bits(outs[1][1]))
+
+
+# ---------------------------------------------------------------- structure, bit for bit
+
+def test_kloop_is_deterministic_and_replay_stable(cfc):
+    d = CASES["pages"]
+    say("kloop determinism")
+    x = cfc_inputs(**d, seed=5, bias_scale=0.1)
+    a, _ = kloop_dev(cfc, x)
+    first = {k: host(getattr(a, k)).copy() for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
+    b, _ = kloop_dev(cfc, x)            # fresh buffers: a new graph
+    t = [dev(v) for v in (x.u, x.y, x.h0, x.W, x.bias)]
+    for _ in range(3):                   # same buffers: replays of one graph
+        cfc.cfc_train_kloop(*t, out=a)
+    for k, v in first.items():
+        np.testing.assert_array_equal(bits(host(getattr(b, k))), bits(v), err_msg=k)
+        np.testing.assert_array_equal(bits(host(getattr(a, k))), bits(v), err_msg=k)
+
+
+@pytest.mark.parametrize("case", ["pages", "ragged_scalar", "sample_tiles"])
+def test_graph_equals_eager_step_calls(cfc, case):
+    d = CASES[case]
+    say("graph == eager", case)
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    x = cfc_inputs(**d, seed=6, bias_scale=0.2)
+    g, (u, y, h0, W, bias) = kloop_dev(cfc, x)
+    h = [h0]
+    acts = []
+    for t in range(K):
+        ht, at = cfc.cfc_fwd_step(u[t], h[-1], W, bias)
+        h.append(ht)
+        acts.append(at)
+    S = torch.zeros((B, 3, C, n_x + C), device="cuda")
+    Sb = torch.zeros((B, 3, C), device="cuda")
+    carry = None
+    for t in range(K, 0, -1):
+        carry, _ = cfc.cfc_bwd_step(u[t - 1], h[t - 1], h[t], y[t - 1], W, acts[t - 1], carry, S, Sb)
+    gW = cfc.reduce_axis0(S.view(B, -1))
+    gb = cfc.reduce_axis0(Sb.view(B, -1))
+    np.testing.assert_array_equal(bits(host(torch.stack(h))), bits(host(g.h_hist)))
+    np.testing.assert_array_equal(bits(host(torch.stack(acts))), bits(host(g.act)))
+    np.testing.assert_array_equal(bits(host(S)), bits(host(g.gW_scratch)))
+    np.testing.assert_array_equal(bits(host(Sb)), bits(host(g.gb_scratch)))
+    np.testing.assert_array_equal(bits(host(gW)), bits(host(g.gW).reshape(-1)))
+    np.testing.assert_array_equal(bits(host(gb)), bits(host(g.gb).reshape(-1)))
+
+
+@pytest.mark.parametrize("case", ["pages", "sample_tiles"])
+def test_batched_rows_equal_single_sample_runs(cfc, case):
+    d = CASES[case]
+    say("batched row == B=1 run", case)
+    x = cfc_inputs(**d, seed=7, bias_scale=0.2)
+    full, _ = kloop_dev(cfc, x)
+    fh, fa, fS, fSb = (host(full.h_hist), host(full.act), host(full.gW_scratch), host(full.gb_scratch))
+    for b in sorted({0, 1, d["B"] // 2, d["B"] - 1}):
+        xb = cfc_inputs(**d, seed=7, bias_scale=0.2)
+        xb.u, xb.y, xb.h0 = x.u[:, b:b + 1].copy(), x.y[:, b:b + 1].copy(), x.h0[b:b + 1].copy()
+        one, _ = kloop_dev(cfc, xb)
+        np.testing.assert_array_equal(bits(host(one.h_hist)[:, 0]), bits(fh[:, b]))
+        np.testing.assert_array_equal(bits(host(one.act)[:, :, 0]), bits(fa[:, :, b]))
+        np.testing.assert_array_equal(bits(host(one.gW_scratch)[0]), bits(fS[b]))
+        np.testing.assert_array_equal(bits(host(one.gb_scratch)[0]), bits(fSb[b]))
+        np.testing.assert_array_equal(bits(host(one.gW)), bits(fS[b]))   # B = 1: exact copy
+
+
+def test_scratch_clears_between_steps(cfc):
+    d = CASES["pages"]
+    say("scratch clears between steps")
+    xa = cfc_inputs(**d, seed=8, bias_scale=0.1)
+    xb = cfc_inputs(**d, seed=9, bias_scale=0.1)
+    t = [dev(v) for v in (xa.u, xa.y, xa.h0, xa.W, xa.bias)]
+    out = cfc.cfc_train_kloop(*t)
+    torch.cuda.synchronize()
+    for dst, src in zip(t, (xb.u, xb.y, xb.h0, xb.W, xb.bias)):
+        dst.copy_(torch.from_numpy(src))
+    cfc.cfc_train_kloop(*t, out=out)           # replay on step B's data
+    ref, _ = kloop_dev(cfc, xb)                # step B alone, fresh buffers
+    for k in ("gW_scratch", "gb_scratch", "gW", "gb", "h_hist"):
+        np.testing.assert_array_equal(bits(host(getattr(out, k))), bits(host(getattr(ref, k))), err_msg=k)
+
+
+def test_final_gradients_are_overwritten(cfc):
+    d = CASES["tiny"]
+    say("overwrite semantics")
+    x = cfc_inputs(**d, seed=10)
+    from recurrent_cell_amd.cfc import KloopBuffers
+    out = KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
+    for tns in (out.gW, out.gb, out.gW_scratch, out.gb_scratch, out.h_hist, out.act):
+        tns.fill_(float("nan"))
+    kloop_dev(cfc, x, out=out)
+    ref, _ = kloop_dev(cfc, x)
+    for k in ("gW", "gb", "gW_scratch", "gb_scratch", "h_hist", "act"):
+        v = host(getattr(out, k))
+        assert np.isfinite(v).all(), k
+        np.testing.assert_array_equal(bits(v), bits(host(getattr(ref, k))))
+
+
+def test_exact_special_cases(cfc):
+    """W_f = 0, b_f = 0 gives gate = 0.5 exactly; W_g = W_h, b_g = b_h gives
+    g == hh bit for bit and exactly zero f-head gradients."""
+    d = CASES["pages"]
+    say("special cases")
+    x = cfc_inputs(**d, seed=11, bias_scale=0.3)
+    x.W[0] = 0.0
+    x.bias[0] = 0.0
+    out, _ = kloop_dev(cfc, x)
+    assert np.all(host(out.act)[:, 0] == 0.5)
+    x = cfc_inputs(**d, seed=12, bias_scale=0.3)
+    x.W[2] = x.W[1]
+    x.bias[2] = x.bias[1]
+    out, _ = kloop_dev(cfc, x)
+    act = host(out.act)
+    np.testing.assert_array_equal(bits(act[:, 1]), bits(act[:, 2]))
+    assert np.all(host(out.gW)[0] == 0.0) and np.all(host(out.gb)[0] == 0.0)
+    h = host(out.h_hist)[1:]
+    assert np.all(np.abs(h) <= 1.0)
+    gate = act[:, 0]
+    assert np.all(gate > 0) and np.all(gate < 1)
+
+
+def test_degenerate_sizes(cfc):
+    say("K = 0 and B = 0")
+    from recurrent_cell_amd.cfc import KloopBuffers
+    x = cfc_inputs(B=3, C=16, n_x=4, K=0, seed=13)
+    out = KloopBuffers.allocate(3, 16, 4, 0, "cuda")
+    out.gW.fill_(float("nan"))
+    out.gb.fill_(float("nan"))
+    kloop_dev(cfc, x, out=out)
+    np.testing.assert_array_equal(host(out.h_hist)[0], x.h0)
+    assert np.all(host(out.gW) == 0) and np.all(host(out.gb) == 0)
+    x = cfc_inputs(B=0, C=16, n_x=4, K=3, seed=13)
+    out = KloopBuffers.allocate(0, 16, 4, 3, "cuda")
+    out.gW.fill_(float("nan"))
+    kloop_dev(cfc, x, out=out)
+    assert np.all(host(out.gW) == 0)
+
+
+# ---------------------------------------------------------------- reduce_axis0
+
+SMALL_SHAPES = [(B, N) for B in (1, 2, 3, 31, 32, 33, 128, 256, 300) for N in (1, 3, 4, 5, 255, 1000, 4097)]
+
+
+@pytest.mark.parametrize("B,N", SMALL_SHAPES)
+def test_reduce_small_and_ragged(cfc, oracle_mod, B, N):
+    say("reduce", B, N)
+    x = reduce_rows(B, N, seed=B * 7 + N)
+    xd = dev(x)
+    out = torch.full((N,), float("nan"), device="cuda")
+    cfc.reduce_axis0(xd, out)
+    got = host(out)
+    ref = oracle_mod.reduce_axis0_f64(x)
+    assert_ok(check_reduce("reduce", got, ref, np.abs(x.astype(np.float64)).sum(0), B))
+    again = host(cfc.reduce_axis0(xd))
+    np.testing.assert_array_equal(bits(again), bits(got))
+
+
+def test_reduce_integer_rows_exact(cfc):
+    for B, N in ((256, 70001), (32, 4096), (3, 7)):
+        say("reduce integer exact", B, N)
+        x = small_int_rows(B, N, seed=B)
+        got = host(cfc.reduce_axis0(dev(x)))
+        np.testing.assert_array_equal(got, x.astype(np.int64).sum(0).astype(np.float32))
+    ones = torch.ones((256, 1000), device="cuda")
+    assert np.all(host(cfc.reduce_axis0(ones)) == 256.0)
+
+
+def test_reduce_degenerate_and_unaligned(cfc):
+    say("reduce degenerate / unaligned")
+    x = reduce_rows(1, 999, seed=1)
+    np.testing.assert_array_equal(bits(host(cfc.reduce_axis0(dev(x)))), bits(x[0]))
+    out = torch.full((8,), float("nan"), device="cuda")
+    cfc.reduce_axis0(torch.empty((0, 8), device="cuda"), out)
+    assert np.all(host(out) == 0)
+    # unaligned base (scalar path) gives the same bits as the aligned copy (vector path)
+    x = reduce_rows(40, 1024, seed=2)
+    flat = torch.zeros(40 * 1024 + 1, device="cuda")
+    flat[1:] = dev(x).view(-1)
+    mis = flat[1:].view(40, 1024)
+    assert mis.data_ptr() % 16 != 0
+    np.testing.assert_array_equal(bits(host(cfc.reduce_axis0(mis))), bits(host(cfc.reduce_axis0(dev(x)))))
+
+
+FULL_B = (32, 128, 256)
+FULL_N = (4096, 73728, 1048576, 8388608)
+
+
+@pytest.mark.parametrize("B", FULL_B)
+@pytest.mark.parametrize("N", FULL_N)
+def test_reduce_full_size_sampled(cfc, oracle_mod, B, N):
+    """Full-size shapes, as the benchmark launches them.  Inputs are N(0,1)
+    from torch's seeded device generator; 4096 sampled columns (plus the first
+    and last 64) are summed by the oracle from the host copy of those columns."""
+    say("reduce full size", B, N)
+    gen = torch.Generator(device="cuda").manual_seed(1000 + B)
+    x = torch.randn((B, N), device="cuda", generator=gen)
+    out = torch.full((N,), float("nan"), device="cuda")
+    cfc.reduce_axis0(x, out)
+    rng = np.random.default_rng(N + B)
+    idx = np.unique(np.concatenate([rng.integers(0, N, 4096), np.arange(64), np.arange(N - 64, N)]))
+    cols = host(x[:, torch.from_numpy(idx).cuda()])
+    ref = oracle_mod.reduce_axis0_f64(np.ascontiguousarray(cols))
+    got = host(out)
+    assert np.isfinite(got).all()
+    assert_ok(check_reduce("reduce", got[idx], ref, np.abs(cols.astype(np.float64)).sum(0), B))
+    again = torch.empty_like(out)
+    cfc.reduce_axis0(x, again)
+    assert torch.equal(again.view(torch.int32), out.view(torch.int32))
+    del x
+    torch.cuda.empty_cache()

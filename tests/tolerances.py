@@ -60,10 +60,13 @@ def check_reduce(name, x, ref, absmass, B, rtol=1e-6):
 
 def grad_mass(u, h_hist, dp):
     """mass for S [B,3,C,n_in], Sb [B,3,C], gW [3,C,n_in], gb [3,C] from the
-    fp64 oracle's h_hist [K+1,B,C] and dp [K,3,B,C] and the inputs u [K,B,n_x]."""
+    fp64 oracle's h_hist [K+1,B,C] and dp [K,3,B,C] and the inputs u [K,B,n_x]:
+    mass_S[b,q,c,k] = sum_t |dp[t,q,b,c]| |z_t[b,k]|."""
     z = np.concatenate([np.asarray(u, np.float64), np.asarray(h_hist, np.float64)[:-1]], axis=2)
-    adp = np.abs(dp)
-    mS = np.einsum("tqbc,tbk->bqck", adp, np.abs(z))
+    adp = np.abs(np.asarray(dp, np.float64))
+    A = np.ascontiguousarray(adp.transpose(2, 1, 3, 0))          # [B,3,C,K]
+    Z = np.ascontiguousarray(np.abs(z).transpose(1, 0, 2))[:, None]  # [B,1,K,n_in]
+    mS = np.matmul(A, Z)
     mSb = adp.sum(axis=0).transpose(1, 0, 2)
     return dict(S=mS, Sb=mSb, gW=mS.sum(axis=0), gb=mSb.sum(axis=0))
 
