@@ -1,16 +1,18 @@
 """Benchmark: CfC K-loop training steps per second on one MI355X.
 
 A step is one replay of the whole K-loop graph (forward t = 1..K, BPTT
-t = K..1 into the per-sample scratch, reduce_axis0 of both scratch tensors)
-on the pages-shaped configuration B=32, C=128, n_x=64 (n_in=192), K=64,
-fp32, inputs seeded and already resident in HBM.  Prints ONE JSON line.
+t = K..1, the per-sample scratch, reduce_axis0 of both scratch tensors) on
+the pages-shaped configuration B=32, C=128, n_x=64 (n_in=192), K=64, fp32,
+inputs seeded and already resident in HBM.  Prints ONE JSON line.
 
-Also measured, in the same run:
-  * per-launch durations of the forward and backward step kernels (HIP
-    events around each launch on the launch stream) -> the roofline object
-    of the kernel with the largest share of the step;
-  * graph-node latency (a graph of dependent tiny kernels) -> the step's
-    latency roofline;
+Also measured in the same run:
+  * the duration of each kernel of the step, live: HIP event pairs around
+    eager launches of each phase on the launch stream, with the stream
+    pre-loaded by a spin kernel so the events time the GPU, not the host;
+    the kernel with the largest share of the step gives the roofline object;
+  * the same step on the 2K-launch step-kernel path, for contrast;
+  * graph-node latency (a graph of dependent one-element kernels), which
+    gives the step's latency roofline;
   * reduce_axis0 GB/s on the standalone [B, N] shapes;
   * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
 """
@@ -27,10 +29,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CfC K=64 fwd+bwd train-steps/s at B=32,C=128; reduce_axis0 GB/s vs HBM peak"
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
-FP32_PEAK = 157.3e12       # flop/s, MI355X fp32 vector
+FP32_PEAK = 157.3e12       # flop/s, MI355X fp32 vector (256 CUs x 2.4 GHz x 256 flop/clk)
 
 
 def step_bytes_flops(B, C, n_x, K):
+    """Algorithmic bytes and flops of one K-loop training step."""
     n_in = n_x + C
     f = 4
     bytes_min = f * (K * B * n_x + K * B * C + B * C + 3 * C * n_in + 3 * C      # u, y, h0, W, bias
@@ -38,17 +41,17 @@ def step_bytes_flops(B, C, n_x, K):
                      + K * B * C + K * 3 * B * C                                 # re-read in backward
                      + 2 * (3 * B * C * n_in + 3 * B * C)                        # scratch once + reduce read
                      + 3 * C * n_in + 3 * C)                                     # gW, gb
-    flops = K * B * 3 * C * n_in * 2 * 3                                        # fwd, scratch, W^T dp
+    flops = K * B * 3 * C * n_in * 2 * 3                                        # fwd, W^T dp, scratch
     return bytes_min, flops
 
 
-def bwd_launch_bytes(B, C, n_x):
-    """Algorithmic bytes of one backward step launch: its inputs read once,
-    the scratch read and written once, its outputs written once."""
+def fwd_bwd_flops(B, C, n_x, K):
+    return K * B * 3 * C * (n_x + C) * 2 * 2
+
+
+def fill_bytes(B, C, n_x, K):
     n_in = n_x + C
-    return 4 * (B * n_x + 6 * B * C + B * C + 3 * C * n_in          # u_t h_prev h_t y_t dh_in act_t(3), W
-                + 2 * 3 * B * C * n_in + 2 * 3 * B * C                # gW / gb scratch read + write
-                + B * C)                                            # dh_out
+    return 4 * (K * B * 3 * C + K * B * n_x + K * B * C + B * 3 * C * n_in + B * 3 * C)
 
 
 def fwd_launch_bytes(B, C, n_x):
@@ -56,16 +59,52 @@ def fwd_launch_bytes(B, C, n_x):
     return 4 * (B * n_x + B * C + 3 * C * n_in + 3 * C + B * C + 3 * B * C)
 
 
-def time_per_launch(torch, fn, n):
-    """Average duration of fn's kernel: an event pair around each launch."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for s, e in ev:
-        s.record()
+def bwd_launch_bytes(B, C, n_x):
+    """One backward step launch of the K-loop: inputs read once, dp and carry written."""
+    n_in = n_x + C
+    return 4 * (6 * B * C + B * C + 3 * C * n_in + 3 * B * C + B * C)
+
+
+class LaunchTimer:
+    """Average GPU duration of one launch of fn: an event pair around each of
+    n launches, with the stream first kept busy by a spin kernel long enough
+    for the host to enqueue them all (so no pair waits on the host)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        try:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            torch.cuda._sleep(1_000_000)
+            b.record()
+            torch.cuda.synchronize()
+            self.cycles_per_s = 1_000_000 / max(a.elapsed_time(b) * 1e-3, 1e-6)
+        except (AttributeError, RuntimeError):
+            self.cycles_per_s = None   # no spin kernel: pairs may include host time
+
+    def _preload(self, seconds):
+        if self.cycles_per_s is not None:
+            self.torch.cuda._sleep(int(seconds * self.cycles_per_s) + 1000)
+
+    def __call__(self, fn, n, host_us=80.0):
+        torch = self.torch
         fn()
-        e.record()
-    torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in ev]
-    return float(np.mean(ms)) * 1e-3, float(np.median(ms)) * 1e-3
+        torch.cuda.synchronize()
+        for _ in range(3):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            self._preload(n * host_us * 1e-6)
+            for s, e in ev:
+                s.record()
+                fn()
+                e.record()
+            torch.cuda.synchronize()
+            ms = np.array([s.elapsed_time(e) for s, e in ev])
+            gaps = np.array([ev[i][1].elapsed_time(ev[i + 1][0]) for i in range(n - 1)]) if n > 1 else np.zeros(1)
+            if np.median(gaps) < 0.002:
+                break
+            host_us *= 3
+        return dict(mean_s=float(ms.mean()) * 1e-3, median_s=float(np.median(ms)) * 1e-3,
+                    gap_median_us=float(np.median(gaps)) * 1e3, n=n)
 
 
 def graph_node_latency(torch, n_nodes=130, reps=50):
@@ -93,7 +132,24 @@ def graph_node_latency(torch, n_nodes=130, reps=50):
     return a.elapsed_time(b) * 1e-3 / (reps * n_nodes)
 
 
-def bench_reduce(torch, cfc, shapes, reps=10):
+def time_steps(torch, cfc, t, out, steps, warmup, trials):
+    for _ in range(warmup):
+        cfc.cfc_train_kloop(*t, out=out)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            cfc.cfc_train_kloop(*t, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / steps)
+    return float(np.median(res)), res
+
+
+def bench_reduce(torch, cfc, timer, shapes):
     res = []
     for B, N in shapes:
         nbytes = (B + 1) * N * 4
@@ -102,17 +158,15 @@ def bench_reduce(torch, cfc, shapes, reps=10):
         gen = torch.Generator(device="cuda").manual_seed(B * 31 + N)
         xs = [torch.randn((B, N), device="cuda", generator=gen) for _ in range(copies)]
         out = torch.empty(N, device="cuda")
-        for i in range(2):
-            cfc.reduce_axis0(xs[i % copies], out)
         i = [0]
 
         def run():
             cfc.reduce_axis0(xs[i[0] % copies], out)
             i[0] += 1
-        mean_s, med_s = time_per_launch(torch, run, max(reps, copies))
-        res.append(dict(B=B, N=N, bytes=nbytes, us=round(med_s * 1e6, 2),
-                        GBps=round(nbytes / med_s / 1e9, 1), frac=round(nbytes / med_s / HBM_PEAK, 3),
-                        cold=copies > 1 or in_bytes >= 512 * 2 ** 20))
+        r = timer(run, max(10, copies))
+        t_s = r["median_s"]
+        res.append(dict(B=B, N=N, bytes=nbytes, us=round(t_s * 1e6, 2), GBps=round(nbytes / t_s / 1e9, 1),
+                        frac=round(nbytes / t_s / HBM_PEAK, 3), cold=copies > 1 or in_bytes >= 512 * 2 ** 20))
         del xs, out
         torch.cuda.empty_cache()
     return res
@@ -136,12 +190,13 @@ def cpu_baseline(x, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--trials", type=int, default=7)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-reduce", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
     ap.add_argument("--workload", default="pages", choices=["tiny", "pages", "wide"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -155,84 +210,99 @@ def main():
 
     d = CONFIGS[args.workload]
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    n_in = n_x + C
     x = cfc_inputs(**d, seed=0)
     t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    path = "persistent" if cfc.cfc_kloop_path(B, C, n_x, K) == cfc.KLOOP_PERSISTENT else "steps"
     out = cfc.cfc_train_kloop(*t)
-    for _ in range(args.warmup):
-        cfc.cfc_train_kloop(*t, out=out)
-    torch.cuda.synchronize()
-
-    trials = []
-    for _ in range(args.trials):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(args.steps):
-            cfc.cfc_train_kloop(*t, out=out)
-        b.record()
-        torch.cuda.synchronize()
-        trials.append(a.elapsed_time(b) / args.steps)
-    ms_per_step = float(np.median(trials))
+    ms_per_step, trials = time_steps(torch, cfc, t, out, args.steps, args.warmup, args.trials)
     value = 1000.0 / ms_per_step
 
-    # Per-launch durations of the step kernels, same shapes and state as the graph.
-    n_in = n_x + C
-    h_hist, act = out.h_hist, out.act
-    S = torch.zeros((B, 3, C, n_in), device="cuda")
-    Sb = torch.zeros((B, 3, C), device="cuda")
-    dh = [torch.zeros((B, C), device="cuda") for _ in range(2)]
-    it = [0]
+    # The 2K-launch step-kernel path on the same inputs, for contrast.
+    cfc.cfc_set_kloop_mode(cfc.KLOOP_STEPS)
+    out_steps = cfc.cfc_train_kloop(*t)
+    ms_steps, _ = time_steps(torch, cfc, t, out_steps, max(20, args.steps // 10), 5, 3)
+    cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
-    def fwd():
-        k = it[0] % K
-        cfc.cfc_fwd_step(t[0][k], h_hist[k], t[3], t[4], h_t=h_hist[k + 1], act_t=act[k])
-        it[0] += 1
-
-    def bwd():
-        k = K - 1 - it[0] % K
-        cfc.cfc_bwd_step(t[0][k], h_hist[k], h_hist[k + 1], t[1][k], t[3], act[k], dh[it[0] % 2], S, Sb,
-                         dh_out=dh[(it[0] + 1) % 2])
-        it[0] += 1
-    nl = 4 * K
-    fwd_mean, fwd_med = time_per_launch(torch, fwd, nl)
-    it[0] = 0
-    bwd_mean, bwd_med = time_per_launch(torch, bwd, nl)
-    fwd_b, bwd_b = fwd_launch_bytes(B, C, n_x), bwd_launch_bytes(B, C, n_x)
-    if bwd_mean * K >= fwd_mean * K:
-        dom = dict(kernel="bwd_step_kernel", bytes=bwd_b, t=bwd_mean)
-    else:
-        dom = dict(kernel="fwd_step_kernel", bytes=fwd_b, t=fwd_mean)
-    achieved = dom["bytes"] / dom["t"] / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
-                "kernel": dom["kernel"], "bytes_per_launch": dom["bytes"],
-                "launch_us": round(dom["t"] * 1e6, 3)}
-
-    t_node = graph_node_latency(torch)
-    n_nodes = 2 * K + 1
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
-    t_roof = n_nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
-    step_roof = {"nodes": n_nodes, "t_node_us": round(t_node * 1e6, 3),
+    t_node = graph_node_latency(torch)
+    kernels = {}
+    roofline = None
+    if not args.no_kernels:
+        timer = LaunchTimer(torch)
+        gW_flat = out.gW_scratch.view(B, -1)
+        red_out = torch.empty(3 * C * n_in, device="cuda")
+        dp = out.ws[:K * B * 3 * C].view(K, B, 3 * C)
+        kt = {}
+        kt["fwd_bwd"] = timer(lambda: cfc.cfc_kloop_fwd_bwd(*t, out=out), 20)
+        kt["scratch_fill"] = timer(lambda: cfc.cfc_scratch_fill(dp, t[0], out.h_hist, out.gW_scratch,
+                                                                out.gb_scratch), 50)
+        kt["reduce_axis0"] = timer(lambda: cfc.reduce_axis0(gW_flat, red_out), 50)
+        # step kernels of the 2K-launch path
+        S = torch.zeros((B, 3, C, n_in), device="cuda")
+        Sb = torch.zeros((B, 3, C), device="cuda")
+        dh = [torch.zeros((B, C), device="cuda") for _ in range(2)]
+        h_hist, act = out.h_hist, out.act
+        it = [0]
+
+        def fwd():
+            k = it[0] % K
+            cfc.cfc_fwd_step(t[0][k], h_hist[k], t[3], t[4], h_t=h_hist[k + 1], act_t=act[k])
+            it[0] += 1
+
+        def bwd():
+            k = K - 1 - it[0] % K
+            cfc.cfc_bwd_step(t[0][k], h_hist[k], h_hist[k + 1], t[1][k], t[3], act[k], dh[it[0] % 2], S, Sb,
+                             dh_out=dh[(it[0] + 1) % 2])
+            it[0] += 1
+        kt["fwd_step"] = timer(fwd, 2 * K)
+        it[0] = 0
+        kt["bwd_step"] = timer(bwd, 2 * K)
+        cfc.cfc_train_kloop(*t, out=out)   # restore the step's own state
+        torch.cuda.synchronize()
+        kernels = {k: dict(mean_us=round(v["mean_s"] * 1e6, 3), median_us=round(v["median_s"] * 1e6, 3),
+                           gap_median_us=round(v["gap_median_us"], 3)) for k, v in kt.items()}
+        if path == "persistent":
+            dur = kt["fwd_bwd"]["mean_s"]
+            fl = fwd_bwd_flops(B, C, n_x, K)
+            achieved = fl / dur
+            roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
+                        "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
+                        "kernel": "kloop_persist_kernel", "flops_per_launch": fl,
+                        "launch_us": round(dur * 1e6, 3)}
+        else:
+            dur = kt["bwd_step"]["mean_s"]
+            by = bwd_launch_bytes(B, C, n_x)
+            roofline = {"bound": "hbm", "achieved": round(by / dur / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                        "unit": "GB/s", "frac": round(by / dur / HBM_PEAK, 4), "traffic": None,
+                        "kernel": "bwd_step_kernel", "bytes_per_launch": by, "launch_us": round(dur * 1e6, 3)}
+
+    nodes = 3 if path == "persistent" else 2 * K + 2
+    t_roof = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
+    step_roof = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3),
                  "t_roof_ms": round(t_roof * 1e3, 4), "step_over_roof": round(ms_per_step / (t_roof * 1e3), 3),
                  "flops": flops, "bytes_min": bytes_min,
-                 "fwd_launch_us": round(fwd_mean * 1e6, 3), "bwd_launch_us": round(bwd_mean * 1e6, 3),
-                 "fwd_launch_median_us": round(fwd_med * 1e6, 3), "bwd_launch_median_us": round(bwd_med * 1e6, 3)}
+                 "steps_path_ms_per_step": round(ms_steps, 5),
+                 "steps_path_over_roof": round(ms_steps / (((2 * K + 2) * t_node + max(
+                     flops / FP32_PEAK, bytes_min / HBM_PEAK)) * 1e3), 3)}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "train-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "CfC K-loop train step (fwd + BPTT + reduce_axis0), one hipGraph replay",
-                   "B": B, "C": C, "n_x": n_x, "n_in": n_in, "K": K, "seed": 0},
+        "config": {"workload": "CfC K-loop train step (fwd + BPTT + scratch + reduce_axis0), one hipGraph replay",
+                   "B": B, "C": C, "n_x": n_x, "n_in": n_in, "K": K, "seed": 0, "path": path},
         "roofline": roofline,
         "step_roofline": step_roof,
+        "kernels": kernels,
         "trials_ms": [round(v, 5) for v in trials],
     }
 
     if not args.no_reduce:
+        timer = LaunchTimer(torch)
         shapes = [(b, n) for b in REDUCE_B for n in REDUCE_N]
-        red = bench_reduce(torch, cfc, shapes)
+        red = bench_reduce(torch, cfc, timer, shapes)
         gate = [r for r in red if r["B"] * r["N"] * 4 >= 512 * 2 ** 20]
         result["reduce_axis0"] = {"shapes": red,
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}

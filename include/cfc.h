@@ -49,6 +49,7 @@
 #ifndef CFC_H
 #define CFC_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -113,27 +114,76 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
 
 /* One whole training step of the K-loop, replayed as one HIP graph
  * ("K-loop Parallelization", sections Trainer Wiring and Architecture
- * Choice): forward t = 1..K, backward t = K..1 into the per-sample scratch
- * (zeroed at step start: the t = K backward step writes where later steps
- * add), then reduce_axis0 over the batch overwrites gW and gb.
+ * Choice): forward t = 1..K, backward t = K..1, the per-sample scratch
+ * (overwritten: it holds this step's sums only, as if zeroed at step start
+ * and added to by every K-iteration), then reduce_axis0 over the batch
+ * overwrites gW and gb.
  *   u [K, B, n_x], y [K, B, C], h0 [B, C], W [3, C, n_in], bias [3, C]
  *   h_hist [K+1, B, C]   out: h_hist[0] = h0, h_hist[t] = h_t
  *   act    [K, 3, B, C]  out: saved (gate, g, hh) of every step
- *   dh_ws  [2, B, C]     workspace for the BPTT carry
+ *   ws, ws_bytes         workspace of at least
+ *                        cfc_train_kloop_workspace_bytes(B, C, n_x, K) bytes
+ *                        (the pre-activation gradients of every step and the
+ *                        BPTT carry); contents are undefined afterwards
  *   gW_scratch [B, 3, C, n_in], gb_scratch [B, 3, C]   out: per-sample sums
+ *                        S[b,q,c,:] = sum_t dp_q[t,b,c] z_t[b,:] (t = K..1)
  *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
  *                        call's work on `stream` has completed
- * The graph is built on the first call for a given (device, pointers, sizes)
- * and cached; later calls with the same key replay it.  Calls sharing a key
- * must be issued on one stream at a time.  K == 0 writes h_hist[0] = h0 and
- * zeros to the scratch and gradients.
+ * Two paths give the same bits: a persistent kernel (one workgroup per
+ * sample runs every K step with W in registers) when W fits, otherwise 2K
+ * step-kernel launches; cfc_set_kloop_mode() can force either.  The graph is
+ * built on the first call for a given (device, path, pointers, sizes) and
+ * cached; later calls with the same key replay it.  Calls sharing a key must
+ * be issued on one stream at a time.  K == 0 or B == 0 writes h_hist[0] = h0
+ * and zeros to the scratch and gradients.
  */
 int cfc_train_kloop(const float* u, const float* y, const float* h0,
                     const float* W, const float* bias,
-                    float* h_hist, float* act, float* dh_ws,
+                    float* h_hist, float* act, float* ws, size_t ws_bytes,
                     float* gW_scratch, float* gb_scratch,
                     float* gW, float* gb,
                     int B, int C, int n_x, int K, void* stream);
+
+/* The two phases of cfc_train_kloop before its reduction, callable on their
+ * own (same kernels, same bits):
+ * cfc_kloop_fwd_bwd -- forward t = 1..K and backward t = K..1 for every
+ *   sample (the persistent kernel or 2K step launches, per the kloop mode).
+ *   Writes h_hist [K+1,B,C] and act [K,3,B,C] as cfc_train_kloop does, and
+ *   the pre-activation gradients dp_t into the first K*B*3C floats of ws as
+ *   [K, B, 3C] (row r = q C + c), which cfc_scratch_fill consumes.
+ * cfc_scratch_fill -- per-sample scratch from saved dp ("K-loop
+ *   Parallelization", section Architecture Choice, "Per-K-iteration
+ *   accumulation invariant": the sum over the K-iterations of each
+ *   sample's terms, computed once rather than in K read-modify-writes):
+ *     gW_scratch[b,q,c,k] = fma chain over t = K..1 of dp[t,b,q,c] z_t[b,k]
+ *     gb_scratch[b,q,c]   = sum over t = K..1 of dp[t,b,q,c]
+ *   with z_t = [u[t-1,b,:] ; h_hist[t-1,b,:]].  Both outputs are overwritten
+ *   (zeros when K == 0).  dp [K,B,3C], u [K,B,n_x], h_hist [K(+1),B,C].
+ */
+int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0,
+                      const float* W, const float* bias,
+                      float* h_hist, float* act, float* ws, size_t ws_bytes,
+                      int B, int C, int n_x, int K, void* stream);
+
+int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist,
+                     float* gW_scratch, float* gb_scratch,
+                     int B, int C, int n_x, int K, void* stream);
+
+/* Bytes of workspace cfc_train_kloop needs: 4 * (3 K B C + 2 B C).
+ * Returns 0 for invalid sizes. */
+size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K);
+
+/* Path selection of cfc_train_kloop for the whole process.
+ * CFC_KLOOP_AUTO (default): persistent kernel when W fits, else step kernels;
+ * CFC_KLOOP_STEPS: always the 2K step-kernel launches;
+ * CFC_KLOOP_PERSISTENT: the persistent kernel (cfc_train_kloop then returns
+ * CFC_EINVAL for shapes it cannot hold).  Both paths give the same bits. */
+enum cfc_kloop_mode { CFC_KLOOP_AUTO = 0, CFC_KLOOP_STEPS = 1, CFC_KLOOP_PERSISTENT = 2 };
+int cfc_set_kloop_mode(int mode);
+
+/* The path cfc_train_kloop takes for these sizes under the current mode
+ * (CFC_KLOOP_STEPS or CFC_KLOOP_PERSISTENT), or -1 for invalid sizes. */
+int cfc_kloop_path(int B, int C, int n_x, int K);
 
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* cfc_last_error(void);

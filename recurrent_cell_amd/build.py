@@ -10,7 +10,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "cfc_kernels.hip"), os.path.join(HERE, "csrc", "cfc_api.hip")]
-HEADERS = [os.path.join(HERE, "csrc", "cfc_kernels.h"), os.path.join(ROOT, "include", "cfc.h")]
+HEADERS = [os.path.join(HERE, "csrc", "cfc_kernels.h"), os.path.join(HERE, "csrc", "cfc_math.h"),
+           os.path.join(ROOT, "include", "cfc.h")]
 LIB = os.path.join(HERE, "libcfc.so")
 ARCH = "gfx950"
 

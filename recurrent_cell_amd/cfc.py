@@ -17,6 +17,9 @@ LIB_PATH = os.path.join(HERE, "libcfc.so")
 CFC_OK = 0
 CFC_EINVAL = -1
 CFC_EHIP = -2
+KLOOP_AUTO = 0
+KLOOP_STEPS = 1
+KLOOP_PERSISTENT = 2
 
 _LIB = None
 _P = ctypes.c_void_p
@@ -40,12 +43,20 @@ def lib():
         L.cfc_fwd_step.argtypes = [_P] * 6 + [_I, _I, _I, _P]
         L.cfc_bwd_step.argtypes = [_P] * 11 + [_I, _I, _I, _P]
         L.reduce_axis0.argtypes = [_P, _I64, _I64, _P, _P]
-        L.cfc_train_kloop.argtypes = [_P] * 12 + [_I, _I, _I, _I, _P]
+        L.cfc_train_kloop.argtypes = [_P] * 8 + [ctypes.c_size_t] + [_P] * 4 + [_I, _I, _I, _I, _P]
+        L.cfc_kloop_fwd_bwd.argtypes = [_P] * 8 + [ctypes.c_size_t, _I, _I, _I, _I, _P]
+        L.cfc_scratch_fill.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
+        L.cfc_train_kloop_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.cfc_train_kloop_workspace_bytes.restype = ctypes.c_size_t
+        L.cfc_set_kloop_mode.argtypes = [_I]
+        L.cfc_kloop_path.argtypes = [_I, _I, _I, _I]
+        L.cfc_kloop_path.restype = _I
         L.cfc_last_error.argtypes = []
         L.cfc_last_error.restype = ctypes.c_char_p
         L.cfc_clear_graph_cache.argtypes = []
         for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
-                  L.cfc_clear_graph_cache):
+                  L.cfc_kloop_fwd_bwd, L.cfc_scratch_fill, L.cfc_clear_graph_cache,
+                  L.cfc_set_kloop_mode):
             f.restype = _I
         _LIB = L
     return _LIB
@@ -123,13 +134,17 @@ def reduce_axis0(per_batch, out=None):
     return out
 
 
+def cfc_train_kloop_workspace_bytes(B, C, n_x, K):
+    return int(lib().cfc_train_kloop_workspace_bytes(B, C, n_x, K))
+
+
 @dataclass
 class KloopBuffers:
-    """Outputs and workspaces of cfc_train_kloop.  Reuse one instance across
+    """Outputs and workspace of cfc_train_kloop.  Reuse one instance across
     steps: the library caches its graph per set of pointers."""
     h_hist: torch.Tensor      # [K+1, B, C]
     act: torch.Tensor         # [K, 3, B, C]
-    dh_ws: torch.Tensor       # [2, B, C]
+    ws: torch.Tensor          # workspace, cfc_train_kloop_workspace_bytes / 4 floats
     gW_scratch: torch.Tensor  # [B, 3, C, n_in]
     gb_scratch: torch.Tensor  # [B, 3, C]
     gW: torch.Tensor          # [3, C, n_in]
@@ -139,27 +154,67 @@ class KloopBuffers:
     def allocate(B, C, n_x, K, device):
         n_in = n_x + C
         e = lambda *s: torch.empty(s, dtype=torch.float32, device=device)  # noqa: E731
-        return KloopBuffers(h_hist=e(K + 1, B, C), act=e(K, 3, B, C), dh_ws=e(2, B, C),
+        ws_floats = cfc_train_kloop_workspace_bytes(B, C, n_x, K) // 4
+        return KloopBuffers(h_hist=e(K + 1, B, C), act=e(K, 3, B, C), ws=e(max(ws_floats, 1)),
                             gW_scratch=e(B, 3, C, n_in), gb_scratch=e(B, 3, C),
                             gW=e(3, C, n_in), gb=e(3, C))
 
 
 def cfc_train_kloop(u, y, h0, W, bias, out=None):
-    """One training step of the K-loop (forward, BPTT, reduce) as one graph
-    replay.  Returns the KloopBuffers holding h_hist, act, scratch, gW, gb."""
+    """One training step of the K-loop (forward, BPTT, scratch, reduce) as
+    one graph replay.  Returns the KloopBuffers holding h_hist, act, the
+    per-sample scratch, gW and gb."""
     K, B, n_x = u.shape
     C = h0.shape[1]
     n_in = n_x + C
     if out is None:
         out = KloopBuffers.allocate(B, C, n_x, K, h0.device)
+    if out.ws.dim() != 1 or not out.ws.is_contiguous():
+        raise ValueError("ws must be a contiguous 1-D tensor")
     args = (_dev(u, "u", (K, B, n_x)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
             _dev(W, "W", (3, C, n_in)), _dev(bias, "bias", (3, C)),
             _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
-            _dev(out.dh_ws, "dh_ws", (2, B, C)), _dev(out.gW_scratch, "gW_scratch", (B, 3, C, n_in)),
+            _dev(out.ws, "ws"), out.ws.numel() * 4,
+            _dev(out.gW_scratch, "gW_scratch", (B, 3, C, n_in)),
             _dev(out.gb_scratch, "gb_scratch", (B, 3, C)), _dev(out.gW, "gW", (3, C, n_in)),
             _dev(out.gb, "gb", (3, C)))
     _check("cfc_train_kloop", lib().cfc_train_kloop(*args, B, C, n_x, K, _stream(h0)))
     return out
+
+
+def cfc_kloop_fwd_bwd(u, y, h0, W, bias, out):
+    """Forward and backward of the K-loop into out.h_hist, out.act and the
+    dp_t block of out.ws (see include/cfc.h); no scratch, no reduction."""
+    K, B, n_x = u.shape
+    C = h0.shape[1]
+    args = (_dev(u, "u", (K, B, n_x)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
+            _dev(W, "W", (3, C, n_x + C)), _dev(bias, "bias", (3, C)),
+            _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
+            _dev(out.ws, "ws"), out.ws.numel() * 4)
+    _check("cfc_kloop_fwd_bwd", lib().cfc_kloop_fwd_bwd(*args, B, C, n_x, K, _stream(h0)))
+    return out
+
+
+def cfc_scratch_fill(dp, u, h_hist, gW_scratch, gb_scratch):
+    """Per-sample scratch from saved dp [K,B,3C] (overwrites both outputs)."""
+    K, B, n_x = u.shape
+    C = h_hist.shape[2]
+    args = (_dev(dp, "dp", (K, B, 3 * C)), _dev(u, "u", (K, B, n_x)), _dev(h_hist, "h_hist"),
+            _dev(gW_scratch, "gW_scratch", (B, 3, C, n_x + C)), _dev(gb_scratch, "gb_scratch", (B, 3, C)))
+    if h_hist.shape[0] < K or tuple(h_hist.shape[1:]) != (B, C):
+        raise ValueError("h_hist must be [>=K, B, C]")
+    _check("cfc_scratch_fill", lib().cfc_scratch_fill(*args, B, C, n_x, K, _stream(u)))
+    return gW_scratch, gb_scratch
+
+
+def cfc_set_kloop_mode(mode):
+    """KLOOP_AUTO, KLOOP_STEPS or KLOOP_PERSISTENT for the whole process."""
+    _check("cfc_set_kloop_mode", lib().cfc_set_kloop_mode(int(mode)))
+
+
+def cfc_kloop_path(B, C, n_x, K):
+    """KLOOP_PERSISTENT or KLOOP_STEPS: the path cfc_train_kloop takes now."""
+    return int(lib().cfc_kloop_path(B, C, n_x, K))
 
 
 def clear_graph_cache():

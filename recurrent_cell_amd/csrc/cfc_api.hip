@@ -3,6 +3,7 @@
 // K-loop training step.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -13,6 +14,7 @@
 
 #include "../../include/cfc.h"
 #include "cfc_kernels.h"
+#include "cfc_math.h"
 
 namespace {
 
@@ -54,7 +56,7 @@ bool overlap(Span a, Span b)
     return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
-Span span(const float* p, int64_t n) { return Span{p, (size_t)(n > 0 ? n : 0) * sizeof(float)}; }
+Span span(const void* p, int64_t n) { return Span{p, (size_t)(n > 0 ? n : 0) * sizeof(float)}; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -67,10 +69,10 @@ int check_dims(int B, int C, int n_x)
     return CFC_OK;
 }
 
-// Tiling: channel tiles of 16 (one XCD per tile index mod 8); several samples
-// per workgroup once the batch is large enough that W re-reads from L2, not
-// the number of workgroups, limit the step.  None of these choices changes
-// the arithmetic of any output.
+// Tiling of the step kernels: channel tiles of 16 (one XCD per tile index
+// mod 8); several samples per workgroup once the batch is large enough that
+// W re-reads from L2, not the number of workgroups, limit the step.  None of
+// these choices changes the arithmetic of any output.
 cfc::StepPlan make_plan(int B, int C, int n_x, const float* W, const float* scratch)
 {
     cfc::StepPlan p{};
@@ -82,15 +84,14 @@ cfc::StepPlan make_plan(int B, int C, int n_x, const float* W, const float* scra
     auto smem = [&](int bt) {
         const size_t fwd = sizeof(float) * ((size_t)bt * p.ldz + (size_t)bt * 3 * p.CT);
         const size_t bwd = sizeof(float) * ((size_t)bt * p.ldz + (size_t)bt * 3 * C +
-                                            (size_t)cfc::kSlices * bt * cfc::kCols);
+                                            (size_t)cfc::kDzGroups * bt * cfc::kCols);
         return std::make_pair(fwd, bwd);
     };
     while (p.BT > 1 && smem(p.BT).second > 64 * 1024) p.BT /= 2;
     p.fwd_smem = smem(p.BT).first;
     p.bwd_smem = smem(p.BT).second;
     p.n_btiles = B > 0 ? (B + p.BT - 1) / p.BT : 0;
-    // The forward's dot-product order follows Vf, so Vf depends on W alone;
-    // the backward's vector width changes no arithmetic.
+    // Only the load width depends on these; the arithmetic does not.
     p.Vf = (n_in % 4 == 0 && aligned16(W)) ? 4 : 1;
     p.Vb = (n_in % 4 == 0 && scratch != nullptr && aligned16(scratch)) ? 4 : 1;
     return p;
@@ -116,12 +117,12 @@ int enqueue_fwd(const float* u_t, const float* h_prev, const float* W, const flo
 
 int enqueue_bwd(const float* u_t, const float* h_prev, const float* h_t, const float* y_t,
                 const float* W, const float* act_t, const float* dh_in, float* dh_out, float* du_t,
-                float* gW_s, float* gb_s, int B, int C, int n_x, int accumulate,
-                const cfc::StepPlan& p, hipStream_t s)
+                float* gW_s, float* gb_s, float* dp_out, int B, int C, int n_x, const cfc::StepPlan& p,
+                hipStream_t s)
 {
     if (B == 0) return CFC_OK;
-    cfc::BwdArgs a{u_t, h_prev, h_t, y_t, W, act_t, dh_in, dh_out, du_t, gW_s, gb_s,
-                   B, C, n_x, p.CT, p.n_ctiles, p.ldz, accumulate};
+    cfc::BwdArgs a{u_t, h_prev, h_t, y_t, W, act_t, dh_in, dh_out, du_t, gW_s, gb_s, dp_out,
+                   B, C, n_x, p.CT, p.n_ctiles, p.ldz};
     CFC_HIP(cfc::launch_bwd(a, p, s), "backward step launch");
     return CFC_OK;
 }
@@ -147,39 +148,76 @@ int enqueue_reduce(const cfc::ReduceSeg* segs_in, int nseg, int64_t B, hipStream
     return CFC_OK;
 }
 
+int64_t kloop_ws_floats(int B, int C, int K) { return (int64_t)K * B * 3 * C + (int64_t)2 * B * C; }
+
 struct KloopArgs {
     const float *u, *y, *h0, *W, *bias;
-    float *h_hist, *act, *dh_ws, *gW_s, *gb_s, *gW, *gb;
+    float *h_hist, *act, *ws, *gW_s, *gb_s, *gW, *gb;
     int B, C, n_x, K;
 };
 
-// The whole K-loop step as a sequence of launches on one stream: K forward
-// steps (the first also copies h0 into h_hist[0]), K backward steps (the
-// t = K step writes the scratch, later steps add to it: the scratch holds
-// only this step's contributions), then one reduction launch over both
-// scratch tensors.
-int enqueue_kloop(const KloopArgs& k, const cfc::StepPlan& p, hipStream_t s)
+std::atomic<int> g_kloop_mode{CFC_KLOOP_AUTO};
+
+bool use_persistent(int mode, int C, int n_x)
+{
+    if (mode == CFC_KLOOP_STEPS) return false;
+    return cfc::persist_smem(C, n_x) != 0;
+}
+
+// Forward t = 1..K and backward t = K..1 of every sample, storing dp_t.
+//  persistent path: one kernel, one workgroup per sample;
+//  step path:       K forward step launches (the first also copies h0 into
+//                   h_hist[0]) and K backward step launches.
+int enqueue_fwd_bwd(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, hipStream_t s)
 {
     const int64_t BC = (int64_t)k.B * k.C;
     const int64_t BX = (int64_t)k.B * k.n_x;
-    const int n_in = k.n_x + k.C;
-    int rc;
+    float* dp = k.ws;                                   // [K, B, 3C]
+    float* dh_ws = k.ws + (int64_t)k.K * 3 * BC;        // [2, B, C]
+    if (persistent) {
+        const cfc::PersistArgs a{k.u, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
+        CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch");
+        return CFC_OK;
+    }
     for (int t = 1; t <= k.K; ++t) {
         const float* h_prev = (t == 1) ? k.h0 : k.h_hist + (t - 1) * BC;
-        rc = enqueue_fwd(k.u + (t - 1) * BX, h_prev, k.W, k.bias, k.h_hist + t * BC,
-                         k.act + (int64_t)(t - 1) * 3 * BC, t == 1 ? k.h_hist : nullptr, k.B, k.C,
-                         k.n_x, p, s);
+        const int rc = enqueue_fwd(k.u + (t - 1) * BX, h_prev, k.W, k.bias, k.h_hist + t * BC,
+                                   k.act + (int64_t)(t - 1) * 3 * BC, t == 1 ? k.h_hist : nullptr, k.B, k.C,
+                                   k.n_x, p, s);
         if (rc) return rc;
     }
     for (int t = k.K; t >= 1; --t) {
         const int step = k.K - t;  // 0 for t = K
-        const float* dh_in = (t == k.K) ? nullptr : k.dh_ws + ((step - 1) % 2) * BC;
-        float* dh_out = k.dh_ws + (step % 2) * BC;
-        rc = enqueue_bwd(k.u + (t - 1) * BX, k.h_hist + (t - 1) * BC, k.h_hist + t * BC,
-                         k.y + (t - 1) * BC, k.W, k.act + (int64_t)(t - 1) * 3 * BC, dh_in, dh_out,
-                         nullptr, k.gW_s, k.gb_s, k.B, k.C, k.n_x, t == k.K ? 0 : 1, p, s);
+        const float* dh_in = (t == k.K) ? nullptr : dh_ws + ((step - 1) % 2) * BC;
+        float* dh_out = dh_ws + (step % 2) * BC;
+        const int rc = enqueue_bwd(k.u + (t - 1) * BX, k.h_hist + (t - 1) * BC, k.h_hist + t * BC,
+                                   k.y + (t - 1) * BC, k.W, k.act + (int64_t)(t - 1) * 3 * BC, dh_in,
+                                   dh_out, nullptr, nullptr, nullptr, dp + (int64_t)(t - 1) * 3 * BC, k.B,
+                                   k.C, k.n_x, p, s);
         if (rc) return rc;
     }
+    return CFC_OK;
+}
+
+int enqueue_fill(const float* dp, const float* u, const float* h_hist, float* gW_s, float* gb_s, int B, int C,
+                 int n_x, int K, hipStream_t s)
+{
+    const int n_in = n_x + C;
+    const cfc::FillArgs f{dp, u, h_hist, gW_s, gb_s, B, C, n_x, K,
+                          (3 * C + cfc::kFillTile - 1) / cfc::kFillTile,
+                          (n_in + cfc::kFillTile - 1) / cfc::kFillTile};
+    CFC_HIP(cfc::launch_fill(f, s), "scratch fill launch");
+    return CFC_OK;
+}
+
+// The whole K-loop step: forward and backward, the scratch fill (each
+// sample's sums over t, written once) and one reduction launch over both
+// scratch tensors.
+int enqueue_kloop(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, hipStream_t s)
+{
+    const int n_in = k.n_x + k.C;
+    if (int rc = enqueue_fwd_bwd(k, persistent, p, s)) return rc;
+    if (int rc = enqueue_fill(k.ws, k.u, k.h_hist, k.gW_s, k.gb_s, k.B, k.C, k.n_x, k.K, s)) return rc;
     cfc::ReduceSeg segs[2] = {
         {k.gW_s, k.gW, (int64_t)3 * k.C * n_in, 0},
         {k.gb_s, k.gb, (int64_t)3 * k.C, 0},
@@ -188,9 +226,10 @@ int enqueue_kloop(const KloopArgs& k, const cfc::StepPlan& p, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Graph cache of the K-loop step, keyed on device, pointer values and sizes.
+// Graph cache of the K-loop step, keyed on device, path, pointer values and
+// sizes.
 // ---------------------------------------------------------------------------
-using GraphKey = std::tuple<int, const void*, const void*, const void*, const void*, const void*,
+using GraphKey = std::tuple<int, int, const void*, const void*, const void*, const void*, const void*,
                             void*, void*, void*, void*, void*, void*, void*, int, int, int, int>;
 
 struct GraphEntry {
@@ -216,7 +255,7 @@ void destroy_entry(GraphEntry& e)
     e = GraphEntry{};
 }
 
-int build_graph(const KloopArgs& k, const cfc::StepPlan& p, int dev, GraphEntry& out)
+int build_graph(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, int dev, GraphEntry& out)
 {
     hipStream_t cap;
     auto it = g_capture_streams.find(dev);
@@ -227,7 +266,7 @@ int build_graph(const KloopArgs& k, const cfc::StepPlan& p, int dev, GraphEntry&
         cap = it->second;
     }
     CFC_HIP(hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal), "graph capture begin");
-    const int rc = enqueue_kloop(k, p, cap);
+    const int rc = enqueue_kloop(k, persistent, p, cap);
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(cap, &graph);
     if (rc != CFC_OK) {
@@ -304,8 +343,8 @@ int cfc_bwd_step(const float* u_t, const float* h_prev, const float* h_t, const 
             if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "cfc_bwd_step: outputs overlap");
     const cfc::StepPlan p = make_plan(B, C, n_x, W, gW_scratch);
     if (int rc = check_plan(p)) return rc;
-    return enqueue_bwd(u_t, h_prev, h_t, y_t, W, act_t, dh_in, dh_out, du_t, gW_scratch, gb_scratch, B,
-                       C, n_x, 1, p, (hipStream_t)stream);
+    return enqueue_bwd(u_t, h_prev, h_t, y_t, W, act_t, dh_in, dh_out, du_t, gW_scratch, gb_scratch, nullptr,
+                       B, C, n_x, p, (hipStream_t)stream);
 }
 
 int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail, float* out, void* stream)
@@ -321,36 +360,81 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail, float*
     return enqueue_reduce(&seg, 1, n_batch, (hipStream_t)stream);
 }
 
-int cfc_train_kloop(const float* u, const float* y, const float* h0, const float* W, const float* bias,
-                    float* h_hist, float* act, float* dh_ws, float* gW_scratch, float* gb_scratch,
-                    float* gW, float* gb, int B, int C, int n_x, int K, void* stream)
+size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K)
+{
+    if (B < 0 || C < 1 || n_x < 0 || K < 0) return 0;
+    return (size_t)kloop_ws_floats(B, C, K) * sizeof(float);
+}
+
+int cfc_set_kloop_mode(int mode)
 {
     g_last_error.clear();
+    if (mode != CFC_KLOOP_AUTO && mode != CFC_KLOOP_STEPS && mode != CFC_KLOOP_PERSISTENT)
+        return fail(CFC_EINVAL, "cfc_set_kloop_mode: unknown mode %d", mode);
+    g_kloop_mode.store(mode);
+    return CFC_OK;
+}
+
+int cfc_kloop_path(int B, int C, int n_x, int K)
+{
+    if (B < 0 || K < 0 || C < 1 || n_x < 0) return -1;
+    return use_persistent(g_kloop_mode.load(), C, n_x) ? CFC_KLOOP_PERSISTENT : CFC_KLOOP_STEPS;
+}
+
+// Checks shared by cfc_train_kloop and cfc_kloop_fwd_bwd; sets *persistent.
+static int check_kloop(const char* fn, const float* u, const float* y, const float* h0, const float* W,
+                const float* bias, float* h_hist, float* act, float* ws, size_t ws_bytes, float* gW_scratch,
+                float* gb_scratch, float* gW, float* gb, int B, int C, int n_x, int K, bool full,
+                bool* persistent)
+{
     if (int rc = check_dims(B, C, n_x)) return rc;
-    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "K=%d out of range", K);
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "%s: K=%d out of range", fn, K);
     const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    const int64_t ws_floats = kloop_ws_floats(B, C, K);
+    if (ws_bytes < (size_t)ws_floats * sizeof(float))
+        return fail(CFC_EINVAL, "%s: workspace of %zu bytes, %lld needed", fn, ws_bytes,
+                    (long long)(ws_floats * 4));
     // a pointer may be null only when its array is empty
     const struct {
         const void* p;
         int64_t n;
     } need[] = {{u, (int64_t)K * B * n_x}, {y, (int64_t)K * BC}, {h0, BC}, {W, 3 * C * n_in},
-                {bias, 3 * C}, {h_hist, (K + 1) * BC}, {act, (int64_t)K * 3 * BC}, {dh_ws, 2 * BC},
-                {gW_scratch, BC * 3 * n_in}, {gb_scratch, 3 * BC}, {gW, 3 * C * n_in}, {gb, 3 * C}};
+                {bias, 3 * C}, {h_hist, (K + 1) * BC}, {act, (int64_t)K * 3 * BC}, {ws, ws_floats},
+                {gW_scratch, full ? BC * 3 * n_in : 0}, {gb_scratch, full ? 3 * BC : 0},
+                {gW, full ? 3 * C * n_in : 0}, {gb, full ? 3 * C : 0}};
     for (const auto& q : need)
-        if (q.n > 0 && q.p == nullptr) return fail(CFC_EINVAL, "cfc_train_kloop: null pointer");
-    const Span outs[] = {span(h_hist, (K + 1) * BC), span(act, (int64_t)K * 3 * BC), span(dh_ws, 2 * BC),
+        if (q.n > 0 && q.p == nullptr) return fail(CFC_EINVAL, "%s: null pointer", fn);
+    const Span outs[] = {span(h_hist, (K + 1) * BC), span(act, (int64_t)K * 3 * BC), span(ws, ws_floats),
                          span(gW_scratch, BC * 3 * n_in), span(gb_scratch, 3 * BC),
                          span(gW, 3 * C * n_in), span(gb, 3 * C)};
     const Span ins[] = {span(u, (int64_t)K * B * n_x), span(y, (int64_t)K * BC), span(h0, BC),
                         span(W, 3 * C * n_in), span(bias, 3 * C)};
     for (const Span& o : outs)
         for (const Span& i : ins)
-            if (overlap(o, i)) return fail(CFC_EINVAL, "cfc_train_kloop: an output overlaps an input");
+            if (overlap(o, i)) return fail(CFC_EINVAL, "%s: an output overlaps an input", fn);
     for (int i = 0; i < 7; ++i)
         for (int j = i + 1; j < 7; ++j)
-            if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "cfc_train_kloop: outputs overlap");
+            if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "%s: outputs overlap", fn);
+    const int mode = g_kloop_mode.load();
+    *persistent = use_persistent(mode, C, n_x);
+    if (mode == CFC_KLOOP_PERSISTENT && !*persistent)
+        return fail(CFC_EINVAL, "%s: the persistent kernel cannot hold W of C=%d n_x=%d", fn, C, n_x);
+    if (!*persistent)
+        if (int rc = check_plan(make_plan(B, C, n_x, W, gW_scratch))) return rc;
+    return CFC_OK;
+}
+
+int cfc_train_kloop(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                    float* h_hist, float* act, float* ws, size_t ws_bytes, float* gW_scratch,
+                    float* gb_scratch, float* gW, float* gb, int B, int C, int n_x, int K, void* stream)
+{
+    g_last_error.clear();
+    bool persistent = false;
+    if (int rc = check_kloop("cfc_train_kloop", u, y, h0, W, bias, h_hist, act, ws, ws_bytes, gW_scratch,
+                             gb_scratch, gW, gb, B, C, n_x, K, true, &persistent))
+        return rc;
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
     const cfc::StepPlan p = make_plan(B, C, n_x, W, gW_scratch);
-    if (int rc = check_plan(p)) return rc;
     hipStream_t s = (hipStream_t)stream;
 
     if (K == 0 || B == 0) {
@@ -365,9 +449,9 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
 
     int dev = 0;
     CFC_HIP(hipGetDevice(&dev), "hipGetDevice");
-    const KloopArgs k{u, y, h0, W, bias, h_hist, act, dh_ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
-    const GraphKey key{dev, u, y, h0, W, bias, h_hist, act, dh_ws, gW_scratch, gb_scratch, gW, gb,
-                       B, C, n_x, K};
+    const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
+    const GraphKey key{dev, persistent ? 1 : 0, u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch,
+                       gW, gb, B, C, n_x, K};
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_graphs.find(key);
     if (it == g_graphs.end()) {
@@ -379,7 +463,7 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
             g_graphs.erase(victim);
         }
         GraphEntry e;
-        if (int rc = build_graph(k, p, dev, e)) return rc;
+        if (int rc = build_graph(k, persistent, p, dev, e)) return rc;
         it = g_graphs.emplace(key, e).first;
     }
     GraphEntry& e = it->second;
@@ -387,6 +471,55 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
     CFC_HIP(hipGraphLaunch(e.exec, s), "graph launch");
     CFC_HIP(hipEventRecord(e.done, s), "event record");
     return CFC_OK;
+}
+
+int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                      float* h_hist, float* act, float* ws, size_t ws_bytes, int B, int C, int n_x, int K,
+                      void* stream)
+{
+    g_last_error.clear();
+    bool persistent = false;
+    if (int rc = check_kloop("cfc_kloop_fwd_bwd", u, y, h0, W, bias, h_hist, act, ws, ws_bytes, nullptr, nullptr,
+                             nullptr, nullptr, B, C, n_x, K, false, &persistent))
+        return rc;
+    const int64_t BC = (int64_t)B * C;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0 || B == 0) {
+        if (BC > 0) CFC_HIP(hipMemcpyAsync(h_hist, h0, BC * 4, hipMemcpyDeviceToDevice, s), "h0 copy");
+        return CFC_OK;
+    }
+    const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, nullptr, nullptr, nullptr, nullptr, B, C, n_x, K};
+    return enqueue_fwd_bwd(k, persistent, make_plan(B, C, n_x, W, nullptr), s);
+}
+
+int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist, float* gW_scratch, float* gb_scratch,
+                     int B, int C, int n_x, int K, void* stream)
+{
+    g_last_error.clear();
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "cfc_scratch_fill: K=%d out of range", K);
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    const struct {
+        const void* p;
+        int64_t n;
+    } need[] = {{dp, (int64_t)K * 3 * BC}, {u, (int64_t)K * B * n_x}, {h_hist, (int64_t)K * BC},
+                {gW_scratch, BC * 3 * n_in}, {gb_scratch, 3 * BC}};
+    for (const auto& q : need)
+        if (q.n > 0 && q.p == nullptr) return fail(CFC_EINVAL, "cfc_scratch_fill: null pointer");
+    const Span outs[] = {span(gW_scratch, BC * 3 * n_in), span(gb_scratch, 3 * BC)};
+    const Span ins[] = {span(dp, (int64_t)K * 3 * BC), span(u, (int64_t)K * B * n_x), span(h_hist, (int64_t)K * BC)};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return fail(CFC_EINVAL, "cfc_scratch_fill: an output overlaps an input");
+    if (overlap(outs[0], outs[1])) return fail(CFC_EINVAL, "cfc_scratch_fill: outputs overlap");
+    if (B == 0) return CFC_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) {
+        CFC_HIP(cfc::launch_fill_zero(gW_scratch, BC * 3 * n_in, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gb_scratch, 3 * BC, s), "zero fill");
+        return CFC_OK;
+    }
+    return enqueue_fill(dp, u, h_hist, gW_scratch, gb_scratch, B, C, n_x, K, s);
 }
 
 int cfc_clear_graph_cache(void)

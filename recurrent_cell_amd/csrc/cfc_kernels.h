@@ -7,12 +7,15 @@
 
 namespace cfc {
 
-constexpr int kThreads = 256;          // every kernel runs 256-lane workgroups (4 wave64)
-constexpr int kGroup = 16;             // lanes that share one forward dot product
+constexpr int kThreads = 256;          // step, fill and reduce kernels: 4 wave64 per workgroup
+constexpr int kGroup = 16;             // lanes that share one forward dot product (one DPP row)
 constexpr int kGroups = kThreads / kGroup;
-constexpr int kSlices = 16;            // row slices of the backward W^T dp reduction
+constexpr int kSlices = 16;            // backward W^T dp: 16 slices x 4 row groups = 64 groups
 constexpr int kCols = kThreads / kSlices;
 constexpr int kMaxReduceSegs = 2;
+constexpr int kPersistThreads = 1024;  // persistent K-loop kernel: 16 wave64, 64 DPP rows
+constexpr int kFillTile = 64;          // scratch fill: 64 rows x 64 columns per workgroup
+constexpr int kFillSteps = 64;         // time steps staged in LDS per pass
 
 struct FwdArgs {
     const float* u_t;     // [B, n_x]
@@ -35,10 +38,31 @@ struct BwdArgs {
     const float* dh_in;   // nullable: zero carry
     float* dh_out;
     float* du_t;          // nullable
-    float* gW_s;          // [B, 3, C, n_in]
-    float* gb_s;          // [B, 3, C]
+    float* gW_s;          // [B, 3, C, n_in] accumulated (when dp_out is null)
+    float* gb_s;          // [B, 3, C]       accumulated (when dp_out is null)
+    float* dp_out;        // nullable [B, 3C]: store dp instead of updating the scratch
     int B, C, n_x, CT, n_ctiles, ldz;
-    int accumulate;       // 0: write dp*z (the scratch is treated as zero), 1: add
+};
+
+struct FillArgs {
+    const float* dp;      // [K, B, 3C]
+    const float* u;       // [K, B, n_x]
+    const float* h_hist;  // [K+1, B, C]
+    float* gW_s;          // [B, 3C, n_in] overwritten
+    float* gb_s;          // [B, 3C]       overwritten
+    int B, C, n_x, K, n_rt, n_kt;
+};
+
+struct PersistArgs {
+    const float* u;       // [K, B, n_x]
+    const float* y;       // [K, B, C]
+    const float* h0;      // [B, C]
+    const float* W;       // [3, C, n_in]
+    const float* bias;    // [3, C]
+    float* h_hist;        // [K+1, B, C]
+    float* act;           // [K, 3, B, C]
+    float* dp;            // [K, B, 3C]
+    int B, C, n_x, K;
 };
 
 struct ReduceSeg {
@@ -56,8 +80,8 @@ struct ReduceArgs {
     int64_t rows_per_slice;
 };
 
-// Tiling chosen on the host; every choice leaves each output's arithmetic
-// unchanged (see DESIGN notes in cfc_kernels.hip).
+// Tiling of the step kernels, chosen on the host.  No choice here changes
+// the arithmetic of any output (see cfc_math.h).
 struct StepPlan {
     int BT;        // samples per workgroup
     int CT;        // channels per workgroup
@@ -71,8 +95,14 @@ struct StepPlan {
 
 int reduce_slices(int64_t B);
 
+// Persistent K-loop kernel: returns the LDS bytes it needs for these sizes,
+// or 0 if no instantiation holds W of this shape in registers.
+size_t persist_smem(int C, int n_x);
+
 hipError_t launch_fwd(const FwdArgs& a, const StepPlan& p, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, const StepPlan& p, hipStream_t s);
+hipError_t launch_fill(const FillArgs& a, hipStream_t s);
+hipError_t launch_persist(const PersistArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 

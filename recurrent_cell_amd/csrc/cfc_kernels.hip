@@ -1,40 +1,32 @@
-// gfx950 kernels of the CfC K-loop: forward step, backward (BPTT) step with
+// gfx950 kernels of the CfC K-loop: forward and backward (BPTT) step
+// kernels, the persistent per-sample K-loop kernel, the deferred fill of the
 // per-sample gradient scratch, and the batch-axis reduction.
 //
 // Parallel structure ("K-loop Parallelization -- Block-per-Batch Kernel
-// Refactor", section Architecture Choice): samples are independent, so every
-// workgroup owns a tile of (samples x channels) and no workgroup waits for
-// another inside a step.  The pages map one block per sample; on MI355X a
-// sample is split over ceil(C / CT) workgroups by channel tile instead, so
-// that B = 32 samples still give >= 256 workgroups for 256 CUs.  Channel tile
-// j of every sample is dispatched to XCD (j mod 8), because workgroup ids go
-// round-robin over the 8 XCDs and the tile index is the fastest-varying part
-// of the id; each XCD's L2 therefore keeps the same scratch rows and the same
-// W rows from one K-step to the next.
+// Refactor", section Architecture Choice): samples are independent, so no
+// workgroup ever waits for another.
+//  * Step kernels: a workgroup owns (a tile of samples) x (16 channels).  A
+//    sample is split over ceil(C / 16) workgroups so that B = 32 samples
+//    still fill the chip.  Channel tile j is the fastest-varying part of the
+//    workgroup id, so it always runs on XCD (j mod 8) and its W rows and
+//    scratch rows stay in that XCD's L2 from one K-step to the next.
+//  * Persistent kernel: one 1024-lane workgroup per sample runs all K forward
+//    and all K backward steps with the sample's W held in registers (when W
+//    fits: 3C x n_in <= 64 DPP rows x 16 lanes x 72 values).
+// Every (sample, channel) scratch row has exactly one writer.  No atomics.
 //
-// Determinism: no atomics anywhere.  Each output element is produced by one
-// lane with a summation order that depends only on the sizes (C, n_in, and B
-// for the reduction) -- not on the sample tile BT, the channel tile CT, the
-// batch position of a sample or whether du is requested -- so repeated runs
-// and a B = 1 run of any single sample reproduce the batched bits exactly.
+// Determinism: every output follows the canonical order of cfc_math.h, which
+// depends only on the sizes, so repeated runs, the step-kernel graph, the
+// persistent kernel and a B = 1 run of any single sample all produce the
+// same bits.
 #include "cfc_kernels.h"
+#include "cfc_math.h"
 
 namespace cfc {
 
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Butterfly sum over the 16 lanes of a group.  Every lane of the group ends
-// with the same bits: each step adds the same two operands on both partners.
-__device__ __forceinline__ float group_sum16(float v)
-{
-    v += __shfl_xor(v, 8, kGroup);
-    v += __shfl_xor(v, 4, kGroup);
-    v += __shfl_xor(v, 2, kGroup);
-    v += __shfl_xor(v, 1, kGroup);
-    return v;
-}
 
 // z_s = [u_t[b0+s] ; h_prev[b0+s]] for the tile's samples into LDS rows of
 // pitch ldz (zero padded past n_in and for absent samples).
@@ -59,11 +51,9 @@ __device__ __forceinline__ void stage_z(float* zs, int ldz, const float* __restr
 // ---------------------------------------------------------------------------
 // Forward step.  Workgroup = (sample tile of BT, channel tile of CT).
 // Rows of the tile: r = q * nc + cl  (head q, channel c0 + cl), 3 * nc rows.
-// A 16-lane group owns one row at a time: lane j multiplies W[row, k] with
-// z_s[k] for k = V*j + 16*V*i (+0..V-1), then the group butterfly-sums.  The
-// W element is loaded once and used for all BT samples.
-// Sum order of a_q[b, c]: per lane, k ascending within its stride; then the
-// 16-lane butterfly; then + bias.
+// A 16-lane DPP row owns one W row at a time; lane j takes the canonical
+// columns k = 64 i + 4 j + e.  The W element is loaded once for all BT
+// samples.  V = 4 reads W with float4 (only the load width differs).
 // ---------------------------------------------------------------------------
 template <int BT, int V>
 __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a)
@@ -92,74 +82,72 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a)
     const int ln = threadIdx.x % kGroup;
     const int rows = 3 * nc;
     for (int r = grp; r < rows; r += kGroups) {
-        // r is uniform over the 16 lanes of the group; shuffles stay inside it.
+        // r is uniform over the 16 lanes of the DPP row.
         const int q = r / nc;
         const int cl = r - q * nc;
         const float* __restrict__ wrow = a.W + ((int64_t)q * a.C + c0 + cl) * n_in;
         float acc[BT];
 #pragma unroll
         for (int s = 0; s < BT; ++s) acc[s] = 0.0f;
-        if constexpr (V == 4) {
-            for (int k = ln * 4; k < n_in; k += kGroup * 4) {
-                const float4 w = *reinterpret_cast<const float4*>(wrow + k);
+        for (int k0 = 4 * ln; k0 < n_in; k0 += 4 * kGroup) {
+            if constexpr (V == 4) {
+                const float4 w = *reinterpret_cast<const float4*>(wrow + k0);
 #pragma unroll
                 for (int s = 0; s < BT; ++s) {
-                    const float4 z = *reinterpret_cast<const float4*>(zs + s * a.ldz + k);
+                    const float4 z = *reinterpret_cast<const float4*>(zs + s * a.ldz + k0);
                     acc[s] = fmaf(w.x, z.x, acc[s]);
                     acc[s] = fmaf(w.y, z.y, acc[s]);
                     acc[s] = fmaf(w.z, z.z, acc[s]);
                     acc[s] = fmaf(w.w, z.w, acc[s]);
                 }
-            }
-        } else {
-            for (int k = ln; k < n_in; k += kGroup) {
-                const float w = wrow[k];
+            } else {
 #pragma unroll
-                for (int s = 0; s < BT; ++s) acc[s] = fmaf(w, zs[s * a.ldz + k], acc[s]);
+                for (int e = 0; e < 4; ++e) {
+                    if (k0 + e < n_in) {
+                        const float w = wrow[k0 + e];
+#pragma unroll
+                        for (int s = 0; s < BT; ++s) acc[s] = fmaf(w, zs[s * a.ldz + k0 + e], acc[s]);
+                    }
+                }
             }
         }
         const float bq = a.bias[q * a.C + c0 + cl];
 #pragma unroll
         for (int s = 0; s < BT; ++s) {
-            const float v = group_sum16(acc[s]);
+            const float v = row_sum16(acc[s]);
             if (ln == 0) as[(s * 3 + q) * a.CT + cl] = v + bq;
         }
     }
     __syncthreads();
 
+    const int64_t BC = (int64_t)a.B * a.C;
     for (int i = threadIdx.x; i < nb * nc; i += kThreads) {
         const int s = i / nc;
         const int cl = i - s * nc;
-        const int64_t b = (int64_t)b0 + s;
-        const int c = c0 + cl;
-        const float af = as[(s * 3 + 0) * a.CT + cl];
-        const float ag = as[(s * 3 + 1) * a.CT + cl];
-        const float ah = as[(s * 3 + 2) * a.CT + cl];
-        const float gate = 1.0f / (1.0f + expf(af));   // sigmoid(-a_f), dt = 1
-        const float g = tanhf(ag);
-        const float hh = tanhf(ah);
-        const float h = fmaf(gate, g, (1.0f - gate) * hh);
-        a.h_t[b * a.C + c] = h;
-        a.act_t[(0 * (int64_t)a.B + b) * a.C + c] = gate;
-        a.act_t[(1 * (int64_t)a.B + b) * a.C + c] = g;
-        a.act_t[(2 * (int64_t)a.B + b) * a.C + c] = hh;
+        const int64_t bc = ((int64_t)b0 + s) * a.C + c0 + cl;
+        const CellOut o = cell_forward(as[(s * 3 + 0) * a.CT + cl], as[(s * 3 + 1) * a.CT + cl],
+                                       as[(s * 3 + 2) * a.CT + cl]);
+        a.h_t[bc] = o.h;
+        a.act_t[bc] = o.gate;
+        a.act_t[BC + bc] = o.g;
+        a.act_t[2 * BC + bc] = o.hh;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Backward step.  Workgroup = (sample tile, channel tile j).
-//  1. dp_q[s, c] for ALL C channels of its samples into LDS (cheap: 6 loads
-//     per channel), because the carry needs every channel.
-//  2. Scratch rows of its own channel tile: gW_s[b, q, c0:c0+nc, :] is one
-//     contiguous block of nc * n_in floats per (b, q); it is streamed with
-//     coalesced V-wide read-modify-writes.  This workgroup is the only writer
-//     of those rows.
-//  3. dz[k] = sum_{q,c} W[q, c, k] dp_q[c] for its slice of columns k:
-//     16 row slices x 16 columns; slice j sums rows r = j, j+16, ... in
-//     ascending order, then slices are added in ascending order.
-//     Columns [n_x, n_in) give the carry dh_out; [0, n_x) give du_t when it
-//     is requested.  Columns are split evenly over the n_ctiles workgroups
-//     of the sample.
+//  1. dp_q[s, c] for ALL C channels of its samples into LDS (the carry needs
+//     every channel; 6 loads per channel, served from L2).
+//  2. Either (dp_out != null, K-loop) store the dp of its own channel tile,
+//     or (ABI step) update its own scratch rows: gW_s[b, q, c0:c0+nc, :] is
+//     one contiguous block of nc * n_in floats per (b, q), streamed with
+//     V-wide read-modify-writes; this workgroup is their only writer.
+//  3. dz = W^T dp for its share of the columns, in the canonical order:
+//     16 slices x 16 columns; slice s forms the channel-group partials P_g of
+//     groups g = 4 s .. 4 s + 3 into LDS; then one lane per column takes
+//     tree_sum64.
+//     Columns [n_x, n_in) give the carry dh_out; [0, n_x) give du_t when
+//     requested.  Columns are split evenly over the sample's workgroups.
 // ---------------------------------------------------------------------------
 template <int BT, int V>
 __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
@@ -173,26 +161,21 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
     const int c0 = ctile * a.CT;
     const int nb = min(BT, a.B - b0);
     const int nc = min(a.CT, a.C - c0);
+    const int64_t BC = (int64_t)a.B * a.C;
     float* zs = smem;                    // [BT][ldz]
     float* dps = zs + BT * a.ldz;        // [BT][3C]
-    float* red = dps + BT * C3;          // [kSlices][BT][kCols]
+    float* red = dps + BT * C3;          // [kDzGroups][BT][kCols]
 
-    stage_z<BT>(zs, a.ldz, a.u_t, a.h_prev, b0, nb, a.C, a.n_x);
+    if (a.dp_out == nullptr) stage_z<BT>(zs, a.ldz, a.u_t, a.h_prev, b0, nb, a.C, a.n_x);
     for (int i = threadIdx.x; i < BT * a.C; i += kThreads) {
         const int s = i / a.C;
         const int c = i - s * a.C;
         float df = 0.0f, dg = 0.0f, dhh = 0.0f;
         if (s < nb) {
-            const int64_t b = (int64_t)b0 + s;
-            const int64_t bc = b * a.C + c;
-            const float gate = a.act_t[(0 * (int64_t)a.B + b) * a.C + c];
-            const float g = a.act_t[(1 * (int64_t)a.B + b) * a.C + c];
-            const float hh = a.act_t[(2 * (int64_t)a.B + b) * a.C + c];
+            const int64_t bc = ((int64_t)b0 + s) * a.C + c;
             float dh = a.h_t[bc] - a.y_t[bc];
             if (a.dh_in != nullptr) dh += a.dh_in[bc];
-            df = dh * (g - hh) * (-gate * (1.0f - gate));
-            dg = dh * gate * (1.0f - g * g);
-            dhh = dh * (1.0f - gate) * (1.0f - hh * hh);
+            cell_backward(dh, a.act_t[bc], a.act_t[BC + bc], a.act_t[2 * BC + bc], df, dg, dhh);
         }
         dps[s * C3 + c] = df;
         dps[s * C3 + a.C + c] = dg;
@@ -200,49 +183,55 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
     }
     __syncthreads();
 
-    // 2. sole-writer scratch update of this workgroup's channel tile
-    const int blk = nc * n_in;
-    for (int s = 0; s < nb; ++s) {
-        const int64_t b = (int64_t)b0 + s;
-        const float* zb = zs + s * a.ldz;
-        for (int q = 0; q < 3; ++q) {
-            float* __restrict__ dst = a.gW_s + ((b * 3 + q) * a.C + c0) * (int64_t)n_in;
-            const float* dq = dps + s * C3 + q * a.C + c0;
-            if constexpr (V == 4) {
-                for (int e = threadIdx.x * 4; e < blk; e += kThreads * 4) {
-                    const int cl = e / n_in;
-                    const int k = e - cl * n_in;
-                    const float d = dq[cl];
-                    const float4 z = *reinterpret_cast<const float4*>(zb + k);
-                    float4 o = a.accumulate ? *reinterpret_cast<const float4*>(dst + e)
-                                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    o.x = fmaf(d, z.x, o.x);
-                    o.y = fmaf(d, z.y, o.y);
-                    o.z = fmaf(d, z.z, o.z);
-                    o.w = fmaf(d, z.w, o.w);
-                    *reinterpret_cast<float4*>(dst + e) = o;
-                }
-            } else {
-                for (int e = threadIdx.x; e < blk; e += kThreads) {
-                    const int cl = e / n_in;
-                    const int k = e - cl * n_in;
-                    const float o = a.accumulate ? dst[e] : 0.0f;
-                    dst[e] = fmaf(dq[cl], zb[k], o);
+    if (a.dp_out != nullptr) {
+        for (int i = threadIdx.x; i < nb * 3 * nc; i += kThreads) {
+            const int s = i / (3 * nc);
+            const int rem = i - s * 3 * nc;
+            const int q = rem / nc;
+            const int r = q * a.C + c0 + (rem - q * nc);
+            a.dp_out[((int64_t)b0 + s) * C3 + r] = dps[s * C3 + r];
+        }
+    } else {
+        const int blk = nc * n_in;
+        for (int s = 0; s < nb; ++s) {
+            const int64_t b = (int64_t)b0 + s;
+            const float* zb = zs + s * a.ldz;
+            for (int q = 0; q < 3; ++q) {
+                float* __restrict__ dst = a.gW_s + ((b * 3 + q) * a.C + c0) * (int64_t)n_in;
+                const float* dq = dps + s * C3 + q * a.C + c0;
+                if constexpr (V == 4) {
+                    for (int e = threadIdx.x * 4; e < blk; e += kThreads * 4) {
+                        const int cl = e / n_in;
+                        const int k = e - cl * n_in;
+                        const float d = dq[cl];
+                        const float4 z = *reinterpret_cast<const float4*>(zb + k);
+                        float4 o = *reinterpret_cast<const float4*>(dst + e);
+                        o.x = fmaf(d, z.x, o.x);
+                        o.y = fmaf(d, z.y, o.y);
+                        o.z = fmaf(d, z.z, o.z);
+                        o.w = fmaf(d, z.w, o.w);
+                        *reinterpret_cast<float4*>(dst + e) = o;
+                    }
+                } else {
+                    for (int e = threadIdx.x; e < blk; e += kThreads) {
+                        const int cl = e / n_in;
+                        const int k = e - cl * n_in;
+                        dst[e] = fmaf(dq[cl], zb[k], dst[e]);
+                    }
                 }
             }
         }
-    }
-    for (int i = threadIdx.x; i < nb * 3 * nc; i += kThreads) {
-        const int s = i / (3 * nc);
-        const int rem = i - s * 3 * nc;
-        const int q = rem / nc;
-        const int cl = rem - q * nc;
-        const int64_t idx = (((int64_t)b0 + s) * 3 + q) * a.C + c0 + cl;
-        const float o = a.accumulate ? a.gb_s[idx] : 0.0f;
-        a.gb_s[idx] = o + dps[s * C3 + q * a.C + c0 + cl];
+        for (int i = threadIdx.x; i < nb * 3 * nc; i += kThreads) {
+            const int s = i / (3 * nc);
+            const int rem = i - s * 3 * nc;
+            const int q = rem / nc;
+            const int r = q * a.C + c0 + (rem - q * nc);
+            const int64_t idx = ((int64_t)b0 + s) * C3 + r;
+            a.gb_s[idx] = a.gb_s[idx] + dps[s * C3 + r];
+        }
     }
 
-    // 3. dz = W^T dp over this workgroup's columns
+    const int cpg = dz_group_channels(a.C);
     const int klo = (a.du_t != nullptr) ? 0 : a.n_x;
     const int span = n_in - klo;
     const int kw = (span + a.n_ctiles - 1) / a.n_ctiles;
@@ -252,26 +241,34 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
     const int col = threadIdx.x % kCols;
     for (int kb = kbeg; kb < kend; kb += kCols) {   // trip count uniform over the workgroup
         const int k = kb + col;
-        float acc[BT];
 #pragma unroll
-        for (int s = 0; s < BT; ++s) acc[s] = 0.0f;
-        if (k < kend) {
-            for (int r = slice; r < C3; r += kSlices) {
-                const float w = a.W[(int64_t)r * n_in + k];
+        for (int gg = 0; gg < kDzGroups / kSlices; ++gg) {
+            const int g = slice * (kDzGroups / kSlices) + gg;
+            float P[BT];
 #pragma unroll
-                for (int s = 0; s < BT; ++s) acc[s] = fmaf(w, dps[s * C3 + r], acc[s]);
+            for (int s = 0; s < BT; ++s) P[s] = 0.0f;
+            if (k < kend) {
+                const int c_end = min((g + 1) * cpg, a.C);
+                for (int c = g * cpg; c < c_end; ++c) {
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) {
+                        const int r = q * a.C + c;
+                        const float w = a.W[(int64_t)r * n_in + k];
+#pragma unroll
+                        for (int s = 0; s < BT; ++s) P[s] = fmaf(w, dps[s * C3 + r], P[s]);
+                    }
+                }
             }
-        }
 #pragma unroll
-        for (int s = 0; s < BT; ++s) red[(slice * BT + s) * kCols + col] = acc[s];
+            for (int s = 0; s < BT; ++s) red[(g * BT + s) * kCols + col] = P[s];
+        }
         __syncthreads();
         if (threadIdx.x < BT * kCols) {
             const int s = threadIdx.x / kCols;
             const int cc = threadIdx.x - s * kCols;
             const int k2 = kb + cc;
             if (s < nb && k2 < kend) {
-                float v = red[(0 * BT + s) * kCols + cc];
-                for (int j = 1; j < kSlices; ++j) v += red[(j * BT + s) * kCols + cc];
+                const float v = tree_sum64(red + s * kCols + cc, BT * kCols);
                 const int64_t b = (int64_t)b0 + s;
                 if (k2 >= a.n_x)
                     a.dh_out[b * a.C + (k2 - a.n_x)] = v;
@@ -280,6 +277,352 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
             }
         }
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Deferred scratch fill (K-loop): S[b, r, k] = fma chain over t = K .. 1 of
+// dp_t[b, r] * z_t[b, k] from +0 -- the same bits as K per-step "+=" updates
+// of a zeroed scratch -- and Sb[b, r] = add chain of dp_t[b, r].  Each
+// workgroup writes one 64 x 64 tile of one sample's scratch once; it stages
+// up to kFillSteps time steps of dp (64 rows) and z (64 columns) per pass,
+// with 16-byte loads where the layout allows, then each lane runs the chains
+// of a 4 x 4 block of the tile.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float dps[kFillSteps][kFillTile];
+    __shared__ __attribute__((aligned(16))) float zs[kFillSteps][kFillTile];
+    const int n_in = a.n_x + a.C;
+    const int R3 = 3 * a.C;
+    const int tiles = a.n_rt * a.n_kt;
+    const int b = blockIdx.x / tiles;
+    const int rem = blockIdx.x - b * tiles;
+    const int rt = rem / a.n_kt;
+    const int kt = rem - rt * a.n_kt;
+    const int r0 = rt * kFillTile;
+    const int k0 = kt * kFillTile;
+    const int tx = threadIdx.x % 16;
+    const int ty = threadIdx.x / 16;
+    const bool do_bias = (kt == 0) && (threadIdx.x < kFillTile);
+    // 16-byte staging needs every 4-float segment to lie inside one row of one tensor
+    const bool vec = (R3 % 4 == 0) && (a.n_x % 4 == 0) && (a.C % 4 == 0) &&
+                     ((((uintptr_t)a.dp) | ((uintptr_t)a.u) | ((uintptr_t)a.h_hist)) & 15u) == 0;
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    float sb = 0.0f;
+
+    for (int t0 = a.K; t0 >= 1; t0 -= kFillSteps) {
+        const int nt = min(kFillSteps, t0);   // steps t0, t0 - 1, .., t0 - nt + 1
+        if (vec) {
+            // 16 segments of 4 floats per staged row, dp and z rows interleaved
+            for (int i = threadIdx.x; i < kFillSteps * 32; i += kThreads) {
+                const int tt = i / 32;
+                const int sgi = i - tt * 32;
+                const bool is_z = sgi >= 16;
+                const int x = 4 * (sgi & 15);
+                f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (tt < nt) {
+                    const int64_t tb = (int64_t)(t0 - tt - 1) * a.B + b;
+                    if (!is_z) {
+                        const int r = r0 + x;
+                        if (r < R3) v = *reinterpret_cast<const f32x4*>(a.dp + tb * R3 + r);
+                    } else {
+                        const int k = k0 + x;
+                        if (k < n_in)
+                            v = (k < a.n_x) ? *reinterpret_cast<const f32x4*>(a.u + tb * a.n_x + k)
+                                            : *reinterpret_cast<const f32x4*>(a.h_hist + tb * a.C + (k - a.n_x));
+                    }
+                }
+                *reinterpret_cast<f32x4*>(is_z ? &zs[tt][x] : &dps[tt][x]) = v;
+            }
+        } else {
+            for (int i = threadIdx.x; i < kFillSteps * kFillTile; i += kThreads) {
+                const int tt = i / kFillTile;
+                const int x = i - tt * kFillTile;
+                float dv = 0.0f, zv = 0.0f;
+                if (tt < nt) {
+                    const int64_t tb = (int64_t)(t0 - tt - 1) * a.B + b;
+                    const int r = r0 + x;
+                    if (r < R3) dv = a.dp[tb * R3 + r];
+                    const int k = k0 + x;
+                    if (k < n_in)
+                        zv = (k < a.n_x) ? a.u[tb * a.n_x + k] : a.h_hist[tb * a.C + (k - a.n_x)];
+                }
+                dps[tt][x] = dv;
+                zs[tt][x] = zv;
+            }
+        }
+        __syncthreads();
+        for (int tt = 0; tt < nt; ++tt) {
+            const f32x4 d = *reinterpret_cast<const f32x4*>(&dps[tt][ty * 4]);
+            const f32x4 z = *reinterpret_cast<const f32x4*>(&zs[tt][tx * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(d[i], z[j], acc[i][j]);
+        }
+        if (do_bias)
+            for (int tt = 0; tt < nt; ++tt) sb = sb + dps[tt][threadIdx.x];
+        __syncthreads();
+    }
+
+    const bool vec_out = (n_in % 4 == 0) && ((((uintptr_t)a.gW_s) & 15u) == 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + ty * 4 + i;
+        if (r < R3) {
+            float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in;
+            const int k = k0 + tx * 4;
+            if (vec_out && k + 4 <= n_in) {
+                f32x4 o;
+                o.x = acc[i][0];
+                o.y = acc[i][1];
+                o.z = acc[i][2];
+                o.w = acc[i][3];
+                *reinterpret_cast<f32x4*>(dst + k) = o;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (k + j < n_in) dst[k + j] = acc[i][j];
+            }
+        }
+    }
+    if (do_bias && r0 + (int)threadIdx.x < R3) a.gb_s[(int64_t)b * R3 + r0 + threadIdx.x] = sb;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent K-loop kernel: workgroup b runs sample b's whole step.
+// DPP row g (16 lanes, g < 64) owns the cpg channels of canonical dz group g,
+// all three heads: W rows (q, c) for c in [g cpg, g cpg + cpg), held in
+// registers as lane j's canonical forward columns 64 i + 4 j + e.
+// The step loops issue no global loads: every kPersistChunk steps the whole
+// workgroup stages the next chunk's per-step inputs (u for the forward;
+// gate, g, hh, h_t, y_t for the backward) into LDS with one coalesced pass and
+// one full barrier; inside a chunk a step is LDS traffic, DPP, arithmetic,
+// stores that nothing waits for, and one LDS-only barrier.
+//  forward, per t : the 3 cpg dot products of the row (row_sum16 leaves every
+//                   lane with every sum); lane j < cpg applies the cell to
+//                   channel g cpg + j at once, writes h_t into the next z
+//                   buffer and stores h_t and (gate, g, hh).
+//  backward, per t: every lane forms dp of the row's channels from the carry
+//                   (shuffled in from the lanes that summed it) and the staged
+//                   operands; lane 4 cc stores dp of channel cc; the group
+//                   partials P_g of the carry columns go to a double-buffered
+//                   LDS block; after the barrier, lanes 4 cc .. 4 cc + 3 sum
+//                   column n_x + g cpg + cc over the 64 groups (tree_sum16
+//                   each, then quad_sum4).
+// ---------------------------------------------------------------------------
+constexpr int kPersistChunk = 16;
+
+template <int CPG, int NI>
+__global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistArgs a)
+{
+    constexpr int ZW = NI * 64;
+    constexpr int CMAX = 64 * CPG;
+    constexpr int STAGE = (5 * CMAX > ZW ? 5 * CMAX : ZW) * kPersistChunk;
+    __shared__ __attribute__((aligned(16))) float zs[2][ZW];
+    __shared__ __attribute__((aligned(16))) float part[2][kDzGroups][ZW];
+    __shared__ __attribute__((aligned(16))) float stage[STAGE];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int g = tid >> 4;
+    const int j = tid & 15;
+    const int C = a.C;
+    const int n_x = a.n_x;
+    const int n_in = n_x + C;
+    const int B = a.B;
+    const int K = a.K;
+    const int R3 = 3 * C;
+    const int c0 = g * CPG;
+    const int ncg = max(0, min(CPG, C - c0));   // channels of this row group
+    const int64_t BC = (int64_t)B * C;
+    const int i0 = n_x / 64;                     // first column block holding carry columns
+    const bool wvec = (n_in % 4 == 0) && ((((uintptr_t)a.W) & 15u) == 0);
+
+    float w[CPG][3][NI][4];
+    float bq[CPG][3];
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const bool ok = cc < ncg;
+            const int r = q * C + c0 + cc;
+            bq[cc][q] = ok ? a.bias[r] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int k = 64 * i + 4 * j;
+                if (ok && wvec && k < n_in) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(a.W + (int64_t)r * n_in + k);
+                    w[cc][q][i][0] = v.x;
+                    w[cc][q][i][1] = v.y;
+                    w[cc][q][i][2] = v.z;
+                    w[cc][q][i][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[cc][q][i][e] = (ok && k + e < n_in) ? a.W[(int64_t)r * n_in + k + e] : 0.0f;
+                }
+            }
+        }
+    for (int i = tid; i < 2 * ZW; i += kPersistThreads) (&zs[0][0])[i] = 0.0f;
+    __syncthreads();
+    if (tid < C) {
+        const float h = a.h0[(int64_t)b * C + tid];
+        zs[0][n_x + tid] = h;
+        a.h_hist[(int64_t)b * C + tid] = h;
+    }
+
+    // ---------------- forward ----------------
+    for (int t0 = 1; t0 <= K; t0 += kPersistChunk) {
+        const int nt = min(kPersistChunk, K - t0 + 1);
+        // stage u_{t0} .. u_{t0+nt-1}; u_{t0} also goes straight into its z buffer
+        __syncthreads();
+        for (int i = tid; i < nt * n_x; i += kPersistThreads) {
+            const int tt = i / n_x;
+            const int k = i - tt * n_x;
+            const float v = a.u[((int64_t)(t0 - 1 + tt) * B + b) * n_x + k];
+            stage[i] = v;
+            if (tt == 0) zs[(t0 - 1) & 1][k] = v;
+        }
+        __syncthreads();
+        for (int tt = 0; tt < nt; ++tt) {
+            const int t = t0 + tt;
+            const float* zc = zs[(t - 1) & 1];
+            float* zn = zs[t & 1];
+            f32x4 zv[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) zv[i] = *reinterpret_cast<const f32x4*>(zc + 64 * i + 4 * j);
+            float av[CPG][3];
+#pragma unroll
+            for (int cc = 0; cc < CPG; ++cc)
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    float p = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) p = fmaf(w[cc][q][i][e], zv[i][e], p);
+                    av[cc][q] = row_sum16(p) + bq[cc][q];
+                }
+            if (j < ncg) {
+                float af = av[0][0], ag = av[0][1], ah = av[0][2];
+#pragma unroll
+                for (int cc = 1; cc < CPG; ++cc)
+                    if (j == cc) {
+                        af = av[cc][0];
+                        ag = av[cc][1];
+                        ah = av[cc][2];
+                    }
+                const CellOut o = cell_forward(af, ag, ah);
+                const int c = c0 + j;
+                const int64_t bc = (int64_t)b * C + c;
+                zn[n_x + c] = o.h;
+                a.h_hist[(int64_t)t * BC + bc] = o.h;
+                float* act_t = a.act + (int64_t)(t - 1) * 3 * BC;
+                act_t[bc] = o.gate;
+                act_t[BC + bc] = o.g;
+                act_t[2 * BC + bc] = o.hh;
+            }
+            if (tid < n_x && tt + 1 < nt) zn[tid] = stage[(tt + 1) * n_x + tid];
+            lds_barrier();
+        }
+    }
+
+    // ---------------- backward ----------------
+    static_assert(CPG <= 2, "the row broadcast of dp covers at most two channels per row");
+    float carry_mine = 0.0f;   // lanes 4 cc .. 4 cc + 3: carry of channel c0 + cc
+    for (int t1 = K; t1 >= 1; t1 -= kPersistChunk) {
+        const int nt = min(kPersistChunk, t1);   // steps t1, t1 - 1, .., t1 - nt + 1
+        // stage (gate, g, hh, h_t, y_t) of every channel for the chunk's steps;
+        // the full barrier also makes the forward's stores visible.
+        __syncthreads();
+        for (int i = tid; i < nt * 5 * C; i += kPersistThreads) {
+            const int tt = i / (5 * C);
+            const int rem = i - tt * 5 * C;
+            const int v = rem / C;
+            const int c = rem - v * C;
+            const int t = t1 - tt;
+            const int64_t bc = (int64_t)b * C + c;
+            float x;
+            if (v < 3)
+                x = a.act[(int64_t)(t - 1) * 3 * BC + v * BC + bc];
+            else if (v == 3)
+                x = a.h_hist[(int64_t)t * BC + bc];
+            else
+                x = a.y[(int64_t)(t - 1) * BC + bc];
+            stage[i] = x;
+        }
+        __syncthreads();
+        for (int tt = 0; tt < nt; ++tt) {
+            const int t = t1 - tt;
+            const int buf = t & 1;
+            const float* st = stage + tt * 5 * C;
+            // quad cc computes dp of channel c0 + cc once (it holds that
+            // channel's carry); the row then reads it from lane 4 cc.
+            const int my_cc = min(j >> 2, CPG - 1);
+            const int my_c = min(c0 + my_cc, C - 1);
+            float mdp[3];
+            {
+                float dh = st[3 * C + my_c] - st[4 * C + my_c];
+                if (t < K) dh += carry_mine;
+                cell_backward(dh, st[my_c], st[C + my_c], st[2 * C + my_c], mdp[0], mdp[1], mdp[2]);
+            }
+            float dp[CPG][3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                dp[0][q] = row_bcast<0>(mdp[q]);
+                if (CPG > 1) dp[CPG - 1][q] = row_bcast<4 * (CPG - 1)>(mdp[q]);
+            }
+#pragma unroll
+            for (int cc = 0; cc < CPG; ++cc)
+                if (cc >= ncg) dp[cc][0] = dp[cc][1] = dp[cc][2] = 0.0f;
+            if ((j & 3) == 0 && (j >> 2) < ncg) {
+                float* dpt = a.dp + ((int64_t)(t - 1) * B + b) * R3;
+                const int c = c0 + (j >> 2);
+                dpt[c] = mdp[0];
+                dpt[C + c] = mdp[1];
+                dpt[2 * C + c] = mdp[2];
+            }
+            float P[NI][4];
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P[i][e] = 0.0f;
+#pragma unroll
+            for (int cc = 0; cc < CPG; ++cc) {
+                if (cc < ncg) {
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+#pragma unroll
+                        for (int i = 0; i < NI; ++i)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) P[i][e] = fmaf(w[cc][q][i][e], dp[cc][q], P[i][e]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                if (i >= i0) {
+                    f32x4 v;
+                    v.x = P[i][0];
+                    v.y = P[i][1];
+                    v.z = P[i][2];
+                    v.w = P[i][3];
+                    *reinterpret_cast<f32x4*>(&part[buf][g][64 * i + 4 * j]) = v;
+                }
+            }
+            lds_barrier();
+            if ((j >> 2) < CPG) {   // uniform over each quad
+                const int cc = j >> 2;
+                const int col = n_x + min(c0 + cc, C - 1);
+                const float v = tree_sum16(&part[buf][16 * (j & 3)][col], ZW);
+                carry_mine = quad_sum4(v);
+            }
+        }
     }
 }
 
@@ -397,6 +740,31 @@ hipError_t launch_bwd_bt(const BwdArgs& a, const StepPlan& p, hipStream_t s)
     return hipGetLastError();
 }
 
+// Persistent-kernel instantiations: CPG channels per DPP row (C <= 64 CPG),
+// NI column blocks of 64 (n_in <= 64 NI); 12 CPG NI W values per lane.
+struct PersistShape {
+    int cpg, ni;
+};
+
+bool persist_shape(int C, int n_x, PersistShape& ps)
+{
+    const int n_in = n_x + C;
+    const int cpg = dz_group_channels(C);
+    const int ni = (n_in + 63) / 64;
+    if ((cpg == 1 && ni <= 4) || (cpg == 2 && ni >= 2 && ni <= 3)) {
+        ps = PersistShape{cpg, ni};
+        return true;
+    }
+    return false;
+}
+
+template <int CPG, int NI>
+hipError_t launch_persist_t(const PersistArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL((kloop_persist_kernel<CPG, NI>), dim3((unsigned)a.B), dim3(kPersistThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Row slices of the reduction: a power of two in [1, 16] with about 8 rows
@@ -406,6 +774,15 @@ int reduce_slices(int64_t B)
     int R = 1;
     while (R < 16 && (int64_t)R * 2 * 8 <= B) R *= 2;
     return R;
+}
+
+size_t persist_smem(int C, int n_x)
+{
+    PersistShape ps;
+    if (!persist_shape(C, n_x, ps)) return 0;
+    const size_t zw = 64 * (size_t)ps.ni;
+    const size_t stage = (5 * 64 * (size_t)ps.cpg > zw ? 5 * 64 * (size_t)ps.cpg : zw) * kPersistChunk;
+    return sizeof(float) * (2 * zw + 2 * (size_t)kDzGroups * zw + stage);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, const StepPlan& p, hipStream_t s)
@@ -430,6 +807,31 @@ hipError_t launch_bwd(const BwdArgs& a, const StepPlan& p, hipStream_t s)
     }
 }
 
+hipError_t launch_fill(const FillArgs& a, hipStream_t s)
+{
+    const int64_t blocks = (int64_t)a.B * a.n_rt * a.n_kt;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scratch_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_persist(const PersistArgs& a, hipStream_t s)
+{
+    PersistShape ps;
+    if (!persist_shape(a.C, a.n_x, ps) || a.B <= 0) return hipErrorInvalidValue;
+#define CFC_PERSIST_CASE(P_, N_) \
+    if (ps.cpg == P_ && ps.ni == N_) return launch_persist_t<P_, N_>(a, s);
+    CFC_PERSIST_CASE(1, 1)
+    CFC_PERSIST_CASE(1, 2)
+    CFC_PERSIST_CASE(1, 3)
+    CFC_PERSIST_CASE(1, 4)
+    CFC_PERSIST_CASE(2, 2)
+    CFC_PERSIST_CASE(2, 3)
+#undef CFC_PERSIST_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s)
 {
     ReduceArgs a{};
@@ -446,7 +848,7 @@ hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipS
     if (total == 0) return hipSuccess;
     const int lanes = kThreads / a.R;
     const int64_t blocks = (total + lanes - 1) / lanes;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (V == 4)
         hipLaunchKernelGGL(reduce_axis0_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else

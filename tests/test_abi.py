@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "cfc.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -83,26 +83,56 @@ def test_step_argument_errors(L):
     assert L.cfc_bwd_step(u, h, ht, y, W, act, dhi, dho, None, S, Sb, B, C, n_x + 9000, None) == -1
 
 
+def _kloop_args(B, C, n_x, K):
+    """Twelve fake, non-overlapping addresses and a large enough workspace size."""
+    a = [FAKE + (i << 28) for i in range(12)]
+    return a[:8] + [4 * (3 * K * B * C + 2 * B * C)] + a[8:]
+
+
 def test_kloop_argument_errors(L):
     B, C, n_x, K = 4, 16, 8, 3
-    a = [FAKE + (i << 24) for i in range(12)]
+    a = _kloop_args(B, C, n_x, K)
     assert L.cfc_train_kloop(*a, B, C, n_x, -1, None) == -1
     assert L.cfc_train_kloop(*a, -2, C, n_x, K, None) == -1
     bad = list(a)
     bad[5] = None  # h_hist
     assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
     bad = list(a)
-    bad[10] = bad[9]  # gW == gb_scratch
+    bad[11] = bad[10]  # gW == gb_scratch
     assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
     assert b"overlap" in L.cfc_last_error()
     bad = list(a)
     bad[6] = a[0]  # act over u
     assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
+    bad = list(a)
+    bad[8] = a[8] - 4  # workspace one float short
+    assert L.cfc_train_kloop(*bad, B, C, n_x, K, None) == -1
+    assert b"workspace" in L.cfc_last_error()
+
+
+def test_workspace_size_and_path_queries(L):
+    assert L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) == 4 * (3 * 64 * 32 * 128 + 2 * 32 * 128)
+    assert L.cfc_train_kloop_workspace_bytes(-1, 128, 64, 64) == 0
+    # W of the pages-shaped cell (3 x 128 x 192) fits the persistent kernel; the wide one does not
+    assert L.cfc_kloop_path(32, 128, 64, 64) == 2
+    assert L.cfc_kloop_path(256, 256, 128, 64) == 1
+    assert L.cfc_kloop_path(4, 16, 8, 4) == 2
+    assert L.cfc_kloop_path(4, 64, 100, 4) == 2     # 3 column blocks
+    assert L.cfc_kloop_path(4, 48, 200, 4) == 2     # 4 column blocks
+    assert L.cfc_kloop_path(4, 100, 20, 4) == 2     # 2 channels per dz group
+    assert L.cfc_kloop_path(4, 48, 300, 4) == 1     # 6 column blocks: step path
+    assert L.cfc_kloop_path(4, 129, 0, 4) == 1      # 3 channels per dz group: step path
+    assert L.cfc_set_kloop_mode(7) == -1
+    assert L.cfc_set_kloop_mode(1) == 0
+    assert L.cfc_kloop_path(32, 128, 64, 64) == 1
+    assert L.cfc_set_kloop_mode(0) == 0
+    assert L.cfc_kloop_path(32, 128, 64, 64) == 2
 
 
 def test_no_atomics_in_kernel_sources():
+    """Device code (kernels and the shared device math) uses no atomics."""
     csrc = os.path.join(ROOT, "recurrent_cell_amd", "csrc")
-    for fn in os.listdir(csrc):
+    for fn in ("cfc_kernels.hip", "cfc_math.h", "cfc_kernels.h"):
         text = open(os.path.join(csrc, fn)).read()
         assert not re.search(r"\batomic\w*\s*\(|__hip_atomic|__atomic_|std::atomic", text), fn
 

@@ -24,6 +24,9 @@ CASES = {
     "three_tiles": dict(B=5, C=40, n_x=12, K=5),       # 3 channel tiles, last one partial
     "sample_tiles": dict(B=130, C=24, n_x=8, K=3),     # 4 samples per workgroup, ragged last
     "no_input": dict(B=2, C=16, n_x=0, K=3),           # n_x = 0: autonomous recurrence
+    "blocks3": dict(B=3, C=64, n_x=100, K=6),          # 3 column blocks, carry columns straddle blocks
+    "blocks4": dict(B=2, C=48, n_x=200, K=5),          # 4 column blocks (n_in = 248)
+    "two_channel_groups": dict(B=3, C=100, n_x=20, K=7),  # 2 channels per dz group, last groups partial
 }
 
 
@@ -39,6 +42,15 @@ def cfc():
     from recurrent_cell_amd import cfc as mod
     mod.lib()
     return mod
+
+
+@pytest.fixture
+def path(cfc, request):
+    """Force a K-loop path for one test ("auto" keeps the default), then restore it."""
+    mode = {"auto": cfc.KLOOP_AUTO, "steps": cfc.KLOOP_STEPS, "persistent": cfc.KLOOP_PERSISTENT}[request.param]
+    cfc.cfc_set_kloop_mode(mode)
+    yield request.param
+    cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
 
 def dev(a):
@@ -61,10 +73,14 @@ def bits(a):
 
 # ---------------------------------------------------------------- K-loop parity
 
+@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
 @pytest.mark.parametrize("case", list(CASES))
-def test_kloop_matches_oracle(cfc, oracle_mod, case):
+def test_kloop_matches_oracle(cfc, oracle_mod, case, path):
     d = CASES[case]
-    say("kloop parity", case, d)
+    taken = cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"], d["K"])
+    if path == "auto" and taken == cfc.KLOOP_STEPS:
+        pytest.skip("auto takes the step path here; covered by the 'steps' case")
+    say("kloop parity", case, d, "path", path, "->", "persistent" if taken == cfc.KLOOP_PERSISTENT else "steps")
     x = cfc_inputs(**d, seed=1, bias_scale=0.2)
     out, _ = kloop_dev(cfc, x)
     g = {k: host(getattr(out, k)) for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
@@ -158,10 +174,14 @@ def test_kloop_is_deterministic_and_replay_stable(cfc):
         np.testing.assert_array_equal(bits(host(getattr(a, k))), bits(v), err_msg=k)
 
 
-@pytest.mark.parametrize("case", ["pages", "ragged_scalar", "sample_tiles"])
-def test_graph_equals_eager_step_calls(cfc, case):
+@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+@pytest.mark.parametrize("case", ["pages", "ragged_scalar", "sample_tiles", "three_tiles", "no_input",
+                                  "blocks3", "two_channel_groups"])
+def test_graph_equals_eager_step_calls(cfc, case, path):
+    """The K-loop graph (persistent kernel or step kernels) gives the bits of
+    the eager composition of single-step ABI calls with per-step scratch +=."""
     d = CASES[case]
-    say("graph == eager", case)
+    say("graph == eager", case, path)
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
     x = cfc_inputs(**d, seed=6, bias_scale=0.2)
     g, (u, y, h0, W, bias) = kloop_dev(cfc, x)
@@ -184,6 +204,81 @@ def test_graph_equals_eager_step_calls(cfc, case):
     np.testing.assert_array_equal(bits(host(Sb)), bits(host(g.gb_scratch)))
     np.testing.assert_array_equal(bits(host(gW)), bits(host(g.gW).reshape(-1)))
     np.testing.assert_array_equal(bits(host(gb)), bits(host(g.gb).reshape(-1)))
+
+
+@pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input",
+                                  "blocks3", "blocks4", "two_channel_groups"])
+def test_persistent_and_step_paths_agree_bitwise(cfc, case):
+    d = CASES[case]
+    say("persistent == steps", case)
+    x = cfc_inputs(**d, seed=14, bias_scale=0.25)
+    res = {}
+    for mode in (cfc.KLOOP_PERSISTENT, cfc.KLOOP_STEPS):
+        cfc.cfc_set_kloop_mode(mode)
+        try:
+            out, _ = kloop_dev(cfc, x)
+            res[mode] = {k: host(getattr(out, k)).copy()
+                         for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
+        finally:
+            cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+    for k in res[cfc.KLOOP_STEPS]:
+        np.testing.assert_array_equal(bits(res[cfc.KLOOP_PERSISTENT][k]), bits(res[cfc.KLOOP_STEPS][k]), err_msg=k)
+
+
+@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+@pytest.mark.parametrize("case", ["pages", "three_tiles"])
+def test_kloop_equals_its_phases(cfc, case, path):
+    """cfc_train_kloop == cfc_kloop_fwd_bwd, then cfc_scratch_fill, then
+    reduce_axis0 on each scratch tensor, bit for bit."""
+    d = CASES[case]
+    say("kloop == phases", case, path)
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    x = cfc_inputs(**d, seed=15, bias_scale=0.2)
+    g, t = kloop_dev(cfc, x)
+    from recurrent_cell_amd.cfc import KloopBuffers
+    ph = KloopBuffers.allocate(B, C, n_x, K, "cuda")
+    cfc.cfc_kloop_fwd_bwd(*t, out=ph)
+    dp = ph.ws[:K * B * 3 * C].view(K, B, 3 * C)
+    cfc.cfc_scratch_fill(dp, t[0], ph.h_hist, ph.gW_scratch, ph.gb_scratch)
+    cfc.reduce_axis0(ph.gW_scratch.view(B, -1), ph.gW.view(-1))
+    cfc.reduce_axis0(ph.gb_scratch.view(B, -1), ph.gb.view(-1))
+    for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb"):
+        np.testing.assert_array_equal(bits(host(getattr(ph, k))), bits(host(getattr(g, k))), err_msg=k)
+
+
+@pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "no_input"])
+def test_scratch_fill_matches_its_definition(cfc, case):
+    """S[b,r,k] = sum_t dp[t,b,r] z_t[b,k], Sb[b,r] = sum_t dp[t,b,r] on
+    arbitrary fp32 inputs, against fp64 sums (numpy matmul)."""
+    d = CASES[case]
+    say("scratch fill", case)
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    x = cfc_inputs(**d, seed=16)
+    dp = normal((K, B, 3 * C), 16, 1)
+    h_hist = normal((K + 1, B, C), 16, 2)
+    S = torch.full((B, 3, C, n_x + C), float("nan"), device="cuda")
+    Sb = torch.full((B, 3, C), float("nan"), device="cuda")
+    cfc.cfc_scratch_fill(dev(dp), dev(x.u), dev(h_hist), S, Sb)
+    z = np.concatenate([x.u, h_hist[:-1]], axis=2).astype(np.float64)          # [K,B,n_in]
+    A = np.ascontiguousarray(dp.astype(np.float64).transpose(1, 2, 0))          # [B,3C,K]
+    Z = np.ascontiguousarray(z.transpose(1, 0, 2))                              # [B,K,n_in]
+    ref = np.matmul(A, Z).reshape(B, 3, C, -1)
+    mass = np.matmul(np.abs(A), np.abs(Z)).reshape(B, 3, C, -1)
+    assert_ok(check_grad("S", host(S), ref, mass))
+    refb = dp.astype(np.float64).sum(0).reshape(B, 3, C)
+    assert_ok(check_grad("Sb", host(Sb), refb, np.abs(dp.astype(np.float64)).sum(0).reshape(B, 3, C)))
+
+
+def test_persistent_mode_refuses_shapes_it_cannot_hold(cfc):
+    d = CASES["wide"]
+    say("persistent refusal", d)
+    cfc.cfc_set_kloop_mode(cfc.KLOOP_PERSISTENT)
+    try:
+        x = cfc_inputs(**dict(d, B=2, K=2), seed=1)
+        with pytest.raises(cfc.CfcError):
+            kloop_dev(cfc, x)
+    finally:
+        cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
 
 @pytest.mark.parametrize("case", ["pages", "sample_tiles"])
@@ -226,7 +321,7 @@ def test_final_gradients_are_overwritten(cfc):
     x = cfc_inputs(**d, seed=10)
     from recurrent_cell_amd.cfc import KloopBuffers
     out = KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
-    for tns in (out.gW, out.gb, out.gW_scratch, out.gb_scratch, out.h_hist, out.act):
+    for tns in (out.gW, out.gb, out.gW_scratch, out.gb_scratch, out.h_hist, out.act, out.ws):
         tns.fill_(float("nan"))
     kloop_dev(cfc, x, out=out)
     ref, _ = kloop_dev(cfc, x)
