@@ -397,40 +397,94 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
 
 // ---------------------------------------------------------------------------
 // Persistent K-loop kernel: workgroup b runs sample b's whole step.
-// DPP row g (16 lanes, g < 64) owns the cpg channels of canonical dz group g,
-// all three heads: W rows (q, c) for c in [g cpg, g cpg + cpg), held in
+// The workgroup has 64 / GPR DPP rows of 16 lanes; row r owns canonical dz
+// groups GPR r .. GPR r + GPR - 1, i.e. the CPR = GPR cpg consecutive
+// channels starting at CPR r, all three heads.  Their W rows sit in
 // registers as lane j's canonical forward columns 64 i + 4 j + e.
-// The step loops issue no global loads: every kPersistChunk steps the whole
-// workgroup stages the next chunk's per-step inputs (u for the forward;
-// gate, g, hh, h_t, y_t for the backward) into LDS with one coalesced pass and
-// one full barrier; inside a chunk a step is LDS traffic, DPP, arithmetic,
-// stores that nothing waits for, and one LDS-only barrier.
-//  forward, per t : the 3 cpg dot products of the row (row_sum16 leaves every
-//                   lane with every sum); lane j < cpg applies the cell to
-//                   channel g cpg + j at once, writes h_t into the next z
-//                   buffer and stores h_t and (gate, g, hh).
-//  backward, per t: every lane forms dp of the row's channels from the carry
-//                   (shuffled in from the lanes that summed it) and the staged
-//                   operands; lane 4 cc stores dp of channel cc; the group
-//                   partials P_g of the carry columns go to a double-buffered
-//                   LDS block; after the barrier, lanes 4 cc .. 4 cc + 3 sum
-//                   column n_x + g cpg + cc over the 64 groups (tree_sum16
-//                   each, then quad_sum4).
+// The step loops touch no global memory.  Steps run in chunks; at each chunk
+// boundary the workgroup
+//   - moves the chunk's inputs into LDS from registers, where they were
+//     loaded during the previous chunk (u for the forward; gate, g, hh, h_t,
+//     y_t for the backward),
+//   - writes the previous chunk's outputs from LDS to memory with coalesced
+//     16-byte stores (h_t and (gate, g, hh); dp_t),
+//   - issues the loads of the next chunk's inputs,
+// so every wait on memory at a boundary is for operations a whole chunk old.
+// Inside a chunk a step is LDS traffic, DPP, arithmetic and one LDS-only
+// barrier.
+//  forward, per t : the 3 CPR dot products of the row (row_sum16 leaves every
+//                   lane with every sum); lane j < CPR applies the cell to
+//                   channel CPR r + j, writes h_t into the next z buffer and
+//                   (h_t, gate, g, hh) into the chunk's output buffer.
+//  backward, per t: quad cc (lanes 4 cc .. 4 cc + 3) computes dp of channel
+//                   CPR r + cc from the carry it summed itself; the row reads
+//                   every dp back with ds_swizzle; lane 4 cc puts dp into the
+//                   chunk's output buffer; the partials P_g of each of the
+//                   row's groups (carry columns) go to a double-buffered LDS
+//                   block; after the barrier quad cc sums column
+//                   n_x + CPR r + cc over the 64 groups (lane q of the quad:
+//                   tree_sum16 over groups q, q+4, ..; then quad_sum4).
 // ---------------------------------------------------------------------------
-constexpr int kPersistChunk = 16;
+constexpr int kFwdChunk = 16;
+constexpr int kBwdChunk = 8;
 
-template <int CPG, int NI>
-__global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistArgs a)
+template <int CPG, int GPR, int NI>
+struct PersistLds {
+    static constexpr int CPR = CPG * GPR;
+    static constexpr int ZW = NI * 64;
+    static constexpr int ZWP = ZW + 8;           // partial row pitch: 8 banks between group rows
+    static constexpr int CMAX = 64 * CPG;
+    static constexpr int STAGE = (5 * CMAX * kBwdChunk > ZW * kFwdChunk) ? 5 * CMAX * kBwdChunk : ZW * kFwdChunk;
+    static constexpr int DBUF = kBwdChunk * 3 * CMAX;
+    static constexpr size_t BYTES = sizeof(float) * (2 * ZW + 2 * kDzGroups * ZWP + STAGE + DBUF);
+    static_assert(4 * CMAX * kFwdChunk <= 2 * kDzGroups * ZWP, "forward output buffer fits in the partials");
+};
+
+// Coalesced move of `rows` rows of `len` floats between LDS (row pitch len)
+// and global memory (row rr at dst(rr)); 16-byte moves when vec.
+template <int THREADS, bool TO_GLOBAL, typename Ptr>
+__device__ __forceinline__ void move_rows(float* lds, int rows, int len, bool vec, Ptr gptr)
 {
-    constexpr int ZW = NI * 64;
-    constexpr int CMAX = 64 * CPG;
-    constexpr int STAGE = (5 * CMAX > ZW ? 5 * CMAX : ZW) * kPersistChunk;
+    if (vec) {
+        const int w = len / 4;
+        for (int i = threadIdx.x; i < rows * w; i += THREADS) {
+            const int rr = i / w;
+            const int x = 4 * (i - rr * w);
+            float* g = gptr(rr) + x;
+            if (TO_GLOBAL)
+                *reinterpret_cast<f32x4*>(g) = *reinterpret_cast<const f32x4*>(lds + rr * len + x);
+            else
+                *reinterpret_cast<f32x4*>(lds + rr * len + x) = *reinterpret_cast<const f32x4*>(g);
+        }
+    } else {
+        for (int i = threadIdx.x; i < rows * len; i += THREADS) {
+            const int rr = i / len;
+            const int x = i - rr * len;
+            if (TO_GLOBAL)
+                gptr(rr)[x] = lds[i];
+            else
+                lds[i] = gptr(rr)[x];
+        }
+    }
+}
+
+template <int CPG, int GPR, int NI>
+__global__ __launch_bounds__(1024 / GPR) void kloop_persist_kernel(PersistArgs a)
+{
+    using L = PersistLds<CPG, GPR, NI>;
+    constexpr int THREADS = 1024 / GPR;
+    constexpr int CPR = L::CPR;
+    constexpr int ZW = L::ZW;
+    constexpr int ZWP = L::ZWP;
+    static_assert(CPR <= 4, "one quad per channel of a row");
     __shared__ __attribute__((aligned(16))) float zs[2][ZW];
-    __shared__ __attribute__((aligned(16))) float part[2][kDzGroups][ZW];
-    __shared__ __attribute__((aligned(16))) float stage[STAGE];
+    __shared__ __attribute__((aligned(16))) float part[2][kDzGroups][ZWP];
+    __shared__ __attribute__((aligned(16))) float stage[L::STAGE];
+    __shared__ __attribute__((aligned(16))) float dbuf[L::DBUF];
+    float* obuf = &part[0][0][0];   // forward output buffer [kFwdChunk][4][C] (partials unused then)
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int g = tid >> 4;
+    const int row = tid >> 4;
     const int j = tid & 15;
     const int C = a.C;
     const int n_x = a.n_x;
@@ -438,19 +492,23 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     const int B = a.B;
     const int K = a.K;
     const int R3 = 3 * C;
-    const int c0 = g * CPG;
-    const int ncg = max(0, min(CPG, C - c0));   // channels of this row group
+    const int c0 = row * CPR;
+    const int ncr = max(0, min(CPR, C - c0));   // channels of this row
     const int64_t BC = (int64_t)B * C;
     const int i0 = n_x / 64;                     // first column block holding carry columns
     const bool wvec = (n_in % 4 == 0) && ((((uintptr_t)a.W) & 15u) == 0);
+    // 16-byte moves need rows of a multiple of 4 floats on 16-byte aligned arrays
+    const bool u_vec = (n_x % 4 == 0) && ((((uintptr_t)a.u) & 15u) == 0);
+    const bool c_vec = (C % 4 == 0) && ((((uintptr_t)a.act) | ((uintptr_t)a.h_hist) | ((uintptr_t)a.y) |
+                                          ((uintptr_t)a.dp)) & 15u) == 0;
 
-    float w[CPG][3][NI][4];
-    float bq[CPG][3];
+    float w[CPR][3][NI][4];
+    float bq[CPR][3];
 #pragma unroll
-    for (int cc = 0; cc < CPG; ++cc)
+    for (int cc = 0; cc < CPR; ++cc)
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            const bool ok = cc < ncg;
+            const bool ok = cc < ncr;
             const int r = q * C + c0 + cc;
             bq[cc][q] = ok ? a.bias[r] : 0.0f;
 #pragma unroll
@@ -469,27 +527,61 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 }
             }
         }
-    for (int i = tid; i < 2 * ZW; i += kPersistThreads) (&zs[0][0])[i] = 0.0f;
+    for (int i = tid; i < 2 * ZW; i += THREADS) (&zs[0][0])[i] = 0.0f;
     __syncthreads();
-    if (tid < C) {
-        const float h = a.h0[(int64_t)b * C + tid];
-        zs[0][n_x + tid] = h;
-        a.h_hist[(int64_t)b * C + tid] = h;
+    for (int c = tid; c < C; c += THREADS) {
+        const float h = a.h0[(int64_t)b * C + c];
+        zs[0][n_x + c] = h;
+        a.h_hist[(int64_t)b * C + c] = h;
     }
 
     // ---------------- forward ----------------
-    for (int t0 = 1; t0 <= K; t0 += kPersistChunk) {
-        const int nt = min(kPersistChunk, K - t0 + 1);
-        // stage u_{t0} .. u_{t0+nt-1}; u_{t0} also goes straight into its z buffer
-        __syncthreads();
-        for (int i = tid; i < nt * n_x; i += kPersistThreads) {
-            const int tt = i / n_x;
-            const int k = i - tt * n_x;
-            const float v = a.u[((int64_t)(t0 - 1 + tt) * B + b) * n_x + k];
-            stage[i] = v;
-            if (tt == 0) zs[(t0 - 1) & 1][k] = v;
+    // u prefetch into registers: a lane moves one float4 of one staged row of
+    // n_x floats per pass, on a map computed once (16-byte path only).
+    const int u_w = n_x / 4;
+    const int u_col = u_w > 0 ? tid % u_w : 0;
+    const int u_row0 = u_w > 0 ? tid / u_w : kFwdChunk;
+    const int u_rstep = u_w > 0 ? THREADS / u_w : 1;
+    constexpr int UPF = (kFwdChunk * 16 * NI + THREADS - 1) / THREADS;
+    f32x4 upf[UPF];
+    auto load_u = [&](int t0, int nt) {
+#pragma unroll
+        for (int m = 0; m < UPF; ++m) {
+            const int rr = u_row0 + m * u_rstep;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (u_row0 < u_rstep && rr < nt)
+                v = *reinterpret_cast<const f32x4*>(a.u + ((int64_t)(t0 - 1 + rr) * B + b) * n_x + 4 * u_col);
+            upf[m] = v;
         }
-        __syncthreads();
+    };
+    auto u_row = [&](int t0) { return [=](int rr) { return const_cast<float*>(a.u) + ((int64_t)(t0 - 1 + rr) * B + b) * n_x; }; };
+    auto out_row = [&](int t0) {
+        return [=](int rr) {
+            const int t = t0 + (rr >> 2);
+            const int v = rr & 3;   // h_t, gate, g, hh
+            return (v == 0 ? a.h_hist + (int64_t)t * BC : a.act + (int64_t)(t - 1) * 3 * BC + (v - 1) * BC) +
+                   (int64_t)b * C;
+        };
+    };
+    if (u_vec && K >= 1) load_u(1, min(kFwdChunk, K));
+    int prev_t0 = 0, prev_nt = 0;
+    for (int t0 = 1; t0 <= K; t0 += kFwdChunk) {
+        const int nt = min(kFwdChunk, K - t0 + 1);
+        if (u_vec) {
+#pragma unroll
+            for (int m = 0; m < UPF; ++m) {
+                const int rr = u_row0 + m * u_rstep;
+                if (u_row0 < u_rstep && rr < nt)
+                    *reinterpret_cast<f32x4*>(stage + rr * n_x + 4 * u_col) = upf[m];
+            }
+        } else {
+            move_rows<THREADS, false>(stage, nt, n_x, false, u_row(t0));
+        }
+        if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, c_vec, out_row(prev_t0));
+        if (u_vec && t0 + kFwdChunk <= K) load_u(t0 + kFwdChunk, min(kFwdChunk, K - t0 - kFwdChunk + 1));
+        lds_barrier();
+        for (int k = tid; k < n_x; k += THREADS) zs[(t0 - 1) & 1][k] = stage[k];
+        lds_barrier();
         for (int tt = 0; tt < nt; ++tt) {
             const int t = t0 + tt;
             const float* zc = zs[(t - 1) & 1];
@@ -497,9 +589,9 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             f32x4 zv[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) zv[i] = *reinterpret_cast<const f32x4*>(zc + 64 * i + 4 * j);
-            float av[CPG][3];
+            float av[CPR][3];
 #pragma unroll
-            for (int cc = 0; cc < CPG; ++cc)
+            for (int cc = 0; cc < CPR; ++cc)
 #pragma unroll
                 for (int q = 0; q < 3; ++q) {
                     float p = 0.0f;
@@ -507,64 +599,91 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                     for (int i = 0; i < NI; ++i)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) p = fmaf(w[cc][q][i][e], zv[i][e], p);
-                    av[cc][q] = row_sum16(p) + bq[cc][q];
+                    av[cc][q] = row_sum16(p);
                 }
-            if (j < ncg) {
-                float af = av[0][0], ag = av[0][1], ah = av[0][2];
+            if (j < ncr) {
+                float af = av[0][0] + bq[0][0], ag = av[0][1] + bq[0][1], ah = av[0][2] + bq[0][2];
 #pragma unroll
-                for (int cc = 1; cc < CPG; ++cc)
+                for (int cc = 1; cc < CPR; ++cc)
                     if (j == cc) {
-                        af = av[cc][0];
-                        ag = av[cc][1];
-                        ah = av[cc][2];
+                        af = av[cc][0] + bq[cc][0];
+                        ag = av[cc][1] + bq[cc][1];
+                        ah = av[cc][2] + bq[cc][2];
                     }
                 const CellOut o = cell_forward(af, ag, ah);
                 const int c = c0 + j;
-                const int64_t bc = (int64_t)b * C + c;
                 zn[n_x + c] = o.h;
-                a.h_hist[(int64_t)t * BC + bc] = o.h;
-                float* act_t = a.act + (int64_t)(t - 1) * 3 * BC;
-                act_t[bc] = o.gate;
-                act_t[BC + bc] = o.g;
-                act_t[2 * BC + bc] = o.hh;
+                float* ob = obuf + (tt * 4) * C + c;
+                ob[0] = o.h;
+                ob[C] = o.gate;
+                ob[2 * C] = o.g;
+                ob[3 * C] = o.hh;
             }
-            if (tid < n_x && tt + 1 < nt) zn[tid] = stage[(tt + 1) * n_x + tid];
+            if (tt + 1 < nt)
+                for (int k = tid; k < n_x; k += THREADS) zn[k] = stage[(tt + 1) * n_x + k];
             lds_barrier();
         }
+        prev_t0 = t0;
+        prev_nt = nt;
     }
+    if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, c_vec, out_row(prev_t0));
+    __syncthreads();   // every forward store is performed and visible to the whole workgroup
 
     // ---------------- backward ----------------
-    static_assert(CPG <= 2, "the row broadcast of dp covers at most two channels per row");
-    float carry_mine = 0.0f;   // lanes 4 cc .. 4 cc + 3: carry of channel c0 + cc
-    for (int t1 = K; t1 >= 1; t1 -= kPersistChunk) {
-        const int nt = min(kPersistChunk, t1);   // steps t1, t1 - 1, .., t1 - nt + 1
-        // stage (gate, g, hh, h_t, y_t) of every channel for the chunk's steps;
-        // the full barrier also makes the forward's stores visible.
-        __syncthreads();
-        for (int i = tid; i < nt * 5 * C; i += kPersistThreads) {
-            const int tt = i / (5 * C);
-            const int rem = i - tt * 5 * C;
-            const int v = rem / C;
-            const int c = rem - v * C;
+    // Staged rows per step tt of a chunk: 5 tt + v, v = gate, g, hh (act), h_t,
+    // y_t, each C floats; register prefetch on the 16-byte path.
+    const int c_w = C / 4;
+    const int c_col = c_w > 0 ? tid % c_w : 0;
+    const int c_row0 = c_w > 0 ? tid / c_w : 5 * kBwdChunk;
+    const int c_rstep = c_w > 0 ? THREADS / c_w : 1;
+    constexpr int BPF = (5 * kBwdChunk * 16 * CPG + THREADS - 1) / THREADS;
+    f32x4 bpf[BPF];
+    auto in_row = [&](int t1) {
+        return [=](int rr) {
+            const int tt = rr / 5;
+            const int v = rr - 5 * tt;
             const int t = t1 - tt;
-            const int64_t bc = (int64_t)b * C + c;
-            float x;
-            if (v < 3)
-                x = a.act[(int64_t)(t - 1) * 3 * BC + v * BC + bc];
-            else if (v == 3)
-                x = a.h_hist[(int64_t)t * BC + bc];
-            else
-                x = a.y[(int64_t)(t - 1) * BC + bc];
-            stage[i] = x;
+            const float* src = (v < 3) ? a.act + (int64_t)(t - 1) * 3 * BC + v * BC
+                             : (v == 3) ? a.h_hist + (int64_t)t * BC : a.y + (int64_t)(t - 1) * BC;
+            return const_cast<float*>(src) + (int64_t)b * C;
+        };
+    };
+    auto dp_row = [&](int t1) {
+        return [=](int tt) { return a.dp + ((int64_t)(t1 - tt - 1) * B + b) * R3; };
+    };
+    auto load_b = [&](int t1, int nt) {
+        const auto src = in_row(t1);
+#pragma unroll
+        for (int m = 0; m < BPF; ++m) {
+            const int rr = c_row0 + m * c_rstep;
+            f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (c_row0 < c_rstep && rr < 5 * nt) x = *reinterpret_cast<const f32x4*>(src(rr) + 4 * c_col);
+            bpf[m] = x;
         }
-        __syncthreads();
+    };
+    if (c_vec && K >= 1) load_b(K, min(kBwdChunk, K));
+    float carry_mine = 0.0f;   // quad cc: carry of channel c0 + cc
+    int prev_t1 = 0;
+    prev_nt = 0;
+    for (int t1 = K; t1 >= 1; t1 -= kBwdChunk) {
+        const int nt = min(kBwdChunk, t1);   // steps t1, t1 - 1, .., t1 - nt + 1
+        if (c_vec) {
+#pragma unroll
+            for (int m = 0; m < BPF; ++m) {
+                const int rr = c_row0 + m * c_rstep;
+                if (c_row0 < c_rstep && rr < 5 * nt) *reinterpret_cast<f32x4*>(stage + rr * C + 4 * c_col) = bpf[m];
+            }
+        } else {
+            move_rows<THREADS, false>(stage, 5 * nt, C, false, in_row(t1));
+        }
+        if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, c_vec, dp_row(prev_t1));
+        if (c_vec && t1 - kBwdChunk >= 1) load_b(t1 - kBwdChunk, min(kBwdChunk, t1 - kBwdChunk));
+        lds_barrier();
         for (int tt = 0; tt < nt; ++tt) {
             const int t = t1 - tt;
             const int buf = t & 1;
             const float* st = stage + tt * 5 * C;
-            // quad cc computes dp of channel c0 + cc once (it holds that
-            // channel's carry); the row then reads it from lane 4 cc.
-            const int my_cc = min(j >> 2, CPG - 1);
+            const int my_cc = min(j >> 2, CPR - 1);
             const int my_c = min(c0 + my_cc, C - 1);
             float mdp[3];
             {
@@ -572,58 +691,69 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 if (t < K) dh += carry_mine;
                 cell_backward(dh, st[my_c], st[C + my_c], st[2 * C + my_c], mdp[0], mdp[1], mdp[2]);
             }
-            float dp[CPG][3];
+            float dp[CPR][3];
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
                 dp[0][q] = row_bcast<0>(mdp[q]);
-                if (CPG > 1) dp[CPG - 1][q] = row_bcast<4 * (CPG - 1)>(mdp[q]);
+                if (CPR > 1) dp[1][q] = row_bcast<4>(mdp[q]);
+                if (CPR > 2) dp[2][q] = row_bcast<8>(mdp[q]);
+                if (CPR > 3) dp[3][q] = row_bcast<12>(mdp[q]);
             }
 #pragma unroll
-            for (int cc = 0; cc < CPG; ++cc)
-                if (cc >= ncg) dp[cc][0] = dp[cc][1] = dp[cc][2] = 0.0f;
-            if ((j & 3) == 0 && (j >> 2) < ncg) {
-                float* dpt = a.dp + ((int64_t)(t - 1) * B + b) * R3;
-                const int c = c0 + (j >> 2);
-                dpt[c] = mdp[0];
-                dpt[C + c] = mdp[1];
-                dpt[2 * C + c] = mdp[2];
+            for (int cc = 0; cc < CPR; ++cc)
+                if (cc >= ncr) dp[cc][0] = dp[cc][1] = dp[cc][2] = 0.0f;
+            if ((j & 3) == 0 && (j >> 2) < ncr) {
+                float* db = dbuf + tt * R3 + c0 + (j >> 2);
+                db[0] = mdp[0];
+                db[C] = mdp[1];
+                db[2 * C] = mdp[2];
             }
-            float P[NI][4];
+            // Partials of the row's groups over the carry columns (blocks
+            // i >= i0; the K-loop produces no du).  Absent channels carry
+            // W = 0 and dp = 0, and fma(0, 0, P) == P exactly (P is never -0),
+            // so the chains need no per-channel branches.
+            float P[GPR][NI][4];
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
+            for (int gi = 0; gi < GPR; ++gi)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) P[i][e] = 0.0f;
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPG; ++cc) {
-                if (cc < ncg) {
-#pragma unroll
-                    for (int q = 0; q < 3; ++q)
-#pragma unroll
-                        for (int i = 0; i < NI; ++i)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) P[i][e] = fmaf(w[cc][q][i][e], dp[cc][q], P[i][e]);
-                }
-            }
+                    for (int e = 0; e < 4; ++e) P[gi][i][e] = 0.0f;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                if (i >= i0) {
-                    f32x4 v;
-                    v.x = P[i][0];
-                    v.y = P[i][1];
-                    v.z = P[i][2];
-                    v.w = P[i][3];
-                    *reinterpret_cast<f32x4*>(&part[buf][g][64 * i + 4 * j]) = v;
+                if (i >= i0) {   // uniform: i0 comes from n_x
+#pragma unroll
+                    for (int cl = 0; cl < CPG; ++cl)
+#pragma unroll
+                        for (int q = 0; q < 3; ++q)
+#pragma unroll
+                            for (int gi = 0; gi < GPR; ++gi)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    P[gi][i][e] = fmaf(w[gi * CPG + cl][q][i][e], dp[gi * CPG + cl][q], P[gi][i][e]);
+#pragma unroll
+                    for (int gi = 0; gi < GPR; ++gi) {
+                        f32x4 v;
+                        v.x = P[gi][i][0];
+                        v.y = P[gi][i][1];
+                        v.z = P[gi][i][2];
+                        v.w = P[gi][i][3];
+                        *reinterpret_cast<f32x4*>(&part[buf][row * GPR + gi][64 * i + 4 * j]) = v;
+                    }
                 }
             }
             lds_barrier();
-            if ((j >> 2) < CPG) {   // uniform over each quad
-                const int cc = j >> 2;
-                const int col = n_x + min(c0 + cc, C - 1);
-                const float v = tree_sum16(&part[buf][16 * (j & 3)][col], ZW);
+            if ((j >> 2) < CPR) {   // uniform over each quad
+                const int col = n_x + min(c0 + (j >> 2), C - 1);
+                const float v = tree_sum16(&part[buf][j & 3][col], 4 * ZWP);
                 carry_mine = quad_sum4(v);
             }
         }
+        prev_t1 = t1;
+        prev_nt = nt;
     }
+    lds_barrier();
+    if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, c_vec, dp_row(prev_t1));
 }
 
 // ---------------------------------------------------------------------------
@@ -740,8 +870,9 @@ hipError_t launch_bwd_bt(const BwdArgs& a, const StepPlan& p, hipStream_t s)
     return hipGetLastError();
 }
 
-// Persistent-kernel instantiations: CPG channels per DPP row (C <= 64 CPG),
-// NI column blocks of 64 (n_in <= 64 NI); 12 CPG NI W values per lane.
+// Persistent-kernel instantiations: CPG channels per canonical group
+// (C <= 64 CPG), two groups per DPP row (512 lanes), NI column blocks of 64
+// (n_in <= 64 NI); 24 CPG NI W values per lane.
 struct PersistShape {
     int cpg, ni;
 };
@@ -758,10 +889,13 @@ bool persist_shape(int C, int n_x, PersistShape& ps)
     return false;
 }
 
+constexpr int kPersistGPR = 2;
+
 template <int CPG, int NI>
 hipError_t launch_persist_t(const PersistArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL((kloop_persist_kernel<CPG, NI>), dim3((unsigned)a.B), dim3(kPersistThreads), 0, s, a);
+    hipLaunchKernelGGL((kloop_persist_kernel<CPG, kPersistGPR, NI>), dim3((unsigned)a.B),
+                       dim3(1024 / kPersistGPR), 0, s, a);
     return hipGetLastError();
 }
 
@@ -780,9 +914,16 @@ size_t persist_smem(int C, int n_x)
 {
     PersistShape ps;
     if (!persist_shape(C, n_x, ps)) return 0;
-    const size_t zw = 64 * (size_t)ps.ni;
-    const size_t stage = (5 * 64 * (size_t)ps.cpg > zw ? 5 * 64 * (size_t)ps.cpg : zw) * kPersistChunk;
-    return sizeof(float) * (2 * zw + 2 * (size_t)kDzGroups * zw + stage);
+#define CFC_PERSIST_LDS(P_, N_) \
+    if (ps.cpg == P_ && ps.ni == N_) return PersistLds<P_, kPersistGPR, N_>::BYTES;
+    CFC_PERSIST_LDS(1, 1)
+    CFC_PERSIST_LDS(1, 2)
+    CFC_PERSIST_LDS(1, 3)
+    CFC_PERSIST_LDS(1, 4)
+    CFC_PERSIST_LDS(2, 2)
+    CFC_PERSIST_LDS(2, 3)
+#undef CFC_PERSIST_LDS
+    return 0;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, const StepPlan& p, hipStream_t s)

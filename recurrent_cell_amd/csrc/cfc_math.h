@@ -9,7 +9,9 @@
 //   dz[k]    = over 64 groups of cpg = ceil(C / 64) consecutive channels:
 //              P_g = fma chain of W[q C + c, k] dp_q[c] over the group's
 //              channels c ascending and, within a channel, heads q = 0, 1, 2;
-//              then the pairwise tree sum64 of P_0 .. P_63 (empty groups: +0);
+//              then tree_sum64 of P_0 .. P_63 (empty groups: +0): subtree T_q
+//              (q = 0..3) is the pairwise sum of P_q, P_{q+4}, .., P_{q+60},
+//              and dz = (T_0 + T_1) + (T_2 + T_3);
 //   S[b,r,k] = fma chain over t = K, K-1, .., 1 of dp_t[r] * z_t[k] from +0;
 //   Sb[b,r]  = add chain over t = K .. 1 of dp_t[r] from +0.
 #pragma once
@@ -84,14 +86,16 @@ __device__ __forceinline__ float tree_sum16(const float* p, int s)
     return a[0] + a[1];
 }
 
-// The canonical sum64 of 64 values at stride s: the four 16-leaf subtrees
-// T0..T3 combined as (T0 + T1) + (T2 + T3).
+// The canonical sum64 of p[0], p[s], .., p[63 s]: subtree T_q is the
+// pairwise sum of p[q s], p[(q + 4) s], .., p[(q + 60) s]; then
+// (T0 + T1) + (T2 + T3).  (Interleaved subtrees let the four lanes that
+// share a column read four different LDS banks in the persistent kernel.)
 __device__ __forceinline__ float tree_sum64(const float* p, int s)
 {
-    const float t0 = tree_sum16(p, s);
-    const float t1 = tree_sum16(p + 16 * s, s);
-    const float t2 = tree_sum16(p + 32 * s, s);
-    const float t3 = tree_sum16(p + 48 * s, s);
+    const float t0 = tree_sum16(p, 4 * s);
+    const float t1 = tree_sum16(p + s, 4 * s);
+    const float t2 = tree_sum16(p + 2 * s, 4 * s);
+    const float t3 = tree_sum16(p + 3 * s, 4 * s);
     return (t0 + t1) + (t2 + t3);
 }
 
