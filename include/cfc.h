@@ -123,14 +123,16 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *   act    [K, 3, B, C]  out: saved (gate, g, hh) of every step
  *   ws, ws_bytes         workspace of at least
  *                        cfc_train_kloop_workspace_bytes(B, C, n_x, K) bytes
- *                        (the pre-activation gradients of every step and the
- *                        BPTT carry); contents are undefined afterwards
+ *                        (the pre-activation gradients of every step, the
+ *                        input projection of every step and the BPTT carry);
+ *                        contents are undefined afterwards
  *   gW_scratch [B, 3, C, n_in], gb_scratch [B, 3, C]   out: per-sample sums
  *                        S[b,q,c,:] = sum_t dp_q[t,b,c] z_t[b,:] (t = K..1)
  *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
  *                        call's work on `stream` has completed
- * Two paths give the same bits: a persistent kernel (one workgroup per
- * sample runs every K step with W in registers) when W fits, otherwise 2K
+ * Two paths give the same bits: an input-projection launch for all steps
+ * followed by a persistent kernel (one workgroup per sample runs every K
+ * step with the recurrent W in registers) when C <= 128, otherwise 2K
  * step-kernel launches; cfc_set_kloop_mode() can force either.  The graph is
  * built on the first call for a given (device, path, pointers, sizes) and
  * cached; later calls with the same key replay it.  Calls sharing a key must
@@ -169,12 +171,12 @@ int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist,
                      float* gW_scratch, float* gb_scratch,
                      int B, int C, int n_x, int K, void* stream);
 
-/* Bytes of workspace cfc_train_kloop needs: 4 * (3 K B C + 2 B C).
+/* Bytes of workspace cfc_train_kloop needs: 4 * (6 K B C + 2 B C).
  * Returns 0 for invalid sizes. */
 size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K);
 
 /* Path selection of cfc_train_kloop for the whole process.
- * CFC_KLOOP_AUTO (default): persistent kernel when W fits, else step kernels;
+ * CFC_KLOOP_AUTO (default): persistent kernel when C <= 128, else step kernels;
  * CFC_KLOOP_STEPS: always the 2K step-kernel launches;
  * CFC_KLOOP_PERSISTENT: the persistent kernel (cfc_train_kloop then returns
  * CFC_EINVAL for shapes it cannot hold).  Both paths give the same bits. */

@@ -81,8 +81,10 @@ cfc::StepPlan make_plan(int B, int C, int n_x, const float* W, const float* scra
     p.n_ctiles = (C + p.CT - 1) / p.CT;
     p.BT = B >= 128 ? 4 : 1;
     p.ldz = (n_in + 3) & ~3;
+    p.ldu = (n_x + 3) & ~3;
+    p.ldh = (C + 3) & ~3;
     auto smem = [&](int bt) {
-        const size_t fwd = sizeof(float) * ((size_t)bt * p.ldz + (size_t)bt * 3 * p.CT);
+        const size_t fwd = sizeof(float) * ((size_t)bt * (p.ldu + p.ldh) + (size_t)bt * 3 * p.CT);
         const size_t bwd = sizeof(float) * ((size_t)bt * p.ldz + (size_t)bt * 3 * C +
                                             (size_t)cfc::kDzGroups * bt * cfc::kCols);
         return std::make_pair(fwd, bwd);
@@ -92,7 +94,7 @@ cfc::StepPlan make_plan(int B, int C, int n_x, const float* W, const float* scra
     p.bwd_smem = smem(p.BT).second;
     p.n_btiles = B > 0 ? (B + p.BT - 1) / p.BT : 0;
     // Only the load width depends on these; the arithmetic does not.
-    p.Vf = (n_in % 4 == 0 && aligned16(W)) ? 4 : 1;
+    p.Vf = (n_in % 4 == 0 && n_x % 4 == 0 && aligned16(W)) ? 4 : 1;
     p.Vb = (n_in % 4 == 0 && scratch != nullptr && aligned16(scratch)) ? 4 : 1;
     return p;
 }
@@ -110,7 +112,7 @@ int enqueue_fwd(const float* u_t, const float* h_prev, const float* W, const flo
                 hipStream_t s)
 {
     if (B == 0) return CFC_OK;
-    cfc::FwdArgs a{u_t, h_prev, W, bias, h_t, act_t, h_prev_copy, B, C, n_x, p.CT, p.n_ctiles, p.ldz};
+    cfc::FwdArgs a{u_t, h_prev, W, bias, h_t, act_t, h_prev_copy, B, C, n_x, p.CT, p.n_ctiles, p.ldu, p.ldh};
     CFC_HIP(cfc::launch_fwd(a, p, s), "forward step launch");
     return CFC_OK;
 }
@@ -148,7 +150,9 @@ int enqueue_reduce(const cfc::ReduceSeg* segs_in, int nseg, int64_t B, hipStream
     return CFC_OK;
 }
 
-int64_t kloop_ws_floats(int B, int C, int K) { return (int64_t)K * B * 3 * C + (int64_t)2 * B * C; }
+// Workspace: dp [K, B, 3C] | X [K, B, 3C] (input projection, persistent
+// path) | dh ping-pong [2, B, C] (step path).
+int64_t kloop_ws_floats(int B, int C, int K) { return (int64_t)2 * K * B * 3 * C + (int64_t)2 * B * C; }
 
 struct KloopArgs {
     const float *u, *y, *h0, *W, *bias;
@@ -161,7 +165,8 @@ std::atomic<int> g_kloop_mode{CFC_KLOOP_AUTO};
 bool use_persistent(int mode, int C, int n_x)
 {
     if (mode == CFC_KLOOP_STEPS) return false;
-    return cfc::persist_smem(C, n_x) != 0;
+    (void)n_x;   // the input projection runs outside the persistent kernel
+    return cfc::persist_smem(C) != 0;
 }
 
 // Forward t = 1..K and backward t = K..1 of every sample, storing dp_t.
@@ -173,9 +178,13 @@ int enqueue_fwd_bwd(const KloopArgs& k, bool persistent, const cfc::StepPlan& p,
     const int64_t BC = (int64_t)k.B * k.C;
     const int64_t BX = (int64_t)k.B * k.n_x;
     float* dp = k.ws;                                   // [K, B, 3C]
-    float* dh_ws = k.ws + (int64_t)k.K * 3 * BC;        // [2, B, C]
+    float* X = k.ws + (int64_t)k.K * 3 * BC;            // [K, B, 3C]
+    float* dh_ws = k.ws + (int64_t)2 * k.K * 3 * BC;    // [2, B, C]
     if (persistent) {
-        const cfc::PersistArgs a{k.u, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
+        const cfc::XprojArgs x{k.u, k.W, k.bias, X, (int64_t)k.K * k.B, 3 * k.C, k.n_x, k.n_x + k.C,
+                               (3 * k.C + 63) / 64};
+        CFC_HIP(cfc::launch_xproj(x, s), "input projection launch");
+        const cfc::PersistArgs a{X, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
         CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch");
         return CFC_OK;
     }
@@ -418,7 +427,7 @@ static int check_kloop(const char* fn, const float* u, const float* y, const flo
     const int mode = g_kloop_mode.load();
     *persistent = use_persistent(mode, C, n_x);
     if (mode == CFC_KLOOP_PERSISTENT && !*persistent)
-        return fail(CFC_EINVAL, "%s: the persistent kernel cannot hold W of C=%d n_x=%d", fn, C, n_x);
+        return fail(CFC_EINVAL, "%s: the persistent kernel holds C <= 128 channels (C=%d)", fn, C);
     if (!*persistent)
         if (int rc = check_plan(make_plan(B, C, n_x, W, gW_scratch))) return rc;
     return CFC_OK;

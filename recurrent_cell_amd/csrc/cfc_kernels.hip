@@ -51,86 +51,212 @@ __device__ __forceinline__ void stage_z(float* zs, int ldz, const float* __restr
 // ---------------------------------------------------------------------------
 // Forward step.  Workgroup = (sample tile of BT, channel tile of CT).
 // Rows of the tile: r = q * nc + cl  (head q, channel c0 + cl), 3 * nc rows.
-// A 16-lane DPP row owns one W row at a time; lane j takes the canonical
-// columns k = 64 i + 4 j + e.  The W element is loaded once for all BT
-// samples.  V = 4 reads W with float4 (only the load width differs).
+// An 8-lane group (half a DPP row) owns one W row at a time, for all BT
+// samples: lane j runs the recurrent chain P_j over the columns
+// n_x + 32 i + 4 j + e, and lanes 0..3 the input chains x_0 .. x_3 (input
+// columns k = j mod 4); sum8 and quad_sum4 combine them in the canonical
+// order.  u and h are staged in separate LDS rows so the recurrent columns
+// start 16-byte aligned whatever n_x is.  V = 4 reads W with float4 (only
+// the load width differs).
 // ---------------------------------------------------------------------------
 template <int BT, int V>
 __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a)
 {
-    extern __shared__ float smem[];
-    const int n_in = a.n_x + a.C;
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int n_x = a.n_x;
+    const int C = a.C;
+    const int n_in = n_x + C;
     const int ctile = blockIdx.x % a.n_ctiles;
     const int btile = blockIdx.x / a.n_ctiles;
     const int b0 = btile * BT;
     const int c0 = ctile * a.CT;
     const int nb = min(BT, a.B - b0);
-    const int nc = min(a.CT, a.C - c0);
-    float* zs = smem;                  // [BT][ldz]
-    float* as = smem + BT * a.ldz;     // [BT][3][CT] pre-activations
+    const int nc = min(a.CT, C - c0);
+    const int ldu = a.ldu;
+    const int ldh = a.ldh;
+    float* us = smem;                  // [BT][ldu]  u_t rows
+    float* hs = us + BT * ldu;         // [BT][ldh]  h_prev rows, zero past C
+    float* as = hs + BT * ldh;         // [BT][3][CT] pre-activations
 
-    stage_z<BT>(zs, a.ldz, a.u_t, a.h_prev, b0, nb, a.C, a.n_x);
+    for (int i = threadIdx.x; i < BT * ldu; i += kThreads) {
+        const int s = i / ldu;
+        const int k = i - s * ldu;
+        us[i] = (s < nb && k < n_x) ? a.u_t[((int64_t)b0 + s) * n_x + k] : 0.0f;
+    }
+    for (int i = threadIdx.x; i < BT * ldh; i += kThreads) {
+        const int s = i / ldh;
+        const int m = i - s * ldh;
+        hs[i] = (s < nb && m < C) ? a.h_prev[((int64_t)b0 + s) * C + m] : 0.0f;
+    }
     if (a.h_prev_copy != nullptr && ctile == 0) {
-        for (int i = threadIdx.x; i < nb * a.C; i += kThreads) {
-            const int64_t idx = (int64_t)b0 * a.C + i;
+        for (int i = threadIdx.x; i < nb * C; i += kThreads) {
+            const int64_t idx = (int64_t)b0 * C + i;
             a.h_prev_copy[idx] = a.h_prev[idx];
         }
     }
     __syncthreads();
 
-    const int grp = threadIdx.x / kGroup;
-    const int ln = threadIdx.x % kGroup;
+    const int grp = threadIdx.x / kHLanes;
+    const int j = threadIdx.x % kHLanes;
+    constexpr int kRowGroups = kThreads / kHLanes;
     const int rows = 3 * nc;
-    for (int r = grp; r < rows; r += kGroups) {
-        // r is uniform over the 16 lanes of the DPP row.
+    for (int r = grp; r < rows; r += kRowGroups) {
+        // r is uniform over the 8 lanes of the group.
         const int q = r / nc;
         const int cl = r - q * nc;
-        const float* __restrict__ wrow = a.W + ((int64_t)q * a.C + c0 + cl) * n_in;
-        float acc[BT];
+        const int wr = q * C + c0 + cl;
+        const float* __restrict__ wrow = a.W + (int64_t)wr * n_in;
+        float hacc[BT], xacc[BT];
 #pragma unroll
-        for (int s = 0; s < BT; ++s) acc[s] = 0.0f;
-        for (int k0 = 4 * ln; k0 < n_in; k0 += 4 * kGroup) {
+        for (int s = 0; s < BT; ++s) hacc[s] = xacc[s] = 0.0f;
+        for (int m0 = 4 * j; m0 < C; m0 += 4 * kHLanes) {
             if constexpr (V == 4) {
-                const float4 w = *reinterpret_cast<const float4*>(wrow + k0);
+                const float4 w = *reinterpret_cast<const float4*>(wrow + n_x + m0);
 #pragma unroll
                 for (int s = 0; s < BT; ++s) {
-                    const float4 z = *reinterpret_cast<const float4*>(zs + s * a.ldz + k0);
-                    acc[s] = fmaf(w.x, z.x, acc[s]);
-                    acc[s] = fmaf(w.y, z.y, acc[s]);
-                    acc[s] = fmaf(w.z, z.z, acc[s]);
-                    acc[s] = fmaf(w.w, z.w, acc[s]);
+                    const float4 z = *reinterpret_cast<const float4*>(hs + s * ldh + m0);
+                    hacc[s] = fmaf(w.x, z.x, hacc[s]);
+                    hacc[s] = fmaf(w.y, z.y, hacc[s]);
+                    hacc[s] = fmaf(w.z, z.z, hacc[s]);
+                    hacc[s] = fmaf(w.w, z.w, hacc[s]);
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (k0 + e < n_in) {
-                        const float w = wrow[k0 + e];
+                    if (m0 + e < C) {
+                        const float w = wrow[n_x + m0 + e];
 #pragma unroll
-                        for (int s = 0; s < BT; ++s) acc[s] = fmaf(w, zs[s * a.ldz + k0 + e], acc[s]);
+                        for (int s = 0; s < BT; ++s) hacc[s] = fmaf(w, hs[s * ldh + m0 + e], hacc[s]);
                     }
                 }
             }
         }
-        const float bq = a.bias[q * a.C + c0 + cl];
+        if (j < 4) {
+            for (int k = j; k < n_x; k += 4) {
+                const float w = wrow[k];
+#pragma unroll
+                for (int s = 0; s < BT; ++s) xacc[s] = fmaf(w, us[s * ldu + k], xacc[s]);
+            }
+        }
+        const float bq = a.bias[wr];
 #pragma unroll
         for (int s = 0; s < BT; ++s) {
-            const float v = row_sum16(acc[s]);
-            if (ln == 0) as[(s * 3 + q) * a.CT + cl] = v + bq;
+            const float hsum = sum8(hacc[s]);
+            const float xsum = bq + quad_sum4(xacc[s]);
+            if (j == 0) as[(s * 3 + q) * a.CT + cl] = xsum + hsum;
         }
     }
     __syncthreads();
 
-    const int64_t BC = (int64_t)a.B * a.C;
+    const int64_t BC = (int64_t)a.B * C;
     for (int i = threadIdx.x; i < nb * nc; i += kThreads) {
         const int s = i / nc;
         const int cl = i - s * nc;
-        const int64_t bc = ((int64_t)b0 + s) * a.C + c0 + cl;
+        const int64_t bc = ((int64_t)b0 + s) * C + c0 + cl;
         const CellOut o = cell_forward(as[(s * 3 + 0) * a.CT + cl], as[(s * 3 + 1) * a.CT + cl],
                                        as[(s * 3 + 2) * a.CT + cl]);
         a.h_t[bc] = o.h;
         a.act_t[bc] = o.gate;
         a.act_t[BC + bc] = o.g;
         a.act_t[2 * BC + bc] = o.hh;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Input projection of the K-loop, all steps at once (fp32 MFMA):
+//   X[row, r] = bias[r] + ((x_0 + x_1) + (x_2 + x_3)),
+//   x_c = fma chain of W[r, k] u[row, k] over k = c, c + 4, .. (< n_x),
+// rows (t, b) of u [K B, n_x], outputs r < 3C.  v_mfma_f32_16x16x4f32
+// accumulates its four k in order as an fma chain, so chain c takes the
+// columns 16 p + 4 kk + c in k-slot kk of its p-th instruction: every lane
+// loads the float4 u[row, 16 p + 4 kk ..] and W[r, 16 p + 4 kk ..] once and
+// feeds component c to chain c.  Operand layout (16 x 16 x 4): lane l holds
+// A[l % 16][l / 16] and B[l / 16][l % 16]; D[i][j] sits in lane
+// j + 16 (i / 4), register i % 4.  Workgroup: 64 rows x 64 outputs, four
+// waves of 32 x 32 (2 x 2 MFMA tiles, 4 chains each).  The chains start
+// from +0 and zero padding past n_x leaves them unchanged.
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ntile = (int)(blockIdx.x % (unsigned)a.n_ntiles);
+    const int64_t mtile = blockIdx.x / (unsigned)a.n_ntiles;
+    const int64_t m0 = mtile * 64 + (wave >> 1) * 32;
+    const int n0 = ntile * 64 + (wave & 1) * 32;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int n_x = a.n_x;
+    const int64_t M = a.M;
+    const int N = a.N;
+
+    f32x4 acc[2][2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[mt][nt][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int k0 = 0; k0 < n_x; k0 += 16) {
+        const int k = k0 + 4 * lk;
+        f32x4 av[2], bv[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int64_t row = m0 + 16 * mt + li;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (row < M) {
+                const float* src = a.u + row * n_x + k;
+                if (VEC) {
+                    if (k < n_x) v = *reinterpret_cast<const f32x4*>(src);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (k + e < n_x) v[e] = src[e];
+                }
+            }
+            av[mt] = v;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int r = n0 + 16 * nt + li;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (r < N) {
+                const float* src = a.W + (int64_t)r * a.n_in + k;
+                if (VEC) {
+                    if (k < n_x) v = *reinterpret_cast<const f32x4*>(src);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (k + e < n_x) v[e] = src[e];
+                }
+            }
+            bv[nt] = v;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][c], bv[nt][c], acc[mt][nt][c], 0, 0, 0);
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int r = n0 + 16 * nt + li;
+        if (r >= N) continue;
+        const float bias = a.bias[r];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + 16 * mt + 4 * lk + i;
+                if (row < M)
+                    a.X[row * N + r] = xproj_combine(bias, acc[mt][nt][0][i], acc[mt][nt][1][i], acc[mt][nt][2][i],
+                                                     acc[mt][nt][3][i]);
+            }
     }
 }
 
@@ -396,48 +522,52 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Persistent K-loop kernel: workgroup b runs sample b's whole step.
-// The workgroup has 64 / GPR DPP rows of 16 lanes; row r owns canonical dz
-// groups GPR r .. GPR r + GPR - 1, i.e. the CPR = GPR cpg consecutive
-// channels starting at CPR r, all three heads.  Their W rows sit in
-// registers as lane j's canonical forward columns 64 i + 4 j + e.
+// Persistent K-loop kernel: workgroup b runs sample b's whole step; the input
+// projection X = W_x u + bias of every step comes precomputed (xproj_kernel),
+// so the recurrence only carries the recurrent columns.
+// 512 lanes = 64 groups of 8 (half a DPP row).  Group g is canonical dz group
+// g: channels g CPG .. g CPG + CPG - 1, all three heads.  Their recurrent W
+// columns sit in registers as lane j's canonical columns 32 i + 4 j + e.
+// Quad jq of the group looks after channel g CPG + jq; lane fn of the quad
+// evaluates the channel's nonlinearity fn (gate, g, hh) in the forward and
+// sums the interleaved dz subtree fn of its column in the backward.
 // The step loops touch no global memory.  Steps run in chunks; at each chunk
 // boundary the workgroup
 //   - moves the chunk's inputs into LDS from registers, where they were
-//     loaded during the previous chunk (u for the forward; gate, g, hh, h_t,
-//     y_t for the backward),
+//     loaded during the previous chunk (X rows for the forward; gate, g, hh,
+//     h_t, y_t for the backward),
 //   - writes the previous chunk's outputs from LDS to memory with coalesced
 //     16-byte stores (h_t and (gate, g, hh); dp_t),
 //   - issues the loads of the next chunk's inputs,
 // so every wait on memory at a boundary is for operations a whole chunk old.
 // Inside a chunk a step is LDS traffic, DPP, arithmetic and one LDS-only
 // barrier.
-//  forward, per t : the 3 CPR dot products of the row (row_sum16 leaves every
-//                   lane with every sum); lane j < CPR applies the cell to
-//                   channel CPR r + j, writes h_t into the next z buffer and
-//                   (h_t, gate, g, hh) into the chunk's output buffer.
-//  backward, per t: quad cc (lanes 4 cc .. 4 cc + 3) computes dp of channel
-//                   CPR r + cc from the carry it summed itself; the row reads
-//                   every dp back with ds_swizzle; lane 4 cc puts dp into the
-//                   chunk's output buffer; the partials P_g of each of the
-//                   row's groups (carry columns) go to a double-buffered LDS
-//                   block; after the barrier quad cc sums column
-//                   n_x + CPR r + cc over the 64 groups (lane q of the quad:
-//                   tree_sum16 over groups q, q+4, ..; then quad_sum4).
+//  forward, per t : 3 CPG recurrent chains per lane; sum8 leaves every lane
+//                   of the group with every H; lane fn of quad jq forms
+//                   a = X + H of (head fn, its channel) and the nonlinearity;
+//                   the quad exchanges the three by DPP and forms h_t, which
+//                   goes into the next z buffer and, with (gate, g, hh), into
+//                   the chunk's output buffer.
+//  backward, per t: quad jq computes dp of its channel from the carry it
+//                   summed itself; the group reads both channels' dp back
+//                   with ds_swizzle; the group's partial P_g over the carry
+//                   columns goes to a double-buffered LDS block; after the
+//                   barrier lane fn of quad jq sums subtree fn of its
+//                   channel's column (groups fn, fn + 4, ..) and quad_sum4
+//                   completes the carry.
 // ---------------------------------------------------------------------------
 constexpr int kFwdChunk = 16;
 constexpr int kBwdChunk = 8;
 
-template <int CPG, int GPR, int NI>
+template <int CPG, int NH>
 struct PersistLds {
-    static constexpr int CPR = CPG * GPR;
-    static constexpr int ZW = NI * 64;
-    static constexpr int ZWP = ZW + 8;           // partial row pitch: 8 banks between group rows
-    static constexpr int CMAX = 64 * CPG;
-    static constexpr int STAGE = (5 * CMAX * kBwdChunk > ZW * kFwdChunk) ? 5 * CMAX * kBwdChunk : ZW * kFwdChunk;
-    static constexpr int DBUF = kBwdChunk * 3 * CMAX;
-    static constexpr size_t BYTES = sizeof(float) * (2 * ZW + 2 * kDzGroups * ZWP + STAGE + DBUF);
-    static_assert(4 * CMAX * kFwdChunk <= 2 * kDzGroups * ZWP, "forward output buffer fits in the partials");
+    static constexpr int HW = 32 * NH;           // recurrent columns held (>= C)
+    static constexpr int HWP = HW + 8;           // partial row pitch: 8 banks between group rows
+    static constexpr int STAGE = (5 * HW * kBwdChunk > 3 * HW * kFwdChunk) ? 5 * HW * kBwdChunk : 3 * HW * kFwdChunk;
+    static constexpr int DBUF = kBwdChunk * 3 * HW;
+    static constexpr size_t BYTES = sizeof(float) * (2 * HW + 2 * kDzGroups * HWP + STAGE + DBUF);
+    static_assert(4 * HW * kFwdChunk <= 2 * kDzGroups * HWP, "forward output buffer fits in the partials");
+    static_assert(HW <= 64 * CPG, "every channel belongs to a group");
 };
 
 // Coalesced move of `rows` rows of `len` floats between LDS (row pitch len)
@@ -468,93 +598,101 @@ __device__ __forceinline__ void move_rows(float* lds, int rows, int len, bool ve
     }
 }
 
-template <int CPG, int GPR, int NI>
-__global__ __launch_bounds__(1024 / GPR) void kloop_persist_kernel(PersistArgs a)
+// Lane SRC (0..7) of this lane's aligned 8-lane group (ds_swizzle bit mode:
+// and_mask 0x18 keeps the group within the 32-lane half, or_mask picks SRC).
+template <int SRC>
+__device__ __forceinline__ float group_bcast(float v)
 {
-    using L = PersistLds<CPG, GPR, NI>;
-    constexpr int THREADS = 1024 / GPR;
-    constexpr int CPR = L::CPR;
-    constexpr int ZW = L::ZW;
-    constexpr int ZWP = L::ZWP;
-    static_assert(CPR <= 4, "one quad per channel of a row");
-    __shared__ __attribute__((aligned(16))) float zs[2][ZW];
-    __shared__ __attribute__((aligned(16))) float part[2][kDzGroups][ZWP];
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x18 | (SRC << 5)));
+}
+
+template <int CPG, int NH>
+__global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistArgs a)
+{
+    using L = PersistLds<CPG, NH>;
+    constexpr int THREADS = kPersistThreads;
+    constexpr int HW = L::HW;
+    constexpr int HWP = L::HWP;
+    static_assert(THREADS == kDzGroups * kHLanes, "one 8-lane group per canonical dz group");
+    __shared__ __attribute__((aligned(16))) float zs[2][HW];
+    __shared__ __attribute__((aligned(16))) float part[2][kDzGroups][HWP];
     __shared__ __attribute__((aligned(16))) float stage[L::STAGE];
     __shared__ __attribute__((aligned(16))) float dbuf[L::DBUF];
     float* obuf = &part[0][0][0];   // forward output buffer [kFwdChunk][4][C] (partials unused then)
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int row = tid >> 4;
-    const int j = tid & 15;
+    const int g = tid >> 3;          // canonical dz group
+    const int j = tid & 7;           // lane of the group: recurrent columns 32 i + 4 j + e
+    const int jq = j >> 2;           // quad of the group
+    const int fn = j & 3;            // lane of the quad
     const int C = a.C;
     const int n_x = a.n_x;
     const int n_in = n_x + C;
     const int B = a.B;
     const int K = a.K;
     const int R3 = 3 * C;
-    const int c0 = row * CPR;
-    const int ncr = max(0, min(CPR, C - c0));   // channels of this row
+    const int cq = g * CPG + jq;                 // the quad's channel
+    const bool q_ok = (jq < CPG) && (cq < C);
+    const int cqc = min(cq, C - 1);              // clamped for addressing
     const int64_t BC = (int64_t)B * C;
-    const int i0 = n_x / 64;                     // first column block holding carry columns
-    const bool wvec = (n_in % 4 == 0) && ((((uintptr_t)a.W) & 15u) == 0);
+    const bool wvec = (n_x % 4 == 0) && (n_in % 4 == 0) && ((((uintptr_t)a.W) & 15u) == 0);
     // 16-byte moves need rows of a multiple of 4 floats on 16-byte aligned arrays
-    const bool u_vec = (n_x % 4 == 0) && ((((uintptr_t)a.u) & 15u) == 0);
     const bool c_vec = (C % 4 == 0) && ((((uintptr_t)a.act) | ((uintptr_t)a.h_hist) | ((uintptr_t)a.y) |
-                                          ((uintptr_t)a.dp)) & 15u) == 0;
+                                          ((uintptr_t)a.dp) | ((uintptr_t)a.X)) & 15u) == 0;
 
-    float w[CPR][3][NI][4];
-    float bq[CPR][3];
+    float w[CPG][3][NH][4];
 #pragma unroll
-    for (int cc = 0; cc < CPR; ++cc)
+    for (int cl = 0; cl < CPG; ++cl)
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            const bool ok = cc < ncr;
-            const int r = q * C + c0 + cc;
-            bq[cc][q] = ok ? a.bias[r] : 0.0f;
+            const int c = g * CPG + cl;
+            const bool ok = c < C;
+            const float* wrow = a.W + (int64_t)(q * C + min(c, C - 1)) * n_in + n_x;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int k = 64 * i + 4 * j;
-                if (ok && wvec && k < n_in) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(a.W + (int64_t)r * n_in + k);
-                    w[cc][q][i][0] = v.x;
-                    w[cc][q][i][1] = v.y;
-                    w[cc][q][i][2] = v.z;
-                    w[cc][q][i][3] = v.w;
+            for (int i = 0; i < NH; ++i) {
+                const int m = 32 * i + 4 * j;
+                if (ok && wvec && m < C) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(wrow + m);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[cl][q][i][e] = v[e];
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[cc][q][i][e] = (ok && k + e < n_in) ? a.W[(int64_t)r * n_in + k + e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) w[cl][q][i][e] = (ok && m + e < C) ? wrow[m + e] : 0.0f;
                 }
             }
         }
-    for (int i = tid; i < 2 * ZW; i += THREADS) (&zs[0][0])[i] = 0.0f;
+    for (int i = tid; i < 2 * HW; i += THREADS) (&zs[0][0])[i] = 0.0f;
     __syncthreads();
     for (int c = tid; c < C; c += THREADS) {
         const float h = a.h0[(int64_t)b * C + c];
-        zs[0][n_x + c] = h;
+        zs[0][c] = h;
         a.h_hist[(int64_t)b * C + c] = h;
     }
 
     // ---------------- forward ----------------
-    // u prefetch into registers: a lane moves one float4 of one staged row of
-    // n_x floats per pass, on a map computed once (16-byte path only).
-    const int u_w = n_x / 4;
-    const int u_col = u_w > 0 ? tid % u_w : 0;
-    const int u_row0 = u_w > 0 ? tid / u_w : kFwdChunk;
-    const int u_rstep = u_w > 0 ? THREADS / u_w : 1;
-    constexpr int UPF = (kFwdChunk * 16 * NI + THREADS - 1) / THREADS;
-    f32x4 upf[UPF];
-    auto load_u = [&](int t0, int nt) {
+    // X prefetch into registers: a lane moves one float4 of one staged row
+    // of 3C floats per pass, on a map computed once (16-byte path only).
+    // A row is x_w <= 3 HW / 4 float4; the lanes cover x_rstep rows per pass.
+    const int x_w = R3 / 4;
+    const int x_col = x_w > 0 ? tid % x_w : 0;
+    const int x_row0 = x_w > 0 ? tid / x_w : kFwdChunk;
+    const int x_rstep = x_w > 0 ? THREADS / x_w : 1;
+    constexpr int XRS_MIN = THREADS / (3 * HW / 4);
+    constexpr int XPF = (kFwdChunk + XRS_MIN - 1) / XRS_MIN;
+    f32x4 xpf[XPF];
+    auto x_row = [&](int t0) {
+        return [=](int rr) { return const_cast<float*>(a.X) + ((int64_t)(t0 - 1 + rr) * B + b) * R3; };
+    };
+    auto load_x = [&](int t0, int nt) {
+        const auto src = x_row(t0);
 #pragma unroll
-        for (int m = 0; m < UPF; ++m) {
-            const int rr = u_row0 + m * u_rstep;
+        for (int m = 0; m < XPF; ++m) {
+            const int rr = x_row0 + m * x_rstep;
             f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (u_row0 < u_rstep && rr < nt)
-                v = *reinterpret_cast<const f32x4*>(a.u + ((int64_t)(t0 - 1 + rr) * B + b) * n_x + 4 * u_col);
-            upf[m] = v;
+            if (x_row0 < x_rstep && rr < nt) v = *reinterpret_cast<const f32x4*>(src(rr) + 4 * x_col);
+            xpf[m] = v;
         }
     };
-    auto u_row = [&](int t0) { return [=](int rr) { return const_cast<float*>(a.u) + ((int64_t)(t0 - 1 + rr) * B + b) * n_x; }; };
     auto out_row = [&](int t0) {
         return [=](int rr) {
             const int t = t0 + (rr >> 2);
@@ -563,64 +701,59 @@ __global__ __launch_bounds__(1024 / GPR) void kloop_persist_kernel(PersistArgs a
                    (int64_t)b * C;
         };
     };
-    if (u_vec && K >= 1) load_u(1, min(kFwdChunk, K));
+    if (c_vec && K >= 1) load_x(1, min(kFwdChunk, K));
     int prev_t0 = 0, prev_nt = 0;
     for (int t0 = 1; t0 <= K; t0 += kFwdChunk) {
         const int nt = min(kFwdChunk, K - t0 + 1);
-        if (u_vec) {
+        if (c_vec) {
 #pragma unroll
-            for (int m = 0; m < UPF; ++m) {
-                const int rr = u_row0 + m * u_rstep;
-                if (u_row0 < u_rstep && rr < nt)
-                    *reinterpret_cast<f32x4*>(stage + rr * n_x + 4 * u_col) = upf[m];
+            for (int m = 0; m < XPF; ++m) {
+                const int rr = x_row0 + m * x_rstep;
+                if (x_row0 < x_rstep && rr < nt)
+                    *reinterpret_cast<f32x4*>(stage + rr * R3 + 4 * x_col) = xpf[m];
             }
         } else {
-            move_rows<THREADS, false>(stage, nt, n_x, false, u_row(t0));
+            move_rows<THREADS, false>(stage, nt, R3, false, x_row(t0));
         }
         if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, c_vec, out_row(prev_t0));
-        if (u_vec && t0 + kFwdChunk <= K) load_u(t0 + kFwdChunk, min(kFwdChunk, K - t0 - kFwdChunk + 1));
-        lds_barrier();
-        for (int k = tid; k < n_x; k += THREADS) zs[(t0 - 1) & 1][k] = stage[k];
+        if (c_vec && t0 + kFwdChunk <= K) load_x(t0 + kFwdChunk, min(kFwdChunk, K - t0 - kFwdChunk + 1));
         lds_barrier();
         for (int tt = 0; tt < nt; ++tt) {
             const int t = t0 + tt;
             const float* zc = zs[(t - 1) & 1];
             float* zn = zs[t & 1];
-            f32x4 zv[NI];
+            const float xv = stage[tt * R3 + min(fn, 2) * C + cqc];
+            f32x4 zv[NH];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) zv[i] = *reinterpret_cast<const f32x4*>(zc + 64 * i + 4 * j);
-            float av[CPR][3];
+            for (int i = 0; i < NH; ++i) zv[i] = *reinterpret_cast<const f32x4*>(zc + 32 * i + 4 * j);
+            float hs[CPG][3];
 #pragma unroll
-            for (int cc = 0; cc < CPR; ++cc)
+            for (int cl = 0; cl < CPG; ++cl)
 #pragma unroll
                 for (int q = 0; q < 3; ++q) {
                     float p = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < NI; ++i)
+                    for (int i = 0; i < NH; ++i)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) p = fmaf(w[cc][q][i][e], zv[i][e], p);
-                    av[cc][q] = row_sum16(p);
+                        for (int e = 0; e < 4; ++e) p = fmaf(w[cl][q][i][e], zv[i][e], p);
+                    hs[cl][q] = sum8(p);
                 }
-            if (j < ncr) {
-                float af = av[0][0] + bq[0][0], ag = av[0][1] + bq[0][1], ah = av[0][2] + bq[0][2];
+            float hsel = hs[0][2];
 #pragma unroll
-                for (int cc = 1; cc < CPR; ++cc)
-                    if (j == cc) {
-                        af = av[cc][0] + bq[cc][0];
-                        ag = av[cc][1] + bq[cc][1];
-                        ah = av[cc][2] + bq[cc][2];
-                    }
-                const CellOut o = cell_forward(af, ag, ah);
-                const int c = c0 + j;
-                zn[n_x + c] = o.h;
-                float* ob = obuf + (tt * 4) * C + c;
-                ob[0] = o.h;
-                ob[C] = o.gate;
-                ob[2 * C] = o.g;
-                ob[3 * C] = o.hh;
+            for (int cl = 0; cl < CPG; ++cl)
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    if (jq == cl && fn == q) hsel = hs[cl][q];
+            const float v = cell_fn(fn, xv + hsel);
+            const float h = cell_h(quad_bcast<0>(v), quad_bcast<1>(v), quad_bcast<2>(v));
+            if (q_ok) {
+                float* ob = obuf + (tt * 4) * C + cq;
+                if (fn == 0) {
+                    zn[cq] = h;
+                    ob[0] = h;
+                }
+                if (fn < 3) ob[(1 + fn) * C] = v;
             }
-            if (tt + 1 < nt)
-                for (int k = tid; k < n_x; k += THREADS) zn[k] = stage[(tt + 1) * n_x + k];
             lds_barrier();
         }
         prev_t0 = t0;
@@ -636,7 +769,8 @@ __global__ __launch_bounds__(1024 / GPR) void kloop_persist_kernel(PersistArgs a
     const int c_col = c_w > 0 ? tid % c_w : 0;
     const int c_row0 = c_w > 0 ? tid / c_w : 5 * kBwdChunk;
     const int c_rstep = c_w > 0 ? THREADS / c_w : 1;
-    constexpr int BPF = (5 * kBwdChunk * 16 * CPG + THREADS - 1) / THREADS;
+    constexpr int CRS_MIN = THREADS / (HW / 4);
+    constexpr int BPF = (5 * kBwdChunk + CRS_MIN - 1) / CRS_MIN;
     f32x4 bpf[BPF];
     auto in_row = [&](int t1) {
         return [=](int rr) {
@@ -662,7 +796,7 @@ __global__ __launch_bounds__(1024 / GPR) void kloop_persist_kernel(PersistArgs a
         }
     };
     if (c_vec && K >= 1) load_b(K, min(kBwdChunk, K));
-    float carry_mine = 0.0f;   // quad cc: carry of channel c0 + cc
+    float carry_mine = 0.0f;   // the carry of the quad's channel
     int prev_t1 = 0;
     prev_nt = 0;
     for (int t1 = K; t1 >= 1; t1 -= kBwdChunk) {
@@ -683,69 +817,44 @@ __global__ __launch_bounds__(1024 / GPR) void kloop_persist_kernel(PersistArgs a
             const int t = t1 - tt;
             const int buf = t & 1;
             const float* st = stage + tt * 5 * C;
-            const int my_cc = min(j >> 2, CPR - 1);
-            const int my_c = min(c0 + my_cc, C - 1);
             float mdp[3];
             {
-                float dh = st[3 * C + my_c] - st[4 * C + my_c];
+                float dh = st[3 * C + cqc] - st[4 * C + cqc];
                 if (t < K) dh += carry_mine;
-                cell_backward(dh, st[my_c], st[C + my_c], st[2 * C + my_c], mdp[0], mdp[1], mdp[2]);
+                cell_backward(dh, st[cqc], st[C + cqc], st[2 * C + cqc], mdp[0], mdp[1], mdp[2]);
             }
-            float dp[CPR][3];
+            float dp[CPG][3];
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
-                dp[0][q] = row_bcast<0>(mdp[q]);
-                if (CPR > 1) dp[1][q] = row_bcast<4>(mdp[q]);
-                if (CPR > 2) dp[2][q] = row_bcast<8>(mdp[q]);
-                if (CPR > 3) dp[3][q] = row_bcast<12>(mdp[q]);
+                dp[0][q] = group_bcast<0>(mdp[q]);
+                if (CPG > 1) dp[CPG - 1][q] = group_bcast<4>(mdp[q]);
             }
 #pragma unroll
-            for (int cc = 0; cc < CPR; ++cc)
-                if (cc >= ncr) dp[cc][0] = dp[cc][1] = dp[cc][2] = 0.0f;
-            if ((j & 3) == 0 && (j >> 2) < ncr) {
-                float* db = dbuf + tt * R3 + c0 + (j >> 2);
-                db[0] = mdp[0];
-                db[C] = mdp[1];
-                db[2 * C] = mdp[2];
-            }
-            // Partials of the row's groups over the carry columns (blocks
-            // i >= i0; the K-loop produces no du).  Absent channels carry
-            // W = 0 and dp = 0, and fma(0, 0, P) == P exactly (P is never -0),
-            // so the chains need no per-channel branches.
-            float P[GPR][NI][4];
+            for (int cl = 0; cl < CPG; ++cl)
+                if (g * CPG + cl >= C) dp[cl][0] = dp[cl][1] = dp[cl][2] = 0.0f;
+            if (q_ok && fn < 3) dbuf[tt * R3 + fn * C + cq] = (fn == 0) ? mdp[0] : (fn == 1) ? mdp[1] : mdp[2];
+            // Partial of the group over the carry columns.  Absent channels
+            // carry W = 0 and dp = 0, and fma(0, 0, P) == P exactly (P is
+            // never -0), so the chains need no per-channel branches.
 #pragma unroll
-            for (int gi = 0; gi < GPR; ++gi)
+            for (int i = 0; i < NH; ++i) {
+                float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
+                for (int cl = 0; cl < CPG; ++cl)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) P[gi][i][e] = 0.0f;
+                    for (int q = 0; q < 3; ++q)
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                if (i >= i0) {   // uniform: i0 comes from n_x
-#pragma unroll
-                    for (int cl = 0; cl < CPG; ++cl)
-#pragma unroll
-                        for (int q = 0; q < 3; ++q)
-#pragma unroll
-                            for (int gi = 0; gi < GPR; ++gi)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    P[gi][i][e] = fmaf(w[gi * CPG + cl][q][i][e], dp[gi * CPG + cl][q], P[gi][i][e]);
-#pragma unroll
-                    for (int gi = 0; gi < GPR; ++gi) {
-                        f32x4 v;
-                        v.x = P[gi][i][0];
-                        v.y = P[gi][i][1];
-                        v.z = P[gi][i][2];
-                        v.w = P[gi][i][3];
-                        *reinterpret_cast<f32x4*>(&part[buf][row * GPR + gi][64 * i + 4 * j]) = v;
-                    }
-                }
+                        for (int e = 0; e < 4; ++e) P[e] = fmaf(w[cl][q][i][e], dp[cl][q], P[e]);
+                f32x4 v;
+                v.x = P[0];
+                v.y = P[1];
+                v.z = P[2];
+                v.w = P[3];
+                *reinterpret_cast<f32x4*>(&part[buf][g][32 * i + 4 * j]) = v;
             }
             lds_barrier();
-            if ((j >> 2) < CPR) {   // uniform over each quad
-                const int col = n_x + min(c0 + (j >> 2), C - 1);
-                const float v = tree_sum16(&part[buf][j & 3][col], 4 * ZWP);
+            if (jq < CPG) {   // uniform over each quad
+                const float v = tree_sum16(&part[buf][fn][cqc], 4 * HWP);
                 carry_mine = quad_sum4(v);
             }
         }
@@ -870,32 +979,24 @@ hipError_t launch_bwd_bt(const BwdArgs& a, const StepPlan& p, hipStream_t s)
     return hipGetLastError();
 }
 
-// Persistent-kernel instantiations: CPG channels per canonical group
-// (C <= 64 CPG), two groups per DPP row (512 lanes), NI column blocks of 64
-// (n_in <= 64 NI); 24 CPG NI W values per lane.
+// Persistent-kernel instantiations: CPG = ceil(C / 64) channels per
+// canonical group, NH = ceil(C / 32) recurrent column blocks of 32;
+// 12 CPG NH W values per lane.
 struct PersistShape {
-    int cpg, ni;
+    int cpg, nh;
 };
 
-bool persist_shape(int C, int n_x, PersistShape& ps)
+bool persist_shape(int C, PersistShape& ps)
 {
-    const int n_in = n_x + C;
-    const int cpg = dz_group_channels(C);
-    const int ni = (n_in + 63) / 64;
-    if ((cpg == 1 && ni <= 4) || (cpg == 2 && ni >= 2 && ni <= 3)) {
-        ps = PersistShape{cpg, ni};
-        return true;
-    }
-    return false;
+    if (C < 1 || C > 128) return false;
+    ps = PersistShape{dz_group_channels(C), (C + 31) / 32};
+    return true;
 }
 
-constexpr int kPersistGPR = 2;
-
-template <int CPG, int NI>
+template <int CPG, int NH>
 hipError_t launch_persist_t(const PersistArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL((kloop_persist_kernel<CPG, kPersistGPR, NI>), dim3((unsigned)a.B),
-                       dim3(1024 / kPersistGPR), 0, s, a);
+    hipLaunchKernelGGL((kloop_persist_kernel<CPG, NH>), dim3((unsigned)a.B), dim3(kPersistThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -910,18 +1011,16 @@ int reduce_slices(int64_t B)
     return R;
 }
 
-size_t persist_smem(int C, int n_x)
+size_t persist_smem(int C)
 {
     PersistShape ps;
-    if (!persist_shape(C, n_x, ps)) return 0;
+    if (!persist_shape(C, ps)) return 0;
 #define CFC_PERSIST_LDS(P_, N_) \
-    if (ps.cpg == P_ && ps.ni == N_) return PersistLds<P_, kPersistGPR, N_>::BYTES;
+    if (ps.cpg == P_ && ps.nh == N_) return PersistLds<P_, N_>::BYTES;
     CFC_PERSIST_LDS(1, 1)
     CFC_PERSIST_LDS(1, 2)
-    CFC_PERSIST_LDS(1, 3)
-    CFC_PERSIST_LDS(1, 4)
-    CFC_PERSIST_LDS(2, 2)
     CFC_PERSIST_LDS(2, 3)
+    CFC_PERSIST_LDS(2, 4)
 #undef CFC_PERSIST_LDS
     return 0;
 }
@@ -957,18 +1056,31 @@ hipError_t launch_fill(const FillArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_xproj(const XprojArgs& a, hipStream_t s)
+{
+    if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    const int64_t mt = (a.M + 63) / 64;
+    const int64_t blocks = mt * a.n_ntiles;
+    if (blocks > 0x7fffffffLL || a.n_ntiles != (a.N + 63) / 64) return hipErrorInvalidValue;
+    const bool vec = (a.n_x % 4 == 0) && (a.n_in % 4 == 0) &&
+                     ((((uintptr_t)a.u) | ((uintptr_t)a.W)) & 15u) == 0;
+    if (vec)
+        hipLaunchKernelGGL((xproj_kernel<true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((xproj_kernel<false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_persist(const PersistArgs& a, hipStream_t s)
 {
     PersistShape ps;
-    if (!persist_shape(a.C, a.n_x, ps) || a.B <= 0) return hipErrorInvalidValue;
+    if (!persist_shape(a.C, ps) || a.B <= 0) return hipErrorInvalidValue;
 #define CFC_PERSIST_CASE(P_, N_) \
-    if (ps.cpg == P_ && ps.ni == N_) return launch_persist_t<P_, N_>(a, s);
+    if (ps.cpg == P_ && ps.nh == N_) return launch_persist_t<P_, N_>(a, s);
     CFC_PERSIST_CASE(1, 1)
     CFC_PERSIST_CASE(1, 2)
-    CFC_PERSIST_CASE(1, 3)
-    CFC_PERSIST_CASE(1, 4)
-    CFC_PERSIST_CASE(2, 2)
     CFC_PERSIST_CASE(2, 3)
+    CFC_PERSIST_CASE(2, 4)
 #undef CFC_PERSIST_CASE
     return hipErrorInvalidValue;
 }

@@ -1,11 +1,17 @@
 // Device arithmetic shared by every kernel of the CfC K-loop.
 //
 // Each output of the library has ONE canonical evaluation order, a function
-// of the sizes (C, n_x, K, B) only.  The per-step kernels, the persistent
-// K-loop kernel and the deferred scratch fill all evaluate through the
-// helpers below, so every path produces the same bits:
-//   a_q[c]   = bias + row_sum16(lane partials); lane j of 16 owns the columns
-//              k = 64 i + 4 j + e (i ascending, e = 0..3), fma chain from +0;
+// of the sizes (C, n_x, K, B) only.  The per-step kernels, the input
+// projection, the persistent K-loop kernel and the deferred scratch fill all
+// evaluate through the helpers below (fp32 MFMA accumulation is the same
+// sequential fma chain in k order), so every path produces the same bits:
+//   X_q[c]   = bias_q[c] + ((x_0 + x_1) + (x_2 + x_3)), x_r = fma chain of
+//              W[q C + c, k] u[k] over the input columns k = r, r+4, r+8, ..
+//              (k < n_x) from +0;
+//   H_q[c]   = sum8 of the lane chains P_0 .. P_7, P_j = fma chain from +0 of
+//              W[q C + c, n_x + m] h[m] over the recurrent columns
+//              m = 32 i + 4 j + e (i ascending, e = 0..3, m < C);
+//   a_q[c]   = X_q[c] + H_q[c];
 //   dz[k]    = over 64 groups of cpg = ceil(C / 64) consecutive channels:
 //              P_g = fma chain of W[q C + c, k] dp_q[c] over the group's
 //              channels c ascending and, within a channel, heads q = 0, 1, 2;
@@ -21,6 +27,7 @@
 namespace cfc {
 
 constexpr int kDzGroups = 64;  // channel groups of the canonical W^T dp sum
+constexpr int kHLanes = 8;     // lanes of one recurrent-column partition (one DPP half row)
 
 __host__ __device__ inline int dz_group_channels(int C) { return (C + kDzGroups - 1) / kDzGroups; }
 
@@ -65,6 +72,23 @@ __device__ __forceinline__ float quad_sum4(float v)
     return v;
 }
 
+// ((v0 + v1) + (v2 + v3)) + ((v4 + v5) + (v6 + v7)) over 8 aligned lanes
+// (half a DPP row; lane 0 holds v0); every lane ends with the same bits.
+__device__ __forceinline__ float sum8(float v)
+{
+    v += dpp_get<kDppQuadXor1>(v);
+    v += dpp_get<kDppQuadXor2>(v);
+    v += dpp_get<kDppRowHalfMirror>(v);
+    return v;
+}
+
+// Value of lane SRC (0..3) of this lane's quad.
+template <int SRC>
+__device__ __forceinline__ float quad_bcast(float v)
+{
+    return dpp_get<SRC * 0x55>(v);
+}
+
 // Value of lane SRC (0..15) of this lane's 16-lane row (ds_swizzle bit mode:
 // and_mask 0x10 keeps the row, or_mask selects the lane).
 template <int SRC>
@@ -99,6 +123,12 @@ __device__ __forceinline__ float tree_sum64(const float* p, int s)
     return (t0 + t1) + (t2 + t3);
 }
 
+// The input projection from its four chains: bias + ((x0 + x1) + (x2 + x3)).
+__device__ __forceinline__ float xproj_combine(float bias, float x0, float x1, float x2, float x3)
+{
+    return bias + ((x0 + x1) + (x2 + x3));
+}
+
 struct CellOut {
     float gate, g, hh, h;
 };
@@ -108,11 +138,23 @@ struct CellOut {
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// tanh(x) = 1 - 2 / (exp(2x) + 1): exact limits +-1 (exp overflowing to inf
-// or underflowing to 0), absolute error a few 1e-8 around 0.
-__device__ __forceinline__ float fast_tanh(float x)
+// One of the cell's three nonlinearities, selected per lane (fn = 0: gate
+// from a_f, 1: g from a_g, 2: hh from a_h), so that a quad can evaluate a
+// channel's three in parallel with the operations of cell_forward:
+// gate = 1 / (exp(a_f) + 1) and tanh(a) = 1 - 2 / (exp(2a) + 1) (exact
+// limits +-1 when exp overflows to inf or underflows to 0; absolute error a
+// few 1e-8 around 0).
+__device__ __forceinline__ float cell_fn(int fn, float a)
 {
-    return fmaf(-2.0f, fast_rcp(fast_exp(2.0f * x) + 1.0f), 1.0f);
+    const float x = (fn == 0) ? a : 2.0f * a;
+    const float r = fast_rcp(fast_exp(x) + 1.0f);
+    return (fn == 0) ? r : fmaf(-2.0f, r, 1.0f);
+}
+
+// h from the three nonlinearities.
+__device__ __forceinline__ float cell_h(float gate, float g, float hh)
+{
+    return fmaf(gate, g, (1.0f - gate) * hh);
 }
 
 // The cell, dt = 1: gate = sigmoid(-a_f) = 1 / (1 + exp(a_f)),
@@ -120,10 +162,10 @@ __device__ __forceinline__ float fast_tanh(float x)
 __device__ __forceinline__ CellOut cell_forward(float af, float ag, float ah)
 {
     CellOut o;
-    o.gate = fast_rcp(1.0f + fast_exp(af));
-    o.g = fast_tanh(ag);
-    o.hh = fast_tanh(ah);
-    o.h = fmaf(o.gate, o.g, (1.0f - o.gate) * o.hh);
+    o.gate = cell_fn(0, af);
+    o.g = cell_fn(1, ag);
+    o.hh = cell_fn(2, ah);
+    o.h = cell_h(o.gate, o.g, o.hh);
     return o;
 }
 

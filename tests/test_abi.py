@@ -86,7 +86,7 @@ def test_step_argument_errors(L):
 def _kloop_args(B, C, n_x, K):
     """Twelve fake, non-overlapping addresses and a large enough workspace size."""
     a = [FAKE + (i << 28) for i in range(12)]
-    return a[:8] + [4 * (3 * K * B * C + 2 * B * C)] + a[8:]
+    return a[:8] + [4 * (6 * K * B * C + 2 * B * C)] + a[8:]
 
 
 def test_kloop_argument_errors(L):
@@ -111,16 +111,16 @@ def test_kloop_argument_errors(L):
 
 
 def test_workspace_size_and_path_queries(L):
-    assert L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) == 4 * (3 * 64 * 32 * 128 + 2 * 32 * 128)
+    assert L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) == 4 * (6 * 64 * 32 * 128 + 2 * 32 * 128)
     assert L.cfc_train_kloop_workspace_bytes(-1, 128, 64, 64) == 0
     # W of the pages-shaped cell (3 x 128 x 192) fits the persistent kernel; the wide one does not
     assert L.cfc_kloop_path(32, 128, 64, 64) == 2
     assert L.cfc_kloop_path(256, 256, 128, 64) == 1
     assert L.cfc_kloop_path(4, 16, 8, 4) == 2
-    assert L.cfc_kloop_path(4, 64, 100, 4) == 2     # 3 column blocks
-    assert L.cfc_kloop_path(4, 48, 200, 4) == 2     # 4 column blocks
+    assert L.cfc_kloop_path(4, 64, 100, 4) == 2     # n_x does not matter: X is precomputed
+    assert L.cfc_kloop_path(4, 48, 300, 4) == 2
     assert L.cfc_kloop_path(4, 100, 20, 4) == 2     # 2 channels per dz group
-    assert L.cfc_kloop_path(4, 48, 300, 4) == 1     # 6 column blocks: step path
+    assert L.cfc_kloop_path(4, 128, 4000, 4) == 2
     assert L.cfc_kloop_path(4, 129, 0, 4) == 1      # 3 channels per dz group: step path
     assert L.cfc_set_kloop_mode(7) == -1
     assert L.cfc_set_kloop_mode(1) == 0

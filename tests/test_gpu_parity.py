@@ -24,9 +24,11 @@ CASES = {
     "three_tiles": dict(B=5, C=40, n_x=12, K=5),       # 3 channel tiles, last one partial
     "sample_tiles": dict(B=130, C=24, n_x=8, K=3),     # 4 samples per workgroup, ragged last
     "no_input": dict(B=2, C=16, n_x=0, K=3),           # n_x = 0: autonomous recurrence
-    "blocks3": dict(B=3, C=64, n_x=100, K=6),          # 3 column blocks, carry columns straddle blocks
-    "blocks4": dict(B=2, C=48, n_x=200, K=5),          # 4 column blocks (n_in = 248)
+    "long_input64": dict(B=3, C=64, n_x=100, K=6),     # n_x > C; one channel per dz group, 2 column blocks
+    "long_input48": dict(B=2, C=48, n_x=200, K=5),     # n_in = 248; ragged second column block
     "two_channel_groups": dict(B=3, C=100, n_x=20, K=7),  # 2 channels per dz group, last groups partial
+    "three_blocks": dict(B=3, C=72, n_x=36, K=5),      # 3 recurrent column blocks of 32, 2 channels per group
+    "odd_channels": dict(B=2, C=37, n_x=3, K=4),       # C and n_x not multiples of 4: scalar moves
 }
 
 
@@ -100,7 +102,8 @@ def test_kloop_matches_oracle(cfc, oracle_mod, case, path):
 
 # ---------------------------------------------------------------- single steps
 
-@pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input"])
+@pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input",
+                                  "long_input48", "odd_channels"])
 def test_fwd_step_matches_oracle(cfc, oracle_mod, case):
     d = CASES[case]
     say("fwd step parity", case)
@@ -176,7 +179,7 @@ def test_kloop_is_deterministic_and_replay_stable(cfc):
 
 @pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "sample_tiles", "three_tiles", "no_input",
-                                  "blocks3", "two_channel_groups"])
+                                  "long_input64", "two_channel_groups", "three_blocks", "odd_channels"])
 def test_graph_equals_eager_step_calls(cfc, case, path):
     """The K-loop graph (persistent kernel or step kernels) gives the bits of
     the eager composition of single-step ABI calls with per-step scratch +=."""
@@ -207,7 +210,8 @@ def test_graph_equals_eager_step_calls(cfc, case, path):
 
 
 @pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input",
-                                  "blocks3", "blocks4", "two_channel_groups"])
+                                  "long_input64", "long_input48", "two_channel_groups", "three_blocks",
+                                  "odd_channels"])
 def test_persistent_and_step_paths_agree_bitwise(cfc, case):
     d = CASES[case]
     say("persistent == steps", case)
