@@ -130,14 +130,17 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *                        S[b,q,c,:] = sum_t dp_q[t,b,c] z_t[b,:] (t = K..1)
  *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
  *                        call's work on `stream` has completed
- * Two paths give the same bits: an input-projection launch for all steps
- * followed by a persistent kernel (one workgroup per sample runs every K
- * step with the recurrent W in registers) when C <= 128, otherwise 2K
- * step-kernel launches; cfc_set_kloop_mode() can force either.  The graph is
- * built on the first call for a given (device, path, pointers, sizes) and
- * cached; later calls with the same key replay it.  Calls sharing a key must
- * be issued on one stream at a time.  K == 0 or B == 0 writes h_hist[0] = h0
- * and zeros to the scratch and gradients.
+ * Two paths give the same bits:
+ *  - persistent (C <= 128): an input-projection launch for all steps, one
+ *    workgroup per sample running every K step with the recurrent W in
+ *    registers, the scratch fill and the reduction -- four launches,
+ *    enqueued directly on `stream`;
+ *  - step kernels (any C): 2K step launches, the fill and the reduction,
+ *    captured once as a HIP graph per (device, pointers, sizes) and replayed
+ *    on later calls with the same key.  Calls sharing a key must be issued
+ *    on one stream at a time.
+ * cfc_set_kloop_mode() can force either path.  K == 0 or B == 0 writes
+ * h_hist[0] = h0 and zeros to the scratch and gradients.
  */
 int cfc_train_kloop(const float* u, const float* y, const float* h0,
                     const float* W, const float* bias,
@@ -166,6 +169,30 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0,
                       const float* W, const float* bias,
                       float* h_hist, float* act, float* ws, size_t ws_bytes,
                       int B, int C, int n_x, int K, void* stream);
+
+/* The two launches of cfc_kloop_fwd_bwd's persistent path, callable on
+ * their own (same kernels, same bits):
+ * cfc_input_projection -- the input part of every step's pre-activations,
+ *   for M rows at once (in the K-loop the rows are (t, b), M = K B):
+ *     X[m, q C + c] = bias[q, c] + sum_{k < n_x} W[q, c, k] u[m, k]
+ *   in the library's canonical order (four fma chains over the input
+ *   columns k = j mod 4, then bias + ((x0 + x1) + (x2 + x3))).
+ *   u [M, n_x], W [3, C, n_in] (only columns < n_x are read), bias [3, C],
+ *   X [M, 3C] out, OVERWRITTEN; X must not overlap the inputs.
+ * cfc_kloop_recurrence -- forward t = 1..K and backward t = K..1 of every
+ *   sample given X [K, B, 3C] from cfc_input_projection (the cell of
+ *   cfc_fwd_step with a_q = X_q + the recurrent part, BPTT of
+ *   cfc_bwd_step), one workgroup per sample ("K-loop Parallelization",
+ *   section Architecture Choice).  Writes h_hist [K+1,B,C], act [K,3,B,C]
+ *   and dp [K,B,3C] (row r = q C + c) as cfc_kloop_fwd_bwd does.  Only for
+ *   C <= 128 (CFC_EINVAL otherwise).  K == 0 or B == 0 writes h_hist[0] = h0.
+ */
+int cfc_input_projection(const float* u, const float* W, const float* bias,
+                         float* X, int64_t M, int C, int n_x, void* stream);
+
+int cfc_kloop_recurrence(const float* X, const float* y, const float* h0,
+                         const float* W, float* h_hist, float* act, float* dp,
+                         int B, int C, int n_x, int K, void* stream);
 
 int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist,
                      float* gW_scratch, float* gb_scratch,

@@ -6,7 +6,8 @@
  * Exported symbols (all sizes are int64, all arrays row-major, host memory):
  *   oracle_fwd_step_{f64,f32}, oracle_bwd_step_{f64,f32},
  *   oracle_sum_axis0_{f64,f32}, oracle_cfc_forward_{f64,f32},
- *   oracle_cfc_train_{f64,f32}, oracle_reduce_axis0_f64.
+ *   oracle_cfc_train_{f64,f32}, oracle_input_projection_{f64,f32},
+ *   oracle_reduce_axis0_f64.
  */
 #include <math.h>
 #include <stdlib.h>

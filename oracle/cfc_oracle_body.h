@@ -69,6 +69,23 @@ void FN(oracle_fwd_step)(const REAL* u_t, const REAL* h_prev, const REAL* W,
     free(z);
 }
 
+/* The input part of the pre-activations for M rows of inputs at once:
+ *   X[m, q C + c] = b_q[c] + sum_{k < n_x} W_q[c, k] u[m, k]
+ * i.e. a_q of oracle_fwd_step restricted to the input columns of z.  The sum
+ * runs k = 0 .. n_x-1, then the bias is added. */
+void FN(oracle_input_projection)(const REAL* u, const REAL* W, const REAL* bias, long M, long C,
+                                 long n_x, REAL* X)
+{
+    const long n_in = n_x + C;
+    for (long m = 0; m < M; ++m)
+        for (long r = 0; r < 3 * C; ++r) {
+            const REAL* row = W + r * n_in;
+            REAL acc = 0;
+            for (long k = 0; k < n_x; ++k) acc += row[k] * u[m * n_x + k];
+            X[m * 3 * C + r] = acc + bias[r];
+        }
+}
+
 /* One backward step for every sample.
  *   dh    = (h_t - y_t) + dh_in                       (loss residual + carry)
  *   dp_f  = dh * (g - hh) * (-gate * (1 - gate))       (d/da_f; dgate/da_f = -gate(1-gate))

@@ -47,6 +47,9 @@ def _lib():
             f = getattr(lib, "oracle_cfc_train_" + suf)
             f.argtypes = [_P] * 5 + [_I64] * 4 + [_P] * 9
             f.restype = real
+            f = getattr(lib, "oracle_input_projection_" + suf)
+            f.argtypes = [_P] * 3 + [_I64] * 3 + [_P]
+            f.restype = None
         lib.oracle_reduce_axis0_f64.argtypes = [_P, _I64, _I64, _P]
         lib.oracle_reduce_axis0_f64.restype = None
         _LIB = lib
@@ -84,6 +87,20 @@ def fwd_step(u_t, h_prev, W, bias, precision="f64"):
     getattr(_lib(), "oracle_fwd_step_" + precision)(
         _p(u_t), _p(h_prev), _p(W), _p(bias), B, C, n_x, _p(h_t), _p(act_t))
     return h_t, act_t
+
+
+def input_projection(u, W, bias, precision="f64"):
+    """X [.., 3C] = bias + W[:, :, :n_x] u for every row of u [.., n_x]."""
+    dt = _dt(precision)
+    u = _in(u, precision)
+    W = _in(W, precision)
+    bias = _in(bias, precision)
+    C = W.shape[1]
+    n_x = u.shape[-1]
+    M = int(np.prod(u.shape[:-1]))
+    X = np.zeros(tuple(u.shape[:-1]) + (3 * C,), dtype=dt)
+    getattr(_lib(), "oracle_input_projection_" + precision)(_p(u), _p(W), _p(bias), M, C, n_x, _p(X))
+    return X
 
 
 def bwd_step(u_t, h_prev, h_t, y_t, W, act_t, dh_in, S, Sb, precision="f64", want_du=True):

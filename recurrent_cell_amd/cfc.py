@@ -46,6 +46,8 @@ def lib():
         L.cfc_train_kloop.argtypes = [_P] * 8 + [ctypes.c_size_t] + [_P] * 4 + [_I, _I, _I, _I, _P]
         L.cfc_kloop_fwd_bwd.argtypes = [_P] * 8 + [ctypes.c_size_t, _I, _I, _I, _I, _P]
         L.cfc_scratch_fill.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
+        L.cfc_input_projection.argtypes = [_P] * 4 + [_I64, _I, _I, _P]
+        L.cfc_kloop_recurrence.argtypes = [_P] * 7 + [_I, _I, _I, _I, _P]
         L.cfc_train_kloop_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.cfc_train_kloop_workspace_bytes.restype = ctypes.c_size_t
         L.cfc_set_kloop_mode.argtypes = [_I]
@@ -56,7 +58,7 @@ def lib():
         L.cfc_clear_graph_cache.argtypes = []
         for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
                   L.cfc_kloop_fwd_bwd, L.cfc_scratch_fill, L.cfc_clear_graph_cache,
-                  L.cfc_set_kloop_mode):
+                  L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence):
             f.restype = _I
         _LIB = L
     return _LIB
@@ -161,9 +163,10 @@ class KloopBuffers:
 
 
 def cfc_train_kloop(u, y, h0, W, bias, out=None):
-    """One training step of the K-loop (forward, BPTT, scratch, reduce) as
-    one graph replay.  Returns the KloopBuffers holding h_hist, act, the
-    per-sample scratch, gW and gb."""
+    """One training step of the K-loop (forward, BPTT, scratch, reduce):
+    four direct launches on the persistent path, one graph replay on the
+    step path.  Returns the KloopBuffers holding h_hist, act, the per-sample
+    scratch, gW and gb."""
     K, B, n_x = u.shape
     C = h0.shape[1]
     n_in = n_x + C
@@ -192,6 +195,37 @@ def cfc_kloop_fwd_bwd(u, y, h0, W, bias, out):
             _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
             _dev(out.ws, "ws"), out.ws.numel() * 4)
     _check("cfc_kloop_fwd_bwd", lib().cfc_kloop_fwd_bwd(*args, B, C, n_x, K, _stream(h0)))
+    return out
+
+
+def cfc_input_projection(u, W, bias, X=None):
+    """X [.., 3C] = bias + W[:, :, :n_x] u for every row of u [.., n_x]
+    (the canonical input part of the pre-activations; see include/cfc.h)."""
+    n_x = u.shape[-1]
+    C = W.shape[1]
+    M = 1
+    for d in u.shape[:-1]:
+        M *= int(d)
+    if X is None:
+        X = torch.empty(tuple(u.shape[:-1]) + (3 * C,), device=W.device, dtype=torch.float32)
+    args = (_dev(u, "u"), _dev(W, "W", (3, C, n_x + C)), _dev(bias, "bias", (3, C)), _dev(X, "X"))
+    if X.numel() != M * 3 * C:
+        raise ValueError("X must hold %d rows of 3C floats" % M)
+    _check("cfc_input_projection", lib().cfc_input_projection(*args, M, C, n_x, _stream(W)))
+    return X
+
+
+def cfc_kloop_recurrence(X, y, h0, W, out):
+    """Forward and backward of the K-loop given X [K,B,3C] from
+    cfc_input_projection, into out.h_hist, out.act and the dp_t block of
+    out.ws (persistent kernel, C <= 128)."""
+    K, B, C = y.shape
+    n_x = W.shape[2] - C
+    dp = out.ws[:K * B * 3 * C]
+    args = (_dev(X, "X", (K, B, 3 * C)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
+            _dev(W, "W", (3, C, n_x + C)), _dev(out.h_hist, "h_hist", (K + 1, B, C)),
+            _dev(out.act, "act", (K, 3, B, C)), _dev(dp, "dp"))
+    _check("cfc_kloop_recurrence", lib().cfc_kloop_recurrence(*args, B, C, n_x, K, _stream(h0)))
     return out
 
 

@@ -456,9 +456,15 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
         return CFC_OK;
     }
 
+    const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
+    // The persistent path is four launches (input projection, K-loop,
+    // scratch fill, reduction), enqueued directly: replaying them as a graph
+    // measured about 5 us slower per step.  The step path's 2K + 2 launches
+    // go through the cached graph.
+    if (persistent) return enqueue_kloop(k, true, p, s);
+
     int dev = 0;
     CFC_HIP(hipGetDevice(&dev), "hipGetDevice");
-    const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
     const GraphKey key{dev, persistent ? 1 : 0, u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch,
                        gW, gb, B, C, n_x, K};
     std::lock_guard<std::mutex> lock(g_mu);
@@ -499,6 +505,59 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
     }
     const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, nullptr, nullptr, nullptr, nullptr, B, C, n_x, K};
     return enqueue_fwd_bwd(k, persistent, make_plan(B, C, n_x, W, nullptr), s);
+}
+
+int cfc_input_projection(const float* u, const float* W, const float* bias, float* X, int64_t M, int C, int n_x,
+                         void* stream)
+{
+    g_last_error.clear();
+    if (int rc = check_dims(0, C, n_x)) return rc;
+    if (M < 0 || M > ((int64_t)1 << 40)) return fail(CFC_EINVAL, "cfc_input_projection: M=%lld out of range",
+                                                     (long long)M);
+    if (M == 0) return CFC_OK;
+    const int64_t n_in = (int64_t)n_x + C;
+    if (!W || !bias || !X || (n_x > 0 && !u)) return fail(CFC_EINVAL, "cfc_input_projection: null pointer");
+    const Span out = span(X, M * 3 * C);
+    const Span ins[] = {span(u, M * n_x), span(W, 3 * C * n_in), span(bias, 3 * C)};
+    for (const Span& i : ins)
+        if (overlap(out, i)) return fail(CFC_EINVAL, "cfc_input_projection: the output overlaps an input");
+    const cfc::XprojArgs x{u, W, bias, X, M, 3 * C, n_x, (int)n_in, (3 * C + 63) / 64};
+    CFC_HIP(cfc::launch_xproj(x, (hipStream_t)stream), "input projection launch");
+    return CFC_OK;
+}
+
+int cfc_kloop_recurrence(const float* X, const float* y, const float* h0, const float* W, float* h_hist,
+                         float* act, float* dp, int B, int C, int n_x, int K, void* stream)
+{
+    g_last_error.clear();
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "cfc_kloop_recurrence: K=%d out of range", K);
+    if (cfc::persist_smem(C) == 0)
+        return fail(CFC_EINVAL, "cfc_kloop_recurrence: the persistent kernel holds C <= 128 channels (C=%d)", C);
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    const struct {
+        const void* p;
+        int64_t n;
+    } need[] = {{X, (int64_t)K * 3 * BC}, {y, (int64_t)K * BC}, {h0, BC}, {W, 3 * C * n_in},
+                {h_hist, (K + 1) * BC}, {act, (int64_t)K * 3 * BC}, {dp, (int64_t)K * 3 * BC}};
+    for (const auto& q : need)
+        if (q.n > 0 && q.p == nullptr) return fail(CFC_EINVAL, "cfc_kloop_recurrence: null pointer");
+    const Span outs[] = {span(h_hist, (K + 1) * BC), span(act, (int64_t)K * 3 * BC), span(dp, (int64_t)K * 3 * BC)};
+    const Span ins[] = {span(X, (int64_t)K * 3 * BC), span(y, (int64_t)K * BC), span(h0, BC), span(W, 3 * C * n_in)};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return fail(CFC_EINVAL, "cfc_kloop_recurrence: an output overlaps an input");
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "cfc_kloop_recurrence: outputs overlap");
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0 || B == 0) {
+        if (BC > 0) CFC_HIP(hipMemcpyAsync(h_hist, h0, BC * 4, hipMemcpyDeviceToDevice, s), "h0 copy");
+        return CFC_OK;
+    }
+    const cfc::PersistArgs a{X, y, h0, W, nullptr, h_hist, act, dp, B, C, n_x, K};
+    CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch");
+    return CFC_OK;
 }
 
 int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist, float* gW_scratch, float* gb_scratch,

@@ -28,6 +28,16 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 16-byte load from an address the caller has clamped into bounds, issued
+// unconditionally; zero where !valid.  Branch-free, so a run of such loads
+// stays in flight together (a load under a branch is waited for where the
+// branch joins).
+__device__ __forceinline__ f32x4 load4_or_zero(const float* clamped, bool valid)
+{
+    const f32x4 v = *reinterpret_cast<const f32x4*>(clamped);
+    return valid ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
 // z_s = [u_t[b0+s] ; h_prev[b0+s]] for the tile's samples into LDS rows of
 // pitch ldz (zero padded past n_in and for absent samples).
 template <int BT>
@@ -199,63 +209,71 @@ __global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[mt][nt][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int k0 = 0; k0 < n_x; k0 += 16) {
-        const int k = k0 + 4 * lk;
-        f32x4 av[2], bv[2];
+    // Groups of XB blocks of 16 columns: all of a group's operands are loaded
+    // before its MFMAs, so their latencies overlap.
+    constexpr int XB = 4;
+    for (int kg = 0; kg < n_x; kg += 16 * XB) {
+        f32x4 av[XB][2], bv[XB][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int64_t row = m0 + 16 * mt + li;
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (row < M) {
-                const float* src = a.u + row * n_x + k;
+        for (int kb = 0; kb < XB; ++kb) {
+            const int k = kg + 16 * kb + 4 * lk;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int64_t row = m0 + 16 * mt + li;
+                const float* src = a.u + min(row, M - 1) * n_x;
                 if (VEC) {
-                    if (k < n_x) v = *reinterpret_cast<const f32x4*>(src);
+                    av[kb][mt] = load4_or_zero(src + min(k, n_x - 4), row < M && k < n_x);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (k + e < n_x) v[e] = src[e];
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = src[min(k + e, n_x - 1)];
+                        av[kb][mt][e] = (row < M && k + e < n_x) ? x : 0.0f;
+                    }
                 }
             }
-            av[mt] = v;
-        }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int r = n0 + 16 * nt + li;
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (r < N) {
-                const float* src = a.W + (int64_t)r * a.n_in + k;
+            for (int nt = 0; nt < 2; ++nt) {
+                const int r = n0 + 16 * nt + li;
+                const float* src = a.W + (int64_t)min(r, N - 1) * a.n_in;
                 if (VEC) {
-                    if (k < n_x) v = *reinterpret_cast<const f32x4*>(src);
+                    bv[kb][nt] = load4_or_zero(src + min(k, n_x - 4), r < N && k < n_x);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (k + e < n_x) v[e] = src[e];
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = src[min(k + e, n_x - 1)];
+                        bv[kb][nt][e] = (r < N && k + e < n_x) ? x : 0.0f;
+                    }
                 }
             }
-            bv[nt] = v;
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep the whole group's loads ahead of its MFMAs
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int kb = 0; kb < XB; ++kb)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt][c], bv[nt][c], acc[mt][nt][c], 0, 0, 0);
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        acc[mt][nt][c] =
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(av[kb][mt][c], bv[kb][nt][c], acc[mt][nt][c], 0, 0, 0);
     }
 
+    float bias[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) bias[nt] = a.bias[min(n0 + 16 * nt + li, N - 1)];
+    wait_vmem_all();   // so that no store below waits behind another
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int r = n0 + 16 * nt + li;
-        if (r >= N) continue;
-        const float bias = a.bias[r];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t row = m0 + 16 * mt + 4 * lk + i;
-                if (row < M)
-                    a.X[row * N + r] = xproj_combine(bias, acc[mt][nt][0][i], acc[mt][nt][1][i], acc[mt][nt][2][i],
-                                                     acc[mt][nt][3][i]);
+                if (r < N && row < M)
+                    a.X[row * N + r] = xproj_combine(bias[nt], acc[mt][nt][0][i], acc[mt][nt][1][i],
+                                                     acc[mt][nt][2][i], acc[mt][nt][3][i]);
             }
     }
 }
@@ -409,16 +427,25 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
 // ---------------------------------------------------------------------------
 // Deferred scratch fill (K-loop): S[b, r, k] = fma chain over t = K .. 1 of
 // dp_t[b, r] * z_t[b, k] from +0 -- the same bits as K per-step "+=" updates
-// of a zeroed scratch -- and Sb[b, r] = add chain of dp_t[b, r].  Each
-// workgroup writes one 64 x 64 tile of one sample's scratch once; it stages
-// up to kFillSteps time steps of dp (64 rows) and z (64 columns) per pass,
-// with 16-byte loads where the layout allows, then each lane runs the chains
-// of a 4 x 4 block of the tile.
+// of a zeroed scratch -- and Sb[b, r] = add chain of dp_t[b, r].  Per sample
+// this is the product dp_b^T z_b over the K steps; each workgroup writes one
+// 64 x 64 tile of one sample's scratch once.  It stages up to kFillSteps
+// steps of dp (64 rows) and z (64 columns) in LDS, t descending, and each
+// wave accumulates a 32 x 32 block with v_mfma_f32_16x16x4f32, whose four
+// k-slots are taken in order as an fma chain: slot kk of the instruction at
+// staged step tt is step t0 - tt - kk.  Steps past the last multiple of 4
+// go through VALU fma on the same accumulators.  Operand layout (16 x 16 x
+// 4): lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; D[i][j] sits in
+// lane j + 16 (i / 4), register i % 4.  The tile leaves through LDS as
+// coalesced rows.
 // ---------------------------------------------------------------------------
+constexpr int kFillPitch = kFillTile + 16;   // staged row pitch: the 4 k-slots of a read hit distinct banks
+static_assert(kFillSteps * 32 % kThreads == 0, "whole staging passes");
+
 __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float dps[kFillSteps][kFillTile];
-    __shared__ __attribute__((aligned(16))) float zs[kFillSteps][kFillTile];
+    __shared__ __attribute__((aligned(16))) float dps[kFillSteps][kFillPitch];
+    __shared__ __attribute__((aligned(16))) float zs[kFillSteps][kFillPitch];
     const int n_in = a.n_x + a.C;
     const int R3 = 3 * a.C;
     const int tiles = a.n_rt * a.n_kt;
@@ -428,50 +455,63 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
     const int kt = rem - rt * a.n_kt;
     const int r0 = rt * kFillTile;
     const int k0 = kt * kFillTile;
-    const int tx = threadIdx.x % 16;
-    const int ty = threadIdx.x / 16;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int wr = 32 * (wave >> 1);   // the wave's 32 x 32 block of the tile
+    const int wc = 32 * (wave & 1);
     const bool do_bias = (kt == 0) && (threadIdx.x < kFillTile);
     // 16-byte staging needs every 4-float segment to lie inside one row of one tensor
     const bool vec = (R3 % 4 == 0) && (a.n_x % 4 == 0) && (a.C % 4 == 0) &&
                      ((((uintptr_t)a.dp) | ((uintptr_t)a.u) | ((uintptr_t)a.h_hist)) & 15u) == 0;
 
-    float acc[4][4];
+    f32x4 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float sb = 0.0f;
 
     for (int t0 = a.K; t0 >= 1; t0 -= kFillSteps) {
-        const int nt = min(kFillSteps, t0);   // steps t0, t0 - 1, .., t0 - nt + 1
+        const int nst = min(kFillSteps, t0);   // steps t0, t0 - 1, .., t0 - nst + 1
         if (vec) {
-            // 16 segments of 4 floats per staged row, dp and z rows interleaved
-            for (int i = threadIdx.x; i < kFillSteps * 32; i += kThreads) {
+            // 16 segments of 4 floats per staged row, dp and z rows
+            // interleaved; every load of the pass is in flight before the
+            // first LDS store.
+            constexpr int kSeg = kFillSteps * 32 / kThreads;
+            f32x4 v[kSeg];
+#pragma unroll
+            for (int m = 0; m < kSeg; ++m) {
+                const int i = threadIdx.x + m * kThreads;
                 const int tt = i / 32;
                 const int sgi = i - tt * 32;
-                const bool is_z = sgi >= 16;
                 const int x = 4 * (sgi & 15);
-                f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (tt < nt) {
-                    const int64_t tb = (int64_t)(t0 - tt - 1) * a.B + b;
-                    if (!is_z) {
-                        const int r = r0 + x;
-                        if (r < R3) v = *reinterpret_cast<const f32x4*>(a.dp + tb * R3 + r);
-                    } else {
-                        const int k = k0 + x;
-                        if (k < n_in)
-                            v = (k < a.n_x) ? *reinterpret_cast<const f32x4*>(a.u + tb * a.n_x + k)
-                                            : *reinterpret_cast<const f32x4*>(a.h_hist + tb * a.C + (k - a.n_x));
-                    }
+                // clamped into bounds; zero outside the tile's rows, columns and steps
+                const int64_t tb = (int64_t)(t0 - min(tt, nst - 1) - 1) * a.B + b;
+                if (sgi < 16) {
+                    const int r = r0 + x;
+                    v[m] = load4_or_zero(a.dp + tb * R3 + min(r, R3 - 4), tt < nst && r < R3);
+                } else {
+                    const int k = min(k0 + x, n_in - 4);
+                    const float* src = (k < a.n_x) ? a.u + tb * a.n_x + k : a.h_hist + tb * a.C + (k - a.n_x);
+                    v[m] = load4_or_zero(src, tt < nst && k0 + x < n_in);
                 }
-                *reinterpret_cast<f32x4*>(is_z ? &zs[tt][x] : &dps[tt][x]) = v;
+            }
+#pragma unroll
+            for (int m = 0; m < kSeg; ++m) {
+                const int i = threadIdx.x + m * kThreads;
+                const int tt = i / 32;
+                const int sgi = i - tt * 32;
+                const int x = 4 * (sgi & 15);
+                *reinterpret_cast<f32x4*>(sgi >= 16 ? &zs[tt][x] : &dps[tt][x]) = v[m];
             }
         } else {
             for (int i = threadIdx.x; i < kFillSteps * kFillTile; i += kThreads) {
                 const int tt = i / kFillTile;
                 const int x = i - tt * kFillTile;
                 float dv = 0.0f, zv = 0.0f;
-                if (tt < nt) {
+                if (tt < nst) {
                     const int64_t tb = (int64_t)(t0 - tt - 1) * a.B + b;
                     const int r = r0 + x;
                     if (r < R3) dv = a.dp[tb * R3 + r];
@@ -484,37 +524,55 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
             }
         }
         __syncthreads();
-        for (int tt = 0; tt < nt; ++tt) {
-            const f32x4 d = *reinterpret_cast<const f32x4*>(&dps[tt][ty * 4]);
-            const f32x4 z = *reinterpret_cast<const f32x4*>(&zs[tt][tx * 4]);
+        const int nst4 = nst & ~3;
+        for (int tt = 0; tt < nst4; tt += 4) {
+            float av[2], bv[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int mt = 0; mt < 2; ++mt) av[mt] = dps[tt + lk][wr + 16 * mt + li];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(d[i], z[j], acc[i][j]);
+            for (int nt = 0; nt < 2; ++nt) bv[nt] = zs[tt + lk][wc + 16 * nt + li];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+        }
+        for (int tt = nst4; tt < nst; ++tt) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[mt][nt][e] = fmaf(dps[tt][wr + 16 * mt + 4 * lk + e], zs[tt][wc + 16 * nt + li], acc[mt][nt][e]);
         }
         if (do_bias)
-            for (int tt = 0; tt < nt; ++tt) sb = sb + dps[tt][threadIdx.x];
+            for (int tt = 0; tt < nst; ++tt) sb = sb + dps[tt][threadIdx.x];
         __syncthreads();
     }
 
-    const bool vec_out = (n_in % 4 == 0) && ((((uintptr_t)a.gW_s) & 15u) == 0);
+    // The tile through LDS (dps reused as [64][kFillPitch]) for row-wise stores.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = r0 + ty * 4 + i;
-        if (r < R3) {
-            float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in;
-            const int k = k0 + tx * 4;
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dps[wr + 16 * mt + 4 * lk + e][wc + 16 * nt + li] = acc[mt][nt][e];
+    __syncthreads();
+    const bool vec_out = (n_in % 4 == 0) && ((((uintptr_t)a.gW_s) & 15u) == 0);
+    for (int u = threadIdx.x; u < kFillTile * (kFillTile / 4); u += kThreads) {
+        const int row = u / (kFillTile / 4);
+        const int c4 = 4 * (u - row * (kFillTile / 4));
+        const int r = r0 + row;
+        const int k = k0 + c4;
+        if (r < R3 && k < n_in) {
+            float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in + k;
             if (vec_out && k + 4 <= n_in) {
-                f32x4 o;
-                o.x = acc[i][0];
-                o.y = acc[i][1];
-                o.z = acc[i][2];
-                o.w = acc[i][3];
-                *reinterpret_cast<f32x4*>(dst + k) = o;
+                *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(&dps[row][c4]);
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (k + j < n_in) dst[k + j] = acc[i][j];
+                for (int e = 0; e < 4; ++e)
+                    if (k + e < n_in) dst[e] = dps[row][c4 + e];
             }
         }
     }
@@ -668,6 +726,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         zs[0][c] = h;
         a.h_hist[(int64_t)b * C + c] = h;
     }
+    wait_vmem_all();   // W is in registers before any step loop reads it
 
     // ---------------- forward ----------------
     // X prefetch into registers: a lane moves one float4 of one staged row
@@ -688,9 +747,8 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
 #pragma unroll
         for (int m = 0; m < XPF; ++m) {
             const int rr = x_row0 + m * x_rstep;
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (x_row0 < x_rstep && rr < nt) v = *reinterpret_cast<const f32x4*>(src(rr) + 4 * x_col);
-            xpf[m] = v;
+            // clamped into bounds; rows past the chunk are loaded but never staged
+            xpf[m] = *reinterpret_cast<const f32x4*>(src(min(rr, nt - 1)) + 4 * x_col);
         }
     };
     auto out_row = [&](int t0) {
@@ -705,6 +763,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     int prev_t0 = 0, prev_nt = 0;
     for (int t0 = 1; t0 <= K; t0 += kFwdChunk) {
         const int nt = min(kFwdChunk, K - t0 + 1);
+        wait_vmem_all();   // loads and stores issued a whole chunk ago; none waits below
         if (c_vec) {
 #pragma unroll
             for (int m = 0; m < XPF; ++m) {
@@ -790,9 +849,8 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
 #pragma unroll
         for (int m = 0; m < BPF; ++m) {
             const int rr = c_row0 + m * c_rstep;
-            f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (c_row0 < c_rstep && rr < 5 * nt) x = *reinterpret_cast<const f32x4*>(src(rr) + 4 * c_col);
-            bpf[m] = x;
+            // clamped into bounds; rows past the chunk are loaded but never staged
+            bpf[m] = *reinterpret_cast<const f32x4*>(src(min(rr, 5 * nt - 1)) + 4 * c_col);
         }
     };
     if (c_vec && K >= 1) load_b(K, min(kBwdChunk, K));
@@ -801,6 +859,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     prev_nt = 0;
     for (int t1 = K; t1 >= 1; t1 -= kBwdChunk) {
         const int nt = min(kBwdChunk, t1);   // steps t1, t1 - 1, .., t1 - nt + 1
+        wait_vmem_all();   // loads and stores issued a whole chunk ago; none waits below
         if (c_vec) {
 #pragma unroll
             for (int m = 0; m < BPF; ++m) {

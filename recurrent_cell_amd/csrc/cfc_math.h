@@ -40,6 +40,14 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until every vector memory load and store of this wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).  Issued
+// through the builtin so that the compiler's wait-count tracking sees it: a
+// register loaded before a loop and first read inside it would otherwise
+// make the compiler wait inside the loop, where gfx9's shared load/store
+// counter forces that wait to drain every later store and prefetch as well.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // gfx9 DPP controls used by row_sum16 and quad_sum4.
 constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]

@@ -110,6 +110,24 @@ def test_kloop_argument_errors(L):
     assert b"workspace" in L.cfc_last_error()
 
 
+def test_projection_and_recurrence_argument_errors(L):
+    # input projection: bad sizes, null pointers, output overlapping an input
+    assert L.cfc_input_projection(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), -1, 8, 4, None) == -1
+    assert L.cfc_input_projection(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), 16, 0, 4, None) == -1
+    assert L.cfc_input_projection(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), None, 16, 8, 4, None) == -1
+    assert L.cfc_input_projection(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + 64, 16, 8, 4, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    assert L.cfc_input_projection(None, None, None, None, 0, 8, 4, None) == 0   # M == 0: nothing to do
+    # recurrence: C above what the persistent kernel holds, nulls, overlaps
+    a = [FAKE + i * (1 << 30) for i in range(7)]
+    assert L.cfc_kloop_recurrence(*a, 4, 129, 8, 4, None) == -1
+    assert b"C <= 128" in L.cfc_last_error()
+    assert L.cfc_kloop_recurrence(*(a[:6] + [None]), 4, 16, 8, 4, None) == -1
+    assert L.cfc_kloop_recurrence(*(a[:4] + [a[0]] + a[5:]), 4, 16, 8, 4, None) == -1   # h_hist == X
+    assert b"overlap" in L.cfc_last_error()
+    assert L.cfc_kloop_recurrence(*a, 4, 16, 8, -1, None) == -1
+
+
 def test_workspace_size_and_path_queries(L):
     assert L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) == 4 * (6 * 64 * 32 * 128 + 2 * 32 * 128)
     assert L.cfc_train_kloop_workspace_bytes(-1, 128, 64, 64) == 0

@@ -1,8 +1,9 @@
 """GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
 
 Every case prints its name before touching the GPU.  Floating-point criteria
-are in tests/tolerances.py; structural properties (determinism, graph ==
-eager, batched row == single-sample run, scratch cleared between steps,
+are in tests/tolerances.py; structural properties (determinism, K-loop
+(graph replay or direct launches) == eager single-step calls, batched row ==
+single-sample run, scratch cleared between steps,
 overwrite semantics, exact special cases) are checked bit for bit.
 """
 import sys
@@ -160,17 +161,55 @@ def test_bwd_carry_bits_do_not_depend_on_du_request(cfc):
     np.testing.assert_array_equal(bits(outs[0][1]), bits(outs[1][1]))
 
 
+@pytest.mark.parametrize("case", ["tiny", "pages", "wide", "ragged_scalar", "no_input", "long_input48",
+                                  "odd_channels"])
+def test_input_projection_matches_oracle(cfc, oracle_mod, case):
+    d = CASES[case]
+    say("input projection parity", case)
+    x = cfc_inputs(**d, seed=8, bias_scale=0.5)
+    X = host(cfc.cfc_input_projection(dev(x.u), dev(x.W), dev(x.bias)))
+    ref = oracle_mod.input_projection(x.u, x.W, x.bias, "f64")
+    n_x = d["n_x"]
+    Wx = np.abs(x.W[:, :, :n_x].reshape(3 * d["C"], n_x).astype(np.float64))
+    mass = np.abs(x.bias.reshape(-1)).astype(np.float64) + np.abs(x.u.astype(np.float64)) @ Wx.T
+    assert_ok(check_grad("X", X, ref, mass))
+
+
+@pytest.mark.parametrize("case", ["pages", "ragged_scalar", "three_blocks", "odd_channels"])
+def test_recurrence_composes_to_fwd_bwd(cfc, case):
+    """cfc_input_projection then cfc_kloop_recurrence gives the bits of
+    cfc_kloop_fwd_bwd (persistent path)."""
+    d = CASES[case]
+    say("projection + recurrence == fwd_bwd", case)
+    x = cfc_inputs(**d, seed=9, bias_scale=0.3)
+    u, y, h0, W, bias = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    cfc.cfc_set_kloop_mode(cfc.KLOOP_PERSISTENT)
+    try:
+        a = cfc.KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
+        cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
+    finally:
+        cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+    b = cfc.KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
+    X = cfc.cfc_input_projection(u, W, bias)
+    cfc.cfc_kloop_recurrence(X, y, h0, W, out=b)
+    n = d["K"] * d["B"] * 3 * d["C"]
+    for k in ("h_hist", "act"):
+        np.testing.assert_array_equal(bits(host(getattr(a, k))), bits(host(getattr(b, k))), err_msg=k)
+    np.testing.assert_array_equal(bits(host(a.ws[:n])), bits(host(b.ws[:n])), err_msg="dp")
+
+
 # ---------------------------------------------------------------- structure, bit for bit
 
-def test_kloop_is_deterministic_and_replay_stable(cfc):
+@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+def test_kloop_is_deterministic_and_replay_stable(cfc, path):
     d = CASES["pages"]
-    say("kloop determinism")
+    say("kloop determinism", path)
     x = cfc_inputs(**d, seed=5, bias_scale=0.1)
     a, _ = kloop_dev(cfc, x)
     first = {k: host(getattr(a, k)).copy() for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
-    b, _ = kloop_dev(cfc, x)            # fresh buffers: a new graph
+    b, _ = kloop_dev(cfc, x)            # fresh buffers (step path: a new graph)
     t = [dev(v) for v in (x.u, x.y, x.h0, x.W, x.bias)]
-    for _ in range(3):                   # same buffers: replays of one graph
+    for _ in range(3):                   # same buffers (step path: replays of one graph)
         cfc.cfc_train_kloop(*t, out=a)
     for k, v in first.items():
         np.testing.assert_array_equal(bits(host(getattr(b, k))), bits(v), err_msg=k)
@@ -180,11 +219,12 @@ def test_kloop_is_deterministic_and_replay_stable(cfc):
 @pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "sample_tiles", "three_tiles", "no_input",
                                   "long_input64", "two_channel_groups", "three_blocks", "odd_channels"])
-def test_graph_equals_eager_step_calls(cfc, case, path):
-    """The K-loop graph (persistent kernel or step kernels) gives the bits of
-    the eager composition of single-step ABI calls with per-step scratch +=."""
+def test_kloop_equals_eager_step_calls(cfc, case, path):
+    """The K-loop step (persistent path: direct launches; step path: graph
+    replay) gives the bits of the eager composition of single-step ABI calls
+    with per-step scratch +=."""
     d = CASES[case]
-    say("graph == eager", case, path)
+    say("kloop == eager", case, path)
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
     x = cfc_inputs(**d, seed=6, bias_scale=0.2)
     g, (u, y, h0, W, bias) = kloop_dev(cfc, x)

@@ -214,3 +214,40 @@ def test_fp32_instantiation_within_fp32_bounds(oracle_mod, cfg):
     assert_ok(check_act("act", r32["act"], r64["act"]))
     for k in ("S", "Sb", "gW", "gb"):
         assert_ok(check_grad(k, r32[k], r64[k], m[k]))
+
+
+# ---------------------------------------------------------------- input projection
+
+def test_input_projection_is_the_zero_state_preactivation(oracle_mod):
+    """With h_{t-1} = 0 the recurrent columns of z contribute nothing, so the
+    forward step's gate, g and hh are the cell functions of X = W_x u + b."""
+    x = cfc_inputs(B=5, C=12, n_x=7, K=1, seed=11, bias_scale=0.4)
+    X = oracle_mod.input_projection(x.u[0], x.W, x.bias, "f64")          # [B, 3C]
+    _, act = oracle_mod.fwd_step(x.u[0], np.zeros_like(x.h0), x.W, x.bias, "f64")
+    C = 12
+    a_f, a_g, a_h = X[:, :C], X[:, C:2 * C], X[:, 2 * C:]
+    np.testing.assert_allclose(act[0], 1.0 / (1.0 + np.exp(a_f)), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(act[1], np.tanh(a_g), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(act[2], np.tanh(a_h), rtol=1e-14, atol=1e-15)
+
+
+def test_input_projection_special_cases(oracle_mod):
+    x = cfc_inputs(B=4, C=6, n_x=5, K=3, seed=12, bias_scale=0.5)
+    C, n_x = 6, 5
+    b = x.bias.reshape(-1).astype(np.float64)
+    # no inputs: X is the bias on every row
+    X0 = oracle_mod.input_projection(np.zeros((3, 4, 0), np.float32), x.W[:, :, n_x:], x.bias, "f64")
+    np.testing.assert_array_equal(X0, np.broadcast_to(b, X0.shape))
+    # one-hot input j: column j of W_x plus the bias, exactly
+    for j in range(n_x):
+        u = np.zeros((1, n_x), np.float32)
+        u[0, j] = 1.0
+        Xj = oracle_mod.input_projection(u, x.W, x.bias, "f64")[0]
+        np.testing.assert_array_equal(Xj, x.W[:, :, j].reshape(-1).astype(np.float64) + b)
+    # rows are independent and the map is affine in u
+    Xa = oracle_mod.input_projection(x.u, x.W, x.bias, "f64")
+    for t in range(3):
+        np.testing.assert_array_equal(Xa[t], oracle_mod.input_projection(x.u[t], x.W, x.bias, "f64"))
+    u2 = x.u[0] * 2.0
+    lin = oracle_mod.input_projection(u2, x.W, x.bias, "f64") - b
+    np.testing.assert_allclose(lin, 2.0 * (Xa[0] - b), rtol=1e-13, atol=1e-14)
