@@ -47,6 +47,31 @@ def step_bytes_flops(B, C, n_x, K):
     return bytes_min, flops
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kloop_persist_pages_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "recurrent_cell_amd", "csrc", f)
+                  for f in ("cfc_kernels.hip", "cfc_kernels.h", "cfc_math.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the persistent kernel from the committed
+    rocprofv3 counter summary, or None if the kernel sources changed since
+    the counters were taken (or the summary is missing)."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(f, "rb").read())
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != h.hexdigest():
+        return None
+    return int(m_bytes.group(1))
+
+
 def recurrence_flops(B, C, K):
     """Persistent kernel: W_h h_{t-1} forward and W_h^T dp (carry) backward."""
     return K * B * 3 * C * C * 2 * 2
@@ -205,6 +230,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
     ap.add_argument("--workload", default="pages", choices=["tiny", "pages", "wide"])
+    ap.add_argument("--no-steps-path", action="store_true", help="skip the step-kernel path contrast")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -218,6 +247,14 @@ def main():
     d = CONFIGS[args.workload]
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
     n_in = n_x + C
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     x = cfc_inputs(**d, seed=0)
     t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]
     path = "persistent" if cfc.cfc_kloop_path(B, C, n_x, K) == cfc.KLOOP_PERSISTENT else "steps"
@@ -226,10 +263,12 @@ def main():
     value = 1000.0 / ms_per_step
 
     # The 2K-launch step-kernel path on the same inputs, for contrast.
-    cfc.cfc_set_kloop_mode(cfc.KLOOP_STEPS)
-    out_steps = cfc.cfc_train_kloop(*t)
-    ms_steps, _ = time_steps(torch, cfc, t, out_steps, max(20, args.steps // 10), 5, 3)
-    cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+    ms_steps = None
+    if not args.no_steps_path:
+        cfc.cfc_set_kloop_mode(cfc.KLOOP_STEPS)
+        out_steps = cfc.cfc_train_kloop(*t)
+        ms_steps, _ = time_steps(torch, cfc, t, out_steps, max(20, args.steps // 10), 5, 3)
+        cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
     t_node = graph_node_latency(torch)
@@ -277,8 +316,10 @@ def main():
             dur = kt["recurrence"]["mean_s"]
             fl = recurrence_flops(B, C, K)
             achieved = fl / dur
+            traffic = measured_traffic() if args.workload == "pages" else None
             roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
-                        "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
+                        "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": traffic,
+                        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                         "kernel": "kloop_persist_kernel", "flops_per_launch": fl,
                         "launch_us": round(dur * 1e6, 3)}
         else:
@@ -293,9 +334,9 @@ def main():
     step_roof = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3),
                  "t_roof_ms": round(t_roof * 1e3, 4), "step_over_roof": round(ms_per_step / (t_roof * 1e3), 3),
                  "flops": flops, "bytes_min": bytes_min,
-                 "steps_path_ms_per_step": round(ms_steps, 5),
+                 "steps_path_ms_per_step": round(ms_steps, 5) if ms_steps else None,
                  "steps_path_over_roof": round(ms_steps / (((2 * K + 2) * t_node + max(
-                     flops / FP32_PEAK, bytes_min / HBM_PEAK)) * 1e3), 3)}
+                     flops / FP32_PEAK, bytes_min / HBM_PEAK)) * 1e3), 3) if ms_steps else None}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "train-steps/s", "n_gpus": 1,
