@@ -257,18 +257,28 @@ def main():
         del src, dst
     x = cfc_inputs(**d, seed=0)
     t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]
-    path = "persistent" if cfc.cfc_kloop_path(B, C, n_x, K) == cfc.KLOOP_PERSISTENT else "steps"
+    names = {cfc.KLOOP_PERSISTENT: "persistent", cfc.KLOOP_STEPS_VALU: "steps_valu",
+             cfc.KLOOP_STEPS_MFMA: "steps_mfma"}
+    path = names[cfc.cfc_kloop_path(B, C, n_x, K)]
     out = cfc.cfc_train_kloop(*t)
     ms_per_step, trials = time_steps(torch, cfc, t, out, args.steps, args.warmup, args.trials)
     value = 1000.0 / ms_per_step
 
-    # The 2K-launch step-kernel path on the same inputs, for contrast.
-    ms_steps = None
+    # Another path on the same inputs, for contrast: the step kernels after
+    # the persistent path; the other step-kernel variant after a step path.
+    ms_steps, contrast = None, None
     if not args.no_steps_path:
-        cfc.cfc_set_kloop_mode(cfc.KLOOP_STEPS)
-        out_steps = cfc.cfc_train_kloop(*t)
-        ms_steps, _ = time_steps(torch, cfc, t, out_steps, max(20, args.steps // 10), 5, 3)
-        cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+        modes = {"persistent": cfc.KLOOP_STEPS, "steps_mfma": cfc.KLOOP_STEPS_VALU,
+                 "steps_valu": cfc.KLOOP_STEPS_MFMA}
+        cfc.cfc_set_kloop_mode(modes[path])
+        try:
+            taken = cfc.cfc_kloop_path(B, C, n_x, K)
+            if taken >= 0:
+                contrast = names[taken]
+                out_steps = cfc.cfc_train_kloop(*t)
+                ms_steps, _ = time_steps(torch, cfc, t, out_steps, max(20, args.steps // 10), 5, 3)
+        finally:
+            cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
     t_node = graph_node_latency(torch)
@@ -322,6 +332,15 @@ def main():
                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                         "kernel": "kloop_persist_kernel", "flops_per_launch": fl,
                         "launch_us": round(dur * 1e6, 3)}
+        elif path == "steps_mfma":
+            # the 2K step launches of the K-loop (and the one W re-layout), per launch on average
+            dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
+            fl = K * B * 3 * C * (n_in + C) * 2 // (2 * K)
+            achieved = fl / dur
+            roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
+                        "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
+                        "kernel": "fwd_mfma_kernel + bwd_mfma_kernel (average over the 2K step launches)",
+                        "flops_per_launch": fl, "launch_us": round(dur * 1e6, 3)}
         else:
             dur = kt["bwd_step"]["mean_s"]
             by = bwd_launch_bytes(B, C, n_x)
@@ -329,14 +348,13 @@ def main():
                         "unit": "GB/s", "frac": round(by / dur / HBM_PEAK, 4), "traffic": None,
                         "kernel": "bwd_step_kernel", "bytes_per_launch": by, "launch_us": round(dur * 1e6, 3)}
 
-    nodes = 4 if path == "persistent" else 2 * K + 2
+    nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3}[path]
     t_roof = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
     step_roof = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3),
                  "t_roof_ms": round(t_roof * 1e3, 4), "step_over_roof": round(ms_per_step / (t_roof * 1e3), 3),
                  "flops": flops, "bytes_min": bytes_min,
-                 "steps_path_ms_per_step": round(ms_steps, 5) if ms_steps else None,
-                 "steps_path_over_roof": round(ms_steps / (((2 * K + 2) * t_node + max(
-                     flops / FP32_PEAK, bytes_min / HBM_PEAK)) * 1e3), 3) if ms_steps else None}
+                 "contrast_path": contrast,
+                 "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "train-steps/s", "n_gpus": 1,

@@ -124,8 +124,9 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *   ws, ws_bytes         workspace of at least
  *                        cfc_train_kloop_workspace_bytes(B, C, n_x, K) bytes
  *                        (the pre-activation gradients of every step, the
- *                        input projection of every step and the BPTT carry);
- *                        contents are undefined afterwards
+ *                        input projection of every step, the BPTT carry and
+ *                        the step kernels' re-laid copy of W); contents are
+ *                        undefined afterwards
  *   gW_scratch [B, 3, C, n_in], gb_scratch [B, 3, C]   out: per-sample sums
  *                        S[b,q,c,:] = sum_t dp_q[t,b,c] z_t[b,:] (t = K..1)
  *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
@@ -198,20 +199,35 @@ int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist,
                      float* gW_scratch, float* gb_scratch,
                      int B, int C, int n_x, int K, void* stream);
 
-/* Bytes of workspace cfc_train_kloop needs: 4 * (6 K B C + 2 B C).
+/* Bytes of workspace cfc_train_kloop needs: 4 * (round_up(6 K B C + 2 B C, 64)
+ *   + 3 C ldf + 1024 C), ldf = round_up(n_x, 16) + round_up(C, 32).
  * Returns 0 for invalid sizes. */
 size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K);
 
 /* Path selection of cfc_train_kloop for the whole process.
- * CFC_KLOOP_AUTO (default): persistent kernel when C <= 128, else step kernels;
- * CFC_KLOOP_STEPS: always the 2K step-kernel launches;
- * CFC_KLOOP_PERSISTENT: the persistent kernel (cfc_train_kloop then returns
- * CFC_EINVAL for shapes it cannot hold).  Both paths give the same bits. */
-enum cfc_kloop_mode { CFC_KLOOP_AUTO = 0, CFC_KLOOP_STEPS = 1, CFC_KLOOP_PERSISTENT = 2 };
+ * CFC_KLOOP_AUTO (default): the persistent kernel when C <= 128; otherwise
+ *   the step kernels, on MFMA when B >= 64 and the shape fits them (C <= 320
+ *   and n_x <= 128, both multiples of 4; 16-byte aligned arrays), else on
+ *   VALU;
+ * CFC_KLOOP_STEPS: the step kernels, MFMA or VALU as in AUTO;
+ * CFC_KLOOP_PERSISTENT: the persistent kernel;
+ * CFC_KLOOP_STEPS_VALU / CFC_KLOOP_STEPS_MFMA: the step kernels on VALU / on
+ *   MFMA.
+ * A mode that forces a path the sizes cannot take makes cfc_train_kloop and
+ * cfc_kloop_fwd_bwd return CFC_EINVAL.  All paths give the same bits. */
+enum cfc_kloop_mode {
+    CFC_KLOOP_AUTO = 0,
+    CFC_KLOOP_STEPS = 1,
+    CFC_KLOOP_PERSISTENT = 2,
+    CFC_KLOOP_STEPS_VALU = 3,
+    CFC_KLOOP_STEPS_MFMA = 4
+};
 int cfc_set_kloop_mode(int mode);
 
-/* The path cfc_train_kloop takes for these sizes under the current mode
- * (CFC_KLOOP_STEPS or CFC_KLOOP_PERSISTENT), or -1 for invalid sizes. */
+/* The path cfc_train_kloop takes for these sizes under the current mode:
+ * CFC_KLOOP_PERSISTENT, CFC_KLOOP_STEPS_VALU or CFC_KLOOP_STEPS_MFMA (the
+ * workspace is assumed 16-byte aligned); -1 for invalid sizes or a forced
+ * path the sizes cannot take. */
 int cfc_kloop_path(int B, int C, int n_x, int K);
 
 /* Text of the last error raised on the calling thread ("" if none). */

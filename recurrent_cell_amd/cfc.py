@@ -20,6 +20,8 @@ CFC_EHIP = -2
 KLOOP_AUTO = 0
 KLOOP_STEPS = 1
 KLOOP_PERSISTENT = 2
+KLOOP_STEPS_VALU = 3
+KLOOP_STEPS_MFMA = 4
 
 _LIB = None
 _P = ctypes.c_void_p
@@ -242,12 +244,14 @@ def cfc_scratch_fill(dp, u, h_hist, gW_scratch, gb_scratch):
 
 
 def cfc_set_kloop_mode(mode):
-    """KLOOP_AUTO, KLOOP_STEPS or KLOOP_PERSISTENT for the whole process."""
+    """KLOOP_AUTO, KLOOP_STEPS, KLOOP_PERSISTENT, KLOOP_STEPS_VALU or
+    KLOOP_STEPS_MFMA for the whole process."""
     _check("cfc_set_kloop_mode", lib().cfc_set_kloop_mode(int(mode)))
 
 
 def cfc_kloop_path(B, C, n_x, K):
-    """KLOOP_PERSISTENT or KLOOP_STEPS: the path cfc_train_kloop takes now."""
+    """KLOOP_PERSISTENT, KLOOP_STEPS_VALU or KLOOP_STEPS_MFMA: the path
+    cfc_train_kloop takes now (-1 if the current mode cannot take these sizes)."""
     return int(lib().cfc_kloop_path(B, C, n_x, K))
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -151,8 +152,10 @@ int enqueue_reduce(const cfc::ReduceSeg* segs_in, int nseg, int64_t B, hipStream
 }
 
 // Workspace: dp [K, B, 3C] | X [K, B, 3C] (input projection, persistent
-// path) | dh ping-pong [2, B, C] (step path).
-int64_t kloop_ws_floats(int B, int C, int K) { return (int64_t)2 * K * B * 3 * C + (int64_t)2 * B * C; }
+// path) | dh ping-pong [2, B, C] (step path) | padding to 256 bytes | the
+// MFMA step path's re-laid W (forward layout, then backward layout).
+int64_t kloop_ws_wofs(int B, int C, int K) { return ((int64_t)2 * K * B * 3 * C + (int64_t)2 * B * C + 63) & ~(int64_t)63; }
+int64_t kloop_ws_floats(int B, int C, int n_x, int K) { return kloop_ws_wofs(B, C, K) + cfc::mfma_w_floats(C, n_x); }
 
 struct KloopArgs {
     const float *u, *y, *h0, *W, *bias;
@@ -160,32 +163,79 @@ struct KloopArgs {
     int B, C, n_x, K;
 };
 
+// K-loop paths: step kernels on VALU, step kernels on MFMA, persistent.
+enum class Path { Steps = 0, StepsMfma = 1, Persistent = 2 };
+
 std::atomic<int> g_kloop_mode{CFC_KLOOP_AUTO};
 
-bool use_persistent(int mode, int C, int n_x)
+// Smallest batch for which the automatic choice takes the MFMA step kernels
+// (a 16-sample MFMA tile wastes most of its rows below this).
+constexpr int kMfmaMinB = 64;
+
+// The path a K-loop call of these sizes takes in `mode`; false if the mode
+// forces a path the sizes cannot take.
+// `ptrs` (nullable) are the arrays the step kernels read with 16-byte loads;
+// null means: assume them aligned.
+bool choose_path(int mode, int B, int C, int n_x, std::initializer_list<const void*> ptrs, Path* out)
 {
-    if (mode == CFC_KLOOP_STEPS) return false;
-    (void)n_x;   // the input projection runs outside the persistent kernel
-    return cfc::persist_smem(C) != 0;
+    const bool pers_ok = cfc::persist_smem(C) != 0;   // the input projection runs outside it: any n_x
+    bool aligned = true;
+    for (const void* p : ptrs) aligned = aligned && (p == nullptr || aligned16(p));
+    const bool mfma_ok = cfc::mfma_fits(C, n_x) && aligned;
+    switch (mode) {
+    case CFC_KLOOP_PERSISTENT: *out = Path::Persistent; return pers_ok;
+    case CFC_KLOOP_STEPS_VALU: *out = Path::Steps; return true;
+    case CFC_KLOOP_STEPS_MFMA: *out = Path::StepsMfma; return mfma_ok;
+    case CFC_KLOOP_STEPS: *out = (mfma_ok && B >= kMfmaMinB) ? Path::StepsMfma : Path::Steps; return true;
+    default:
+        *out = pers_ok ? Path::Persistent : (mfma_ok && B >= kMfmaMinB) ? Path::StepsMfma : Path::Steps;
+        return true;
+    }
 }
 
 // Forward t = 1..K and backward t = K..1 of every sample, storing dp_t.
-//  persistent path: one kernel, one workgroup per sample;
-//  step path:       K forward step launches (the first also copies h0 into
-//                   h_hist[0]) and K backward step launches.
-int enqueue_fwd_bwd(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, hipStream_t s)
+//  persistent path: the input projection of all steps, then one kernel
+//                   with one workgroup per sample;
+//  step paths:      K forward step launches (the first also copies h0 into
+//                   h_hist[0]) and K backward step launches; the MFMA ones
+//                   after one launch that re-lays W into their operand
+//                   layouts.
+int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipStream_t s)
 {
     const int64_t BC = (int64_t)k.B * k.C;
     const int64_t BX = (int64_t)k.B * k.n_x;
     float* dp = k.ws;                                   // [K, B, 3C]
     float* X = k.ws + (int64_t)k.K * 3 * BC;            // [K, B, 3C]
     float* dh_ws = k.ws + (int64_t)2 * k.K * 3 * BC;    // [2, B, C]
-    if (persistent) {
+    if (path == Path::Persistent) {
         const cfc::XprojArgs x{k.u, k.W, k.bias, X, (int64_t)k.K * k.B, 3 * k.C, k.n_x, k.n_x + k.C,
                                (3 * k.C + 63) / 64};
         CFC_HIP(cfc::launch_xproj(x, s), "input projection launch");
         const cfc::PersistArgs a{X, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
         CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch");
+        return CFC_OK;
+    }
+    if (path == Path::StepsMfma) {
+        const cfc::MfmaLayout L = cfc::mfma_layout(k.C, k.n_x);
+        float* Wf = k.ws + kloop_ws_wofs(k.B, k.C, k.K);
+        float* Wb = Wf + (int64_t)3 * k.C * L.ldf;
+        CFC_HIP(cfc::launch_permute_w(cfc::PermuteArgs{k.W, Wf, Wb, k.C, k.n_x, L}, s), "W re-layout launch");
+        const int nct = (k.C + 15) / 16;
+        for (int t = 1; t <= k.K; ++t) {
+            const float* h_prev = (t == 1) ? k.h0 : k.h_hist + (t - 1) * BC;
+            const cfc::FwdMfmaArgs a{k.u + (t - 1) * BX, h_prev, Wf, k.bias, k.h_hist + t * BC,
+                                     k.act + (int64_t)(t - 1) * 3 * BC, t == 1 ? k.h_hist : nullptr,
+                                     k.B, k.C, k.n_x, nct, L};
+            CFC_HIP(cfc::launch_fwd_mfma(a, s), "forward step launch");
+        }
+        for (int t = k.K; t >= 1; --t) {
+            const int step = k.K - t;  // 0 for t = K
+            const float* dh_in = (t == k.K) ? nullptr : dh_ws + ((step - 1) % 2) * BC;
+            const cfc::BwdMfmaArgs a{k.h_hist + t * BC, k.y + (t - 1) * BC, k.act + (int64_t)(t - 1) * 3 * BC,
+                                     dh_in, Wb, dh_ws + (step % 2) * BC, dp + (int64_t)(t - 1) * 3 * BC,
+                                     k.B, k.C, nct, L};
+            CFC_HIP(cfc::launch_bwd_mfma(a, s), "backward step launch");
+        }
         return CFC_OK;
     }
     for (int t = 1; t <= k.K; ++t) {
@@ -222,10 +272,10 @@ int enqueue_fill(const float* dp, const float* u, const float* h_hist, float* gW
 // The whole K-loop step: forward and backward, the scratch fill (each
 // sample's sums over t, written once) and one reduction launch over both
 // scratch tensors.
-int enqueue_kloop(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, hipStream_t s)
+int enqueue_kloop(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipStream_t s)
 {
     const int n_in = k.n_x + k.C;
-    if (int rc = enqueue_fwd_bwd(k, persistent, p, s)) return rc;
+    if (int rc = enqueue_fwd_bwd(k, path, p, s)) return rc;
     if (int rc = enqueue_fill(k.ws, k.u, k.h_hist, k.gW_s, k.gb_s, k.B, k.C, k.n_x, k.K, s)) return rc;
     cfc::ReduceSeg segs[2] = {
         {k.gW_s, k.gW, (int64_t)3 * k.C * n_in, 0},
@@ -264,7 +314,7 @@ void destroy_entry(GraphEntry& e)
     e = GraphEntry{};
 }
 
-int build_graph(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, int dev, GraphEntry& out)
+int build_graph(const KloopArgs& k, Path path, const cfc::StepPlan& p, int dev, GraphEntry& out)
 {
     hipStream_t cap;
     auto it = g_capture_streams.find(dev);
@@ -275,7 +325,7 @@ int build_graph(const KloopArgs& k, bool persistent, const cfc::StepPlan& p, int
         cap = it->second;
     }
     CFC_HIP(hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal), "graph capture begin");
-    const int rc = enqueue_kloop(k, persistent, p, cap);
+    const int rc = enqueue_kloop(k, path, p, cap);
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(cap, &graph);
     if (rc != CFC_OK) {
@@ -372,13 +422,13 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail, float*
 size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K)
 {
     if (B < 0 || C < 1 || n_x < 0 || K < 0) return 0;
-    return (size_t)kloop_ws_floats(B, C, K) * sizeof(float);
+    return (size_t)kloop_ws_floats(B, C, n_x, K) * sizeof(float);
 }
 
 int cfc_set_kloop_mode(int mode)
 {
     g_last_error.clear();
-    if (mode != CFC_KLOOP_AUTO && mode != CFC_KLOOP_STEPS && mode != CFC_KLOOP_PERSISTENT)
+    if (mode < CFC_KLOOP_AUTO || mode > CFC_KLOOP_STEPS_MFMA)
         return fail(CFC_EINVAL, "cfc_set_kloop_mode: unknown mode %d", mode);
     g_kloop_mode.store(mode);
     return CFC_OK;
@@ -387,19 +437,22 @@ int cfc_set_kloop_mode(int mode)
 int cfc_kloop_path(int B, int C, int n_x, int K)
 {
     if (B < 0 || K < 0 || C < 1 || n_x < 0) return -1;
-    return use_persistent(g_kloop_mode.load(), C, n_x) ? CFC_KLOOP_PERSISTENT : CFC_KLOOP_STEPS;
+    Path path;
+    if (!choose_path(g_kloop_mode.load(), B, C, n_x, {}, &path)) return -1;
+    return path == Path::Persistent ? CFC_KLOOP_PERSISTENT
+         : path == Path::StepsMfma  ? CFC_KLOOP_STEPS_MFMA : CFC_KLOOP_STEPS_VALU;
 }
 
-// Checks shared by cfc_train_kloop and cfc_kloop_fwd_bwd; sets *persistent.
+// Checks shared by cfc_train_kloop and cfc_kloop_fwd_bwd; sets *path.
 static int check_kloop(const char* fn, const float* u, const float* y, const float* h0, const float* W,
                 const float* bias, float* h_hist, float* act, float* ws, size_t ws_bytes, float* gW_scratch,
                 float* gb_scratch, float* gW, float* gb, int B, int C, int n_x, int K, bool full,
-                bool* persistent)
+                Path* path)
 {
     if (int rc = check_dims(B, C, n_x)) return rc;
     if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "%s: K=%d out of range", fn, K);
     const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
-    const int64_t ws_floats = kloop_ws_floats(B, C, K);
+    const int64_t ws_floats = kloop_ws_floats(B, C, n_x, K);
     if (ws_bytes < (size_t)ws_floats * sizeof(float))
         return fail(CFC_EINVAL, "%s: workspace of %zu bytes, %lld needed", fn, ws_bytes,
                     (long long)(ws_floats * 4));
@@ -425,10 +478,13 @@ static int check_kloop(const char* fn, const float* u, const float* y, const flo
         for (int j = i + 1; j < 7; ++j)
             if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "%s: outputs overlap", fn);
     const int mode = g_kloop_mode.load();
-    *persistent = use_persistent(mode, C, n_x);
-    if (mode == CFC_KLOOP_PERSISTENT && !*persistent)
-        return fail(CFC_EINVAL, "%s: the persistent kernel holds C <= 128 channels (C=%d)", fn, C);
-    if (!*persistent)
+    if (!choose_path(mode, B, C, n_x, {ws, u, y, h0, h_hist, act}, path)) {
+        if (mode == CFC_KLOOP_PERSISTENT)
+            return fail(CFC_EINVAL, "%s: the persistent kernel holds C <= 128 channels (C=%d)", fn, C);
+        return fail(CFC_EINVAL, "%s: the MFMA step kernels take C <= 320 and n_x <= 128, both multiples of 4, "
+                    "and 16-byte aligned arrays (C=%d n_x=%d)", fn, C, n_x);
+    }
+    if (*path == Path::Steps)
         if (int rc = check_plan(make_plan(B, C, n_x, W, gW_scratch))) return rc;
     return CFC_OK;
 }
@@ -438,9 +494,9 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
                     float* gb_scratch, float* gW, float* gb, int B, int C, int n_x, int K, void* stream)
 {
     g_last_error.clear();
-    bool persistent = false;
+    Path path = Path::Steps;
     if (int rc = check_kloop("cfc_train_kloop", u, y, h0, W, bias, h_hist, act, ws, ws_bytes, gW_scratch,
-                             gb_scratch, gW, gb, B, C, n_x, K, true, &persistent))
+                             gb_scratch, gW, gb, B, C, n_x, K, true, &path))
         return rc;
     const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
     const cfc::StepPlan p = make_plan(B, C, n_x, W, gW_scratch);
@@ -461,11 +517,11 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
     // scratch fill, reduction), enqueued directly: replaying them as a graph
     // measured about 5 us slower per step.  The step path's 2K + 2 launches
     // go through the cached graph.
-    if (persistent) return enqueue_kloop(k, true, p, s);
+    if (path == Path::Persistent) return enqueue_kloop(k, path, p, s);
 
     int dev = 0;
     CFC_HIP(hipGetDevice(&dev), "hipGetDevice");
-    const GraphKey key{dev, persistent ? 1 : 0, u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch,
+    const GraphKey key{dev, (int)path, u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch,
                        gW, gb, B, C, n_x, K};
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_graphs.find(key);
@@ -478,7 +534,7 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
             g_graphs.erase(victim);
         }
         GraphEntry e;
-        if (int rc = build_graph(k, persistent, p, dev, e)) return rc;
+        if (int rc = build_graph(k, path, p, dev, e)) return rc;
         it = g_graphs.emplace(key, e).first;
     }
     GraphEntry& e = it->second;
@@ -493,9 +549,9 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
                       void* stream)
 {
     g_last_error.clear();
-    bool persistent = false;
+    Path path = Path::Steps;
     if (int rc = check_kloop("cfc_kloop_fwd_bwd", u, y, h0, W, bias, h_hist, act, ws, ws_bytes, nullptr, nullptr,
-                             nullptr, nullptr, B, C, n_x, K, false, &persistent))
+                             nullptr, nullptr, B, C, n_x, K, false, &path))
         return rc;
     const int64_t BC = (int64_t)B * C;
     hipStream_t s = (hipStream_t)stream;
@@ -504,7 +560,7 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
         return CFC_OK;
     }
     const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, nullptr, nullptr, nullptr, nullptr, B, C, n_x, K};
-    return enqueue_fwd_bwd(k, persistent, make_plan(B, C, n_x, W, nullptr), s);
+    return enqueue_fwd_bwd(k, path, make_plan(B, C, n_x, W, nullptr), s);
 }
 
 int cfc_input_projection(const float* u, const float* W, const float* bias, float* X, int64_t M, int C, int n_x,

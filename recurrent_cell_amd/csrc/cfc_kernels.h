@@ -53,6 +53,55 @@ struct FillArgs {
     int B, C, n_x, K, n_rt, n_kt;
 };
 
+// MFMA step path (the K-loop's step kernels at large B).  W is re-laid once
+// per K-loop call into two operand layouts in the workspace:
+//  Wf [3C][ldf]: row r = W[r] with the input columns as they are (zero padded
+//     to nxp = round_up(n_x, 16)) followed by the recurrent columns of each
+//     block of 32 permuted as  Wf[r][nxp + 32 i + 8 e + j] = W[r][n_x + 32 i + 4 j + e]
+//     (zero past C), so that MFMA k-slot e of the eight recurrent partitions
+//     j is one 32-byte run;
+//  Wb [C][64][4][4]: Wb[k][g][kk][p] = W[row of element 4 p + kk of dz group
+//     g][n_x + k] (zero past the group), the carry columns transposed so that
+//     a lane's four k-slots of a group are one float4.
+struct MfmaLayout {
+    int nxp;   // input columns, padded to 16
+    int cp;    // recurrent columns, padded to 32
+    int ldf;   // nxp + cp
+    int pg;    // MFMA instructions per dz group: ceil(3 cpg / 4) (<= 4)
+};
+
+struct PermuteArgs {
+    const float* W;       // [3, C, n_in]
+    float* Wf;            // [3C, ldf]
+    float* Wb;            // [C, 64, 4, 4]
+    int C, n_x;
+    MfmaLayout L;
+};
+
+struct FwdMfmaArgs {
+    const float* u_t;     // [B, n_x]
+    const float* h_prev;  // [B, C]
+    const float* Wf;      // MFMA forward layout
+    const float* bias;    // [3, C]
+    float* h_t;           // [B, C]
+    float* act_t;         // [3, B, C]
+    float* h_prev_copy;   // nullable [B, C]
+    int B, C, n_x, n_ctiles;
+    MfmaLayout L;
+};
+
+struct BwdMfmaArgs {
+    const float* h_t;     // [B, C]
+    const float* y_t;     // [B, C]
+    const float* act_t;   // [3, B, C]
+    const float* dh_in;   // nullable [B, C]
+    const float* Wb;      // MFMA backward layout
+    float* dh_out;        // [B, C] carry to step t - 1
+    float* dp_out;        // [B, 3C] dp of this step
+    int B, C, n_ctiles;
+    MfmaLayout L;
+};
+
 struct XprojArgs {
     const float* u;       // [M, n_x], rows (t, b)
     const float* W;       // [3C, n_in]; columns 0 .. n_x - 1 are used
@@ -117,5 +166,14 @@ hipError_t launch_xproj(const XprojArgs& a, hipStream_t s);
 hipError_t launch_persist(const PersistArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+// MFMA step path: layout for (C, n_x) (valid iff pg <= 4, i.e. C <= 320),
+// workspace floats of the two re-laid copies of W, and the launches.
+MfmaLayout mfma_layout(int C, int n_x);
+int64_t mfma_w_floats(int C, int n_x);
+bool mfma_fits(int C, int n_x);   // both MFMA step kernels can take this shape
+hipError_t launch_permute_w(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_fwd_mfma(const FwdMfmaArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma(const BwdMfmaArgs& a, hipStream_t s);
 
 }  // namespace cfc

@@ -425,6 +425,329 @@ __global__ __launch_bounds__(kThreads) void bwd_step_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// MFMA step path.  Same canonical arithmetic as fwd_step_kernel /
+// bwd_step_kernel (fp32 MFMA accumulates its k-slots in order as an fma
+// chain), with the operands laid out so that every MFMA operand is a float4.
+// ---------------------------------------------------------------------------
+
+// Re-lays W into the forward (Wf) and backward (Wb) operand layouts (see
+// MfmaLayout); zeros wherever the canonical chains have no term.
+__global__ __launch_bounds__(kThreads) void permute_w_kernel(PermuteArgs a)
+{
+    const int C = a.C;
+    const int n_x = a.n_x;
+    const int64_t n_in = (int64_t)n_x + C;
+    const MfmaLayout L = a.L;
+    const int cpg = dz_group_channels(C);
+    const int64_t nf = (int64_t)3 * C * L.ldf;
+    const int64_t nb = (int64_t)C * kDzGroups * 16;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nf + nb; i += (int64_t)gridDim.x * kThreads) {
+        if (i < nf) {
+            const int64_t r = i / L.ldf;
+            const int col = (int)(i - r * L.ldf);
+            float v = 0.0f;
+            if (col < L.nxp) {
+                if (col < n_x) v = a.W[r * n_in + col];
+            } else {
+                const int m = col - L.nxp;   // 32 blk + 8 e + j  <-  recurrent column 32 blk + 4 j + e
+                const int src = 32 * (m >> 5) + 4 * (m & 7) + ((m >> 3) & 3);
+                if (src < C) v = a.W[r * n_in + n_x + src];
+            }
+            a.Wf[i] = v;
+        } else {
+            const int64_t o = i - nf;
+            const int k = (int)(o >> 10);            // carry column
+            const int g = (int)((o >> 4) & 63);
+            const int kk = (int)((o >> 2) & 3);
+            const int p = (int)(o & 3);
+            const int m = 4 * p + kk;                // element of group g's chain
+            float v = 0.0f;
+            if (m < 3 * cpg) {
+                const int c = g * cpg + m / 3;
+                const int q = m - 3 * (m / 3);
+                if (c < C) v = a.W[((int64_t)q * C + c) * n_in + n_x + k];
+            }
+            a.Wb[o] = v;
+        }
+    }
+}
+
+constexpr int kFwdMfmaThreads = 192;   // one wave per head
+constexpr int kMfmaMaxNxb = 8;         // input column blocks of 16: n_x <= 128
+constexpr int kMfmaMaxNhb = 10;        // recurrent column blocks of 32: C <= 320
+constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
+
+// Forward step on MFMA.  Workgroup = 16 samples x 16 channels; wave q forms
+// head q's pre-activations: four input chains (x_r: k-slot kk of block p is
+// column 16 p + 4 kk + r) and eight recurrent partitions (P_j: k-slot e of
+// block i is column n_x + 32 i + 4 j + e), then bias + ((x0+x1)+(x2+x3)) and
+// sum8 -- the canonical order.  A lane's W operands (its channel's row, its
+// k-slot) come straight from the forward layout in global memory, all loads
+// issued up front; z (u as is, h permuted like Wf), shared by the three
+// waves, is staged in LDS with every load in flight before the first store.
+// Then all 192 lanes apply the cell.  Needs n_x, C multiples of 4 and 16-byte
+// aligned rows.  Operand layout (16 x 16 x 4): A[sample l % 16][k-slot l /
+// 16], B[k-slot l / 16][channel l % 16]; D[sample i][channel j] in lane
+// j + 16 (i / 4), register i % 4.
+__global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float zs[16 * (kMfmaMaxLdf + 4)];
+    __shared__ float as[3 * 16 * 16];
+    const MfmaLayout L = a.L;
+    const int C = a.C;
+    const int n_x = a.n_x;
+    const int nxb = L.nxp / 16;
+    const int nhb = L.cp / 32;
+    const int ctile = blockIdx.x % a.n_ctiles;
+    const int btile = blockIdx.x / a.n_ctiles;
+    const int s0 = btile * 16;
+    const int c0 = ctile * 16;
+    const int ldp = L.ldf + 4;              // row pitch: 4 banks between rows
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int q = tid >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+
+    // W operands of this lane: channel c0 + li of head q, k-slot lk
+    // (indices clamped into the row; the extra loads are never used).
+    const float* wrow = a.Wf + ((int64_t)q * C + min(c0 + li, C - 1)) * L.ldf;
+    f32x4 wx[kMfmaMaxNxb], wh[kMfmaMaxNhb][2];
+#pragma unroll
+    for (int p = 0; p < kMfmaMaxNxb; ++p)
+        wx[p] = *reinterpret_cast<const f32x4*>(wrow + 16 * min(p, max(nxb - 1, 0)) + 4 * lk);
+#pragma unroll
+    for (int i = 0; i < kMfmaMaxNhb; ++i) {
+        const float* w = wrow + L.nxp + 32 * min(i, nhb - 1) + 8 * lk;
+        wh[i][0] = *reinterpret_cast<const f32x4*>(w);
+        wh[i][1] = *reinterpret_cast<const f32x4*>(w + 4);
+    }
+
+    // z rows in float4 units: unit u of row s covers columns 4 u .. 4 u + 3
+    // of [u ; h] in their natural order (zero past n_x, past C and for
+    // absent samples); h goes to its permuted LDS place.
+    {
+        const int w4 = L.ldf / 4;
+        constexpr int kZSlots = (16 * kMfmaMaxLdf / 4 + kFwdMfmaThreads - 1) / kFwdMfmaThreads;
+        f32x4 v[kZSlots];
+#pragma unroll
+        for (int m = 0; m < kZSlots; ++m) {
+            const int i = min(tid + m * kFwdMfmaThreads, 16 * w4 - 1);
+            const int s = i / w4;
+            const int u4 = i - s * w4;
+            const int64_t b = min(s0 + s, a.B - 1);
+            const float* src = (4 * u4 < L.nxp) ? a.u_t + b * n_x + min(4 * u4, max(n_x - 4, 0))
+                                                : a.h_prev + b * C + min(4 * u4 - L.nxp, C - 4);
+            v[m] = *reinterpret_cast<const f32x4*>(src);
+        }
+#pragma unroll
+        for (int m = 0; m < kZSlots; ++m) {
+            const int i = tid + m * kFwdMfmaThreads;
+            if (i < 16 * w4) {
+                const int s = i / w4;
+                const int u4 = i - s * w4;
+                const bool live = s0 + s < a.B;
+                float* row = zs + s * ldp;
+                if (4 * u4 < L.nxp) {
+                    const bool ok = live && 4 * u4 < n_x;
+                    *reinterpret_cast<f32x4*>(row + 4 * u4) = ok ? v[m] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                } else {
+                    const int m0 = 4 * u4 - L.nxp;              // recurrent columns m0 .. m0 + 3
+                    const bool ok = live && m0 < C;
+                    const int base = L.nxp + 32 * (m0 >> 5) + ((m0 & 31) >> 2);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) row[base + 8 * e] = ok ? v[m][e] : 0.0f;
+                }
+            }
+        }
+    }
+    if (a.h_prev_copy != nullptr && ctile == 0) {
+        const int nb = min(16, a.B - s0);
+        for (int i = tid; i < nb * C; i += kFwdMfmaThreads) {
+            const int64_t idx = (int64_t)s0 * C + i;
+            a.h_prev_copy[idx] = a.h_prev[idx];
+        }
+    }
+    __syncthreads();
+
+    const float* zr = zs + li * ldp;                 // sample li
+    f32x4 ax[4], ah[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ax[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ah[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < kMfmaMaxNxb; ++p) {
+        if (p < nxb) {
+            const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ax[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wx[p][c], ax[c], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMfmaMaxNhb; ++i) {
+        if (i < nhb) {
+            const int o = L.nxp + 32 * i + 8 * lk;
+            const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + o);
+            const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + o + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ah[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z0[j], wh[i][0][j], ah[j], 0, 0, 0);
+                ah[4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z1[j], wh[i][1][j], ah[4 + j], 0, 0, 0);
+            }
+        }
+    }
+    const float bias = a.bias[q * C + min(c0 + li, C - 1)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float X = xproj_combine(bias, ax[0][e], ax[1][e], ax[2][e], ax[3][e]);
+        const float H = ((ah[0][e] + ah[1][e]) + (ah[2][e] + ah[3][e])) + ((ah[4][e] + ah[5][e]) + (ah[6][e] + ah[7][e]));
+        as[(q * 16 + 4 * lk + e) * 16 + li] = X + H;
+    }
+    __syncthreads();
+
+    const int64_t BC = (int64_t)a.B * C;
+    for (int i = tid; i < 256; i += kFwdMfmaThreads) {
+        const int s = i >> 4;
+        const int cl = i & 15;
+        const int b = s0 + s;
+        const int c = c0 + cl;
+        if (b < a.B && c < C) {
+            const CellOut o = cell_forward(as[s * 16 + cl], as[(16 + s) * 16 + cl], as[(32 + s) * 16 + cl]);
+            const int64_t bc = (int64_t)b * C + c;
+            a.h_t[bc] = o.h;
+            a.act_t[bc] = o.gate;
+            a.act_t[BC + bc] = o.g;
+            a.act_t[2 * BC + bc] = o.hh;
+        }
+    }
+}
+
+// Backward step (K-loop: dp out, carry) on MFMA.  Workgroup = 16 samples x
+// 16 carry columns.  dp of the tile's samples for every channel goes to LDS
+// in the MFMA layout dps[s][g][kk][p] (element 4 p + kk of group g's chain);
+// the workgroup stores dp of its own 16 channels.  Wave w forms the canonical
+// subtree T_w of dz over groups g = w + 4 m (m = 0..15): P_g is pg MFMAs
+// from +0, and the pairwise tree is built as the groups arrive (a binary
+// counter of partial sums -- the pairing of tree_sum16).  Then
+// dz = (T0 + T1) + (T2 + T3).
+constexpr int kBwdMfmaThreads = 256;
+
+__global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float dps[16 * kDzGroups * 16];
+    __shared__ __attribute__((aligned(16))) float ts[4][16][17];
+    const MfmaLayout L = a.L;
+    const int C = a.C;
+    const int cpg = dz_group_channels(C);
+    const int ctile = blockIdx.x % a.n_ctiles;
+    const int btile = blockIdx.x / a.n_ctiles;
+    const int s0 = btile * 16;
+    const int k0 = ctile * 16;
+    const int tid = threadIdx.x;
+    const int64_t BC = (int64_t)a.B * C;
+
+    for (int i = tid; i < 16 * kDzGroups * 16; i += kBwdMfmaThreads) dps[i] = 0.0f;
+    // dp of (sample s, channels 4 c4 .. 4 c4 + 3) for the tile's samples and
+    // every channel: every load of the pass in flight before the arithmetic.
+    const int c4n = C / 4;
+    constexpr int kDSlots = (16 * 320 / 4 + kBwdMfmaThreads - 1) / kBwdMfmaThreads;
+    f32x4 vh[kDSlots], vy[kDSlots], vd[kDSlots], vg0[kDSlots], vg1[kDSlots], vg2[kDSlots];
+#pragma unroll
+    for (int m = 0; m < kDSlots; ++m) {
+        const int i = min(tid + m * kBwdMfmaThreads, 16 * c4n - 1);
+        const int s = i / c4n;
+        const int64_t bc = (int64_t)min(s0 + s, a.B - 1) * C + 4 * (i - s * c4n);
+        vh[m] = *reinterpret_cast<const f32x4*>(a.h_t + bc);
+        vy[m] = *reinterpret_cast<const f32x4*>(a.y_t + bc);
+        vd[m] = (a.dh_in != nullptr) ? *reinterpret_cast<const f32x4*>(a.dh_in + bc) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        vg0[m] = *reinterpret_cast<const f32x4*>(a.act_t + bc);
+        vg1[m] = *reinterpret_cast<const f32x4*>(a.act_t + BC + bc);
+        vg2[m] = *reinterpret_cast<const f32x4*>(a.act_t + 2 * BC + bc);
+    }
+    __syncthreads();   // zeros of dps in place before the dp stores
+#pragma unroll
+    for (int m = 0; m < kDSlots; ++m) {
+        const int i = tid + m * kBwdMfmaThreads;
+        const int s = i / c4n;
+        if (i < 16 * c4n && s0 + s < a.B) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 4 * (i - s * c4n) + e;
+                float dh = vh[m][e] - vy[m][e];
+                if (a.dh_in != nullptr) dh += vd[m][e];
+                float d[3];
+                cell_backward(dh, vg0[m][e], vg1[m][e], vg2[m][e], d[0], d[1], d[2]);
+                const int g = c / cpg;
+                const int cl = c - g * cpg;
+#pragma unroll
+                for (int qq = 0; qq < 3; ++qq) {
+                    const int el = 3 * cl + qq;
+                    dps[(s * kDzGroups + g) * 16 + 4 * (el & 3) + (el >> 2)] = d[qq];
+                }
+                if (c >= k0 && c < k0 + 16) {
+                    const int64_t row = (int64_t)(s0 + s) * 3 * C;
+#pragma unroll
+                    for (int qq = 0; qq < 3; ++qq) a.dp_out[row + qq * C + c] = d[qq];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const float* wb = a.Wb + ((int64_t)min(k0 + li, C - 1) * kDzGroups) * 16 + 4 * lk;   // + 16 g
+    const float* da = dps + li * kDzGroups * 16 + 4 * lk;                                 // + 16 g
+    f32x4 bv[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) bv[m] = *reinterpret_cast<const f32x4*>(wb + 16 * (w + 4 * m));
+    __builtin_amdgcn_sched_barrier(0);   // the 16 loads ahead of the MFMAs
+    f32x4 l0 = {0.0f, 0.0f, 0.0f, 0.0f}, l1 = l0, l2 = l0, l3 = l0, T = l0;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * m));
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            if (p < L.pg) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[p], bv[m][p], acc, 0, 0, 0);
+        // pairwise tree of the 16 group partials, in tree_sum16's pairing
+        if ((m & 1) == 0) {
+            l0 = acc;
+        } else {
+            const f32x4 x = l0 + acc;
+            if ((m & 2) == 0) {
+                l1 = x;
+            } else {
+                const f32x4 y = l1 + x;
+                if ((m & 4) == 0) {
+                    l2 = y;
+                } else {
+                    const f32x4 z = l2 + y;
+                    if ((m & 8) == 0)
+                        l3 = z;
+                    else
+                        T = l3 + z;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ts[w][4 * lk + e][li] = T[e];
+    __syncthreads();
+    {
+        const int s = tid >> 4;
+        const int col = tid & 15;
+        const int b = s0 + s;
+        const int k = k0 + col;
+        if (b < a.B && k < C)
+            a.dh_out[(int64_t)b * C + k] = (ts[0][s][col] + ts[1][s][col]) + (ts[2][s][col] + ts[3][s][col]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Deferred scratch fill (K-loop): S[b, r, k] = fma chain over t = K .. 1 of
 // dp_t[b, r] * z_t[b, k] from +0 -- the same bits as K per-step "+=" updates
 // of a zeroed scratch -- and Sb[b, r] = add chain of dp_t[b, r].  Per sample
@@ -1112,6 +1435,57 @@ hipError_t launch_fill(const FillArgs& a, hipStream_t s)
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(scratch_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+MfmaLayout mfma_layout(int C, int n_x)
+{
+    MfmaLayout L;
+    L.nxp = (n_x + 15) & ~15;
+    L.cp = (C + 31) & ~31;
+    L.ldf = L.nxp + L.cp;
+    L.pg = (3 * dz_group_channels(C) + 3) / 4;
+    return L;
+}
+
+int64_t mfma_w_floats(int C, int n_x)
+{
+    const MfmaLayout L = mfma_layout(C, n_x);
+    return (int64_t)3 * C * L.ldf + (int64_t)C * kDzGroups * 16;
+}
+
+bool mfma_fits(int C, int n_x)
+{
+    const MfmaLayout L = mfma_layout(C, n_x);
+    return L.pg <= 4 && n_x % 4 == 0 && C % 4 == 0 && L.nxp <= 16 * kMfmaMaxNxb && L.cp <= 32 * kMfmaMaxNhb;
+}
+
+hipError_t launch_permute_w(const PermuteArgs& a, hipStream_t s)
+{
+    const int64_t total = (int64_t)3 * a.C * a.L.ldf + (int64_t)a.C * kDzGroups * 16;
+    const int64_t blocks = min((total + kThreads - 1) / kThreads, (int64_t)4096);
+    hipLaunchKernelGGL(permute_w_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma(const FwdMfmaArgs& a, hipStream_t s)
+{
+    if (!mfma_fits(a.C, a.n_x) || a.n_ctiles != (a.C + 15) / 16) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)((a.B + 15) / 16) * a.n_ctiles;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fwd_mfma_kernel, dim3((unsigned)blocks), dim3(kFwdMfmaThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_mfma(const BwdMfmaArgs& a, hipStream_t s)
+{
+    if (a.L.pg > 4 || a.C % 4 != 0 || a.C > 32 * kMfmaMaxNhb || a.n_ctiles != (a.C + 15) / 16)
+        return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)((a.B + 15) / 16) * a.n_ctiles;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_mfma_kernel, dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a);
     return hipGetLastError();
 }
 

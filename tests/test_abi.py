@@ -86,7 +86,7 @@ def test_step_argument_errors(L):
 def _kloop_args(B, C, n_x, K):
     """Twelve fake, non-overlapping addresses and a large enough workspace size."""
     a = [FAKE + (i << 28) for i in range(12)]
-    return a[:8] + [4 * (6 * K * B * C + 2 * B * C)] + a[8:]
+    return a[:8] + [ws_bytes(B, C, n_x, K)] + a[8:]
 
 
 def test_kloop_argument_errors(L):
@@ -128,23 +128,42 @@ def test_projection_and_recurrence_argument_errors(L):
     assert L.cfc_kloop_recurrence(*a, 4, 16, 8, -1, None) == -1
 
 
+def ws_bytes(B, C, n_x, K):
+    ldf = (n_x + 15) // 16 * 16 + (C + 31) // 32 * 32
+    return 4 * (((6 * K * B * C + 2 * B * C + 63) // 64) * 64 + 3 * C * ldf + 1024 * C)
+
+
 def test_workspace_size_and_path_queries(L):
-    assert L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) == 4 * (6 * 64 * 32 * 128 + 2 * 32 * 128)
+    assert L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) == ws_bytes(32, 128, 64, 64)
+    assert L.cfc_train_kloop_workspace_bytes(3, 37, 5, 7) == ws_bytes(3, 37, 5, 7)
     assert L.cfc_train_kloop_workspace_bytes(-1, 128, 64, 64) == 0
-    # W of the pages-shaped cell (3 x 128 x 192) fits the persistent kernel; the wide one does not
-    assert L.cfc_kloop_path(32, 128, 64, 64) == 2
-    assert L.cfc_kloop_path(256, 256, 128, 64) == 1
-    assert L.cfc_kloop_path(4, 16, 8, 4) == 2
-    assert L.cfc_kloop_path(4, 64, 100, 4) == 2     # n_x does not matter: X is precomputed
-    assert L.cfc_kloop_path(4, 48, 300, 4) == 2
-    assert L.cfc_kloop_path(4, 100, 20, 4) == 2     # 2 channels per dz group
-    assert L.cfc_kloop_path(4, 128, 4000, 4) == 2
-    assert L.cfc_kloop_path(4, 129, 0, 4) == 1      # 3 channels per dz group: step path
+    # persistent kernel for C <= 128 (any n_x: X is precomputed); step kernels otherwise,
+    # on MFMA from B = 64 where the shape fits them (C <= 320, n_x + C up to ~540)
+    P, VALU, MFMA = 2, 3, 4
+    assert L.cfc_kloop_path(32, 128, 64, 64) == P
+    assert L.cfc_kloop_path(256, 256, 128, 64) == MFMA
+    assert L.cfc_kloop_path(32, 256, 128, 64) == VALU      # B below the MFMA threshold
+    assert L.cfc_kloop_path(256, 512, 0, 64) == VALU       # 8 channels per dz group: no MFMA layout
+    assert L.cfc_kloop_path(256, 256, 400, 64) == VALU     # rows too long for the MFMA LDS tile
+    assert L.cfc_kloop_path(4, 16, 8, 4) == P
+    assert L.cfc_kloop_path(4, 64, 100, 4) == P
+    assert L.cfc_kloop_path(4, 48, 300, 4) == P
+    assert L.cfc_kloop_path(4, 100, 20, 4) == P              # 2 channels per dz group
+    assert L.cfc_kloop_path(4, 128, 4000, 4) == P
+    assert L.cfc_kloop_path(4, 129, 0, 4) == VALU
     assert L.cfc_set_kloop_mode(7) == -1
-    assert L.cfc_set_kloop_mode(1) == 0
-    assert L.cfc_kloop_path(32, 128, 64, 64) == 1
+    assert L.cfc_set_kloop_mode(1) == 0                      # steps: MFMA or VALU by shape
+    assert L.cfc_kloop_path(32, 128, 64, 64) == VALU
+    assert L.cfc_kloop_path(64, 128, 64, 64) == MFMA
+    assert L.cfc_set_kloop_mode(4) == 0                      # MFMA forced
+    assert L.cfc_kloop_path(4, 16, 8, 4) == MFMA
+    assert L.cfc_kloop_path(256, 512, 0, 64) == -1
+    assert L.cfc_set_kloop_mode(3) == 0                      # VALU forced
+    assert L.cfc_kloop_path(256, 256, 128, 64) == VALU
+    assert L.cfc_set_kloop_mode(2) == 0                      # persistent forced
+    assert L.cfc_kloop_path(4, 129, 0, 4) == -1
     assert L.cfc_set_kloop_mode(0) == 0
-    assert L.cfc_kloop_path(32, 128, 64, 64) == 2
+    assert L.cfc_kloop_path(32, 128, 64, 64) == P
 
 
 def test_no_atomics_in_kernel_sources():

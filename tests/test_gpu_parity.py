@@ -33,6 +33,12 @@ CASES = {
 }
 
 
+def need_path(cfc, d):
+    """Skip when the forced K-loop path cannot take this shape."""
+    if cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"], d["K"]) < 0:
+        pytest.skip("the forced path cannot take this shape")
+
+
 def say(*a):
     print("[gpu-case]", *a, flush=True)
     sys.stdout.flush()
@@ -50,7 +56,8 @@ def cfc():
 @pytest.fixture
 def path(cfc, request):
     """Force a K-loop path for one test ("auto" keeps the default), then restore it."""
-    mode = {"auto": cfc.KLOOP_AUTO, "steps": cfc.KLOOP_STEPS, "persistent": cfc.KLOOP_PERSISTENT}[request.param]
+    mode = {"auto": cfc.KLOOP_AUTO, "steps": cfc.KLOOP_STEPS, "persistent": cfc.KLOOP_PERSISTENT,
+            "steps_valu": cfc.KLOOP_STEPS_VALU, "steps_mfma": cfc.KLOOP_STEPS_MFMA}[request.param]
     cfc.cfc_set_kloop_mode(mode)
     yield request.param
     cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
@@ -76,14 +83,19 @@ def bits(a):
 
 # ---------------------------------------------------------------- K-loop parity
 
-@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+PATH_NAMES = {2: "persistent", 3: "steps_valu", 4: "steps_mfma"}
+
+
+@pytest.mark.parametrize("path", ["auto", "steps_valu", "steps_mfma"], indirect=True)
 @pytest.mark.parametrize("case", list(CASES))
 def test_kloop_matches_oracle(cfc, oracle_mod, case, path):
     d = CASES[case]
     taken = cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"], d["K"])
-    if path == "auto" and taken == cfc.KLOOP_STEPS:
-        pytest.skip("auto takes the step path here; covered by the 'steps' case")
-    say("kloop parity", case, d, "path", path, "->", "persistent" if taken == cfc.KLOOP_PERSISTENT else "steps")
+    if taken < 0:
+        pytest.skip("the forced path cannot take this shape")
+    if path == "auto" and taken != cfc.KLOOP_PERSISTENT:
+        pytest.skip("auto takes a step path here; covered by the forced step cases")
+    say("kloop parity", case, d, "path", path, "->", PATH_NAMES[taken])
     x = cfc_inputs(**d, seed=1, bias_scale=0.2)
     out, _ = kloop_dev(cfc, x)
     g = {k: host(getattr(out, k)) for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
@@ -200,9 +212,10 @@ def test_recurrence_composes_to_fwd_bwd(cfc, case):
 
 # ---------------------------------------------------------------- structure, bit for bit
 
-@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+@pytest.mark.parametrize("path", ["auto", "steps_valu", "steps_mfma"], indirect=True)
 def test_kloop_is_deterministic_and_replay_stable(cfc, path):
     d = CASES["pages"]
+    need_path(cfc, d)
     say("kloop determinism", path)
     x = cfc_inputs(**d, seed=5, bias_scale=0.1)
     a, _ = kloop_dev(cfc, x)
@@ -216,7 +229,7 @@ def test_kloop_is_deterministic_and_replay_stable(cfc, path):
         np.testing.assert_array_equal(bits(host(getattr(a, k))), bits(v), err_msg=k)
 
 
-@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+@pytest.mark.parametrize("path", ["auto", "steps_valu", "steps_mfma"], indirect=True)
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "sample_tiles", "three_tiles", "no_input",
                                   "long_input64", "two_channel_groups", "three_blocks", "odd_channels"])
 def test_kloop_equals_eager_step_calls(cfc, case, path):
@@ -224,6 +237,7 @@ def test_kloop_equals_eager_step_calls(cfc, case, path):
     replay) gives the bits of the eager composition of single-step ABI calls
     with per-step scratch +=."""
     d = CASES[case]
+    need_path(cfc, d)
     say("kloop == eager", case, path)
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
     x = cfc_inputs(**d, seed=6, bias_scale=0.2)
@@ -252,29 +266,36 @@ def test_kloop_equals_eager_step_calls(cfc, case, path):
 @pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input",
                                   "long_input64", "long_input48", "two_channel_groups", "three_blocks",
                                   "odd_channels"])
-def test_persistent_and_step_paths_agree_bitwise(cfc, case):
+def test_all_kloop_paths_agree_bitwise(cfc, case):
+    """Persistent kernel, VALU step kernels and MFMA step kernels: the same bits."""
     d = CASES[case]
-    say("persistent == steps", case)
+    say("persistent == steps_valu == steps_mfma", case)
     x = cfc_inputs(**d, seed=14, bias_scale=0.25)
     res = {}
-    for mode in (cfc.KLOOP_PERSISTENT, cfc.KLOOP_STEPS):
+    for mode in (cfc.KLOOP_PERSISTENT, cfc.KLOOP_STEPS_VALU, cfc.KLOOP_STEPS_MFMA):
         cfc.cfc_set_kloop_mode(mode)
         try:
+            if cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"], d["K"]) < 0:
+                continue
             out, _ = kloop_dev(cfc, x)
             res[mode] = {k: host(getattr(out, k)).copy()
                          for k in ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")}
         finally:
             cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
-    for k in res[cfc.KLOOP_STEPS]:
-        np.testing.assert_array_equal(bits(res[cfc.KLOOP_PERSISTENT][k]), bits(res[cfc.KLOOP_STEPS][k]), err_msg=k)
+    assert len(res) >= 2
+    ref_mode = cfc.KLOOP_STEPS_VALU
+    for mode, r in res.items():
+        for k in r:
+            np.testing.assert_array_equal(bits(r[k]), bits(res[ref_mode][k]), err_msg="%s %d" % (k, mode))
 
 
-@pytest.mark.parametrize("path", ["auto", "steps"], indirect=True)
+@pytest.mark.parametrize("path", ["auto", "steps_valu", "steps_mfma"], indirect=True)
 @pytest.mark.parametrize("case", ["pages", "three_tiles"])
 def test_kloop_equals_its_phases(cfc, case, path):
     """cfc_train_kloop == cfc_kloop_fwd_bwd, then cfc_scratch_fill, then
     reduce_axis0 on each scratch tensor, bit for bit."""
     d = CASES[case]
+    need_path(cfc, d)
     say("kloop == phases", case, path)
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
     x = cfc_inputs(**d, seed=15, bias_scale=0.2)
