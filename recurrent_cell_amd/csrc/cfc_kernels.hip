@@ -481,17 +481,16 @@ constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
 // head q's pre-activations: four input chains (x_r: k-slot kk of block p is
 // column 16 p + 4 kk + r) and eight recurrent partitions (P_j: k-slot e of
 // block i is column n_x + 32 i + 4 j + e), then bias + ((x0+x1)+(x2+x3)) and
-// sum8 -- the canonical order.  A lane's W operands (its channel's row, its
-// k-slot) come straight from the forward layout in global memory, all loads
-// issued up front; z (u as is, h permuted like Wf), shared by the three
-// waves, is staged in LDS with every load in flight before the first store.
-// Then all 192 lanes apply the cell.  Needs n_x, C multiples of 4 and 16-byte
+// sum8 -- the canonical order.  The tile's 48 W rows (forward layout) and z
+// (u as is, h permuted like Wf) are staged in LDS, every load in flight
+// before the first LDS store.  Then all 192 lanes apply the cell.  Needs n_x, C multiples of 4 and 16-byte
 // aligned rows.  Operand layout (16 x 16 x 4): A[sample l % 16][k-slot l /
 // 16], B[k-slot l / 16][channel l % 16]; D[sample i][channel j] in lane
 // j + 16 (i / 4), register i % 4.
 __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a)
 {
     __shared__ __attribute__((aligned(16))) float zs[16 * (kMfmaMaxLdf + 4)];
+    __shared__ __attribute__((aligned(16))) float wsm[48 * (kMfmaMaxLdf + 4)];
     __shared__ float as[3 * 16 * 16];
     const MfmaLayout L = a.L;
     const int C = a.C;
@@ -509,18 +508,28 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     const int li = lane & 15;
     const int lk = lane >> 4;
 
-    // W operands of this lane: channel c0 + li of head q, k-slot lk
-    // (indices clamped into the row; the extra loads are never used).
-    const float* wrow = a.Wf + ((int64_t)q * C + min(c0 + li, C - 1)) * L.ldf;
-    f32x4 wx[kMfmaMaxNxb], wh[kMfmaMaxNhb][2];
+    // The tile's 48 W rows (head-major, channels c0 .. c0 + 15) from the
+    // forward layout into LDS: contiguous float4 loads, all in flight before
+    // the first LDS store (indices clamped; the extra loads are not stored).
+    {
+        const int w4 = L.ldf / 4;
+        constexpr int kWSlots = (48 * kMfmaMaxLdf / 4 + kFwdMfmaThreads - 1) / kFwdMfmaThreads;
+        f32x4 v[kWSlots];
 #pragma unroll
-    for (int p = 0; p < kMfmaMaxNxb; ++p)
-        wx[p] = *reinterpret_cast<const f32x4*>(wrow + 16 * min(p, max(nxb - 1, 0)) + 4 * lk);
+        for (int m = 0; m < kWSlots; ++m) {
+            const int i = min(tid + m * kFwdMfmaThreads, 48 * w4 - 1);
+            const int row = i / w4;
+            const int c = min(c0 + (row & 15), C - 1);
+            v[m] = *reinterpret_cast<const f32x4*>(a.Wf + ((int64_t)(row >> 4) * C + c) * L.ldf + 4 * (i - row * w4));
+        }
 #pragma unroll
-    for (int i = 0; i < kMfmaMaxNhb; ++i) {
-        const float* w = wrow + L.nxp + 32 * min(i, nhb - 1) + 8 * lk;
-        wh[i][0] = *reinterpret_cast<const f32x4*>(w);
-        wh[i][1] = *reinterpret_cast<const f32x4*>(w + 4);
+        for (int m = 0; m < kWSlots; ++m) {
+            const int i = tid + m * kFwdMfmaThreads;
+            if (i < 48 * w4) {
+                const int row = i / w4;
+                *reinterpret_cast<f32x4*>(wsm + row * ldp + 4 * (i - row * w4)) = v[m];
+            }
+        }
     }
 
     // z rows in float4 units: unit u of row s covers columns 4 u .. 4 u + 3
@@ -571,30 +580,32 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     __syncthreads();
 
     const float* zr = zs + li * ldp;                 // sample li
+    const float* wr = wsm + (q * 16 + li) * ldp;     // channel c0 + li, head q
     f32x4 ax[4], ah[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) ax[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) ah[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Runtime trip counts keep the accumulators in place across iterations;
+    // unrolling by 2 lets the next iteration's LDS reads overlap the MFMAs.
+#pragma unroll 2
+    for (int p = 0; p < nxb; ++p) {
+        const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + 16 * p + 4 * lk);
 #pragma unroll
-    for (int p = 0; p < kMfmaMaxNxb; ++p) {
-        if (p < nxb) {
-            const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) ax[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wx[p][c], ax[c], 0, 0, 0);
-        }
+        for (int c = 0; c < 4; ++c) ax[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wv[c], ax[c], 0, 0, 0);
     }
+#pragma unroll 2
+    for (int i = 0; i < nhb; ++i) {
+        const int o = L.nxp + 32 * i + 8 * lk;
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + o);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + o + 4);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wr + o);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wr + o + 4);
 #pragma unroll
-    for (int i = 0; i < kMfmaMaxNhb; ++i) {
-        if (i < nhb) {
-            const int o = L.nxp + 32 * i + 8 * lk;
-            const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + o);
-            const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + o + 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ah[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z0[j], wh[i][0][j], ah[j], 0, 0, 0);
-                ah[4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z1[j], wh[i][1][j], ah[4 + j], 0, 0, 0);
-            }
+        for (int j = 0; j < 4; ++j) {
+            ah[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z0[j], w0[j], ah[j], 0, 0, 0);
+            ah[4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z1[j], w1[j], ah[4 + j], 0, 0, 0);
         }
     }
     const float bias = a.bias[q * C + min(c0 + li, C - 1)];
@@ -627,12 +638,13 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
 // 16 carry columns.  dp of the tile's samples for every channel goes to LDS
 // in the MFMA layout dps[s][g][kk][p] (element 4 p + kk of group g's chain);
 // the workgroup stores dp of its own 16 channels.  Wave w forms the canonical
-// subtree T_w of dz over groups g = w + 4 m (m = 0..15): P_g is pg MFMAs
-// from +0, and the pairwise tree is built as the groups arrive (a binary
-// counter of partial sums -- the pairing of tree_sum16).  Then
+// subtree T_w of dz over groups g = w + 4 m (m = 0..15): P_g is a chain of
+// PG MFMAs from +0 (the 16 chains independent, so their instructions
+// interleave), then the pairwise tree of tree_sum16.  Then
 // dz = (T0 + T1) + (T2 + T3).
 constexpr int kBwdMfmaThreads = 256;
 
+template <int PG>
 __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a)
 {
     __shared__ __attribute__((aligned(16))) float dps[16 * kDzGroups * 16];
@@ -705,35 +717,24 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
 #pragma unroll
     for (int m = 0; m < 16; ++m) bv[m] = *reinterpret_cast<const f32x4*>(wb + 16 * (w + 4 * m));
     __builtin_amdgcn_sched_barrier(0);   // the 16 loads ahead of the MFMAs
-    f32x4 l0 = {0.0f, 0.0f, 0.0f, 0.0f}, l1 = l0, l2 = l0, l3 = l0, T = l0;
+    // The 16 group partials as independent MFMA chains (so that their
+    // instructions interleave), then the pairwise tree of tree_sum16.
+    f32x4 av[16], P[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * m));
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < 16; ++m) av[m] = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * m));
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            if (p < L.pg) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[p], bv[m][p], acc, 0, 0, 0);
-        // pairwise tree of the 16 group partials, in tree_sum16's pairing
-        if ((m & 1) == 0) {
-            l0 = acc;
-        } else {
-            const f32x4 x = l0 + acc;
-            if ((m & 2) == 0) {
-                l1 = x;
-            } else {
-                const f32x4 y = l1 + x;
-                if ((m & 4) == 0) {
-                    l2 = y;
-                } else {
-                    const f32x4 z = l2 + y;
-                    if ((m & 8) == 0)
-                        l3 = z;
-                    else
-                        T = l3 + z;
-                }
-            }
-        }
-    }
+    for (int m = 0; m < 16; ++m) P[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < PG; ++p)
+#pragma unroll
+        for (int m = 0; m < 16; ++m) P[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][p], bv[m][p], P[m], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) P[m] = P[2 * m] + P[2 * m + 1];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) P[m] = P[2 * m] + P[2 * m + 1];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) P[m] = P[2 * m] + P[2 * m + 1];
+    const f32x4 T = P[0] + P[1];
 #pragma unroll
     for (int e = 0; e < 4; ++e) ts[w][4 * lk + e][li] = T[e];
     __syncthreads();
@@ -1485,7 +1486,12 @@ hipError_t launch_bwd_mfma(const BwdMfmaArgs& a, hipStream_t s)
     const int64_t blocks = (int64_t)((a.B + 15) / 16) * a.n_ctiles;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_mfma_kernel, dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a);
+    switch (a.L.pg) {
+    case 1: hipLaunchKernelGGL((bwd_mfma_kernel<1>), dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((bwd_mfma_kernel<2>), dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((bwd_mfma_kernel<3>), dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((bwd_mfma_kernel<4>), dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
