@@ -204,6 +204,26 @@ def bench_reduce(torch, cfc, timer, shapes):
     return res
 
 
+def bench_adamw(torch, cfc, timer, sizes_list):
+    """AdamW after the reducer: one fused launch over the given segments.
+    Algorithmic bytes per element: read p, g, m, v and write p, m, v (28 B)."""
+    rows = []
+    for sizes in sizes_list:
+        segs = [[torch.randn(n, device="cuda") * s for n in sizes] for s in (0.5, 1e-2, 1e-2, 1e-2)]
+        segs[3] = [v.square() for v in segs[3]]
+        it = [0]
+
+        def run():
+            it[0] += 1
+            cfc.cfc_adamw_step(*segs, 1e-3, 0.9, 0.999, 1e-8, 0.01, it[0])
+        r = timer(run, 20 if sum(sizes) > (1 << 22) else 50)
+        by = 28 * sum(sizes)
+        rows.append(dict(sizes=list(sizes), bytes=by, mean_us=round(r["mean_s"] * 1e6, 3),
+                         gbps=round(by / r["mean_s"] / 1e9, 1), frac=round(by / r["mean_s"] / HBM_PEAK, 4)))
+        del segs
+    return rows
+
+
 def cpu_baseline(x, budget_s):
     """The fp64 oracle, single thread, on whole training steps of the same
     configuration until budget_s has passed."""
@@ -350,11 +370,31 @@ def main():
 
     nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3}[path]
     t_roof = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
+    # Critical-path roofline of the persistent path: the 2K recurrence steps
+    # of a sample run in order on one CU, so they are bounded by one CU's
+    # fp32 rate (the published peak per CU: 256 flop/clk at 2.4 GHz; half
+    # that without packed fp32), not by the chip's; the parallel kernels by
+    # their own whole-chip bounds; plus one node latency per launch.
+    crit = None
+    if path == "persistent":
+        cu_clk = 2.4e9
+        t_rec = recurrence_flops(B, C, K) / B / (256 * cu_clk)
+        par_flops = projection_flops(B, C, n_x, K) + 2 * K * B * 3 * C * n_in
+        par_bytes = fill_bytes(B, C, n_x, K) + 4 * (B + 1) * 3 * C * n_in + 4 * K * B * (n_x + 3 * C)
+        t_par = max(par_flops / FP32_PEAK, par_bytes / HBM_PEAK)
+        t_crit = nodes * t_node + t_rec + t_par
+        t_crit_np = nodes * t_node + 2 * t_rec + t_par
+        crit = {"recurrence_floor_us": round(t_rec * 1e6, 2), "parallel_floor_us": round(t_par * 1e6, 2),
+                "critical_path_roof_ms": round(t_crit * 1e3, 4),
+                "step_over_critical_path_roof": round(ms_per_step / (t_crit * 1e3), 3),
+                "critical_path_roof_nonpacked_ms": round(t_crit_np * 1e3, 4),
+                "step_over_critical_path_roof_nonpacked": round(ms_per_step / (t_crit_np * 1e3), 3)}
     step_roof = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3),
                  "t_roof_ms": round(t_roof * 1e3, 4), "step_over_roof": round(ms_per_step / (t_roof * 1e3), 3),
                  "flops": flops, "bytes_min": bytes_min,
                  "contrast_path": contrast,
-                 "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None}
+                 "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None,
+                 "critical_path": crit}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "train-steps/s", "n_gpus": 1,
@@ -376,6 +416,11 @@ def main():
         gate = [r for r in red if r["B"] * r["N"] * 4 >= 512 * 2 ** 20]
         result["reduce_axis0"] = {"shapes": red,
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}
+
+    if not args.no_kernels:
+        # the optimizer step beside the path: W and bias of this cell, then large flat tensors
+        result["adamw"] = bench_adamw(torch, cfc, LaunchTimer(torch),
+                                      [(3 * C * n_in, 3 * C), (1 << 24,), (1 << 26,)])
 
     if not args.no_cpu:
         n, el = cpu_baseline(x, args.cpu_seconds)

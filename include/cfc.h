@@ -171,6 +171,23 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0,
                       float* h_hist, float* act, float* ws, size_t ws_bytes,
                       int B, int C, int n_x, int K, void* stream);
 
+/* AdamW after the reducer ("K-loop Parallelization", section Trainer Wiring:
+ * the optimizer consumes the final gradient buffers and runs strictly after
+ * every reducer -- on the same stream after cfc_train_kloop, stream order
+ * guarantees it).  One launch updates up to 4 tensors (a flat fused update,
+ * as in "H100 Epoch Optimization Phase 2", the single-flat-kernel tasks):
+ * for segment i, arrays params[i], grads[i], m[i], v[i] of n[i] floats each
+ * (device pointers, host arrays of nseg entries), with decoupled weight
+ * decay:
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   p <- p - (lr / (1 - b1^step)) m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * params, m and v are updated in place; grads are read only.  step is the
+ * 1-based step count.  nseg in [0, 4]; step >= 1; lr, wd >= 0; b1, b2 in
+ * [0, 1); eps > 0; arrays that overlap give CFC_EINVAL. */
+int cfc_adamw_step(float* const* params, const float* const* grads, float* const* m, float* const* v,
+                   const int64_t* n, int nseg, float lr, float beta1, float beta2, float eps,
+                   float weight_decay, int step, void* stream);
+
 /* The two launches of cfc_kloop_fwd_bwd's persistent path, callable on
  * their own (same kernels, same bits):
  * cfc_input_projection -- the input part of every step's pre-activations,

@@ -5,5 +5,5 @@ import this package.  The GPU library never does, and this package imports
 nothing from it.
 """
 from .oracle import (  # noqa: F401
-    fwd_step, bwd_step, forward, train, reduce_axis0_f64, sum_axis0, input_projection, lib_path,
+    fwd_step, bwd_step, forward, train, reduce_axis0_f64, sum_axis0, input_projection, adamw_step, lib_path,
 )

@@ -1,7 +1,8 @@
 """ctypes front end of the CPU oracle -- TEST INFRASTRUCTURE ONLY.
 
-Argument marshalling only: every number is computed by the C oracle in
-cfc_oracle_body.h.  Inputs are numpy arrays; for precision "f64" they are
+Argument marshalling only: every number of the cell, the BPTT and the
+reductions is computed by the C oracle in cfc_oracle_body.h; adamw_step is
+the optimizer's definition written out in fp64 numpy.  Inputs are numpy arrays; for precision "f64" they are
 upcast exactly (fp32 -> fp64 is exact), for "f32" they must already be fp32.
 
 Shapes (row-major): u [K,B,n_x], y [K,B,C], h0 [B,C], W [3,C,n_in],
@@ -185,3 +186,21 @@ def reduce_axis0_f64(x):
     out = np.zeros(N, np.float64)
     _lib().oracle_reduce_axis0_f64(_p(x), B, N, _p(out))
     return out
+
+
+def adamw_step(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step):
+    """One AdamW step in fp64 (decoupled weight decay), from its definition:
+    p <- p (1 - lr wd); m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
+    p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+    Returns new (p, m, v); the inputs are not modified."""
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    p = p * (1.0 - lr * weight_decay)
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** step)
+    v_hat = v / (1.0 - beta2 ** step)
+    p = p - lr * m_hat / (np.sqrt(v_hat) + eps)
+    return p, m, v

@@ -50,6 +50,8 @@ def lib():
         L.cfc_scratch_fill.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
         L.cfc_input_projection.argtypes = [_P] * 4 + [_I64, _I, _I, _P]
         L.cfc_kloop_recurrence.argtypes = [_P] * 7 + [_I, _I, _I, _I, _P]
+        _F = ctypes.c_float
+        L.cfc_adamw_step.argtypes = [_P] * 5 + [_I, _F, _F, _F, _F, _F, _I, _P]
         L.cfc_train_kloop_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.cfc_train_kloop_workspace_bytes.restype = ctypes.c_size_t
         L.cfc_set_kloop_mode.argtypes = [_I]
@@ -60,7 +62,7 @@ def lib():
         L.cfc_clear_graph_cache.argtypes = []
         for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
                   L.cfc_kloop_fwd_bwd, L.cfc_scratch_fill, L.cfc_clear_graph_cache,
-                  L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence):
+                  L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence, L.cfc_adamw_step):
             f.restype = _I
         _LIB = L
     return _LIB
@@ -229,6 +231,24 @@ def cfc_kloop_recurrence(X, y, h0, W, out):
             _dev(out.act, "act", (K, 3, B, C)), _dev(dp, "dp"))
     _check("cfc_kloop_recurrence", lib().cfc_kloop_recurrence(*args, B, C, n_x, K, _stream(h0)))
     return out
+
+
+def cfc_adamw_step(params, grads, ms, vs, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1):
+    """One AdamW step over the tensors of `params` (lists of up to 4 same-shaped
+    parameter / gradient / moment tensors), one launch, in place."""
+    n = len(params)
+    if not (len(grads) == len(ms) == len(vs) == n):
+        raise ValueError("params, grads, ms and vs must have the same length")
+    arr = lambda xs, name: (ctypes.c_void_p * max(n, 1))(*[_dev(x, name) for x in xs])  # noqa: E731
+    for p, g, m, v in zip(params, grads, ms, vs):
+        if not (p.shape == g.shape == m.shape == v.shape):
+            raise ValueError("a segment's tensors must have one shape")
+    counts = (ctypes.c_int64 * max(n, 1))(*[p.numel() for p in params])
+    stream = _stream(params[0]) if n else None
+    _check("cfc_adamw_step", lib().cfc_adamw_step(arr(params, "param"), arr(grads, "grad"), arr(ms, "m"),
+                                                  arr(vs, "v"), counts, n, lr, beta1, beta2, eps,
+                                                  weight_decay, int(step), stream))
+    return params
 
 
 def cfc_scratch_fill(dp, u, h_hist, gW_scratch, gb_scratch):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -561,6 +562,52 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
     }
     const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, nullptr, nullptr, nullptr, nullptr, B, C, n_x, K};
     return enqueue_fwd_bwd(k, path, make_plan(B, C, n_x, W, nullptr), s);
+}
+
+int cfc_adamw_step(float* const* params, const float* const* grads, float* const* m, float* const* v,
+                   const int64_t* n, int nseg, float lr, float beta1, float beta2, float eps, float weight_decay,
+                   int step, void* stream)
+{
+    g_last_error.clear();
+    if (nseg < 0 || nseg > cfc::kMaxAdamwSegs)
+        return fail(CFC_EINVAL, "cfc_adamw_step: nseg=%d out of range [0, %d]", nseg, cfc::kMaxAdamwSegs);
+    if (step < 1) return fail(CFC_EINVAL, "cfc_adamw_step: step=%d (the first step is 1)", step);
+    if (!(lr >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) ||
+        !(weight_decay >= 0.0f))
+        return fail(CFC_EINVAL, "cfc_adamw_step: hyperparameters out of range");
+    if (nseg > 0 && (!params || !grads || !m || !v || !n)) return fail(CFC_EINVAL, "cfc_adamw_step: null array");
+    cfc::AdamwArgs a{};
+    a.nseg = nseg;
+    a.start[0] = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (n[i] < 0) return fail(CFC_EINVAL, "cfc_adamw_step: n[%d] < 0", i);
+        if (n[i] > 0 && (!params[i] || !grads[i] || !m[i] || !v[i]))
+            return fail(CFC_EINVAL, "cfc_adamw_step: null pointer in segment %d", i);
+        a.seg[i] = cfc::AdamwSeg{params[i], grads[i], m[i], v[i], n[i]};
+        a.start[i + 1] = a.start[i] + n[i];
+    }
+    // every array of every segment must be disjoint from every other one
+    for (int i = 0; i < nseg; ++i) {
+        const Span si[] = {span(params[i], n[i]), span(grads[i], n[i]), span(m[i], n[i]), span(v[i], n[i])};
+        for (int j = i; j < nseg; ++j) {
+            const Span sj[] = {span(params[j], n[j]), span(grads[j], n[j]), span(m[j], n[j]), span(v[j], n[j])};
+            for (int x = 0; x < 4; ++x)
+                for (int y = (i == j ? x + 1 : 0); y < 4; ++y)
+                    if (overlap(si[x], sj[y])) return fail(CFC_EINVAL, "cfc_adamw_step: arrays overlap");
+        }
+    }
+    a.decay = 1.0f - lr * weight_decay;
+    a.beta1 = beta1;
+    a.one_minus_beta1 = 1.0f - beta1;
+    a.beta2 = beta2;
+    a.one_minus_beta2 = 1.0f - beta2;
+    const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+    const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+    a.step_size = (float)((double)lr / bc1);
+    a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+    a.eps = eps;
+    CFC_HIP(cfc::launch_adamw(a, (hipStream_t)stream), "adamw launch");
+    return CFC_OK;
 }
 
 int cfc_input_projection(const float* u, const float* W, const float* bias, float* X, int64_t M, int C, int n_x,

@@ -124,6 +124,27 @@ struct PersistArgs {
     int B, C, n_x, K;
 };
 
+constexpr int kMaxAdamwSegs = 4;
+
+struct AdamwSeg {
+    float* p;             // parameters, updated in place
+    const float* g;       // gradients
+    float* m;             // first moments, updated in place
+    float* v;             // second moments, updated in place
+    int64_t n;
+};
+
+struct AdamwArgs {
+    AdamwSeg seg[kMaxAdamwSegs];
+    int64_t start[kMaxAdamwSegs + 1];   // prefix sums of n
+    int nseg;
+    float decay;          // 1 - lr * weight_decay
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float step_size;      // lr / (1 - beta1^step)
+    float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^step)
+    float eps;
+};
+
 struct ReduceSeg {
     const float* in;      // [B, N]
     float* out;           // [N]
@@ -166,6 +187,7 @@ hipError_t launch_xproj(const XprojArgs& a, hipStream_t s);
 hipError_t launch_persist(const PersistArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_adamw(const AdamwArgs& a, hipStream_t s);
 
 // MFMA step path: layout for (C, n_x) (valid iff pg <= 4, i.e. C <= 320),
 // workspace floats of the two re-laid copies of W, and the launches.

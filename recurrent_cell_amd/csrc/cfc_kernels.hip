@@ -1334,6 +1334,34 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
     }
 }
 
+// AdamW over up to four tensors in one launch (flat index space, grid
+// stride), decoupled weight decay:
+//   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+//   p <- p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps).
+// fp32 arithmetic with correctly rounded sqrt and divide; every element is
+// independent, so the result does not depend on the grid.
+__global__ __launch_bounds__(kThreads) void adamw_kernel(AdamwArgs a)
+{
+    const int64_t total = a.start[a.nseg];
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        int sg = 0;
+#pragma unroll
+        for (int k = 1; k < kMaxAdamwSegs; ++k)
+            if (k < a.nseg && i >= a.start[k]) sg = k;
+        const AdamwSeg& S = a.seg[sg];
+        const int64_t j = i - a.start[sg];
+        const float g = S.g[j];
+        float p = S.p[j] * a.decay;
+        const float m = a.beta1 * S.m[j] + a.one_minus_beta1 * g;
+        const float v = a.beta2 * S.v[j] + a.one_minus_beta2 * (g * g);
+        const float denom = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
+        p = p - a.step_size * (m / denom);
+        S.p[j] = p;
+        S.m[j] = m;
+        S.v[j] = v;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* p, int64_t n)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -1545,6 +1573,15 @@ hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipS
         hipLaunchKernelGGL(reduce_axis0_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL(reduce_axis0_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamwArgs& a, hipStream_t s)
+{
+    const int64_t total = a.start[a.nseg];
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = min((total + kThreads - 1) / kThreads, (int64_t)8192);
+    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -69,6 +69,21 @@ def normal(shape, seed: int, stream: int = 0) -> np.ndarray:
     return np.random.default_rng([seed, 0x5EED, stream]).standard_normal(shape).astype(np.float32)
 
 
+def adamw_inputs(sizes, seed: int):
+    """Optimizer state for one AdamW step over segments of the given sizes:
+    parameters ~ N(0, 0.25), gradients and first moments ~ N(0, 1e-4), second
+    moments = squares of N(0, 1e-4) draws (non-negative, as the method keeps
+    them), all fp32.  Returns four lists (p, g, m, v)."""
+    out = ([], [], [], [])
+    for i, n in enumerate(sizes):
+        rng = np.random.default_rng([seed, 0xADA, i])
+        d = rng.standard_normal((4, n))
+        vals = (0.5 * d[0], 1e-2 * d[1], 1e-2 * d[2], (1e-2 * d[3]) ** 2)
+        for lst, a in zip(out, vals):
+            lst.append(a.astype(np.float32))
+    return out
+
+
 def small_int_rows(B: int, N: int, seed: int = 0, lo: int = -8, hi: int = 8) -> np.ndarray:
     """Integers in [lo, hi] stored as fp32: every partial sum of at most 2^20 such
     rows is an integer below 2^24 in magnitude, so fp32 sums of them are exact."""

@@ -182,3 +182,39 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), fn
                 assert "liboracle" not in text, fn
+
+
+def _ptrs(*xs):
+    return (ctypes.c_void_p * len(xs))(*xs)
+
+
+def test_adamw_argument_errors(L):
+    P = [FAKE + i * (1 << 30) for i in range(4)]
+    n = (ctypes.c_int64 * 1)(1000)
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.01)
+    args = lambda nseg, hp=hp, step=1: (_ptrs(P[0]), _ptrs(P[1]), _ptrs(P[2]), _ptrs(P[3]), n, nseg,  # noqa: E731
+                                        *hp, step, None)
+    assert L.cfc_adamw_step(*args(5)) == -1
+    assert L.cfc_adamw_step(*args(-1)) == -1
+    assert L.cfc_adamw_step(*args(1, step=0)) == -1
+    for bad in ((-1e-3, 0.9, 0.999, 1e-8, 0.01), (1e-3, 1.0, 0.999, 1e-8, 0.01), (1e-3, 0.9, 1.0, 1e-8, 0.01),
+                (1e-3, 0.9, 0.999, 0.0, 0.01), (1e-3, 0.9, 0.999, 1e-8, -0.1),
+                (float("nan"), 0.9, 0.999, 1e-8, 0.01)):
+        assert L.cfc_adamw_step(*args(1, hp=bad)) == -1
+        assert b"hyperparameters" in L.cfc_last_error()
+    assert L.cfc_adamw_step(None, None, None, None, None, 1, *hp, 1, None) == -1
+    assert L.cfc_adamw_step(_ptrs(P[0]), _ptrs(None), _ptrs(P[2]), _ptrs(P[3]), n, 1, *hp, 1, None) == -1
+    neg = (ctypes.c_int64 * 1)(-4)
+    assert L.cfc_adamw_step(_ptrs(P[0]), _ptrs(P[1]), _ptrs(P[2]), _ptrs(P[3]), neg, 1, *hp, 1, None) == -1
+    # a parameter aliasing its own gradient, and two segments sharing a moment buffer
+    assert L.cfc_adamw_step(_ptrs(P[0]), _ptrs(P[0] + 64), _ptrs(P[2]), _ptrs(P[3]), n, 1, *hp, 1, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    n2 = (ctypes.c_int64 * 2)(1000, 1000)
+    Q = [p + (1 << 28) for p in P]
+    assert L.cfc_adamw_step(_ptrs(P[0], Q[0]), _ptrs(P[1], Q[1]), _ptrs(P[2], P[2] + 256), _ptrs(P[3], Q[3]),
+                            n2, 2, *hp, 1, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    # nothing to update: no launch
+    assert L.cfc_adamw_step(None, None, None, None, None, 0, *hp, 1, None) == 0
+    n0 = (ctypes.c_int64 * 1)(0)
+    assert L.cfc_adamw_step(_ptrs(None), _ptrs(None), _ptrs(None), _ptrs(None), n0, 1, *hp, 1, None) == 0

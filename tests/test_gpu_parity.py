@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from recurrent_cell_amd.inputs import CONFIGS, cfc_inputs, normal, reduce_rows, small_int_rows
-from tests.tolerances import (assert_ok, check_act, check_grad, check_reduce, grad_mass)
+from recurrent_cell_amd.inputs import CONFIGS, adamw_inputs, cfc_inputs, normal, reduce_rows, small_int_rows
+from tests.tolerances import (assert_ok, check_act, check_adamw, check_grad, check_reduce, grad_mass)
 
 pytestmark = pytest.mark.gpu
 
@@ -508,3 +508,66 @@ def test_reduce_full_size_sampled(cfc, oracle_mod, B, N):
     assert torch.equal(again.view(torch.int32), out.view(torch.int32))
     del x
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- AdamW after the reducer
+
+def f32(x):
+    return float(np.float32(x))
+
+
+@pytest.mark.parametrize("sizes,step,hp", [
+    ((73728, 384), 1, (1e-3, 0.9, 0.999, 1e-8, 0.01)),           # W and bias of the 128-channel cell
+    ((1, 3, 1000, 4097), 7, (3e-3, 0.8, 0.95, 1e-6, 0.1)),      # four ragged segments
+    ((0, 5, 0), 1000, (1e-2, 0.9, 0.999, 1e-8, 0.0)),           # empty segments, late step, no decay
+    ((2_000_003,), 3, (1e-4, 0.5, 0.5, 1e-3, 0.5)),             # grid-stride loop, odd length
+])
+def test_adamw_matches_oracle(cfc, oracle_mod, sizes, step, hp):
+    say("adamw parity", sizes, step, hp)
+    p, g, m, v = adamw_inputs(sizes, seed=31)
+    tp, tg, tm, tv = ([dev(a) for a in xs] for xs in (p, g, m, v))
+    lr, b1, b2, eps, wd = (f32(h) for h in hp)
+    cfc.cfc_adamw_step(tp, tg, tm, tv, lr, b1, b2, eps, wd, step)
+    for i in range(len(sizes)):
+        ref = oracle_mod.adamw_step(p[i], g[i], m[i], v[i], lr, b1, b2, eps, wd, step)
+        for rep in check_adamw(host(tp[i]), host(tm[i]), host(tv[i]), ref, p[i], m[i], g[i], lr, b1, b2, eps,
+                               step):
+            assert_ok(rep)
+
+
+def test_adamw_reads_only_post_reducer_gradients(cfc):
+    """The final gradient buffers hold the previous step's values until the
+    reducer of this step overwrites them.  AdamW enqueued right after
+    cfc_train_kloop on the same stream (no synchronisation) must apply this
+    step's reduced gradients: the result equals, bit for bit, AdamW applied
+    after a synchronisation to a snapshot of those gradients, and differs from
+    AdamW on the previous step's gradients."""
+    d = CASES["pages"]
+    say("adamw after the reducer", d)
+    xa = cfc_inputs(**d, seed=41)
+    xb = cfc_inputs(**d, seed=42)
+    out = cfc.KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
+    kloop_dev(cfc, xa, out=out)
+    torch.cuda.synchronize()
+    stale_gW, stale_gb = out.gW.clone(), out.gb.clone()
+    W0, b0 = dev(xb.W), dev(xb.bias)
+    state = lambda: ([W0.clone(), b0.clone()], [torch.zeros_like(W0), torch.zeros_like(b0)],  # noqa: E731
+                     [torch.zeros_like(W0), torch.zeros_like(b0)])
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.01)
+    # the fused order: K-loop then AdamW on the same stream, nothing in between
+    pa, ma, va = state()
+    t = [dev(a) for a in (xb.u, xb.y, xb.h0)]
+    cfc.cfc_train_kloop(t[0], t[1], t[2], W0, b0, out=out)
+    cfc.cfc_adamw_step(pa, [out.gW, out.gb], ma, va, *hp, 2)
+    torch.cuda.synchronize()
+    # the same update from a snapshot taken after synchronising
+    gW, gb = out.gW.clone(), out.gb.clone()
+    pb, mb, vb = state()
+    cfc.cfc_adamw_step(pb, [gW, gb], mb, vb, *hp, 2)
+    for x, y in zip(pa + ma + va, pb + mb + vb):
+        np.testing.assert_array_equal(bits(host(x)), bits(host(y)))
+    # and not the stale gradients
+    pc, mc, vc = state()
+    cfc.cfc_adamw_step(pc, [stale_gW, stale_gb], mc, vc, *hp, 2)
+    assert not np.array_equal(host(pa[0]), host(pc[0]))
+    assert not torch.equal(gW, stale_gW)

@@ -251,3 +251,41 @@ def test_input_projection_special_cases(oracle_mod):
     u2 = x.u[0] * 2.0
     lin = oracle_mod.input_projection(u2, x.W, x.bias, "f64") - b
     np.testing.assert_allclose(lin, 2.0 * (Xa[0] - b), rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- AdamW
+
+def test_adamw_oracle_matches_torch_adamw(oracle_mod):
+    """The fp64 oracle against the library routine torch.optim.AdamW (CPU,
+    fp64) over three steps with fresh gradients each step."""
+    rng = np.random.default_rng(21)
+    p0 = rng.standard_normal(257)
+    hp = dict(lr=3e-3, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.05)
+    tp = torch.tensor(p0.copy(), dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    p, m, v = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    for step in range(1, 4):
+        g = rng.standard_normal(257)
+        tp.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        p, m, v = oracle_mod.adamw_step(p, g, m, v, step=step, **hp)
+        np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-13, atol=1e-15)
+        st = opt.state[tp]
+        np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_adamw_oracle_special_cases(oracle_mod):
+    rng = np.random.default_rng(22)
+    p0 = rng.standard_normal(33)
+    # zero gradient and zero moments: only the decay acts
+    p, m, v = oracle_mod.adamw_step(p0, np.zeros(33), np.zeros(33), np.zeros(33), lr=1e-2, beta1=0.9,
+                                    beta2=0.999, eps=1e-8, weight_decay=0.1, step=1)
+    np.testing.assert_array_equal(p, p0 * (1.0 - 1e-3))
+    assert not m.any() and not v.any()
+    # first step, no decay, eps -> 0: the update is lr * sign(g)
+    g = rng.standard_normal(33)
+    p, _, _ = oracle_mod.adamw_step(p0, g, np.zeros(33), np.zeros(33), lr=1e-2, beta1=0.9, beta2=0.999,
+                                    eps=1e-30, weight_decay=0.0, step=1)
+    np.testing.assert_allclose(p, p0 - 1e-2 * np.sign(g), rtol=0, atol=1e-15)

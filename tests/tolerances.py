@@ -15,6 +15,18 @@ term is the first-order forward-error bound of a sum of rounded terms;
 KAPPA = 16 leaves at least 2x margin over the worst error of the plain fp32
 oracle measured on the tiny, pages-shaped and wide configurations.
 
+AdamW (one step from fp32 state; the oracle evaluates the definition in
+fp64 on the same fp32 inputs and fp32-rounded hyperparameters):
+    m: |x - ref| <= 4 u (|beta1 m0| + |(1 - beta1) g|)
+    v: |x - ref| <= 4 u v_ref                      (terms of one sign)
+    p: |x - ref| <= 16 u (|p0| + step_size (|beta1 m0| + |(1 - beta1) g|) / den)
+with den = sqrt(v_ref / (1 - beta2^t)) + eps and step_size = lr / (1 - beta1^t):
+each of m, v takes at most three roundings of terms bounded by that mass
+(1 - beta for beta in [0.5, 1) is exact in fp32), and the update's quotient,
+square root, bias-correction constants, decay and final subtraction add a
+handful more relative roundings of |p0| and of the update; 16 covers them
+with margin.
+
 Batch-axis reduction: |x - ref| <= 1e-6 |ref| + 2^-24 * |ref| + eps64, where
 the reference is the fp64 column sum; the library rounds an fp64 sum once,
 so the only error besides that rounding is the fp64 reordering term
@@ -73,3 +85,16 @@ def grad_mass(u, h_hist, dp):
 
 def assert_ok(rep):
     assert rep["fails"] == 0, rep
+
+
+def check_adamw(p, m, v, ref, p0, m0, g, lr, beta1, beta2, eps, step):
+    """Reports for (p, m, v) against ref = oracle (p, m, v); see the module
+    docstring for the bounds."""
+    p0, m0, g = (np.asarray(a, np.float64) for a in (p0, m0, g))
+    rp, rm, rv = (np.asarray(a, np.float64) for a in ref)
+    mass_m = np.abs(beta1 * m0) + np.abs((1.0 - beta1) * g)
+    den = np.sqrt(rv / (1.0 - beta2 ** step)) + eps
+    step_size = lr / (1.0 - beta1 ** step)
+    return [_report("p", p, rp, 16 * U32 * (np.abs(p0) + step_size * mass_m / den)),
+            _report("m", m, rm, 4 * U32 * mass_m),
+            _report("v", v, rv, np.maximum(4 * U32 * rv, np.finfo(np.float32).tiny))]
