@@ -164,6 +164,58 @@ def graph_node_latency(torch, n_nodes=130, reps=50):
     return a.elapsed_time(b) * 1e-3 / (reps * n_nodes)
 
 
+def copy_peak(torch, mib=2048, reps=10):
+    """Measured HBM rate of a plain fp32 device copy (mib MiB read + mib MiB
+    written per copy), median over reps, in B/s."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / float(np.median(ts))
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = None
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "model": model}
+
+
+def deterministic_runs(torch, cfc, t, n=3):
+    """True iff n K-loop calls into fresh buffers give the same gradient bits."""
+    ref = None
+    for _ in range(n):
+        o = cfc.cfc_train_kloop(*t)
+        torch.cuda.synchronize()
+        bits = (o.gW.view(torch.int32).cpu(), o.gb.view(torch.int32).cpu())
+        if ref is None:
+            ref = bits
+        elif not (torch.equal(ref[0], bits[0]) and torch.equal(ref[1], bits[1])):
+            return False
+    return True
+
+
 def time_steps(torch, cfc, t, out, steps, warmup, trials):
     for _ in range(warmup):
         cfc.cfc_train_kloop(*t, out=out)
@@ -370,6 +422,10 @@ def main():
 
     nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3}[path]
     t_roof = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
+    # the same formula over the pages' own K-loop structure: one memset, K
+    # forward and K backward launches and two reductions as dependent nodes
+    pages_nodes = 2 * K + 3
+    t_roof_pages = pages_nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
     # Critical-path roofline of the persistent path: the 2K recurrence steps
     # of a sample run in order on one CU, so they are bounded by one CU's
     # fp32 rate (the published peak per CU: 256 flop/clk at 2.4 GHz; half
@@ -391,6 +447,8 @@ def main():
                 "step_over_critical_path_roof_nonpacked": round(ms_per_step / (t_crit_np * 1e3), 3)}
     step_roof = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3),
                  "t_roof_ms": round(t_roof * 1e3, 4), "step_over_roof": round(ms_per_step / (t_roof * 1e3), 3),
+                 "pages_graph_nodes": pages_nodes, "t_roof_pages_graph_ms": round(t_roof_pages * 1e3, 4),
+                 "step_over_roof_pages_graph": round(ms_per_step / (t_roof_pages * 1e3), 3),
                  "flops": flops, "bytes_min": bytes_min,
                  "contrast_path": contrast,
                  "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None,
@@ -409,10 +467,21 @@ def main():
         "trials_ms": [round(v, 5) for v in trials],
     }
 
+    if not args.no_kernels:
+        result["deterministic_3_runs"] = deterministic_runs(torch, cfc, t)
+    result["host"] = host_info()
+    if not (args.no_kernels and args.no_reduce):
+        peak = copy_peak(torch)
+        result["hbm_copy_peak"] = {"GBps": round(peak / 1e9, 1), "frac_of_datasheet": round(peak / HBM_PEAK, 4),
+                                   "what": "torch fp32 device copy, 2 GiB read + 2 GiB written, median of 10"}
+
     if not args.no_reduce:
         timer = LaunchTimer(torch)
         shapes = [(b, n) for b in REDUCE_B for n in REDUCE_N]
         red = bench_reduce(torch, cfc, timer, shapes)
+        if "hbm_copy_peak" in result:
+            for r in red:
+                r["frac_copy"] = round(r["GBps"] / result["hbm_copy_peak"]["GBps"], 3)
         gate = [r for r in red if r["B"] * r["N"] * 4 >= 512 * 2 ** 20]
         result["reduce_axis0"] = {"shapes": red,
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}

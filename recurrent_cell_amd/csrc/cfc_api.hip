@@ -578,13 +578,14 @@ int cfc_adamw_step(float* const* params, const float* const* grads, float* const
     if (nseg > 0 && (!params || !grads || !m || !v || !n)) return fail(CFC_EINVAL, "cfc_adamw_step: null array");
     cfc::AdamwArgs a{};
     a.nseg = nseg;
-    a.start[0] = 0;
+    a.qstart[0] = 0;
     for (int i = 0; i < nseg; ++i) {
-        if (n[i] < 0) return fail(CFC_EINVAL, "cfc_adamw_step: n[%d] < 0", i);
+        if (n[i] < 0 || n[i] > ((int64_t)1 << 40)) return fail(CFC_EINVAL, "cfc_adamw_step: n[%d] out of range", i);
         if (n[i] > 0 && (!params[i] || !grads[i] || !m[i] || !v[i]))
             return fail(CFC_EINVAL, "cfc_adamw_step: null pointer in segment %d", i);
-        a.seg[i] = cfc::AdamwSeg{params[i], grads[i], m[i], v[i], n[i]};
-        a.start[i + 1] = a.start[i] + n[i];
+        const int vec = (aligned16(params[i]) && aligned16(grads[i]) && aligned16(m[i]) && aligned16(v[i])) ? 1 : 0;
+        a.seg[i] = cfc::AdamwSeg{params[i], grads[i], m[i], v[i], n[i], vec};
+        a.qstart[i + 1] = a.qstart[i] + (n[i] + 3) / 4;
     }
     // every array of every segment must be disjoint from every other one
     for (int i = 0; i < nseg; ++i) {

@@ -132,11 +132,12 @@ struct AdamwSeg {
     float* m;             // first moments, updated in place
     float* v;             // second moments, updated in place
     int64_t n;
+    int vec;              // 1: all four arrays 16-byte aligned (float4 moves)
 };
 
 struct AdamwArgs {
     AdamwSeg seg[kMaxAdamwSegs];
-    int64_t start[kMaxAdamwSegs + 1];   // prefix sums of n
+    int64_t qstart[kMaxAdamwSegs + 1];  // prefix sums of ceil(n / 4): chunks of 4 elements
     int nseg;
     float decay;          // 1 - lr * weight_decay
     float beta1, one_minus_beta1, beta2, one_minus_beta2;

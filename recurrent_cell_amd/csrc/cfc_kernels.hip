@@ -649,7 +649,6 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
 {
     __shared__ __attribute__((aligned(16))) float dps[16 * kDzGroups * 16];
     __shared__ __attribute__((aligned(16))) float ts[4][16][17];
-    const MfmaLayout L = a.L;
     const int C = a.C;
     const int cpg = dz_group_channels(C);
     const int ctile = blockIdx.x % a.n_ctiles;
@@ -1340,25 +1339,50 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
 //   p <- p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps).
 // fp32 arithmetic with correctly rounded sqrt and divide; every element is
 // independent, so the result does not depend on the grid.
+__device__ __forceinline__ void adamw_one(const AdamwArgs& a, float& p, float g, float& m, float& v)
+{
+    m = a.beta1 * m + a.one_minus_beta1 * g;
+    v = a.beta2 * v + a.one_minus_beta2 * (g * g);
+    const float denom = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
+    p = p * a.decay - a.step_size * (m / denom);
+}
+
+// One thread per chunk of 4 consecutive elements of a segment (chunks of all
+// segments numbered one after another, grid-stride): a float4 move of each
+// array when the segment's arrays are 16-byte aligned and the chunk is whole,
+// else element by element.
 __global__ __launch_bounds__(kThreads) void adamw_kernel(AdamwArgs a)
 {
-    const int64_t total = a.start[a.nseg];
+    const int64_t total = a.qstart[a.nseg];
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
         int sg = 0;
 #pragma unroll
         for (int k = 1; k < kMaxAdamwSegs; ++k)
-            if (k < a.nseg && i >= a.start[k]) sg = k;
+            if (k < a.nseg && i >= a.qstart[k]) sg = k;
         const AdamwSeg& S = a.seg[sg];
-        const int64_t j = i - a.start[sg];
-        const float g = S.g[j];
-        float p = S.p[j] * a.decay;
-        const float m = a.beta1 * S.m[j] + a.one_minus_beta1 * g;
-        const float v = a.beta2 * S.v[j] + a.one_minus_beta2 * (g * g);
-        const float denom = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
-        p = p - a.step_size * (m / denom);
-        S.p[j] = p;
-        S.m[j] = m;
-        S.v[j] = v;
+        const int64_t j = 4 * (i - a.qstart[sg]);
+        if (S.vec && j + 4 <= S.n) {
+            float4 p = *reinterpret_cast<const float4*>(S.p + j);
+            const float4 g = *reinterpret_cast<const float4*>(S.g + j);
+            float4 m = *reinterpret_cast<const float4*>(S.m + j);
+            float4 v = *reinterpret_cast<const float4*>(S.v + j);
+            adamw_one(a, p.x, g.x, m.x, v.x);
+            adamw_one(a, p.y, g.y, m.y, v.y);
+            adamw_one(a, p.z, g.z, m.z, v.z);
+            adamw_one(a, p.w, g.w, m.w, v.w);
+            *reinterpret_cast<float4*>(S.p + j) = p;
+            *reinterpret_cast<float4*>(S.m + j) = m;
+            *reinterpret_cast<float4*>(S.v + j) = v;
+        } else {
+            const int64_t e = min(j + 4, S.n);
+            for (int64_t q = j; q < e; ++q) {
+                float p = S.p[q], m = S.m[q], v = S.v[q];
+                adamw_one(a, p, S.g[q], m, v);
+                S.p[q] = p;
+                S.m[q] = m;
+                S.v[q] = v;
+            }
+        }
     }
 }
 
@@ -1578,9 +1602,9 @@ hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipS
 
 hipError_t launch_adamw(const AdamwArgs& a, hipStream_t s)
 {
-    const int64_t total = a.start[a.nseg];
+    const int64_t total = a.qstart[a.nseg];
     if (total == 0) return hipSuccess;
-    const int64_t blocks = min((total + kThreads - 1) / kThreads, (int64_t)8192);
+    const int64_t blocks = min((total + kThreads - 1) / kThreads, (int64_t)4096);
     hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
