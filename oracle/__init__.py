@@ -1,4 +1,5 @@
-"""CPU oracle for the CfC K-loop -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracles for the CfC K-loop and the batched MLP step (mlp_oracle) --
+TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the smoke entry point and the benchmark's CPU-baseline leg may
 import this package.  The GPU library never does, and this package imports

@@ -92,6 +92,31 @@ def small_int_rows(B: int, N: int, seed: int = 0, lo: int = -8, hi: int = 8) -> 
 
 
 # The configurations the library is measured and checked on.
+class MlpInputs:
+    """Seeded MLP training-step inputs: X [B, dims[0]], T [B, dims[-1]] ~ N(0, 1);
+    W_l [dims[l+1], dims[l]] He-uniform U(+-sqrt(6 / dims[l])); b_l zero, or
+    U(+-bias_scale) when bias_scale > 0 (parity cases, so that the bias path
+    is exercised).  All fp32."""
+
+    def __init__(self, B, dims, seed=0, bias_scale=0.0):
+        rng = np.random.default_rng([seed, 0x4D4C50])
+        self.dims = list(dims)
+        self.X = rng.standard_normal((B, dims[0])).astype(np.float32)
+        self.T = rng.standard_normal((B, dims[-1])).astype(np.float32)
+        self.W, self.b = [], []
+        for l in range(len(dims) - 1):
+            bound = np.sqrt(6.0 / dims[l])
+            self.W.append(rng.uniform(-bound, bound, (dims[l + 1], dims[l])).astype(np.float32))
+        for l in range(len(dims) - 1):
+            if bias_scale > 0:
+                self.b.append(rng.uniform(-bias_scale, bias_scale, dims[l + 1]).astype(np.float32))
+            else:
+                self.b.append(np.zeros(dims[l + 1], np.float32))
+
+
+MLP_DIMS = (48, 256, 256, 128, 51)
+MLP_B = 16384
+
 CONFIGS = {
     "tiny": dict(B=4, C=16, n_x=8, K=4),
     "pages": dict(B=32, C=128, n_x=64, K=64),
