@@ -276,6 +276,85 @@ def bench_adamw(torch, cfc, timer, sizes_list):
     return rows
 
 
+def mlp_flops(B, dims):
+    """Algorithmic flops of one MLP step: forward and weight gradient of every
+    layer, upstream gradient of every layer but the first (2 per fma)."""
+    f = sum(2 * B * dims[l] * dims[l + 1] for l in range(len(dims) - 1))
+    dx = sum(2 * B * dims[l] * dims[l + 1] for l in range(1, len(dims) - 1))
+    return 2 * f + dx
+
+
+def bench_mlp(torch, timer, steps, trials, cpu_seconds):
+    """The batched MLP training step (48-256-256-128-51, B = 16384): steps/s,
+    the matrix-core roofline, per-launch timing, and the oracle's time for
+    one step on the host."""
+    from recurrent_cell_amd import mlp
+    from recurrent_cell_amd.inputs import MLP_B, MLP_DIMS, MlpInputs
+    B, dims = MLP_B, list(MLP_DIMS)
+    x = MlpInputs(B, dims, seed=0)
+    Xd, Td = torch.from_numpy(x.X).cuda(), torch.from_numpy(x.T).cuda()
+    params = mlp.pack_params([torch.from_numpy(w).cuda() for w in x.W], [torch.from_numpy(b).cuda() for b in x.b],
+                             dims)
+    out = mlp.MlpBuffers.allocate(B, dims, "cuda")
+    for _ in range(10):
+        mlp.mlp_train_step(Xd, Td, dims, params, out=out)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            mlp.mlp_train_step(Xd, Td, dims, params, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / steps)
+    ms = float(np.median(res))
+    fl = mlp_flops(B, dims)
+    # per launch: the layer products of one step, timed one by one
+    L = len(dims) - 1
+    Ws = [w for w, _ in mlp.unpack(params, dims)]
+    bs = [b for _, b in mlp.unpack(params, dims)]
+    acts = out.act
+    kt = {}
+    for l in range(L):
+        xin = Xd if l == 0 else acts[l - 1]
+        r = timer(lambda: mlp.mlp_linear_fwd(xin, Ws[l], bs[l], Y=acts[l], relu=l < L - 1), 30)
+        kt["fwd%d" % l] = dict(us=round(r["mean_s"] * 1e6, 2), flops=2 * B * dims[l] * dims[l + 1])
+    gy = [torch.randn((B, d), device="cuda") for d in dims[1:]]
+    for l in range(1, L):
+        r = timer(lambda: mlp.mlp_linear_bwd_data(gy[l], Ws[l], mask=acts[l - 1], dX=gy[l - 1]), 30)
+        kt["dx%d" % l] = dict(us=round(r["mean_s"] * 1e6, 2), flops=2 * B * dims[l] * dims[l + 1])
+    ws = torch.empty(mlp.lib().mlp_linear_bwd_weight_workspace_bytes(B, dims[1], dims[2]) // 4 + 1, device="cuda")
+    gW = torch.empty((dims[2], dims[1]), device="cuda")
+    gb = torch.empty((dims[2],), device="cuda")
+    r = timer(lambda: mlp.mlp_linear_bwd_weight(gy[1], acts[0], gW=gW, gb=gb, ws=ws), 30)
+    kt["dw1 (with its reduce)"] = dict(us=round(r["mean_s"] * 1e6, 2), flops=2 * B * dims[1] * dims[2])
+    for v in kt.values():
+        v["TFLOPs"] = round(v["flops"] / (v["us"] * 1e-6) / 1e12, 2)
+    big = kt["fwd1"]
+    roof = {"bound": "mfma", "achieved": big["TFLOPs"], "peak": FP32_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": round(big["TFLOPs"] * 1e12 / FP32_PEAK, 4), "traffic": None,
+            "kernel": "gemm_mfma_kernel (layer 1 forward, [16384 x 256] x [256 x 256])",
+            "flops_per_launch": big["flops"], "launch_us": big["us"]}
+    from oracle.mlp_oracle import mlp_train_step as oracle_step
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle_step(x.X, x.T, x.W, x.b)
+        n += 1
+        if time.perf_counter() - t0 >= min(cpu_seconds, 5.0):
+            break
+    el = time.perf_counter() - t0
+    return {"workload": "batched MLP train step (forward, MSE loss, backward, every gradient), one mlp_train_step "
+                        "call", "B": B, "dims": dims, "value": round(1000.0 / ms, 2), "unit": "train-steps/s",
+            "ms_per_step": round(ms, 5), "trials_ms": [round(v, 5) for v in res], "flops_per_step": fl,
+            "step_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2), "step_frac_fp32_peak": round(fl / (ms * 1e-3) /
+                                                                                         FP32_PEAK, 4),
+            "roofline": roof, "launches": kt,
+            "cpu_oracle": {"value": round(n / el, 3), "unit": "train-steps/s", "cores": "numpy fp64 (BLAS threads)",
+                           "kind": "oracle", "sample": "%d whole steps, %.1f s" % (n, el)}}
+
+
 def cpu_baseline(x, budget_s):
     """The fp64 oracle, single thread, on whole training steps of the same
     configuration until budget_s has passed."""
@@ -303,6 +382,7 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
     ap.add_argument("--workload", default="pages", choices=["tiny", "pages", "wide"])
     ap.add_argument("--no-steps-path", action="store_true", help="skip the step-kernel path contrast")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the batched MLP step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size reference for "
                          "hardware byte counters)")
@@ -485,6 +565,9 @@ def main():
         gate = [r for r in red if r["B"] * r["N"] * 4 >= 512 * 2 ** 20]
         result["reduce_axis0"] = {"shapes": red,
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}
+
+    if not args.no_mlp:
+        result["mlp"] = bench_mlp(torch, LaunchTimer(torch), 50, 5, args.cpu_seconds)
 
     if not args.no_kernels:
         # the optimizer step beside the path: W and bias of this cell, then large flat tensors

@@ -61,3 +61,28 @@ def mlp_train_step(X, T, Ws, bs):
             dx = g @ _f64(Ws[l])                 # dX = dY W
             g = dx * (pre[l - 1] > 0.0)          # through the previous layer's ReLU
     return dict(loss=loss, gW=gW, gb=gb, pre=pre, post=post, dA=dA)
+
+
+def linear_fwd(X, W, b, relu):
+    """One layer's forward (Task 1): X W^T + b, then ReLU when relu."""
+    a = _f64(X) @ _f64(W).T
+    if b is not None:
+        a = a + _f64(b)
+    return np.maximum(a, 0.0) if relu else a
+
+
+def linear_bwd_data(dY, W, mask):
+    """One layer's upstream gradient (Task 2): dY W, zeroed where mask <= 0."""
+    dx = _f64(dY) @ _f64(W)
+    return dx if mask is None else dx * (_f64(mask) > 0.0)
+
+
+def linear_bwd_weight(dY, X):
+    """One layer's parameter gradients (Task 2): dY^T X and the column sums of dY."""
+    return _f64(dY).T @ _f64(X), _f64(dY).sum(axis=0)
+
+
+def mse_loss_grad(Y, T):
+    """Mean of (Y - T)^2 and its gradient 2 (Y - T) / Y.size."""
+    d = _f64(Y) - _f64(T)
+    return float(np.sum(d * d) / d.size), 2.0 * d / d.size

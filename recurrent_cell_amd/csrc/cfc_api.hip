@@ -15,52 +15,20 @@
 #include <tuple>
 
 #include "../../include/cfc.h"
+#include "api_common.h"
 #include "cfc_kernels.h"
 #include "cfc_math.h"
 
 namespace {
 
-thread_local std::string g_last_error;
-
-int fail(int code, const char* fmt, ...)
-{
-    char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
-    g_last_error = buf;
-    return code;
-}
-
-int hip_fail(hipError_t e, const char* what)
-{
-    return fail(CFC_EHIP, "%s: %s", what, hipGetErrorString(e));
-}
-
-#define CFC_HIP(call, what)                              \
-    do {                                                 \
-        hipError_t e_ = (call);                          \
-        if (e_ != hipSuccess) return hip_fail(e_, what); \
-    } while (0)
+using cfc_host::fail;
+using cfc_host::hip_fail;
+using cfc_host::Span;
+using cfc_host::overlap;
+using cfc_host::span;
+using cfc_host::aligned16;
 
 constexpr int64_t kMaxB = int64_t(1) << 24;
-
-struct Span {
-    const void* p;
-    size_t bytes;
-};
-
-bool overlap(Span a, Span b)
-{
-    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
-    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
-    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
-}
-
-Span span(const void* p, int64_t n) { return Span{p, (size_t)(n > 0 ? n : 0) * sizeof(float)}; }
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_dims(int B, int C, int n_x)
 {
@@ -356,12 +324,12 @@ int build_graph(const KloopArgs& k, Path path, const cfc::StepPlan& p, int dev, 
 
 extern "C" {
 
-const char* cfc_last_error(void) { return g_last_error.c_str(); }
+const char* cfc_last_error(void) { return cfc_host::last_error().c_str(); }
 
 int cfc_fwd_step(const float* u_t, const float* h_prev, const float* W, const float* bias, float* h_t,
                  float* act_t, int B, int C, int n_x, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (int rc = check_dims(B, C, n_x)) return rc;
     if (B == 0) return CFC_OK;
     const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
@@ -383,7 +351,7 @@ int cfc_bwd_step(const float* u_t, const float* h_prev, const float* h_t, const 
                  const float* W, const float* act_t, const float* dh_in, float* dh_out, float* du_t,
                  float* gW_scratch, float* gb_scratch, int B, int C, int n_x, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (int rc = check_dims(B, C, n_x)) return rc;
     if (B == 0) return CFC_OK;
     const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
@@ -409,7 +377,7 @@ int cfc_bwd_step(const float* u_t, const float* h_prev, const float* h_t, const 
 
 int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail, float* out, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (n_batch < 0 || n_tail < 0) return fail(CFC_EINVAL, "reduce_axis0: negative size");
     if (n_tail == 0) return CFC_OK;
     if (!out || (n_batch > 0 && !per_batch)) return fail(CFC_EINVAL, "reduce_axis0: null pointer");
@@ -428,7 +396,7 @@ size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K)
 
 int cfc_set_kloop_mode(int mode)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (mode < CFC_KLOOP_AUTO || mode > CFC_KLOOP_STEPS_MFMA)
         return fail(CFC_EINVAL, "cfc_set_kloop_mode: unknown mode %d", mode);
     g_kloop_mode.store(mode);
@@ -494,7 +462,7 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
                     float* h_hist, float* act, float* ws, size_t ws_bytes, float* gW_scratch,
                     float* gb_scratch, float* gW, float* gb, int B, int C, int n_x, int K, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     Path path = Path::Steps;
     if (int rc = check_kloop("cfc_train_kloop", u, y, h0, W, bias, h_hist, act, ws, ws_bytes, gW_scratch,
                              gb_scratch, gW, gb, B, C, n_x, K, true, &path))
@@ -549,7 +517,7 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
                       float* h_hist, float* act, float* ws, size_t ws_bytes, int B, int C, int n_x, int K,
                       void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     Path path = Path::Steps;
     if (int rc = check_kloop("cfc_kloop_fwd_bwd", u, y, h0, W, bias, h_hist, act, ws, ws_bytes, nullptr, nullptr,
                              nullptr, nullptr, B, C, n_x, K, false, &path))
@@ -568,7 +536,7 @@ int cfc_adamw_step(float* const* params, const float* const* grads, float* const
                    const int64_t* n, int nseg, float lr, float beta1, float beta2, float eps, float weight_decay,
                    int step, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (nseg < 0 || nseg > cfc::kMaxAdamwSegs)
         return fail(CFC_EINVAL, "cfc_adamw_step: nseg=%d out of range [0, %d]", nseg, cfc::kMaxAdamwSegs);
     if (step < 1) return fail(CFC_EINVAL, "cfc_adamw_step: step=%d (the first step is 1)", step);
@@ -614,7 +582,7 @@ int cfc_adamw_step(float* const* params, const float* const* grads, float* const
 int cfc_input_projection(const float* u, const float* W, const float* bias, float* X, int64_t M, int C, int n_x,
                          void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (int rc = check_dims(0, C, n_x)) return rc;
     if (M < 0 || M > ((int64_t)1 << 40)) return fail(CFC_EINVAL, "cfc_input_projection: M=%lld out of range",
                                                      (long long)M);
@@ -633,7 +601,7 @@ int cfc_input_projection(const float* u, const float* W, const float* bias, floa
 int cfc_kloop_recurrence(const float* X, const float* y, const float* h0, const float* W, float* h_hist,
                          float* act, float* dp, int B, int C, int n_x, int K, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (int rc = check_dims(B, C, n_x)) return rc;
     if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "cfc_kloop_recurrence: K=%d out of range", K);
     if (cfc::persist_smem(C) == 0)
@@ -667,7 +635,7 @@ int cfc_kloop_recurrence(const float* X, const float* y, const float* h0, const 
 int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist, float* gW_scratch, float* gb_scratch,
                      int B, int C, int n_x, int K, void* stream)
 {
-    g_last_error.clear();
+    cfc_host::last_error().clear();
     if (int rc = check_dims(B, C, n_x)) return rc;
     if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "cfc_scratch_fill: K=%d out of range", K);
     const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;

@@ -1331,6 +1331,11 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
                 if (n0 + j < N) out[n0 + j] = (float)s[j];
         }
     }
+    if (a.xn > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+        double t = 0.0;
+        for (int64_t i = 0; i < a.xn; ++i) t += (double)a.xin[i];
+        a.xout[0] = (float)t;
+    }
 }
 
 // AdamW over up to four tensors in one launch (flat index space, grid
@@ -1578,7 +1583,16 @@ hipError_t launch_persist(const PersistArgs& a, hipStream_t s)
 
 hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s)
 {
+    return launch_reduce_with_sum(segs, nseg, B, V, nullptr, 0, nullptr, s);
+}
+
+hipError_t launch_reduce_with_sum(const ReduceSeg* segs, int nseg, int64_t B, int V, const float* xin, int64_t xn,
+                                  float* xout, hipStream_t s)
+{
     ReduceArgs a{};
+    a.xin = xin;
+    a.xout = xout;
+    a.xn = xn > 0 ? xn : 0;
     a.nseg = nseg;
     a.B = B;
     a.R = reduce_slices(B);
@@ -1589,9 +1603,9 @@ hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipS
         total += segs[i].groups;
     }
     for (int i = nseg; i < kMaxReduceSegs; ++i) a.seg[i] = ReduceSeg{nullptr, nullptr, 0, 0};
-    if (total == 0) return hipSuccess;
+    if (total == 0 && a.xn == 0) return hipSuccess;
     const int lanes = kThreads / a.R;
-    const int64_t blocks = (total + lanes - 1) / lanes;
+    const int64_t blocks = total > 0 ? (total + lanes - 1) / lanes : 1;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (V == 4)
         hipLaunchKernelGGL(reduce_axis0_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);

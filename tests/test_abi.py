@@ -14,13 +14,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "cfc.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("cfc.h", "mlp.h")]
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|int64_t|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +35,9 @@ def L():
 
 def test_header_declares_the_four_entry_points():
     names = _declared()
-    for n in ("cfc_fwd_step", "cfc_bwd_step", "reduce_axis0", "cfc_train_kloop"):
+    for n in ("cfc_fwd_step", "cfc_bwd_step", "reduce_axis0", "cfc_train_kloop", "cfc_adamw_step",
+              "mlp_linear_fwd", "mlp_linear_bwd_data", "mlp_linear_bwd_weight", "mlp_mse_loss_grad",
+              "mlp_train_step", "mlp_param_offsets"):
         assert n in names
 
 
@@ -169,7 +173,7 @@ def test_workspace_size_and_path_queries(L):
 def test_no_atomics_in_kernel_sources():
     """Device code (kernels and the shared device math) uses no atomics."""
     csrc = os.path.join(ROOT, "recurrent_cell_amd", "csrc")
-    for fn in ("cfc_kernels.hip", "cfc_math.h", "cfc_kernels.h"):
+    for fn in ("cfc_kernels.hip", "cfc_math.h", "cfc_kernels.h", "mlp_kernels.hip", "mlp_kernels.h"):
         text = open(os.path.join(csrc, fn)).read()
         assert not re.search(r"\batomic\w*\s*\(|__hip_atomic|__atomic_|std::atomic", text), fn
 
@@ -218,3 +222,101 @@ def test_adamw_argument_errors(L):
     assert L.cfc_adamw_step(None, None, None, None, None, 0, *hp, 1, None) == 0
     n0 = (ctypes.c_int64 * 1)(0)
     assert L.cfc_adamw_step(_ptrs(None), _ptrs(None), _ptrs(None), _ptrs(None), n0, 1, *hp, 1, None) == 0
+
+
+# ---------------------------------------------------------------- MLP
+
+@pytest.fixture(scope="module")
+def ML(L):
+    from recurrent_cell_amd import mlp
+    return mlp.lib()
+
+
+def _dims(*d):
+    return (ctypes.c_int * len(d))(*d)
+
+
+def test_mlp_param_layout(ML):
+    """W_0, b_0, W_1, .. each starting at a multiple of 4 floats."""
+    dims = (48, 256, 256, 128, 51)
+    w = (ctypes.c_int64 * 4)()
+    b = (ctypes.c_int64 * 4)()
+    total = ML.mlp_param_offsets(_dims(*dims), 4, w, b)
+    expect_w, expect_b, off = [], [], 0
+    for l in range(4):
+        expect_w.append(off)
+        off += dims[l + 1] * dims[l]
+        off = -(-off // 4) * 4
+        expect_b.append(off)
+        off += dims[l + 1]
+        off = -(-off // 4) * 4
+    assert list(w) == expect_w and list(b) == expect_b and total == off == 117812
+    assert sum(dims[l + 1] * (dims[l] + 1) for l in range(4)) == 117811   # the parameters themselves
+    assert ML.mlp_param_offsets(_dims(3, 5), 1, None, None) == 16 + 8
+    assert ML.mlp_param_offsets(_dims(3, 0), 1, None, None) == -1
+    assert ML.mlp_param_offsets(_dims(3, 5), 0, None, None) == -1
+    assert ML.mlp_param_offsets(_dims(*([4] * 10)), 9, None, None) == -1
+    assert ML.mlp_param_offsets(_dims(4097, 5), 1, None, None) == -1
+
+
+def test_mlp_splits_and_workspace(ML):
+    assert ML.mlp_weight_grad_splits(16384) == 32
+    assert ML.mlp_weight_grad_splits(1) == 1
+    assert ML.mlp_weight_grad_splits(1000) == 1
+    assert ML.mlp_weight_grad_splits(1100) == 2
+    # splits of at most 2^24 rows still 32
+    assert ML.mlp_weight_grad_splits(1 << 24) == 32
+    S = 32
+    assert ML.mlp_linear_bwd_weight_workspace_bytes(16384, 256, 256) == 4 * (S * 65536 + S * 256)
+    assert ML.mlp_linear_bwd_weight_workspace_bytes(16384, 128, 51) == 4 * (S * 51 * 128 + (-(-S * 51 // 4)) * 4)
+    assert ML.mlp_linear_bwd_weight_workspace_bytes(-1, 4, 4) == 0
+    assert ML.mlp_mse_workspace_bytes(16384) == 4 * 256
+    dims = _dims(48, 256, 256, 128, 51)
+    ldy = [256, 256, 128, 52]
+    expect = 16384 * sum(ldy) + S * 117812 + 256
+    assert ML.mlp_train_step_workspace_bytes(16384, dims, 4) == 4 * expect
+    assert ML.mlp_train_step_workspace_bytes(0, dims, 4) == 0
+
+
+def test_mlp_argument_errors(ML):
+    F = FAKE
+    a = [F + i * (1 << 32) for i in range(8)]
+    assert ML.mlp_linear_fwd(a[0], a[1], a[2], a[3], -1, 4, 4, 1, None) == -1
+    assert ML.mlp_linear_fwd(a[0], a[1], a[2], a[3], 16, 0, 4, 1, None) == -1
+    assert ML.mlp_linear_fwd(a[0], a[1], a[2], a[3], 16, 4, 4097, 1, None) == -1
+    assert ML.mlp_linear_fwd(None, a[1], a[2], a[3], 16, 4, 4, 1, None) == -1
+    assert ML.mlp_linear_fwd(a[0], a[1], a[2], a[0] + 32, 16, 4, 4, 1, None) == -1   # Y overlaps X
+    assert b"overlap" in ML.cfc_last_error()
+    assert ML.mlp_linear_fwd(None, None, None, None, 0, 4, 4, 1, None) == 0           # M == 0: nothing to do
+    assert ML.mlp_linear_bwd_data(a[0], a[1], a[2], a[2] + 16, 16, 4, 4, None) == -1  # dX overlaps the mask
+    assert ML.mlp_linear_bwd_data(a[0], None, None, a[3], 16, 4, 4, None) == -1
+    ws_need = ML.mlp_linear_bwd_weight_workspace_bytes(16, 4, 4)
+    assert ML.mlp_linear_bwd_weight(a[0], a[1], a[2], a[3], 16, 4, 4, a[4], ws_need - 4, None) == -1
+    assert b"workspace" in ML.cfc_last_error()
+    assert ML.mlp_linear_bwd_weight(a[0], a[1], a[2], a[2] + 8, 16, 4, 4, a[4], ws_need, None) == -1
+    assert ML.mlp_linear_bwd_weight(a[0], a[1], None, a[3], 16, 4, 4, a[4], ws_need, None) == -1
+    assert ML.mlp_mse_loss_grad(a[0], a[1], a[2], a[3], 0, 4, a[4], 4096, None) == -1
+    assert ML.mlp_mse_loss_grad(a[0], a[1], a[0], a[3], 16, 4, a[4], 4096, None) == -1
+    assert ML.mlp_mse_loss_grad(a[0], a[1], a[2], a[3], 16, 4, a[4], 0, None) == -1
+    dims = _dims(8, 16, 4)
+    acts = (ctypes.c_void_p * 2)(a[5], a[6])
+    need = ML.mlp_train_step_workspace_bytes(32, dims, 2)
+    ok = (a[0], a[1], 32, dims, 2, a[2], a[3], acts, a[4], a[7], need, None)
+    bad = list(ok)
+    bad[10] = need - 4
+    assert ML.mlp_train_step(*bad) == -1 and b"workspace" in ML.cfc_last_error()
+    bad = list(ok)
+    bad[2] = 0
+    assert ML.mlp_train_step(*bad) == -1
+    bad = list(ok)
+    bad[4] = 0
+    assert ML.mlp_train_step(*bad) == -1
+    bad = list(ok)
+    bad[7] = (ctypes.c_void_p * 2)(a[5], None)
+    assert ML.mlp_train_step(*bad) == -1
+    bad = list(ok)
+    bad[7] = (ctypes.c_void_p * 2)(a[5], a[5] + 64)                                      # two outputs overlap
+    assert ML.mlp_train_step(*bad) == -1 and b"overlap" in ML.cfc_last_error()
+    bad = list(ok)
+    bad[3] = (ctypes.c_int * 3)(8, 0, 4)
+    assert ML.mlp_train_step(*bad) == -1

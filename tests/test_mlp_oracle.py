@@ -90,3 +90,32 @@ def test_mlp_oracle_relu_derivative_at_zero():
     assert r["gb"][1][0] != 0.0
     pre, post = mlp_forward(X, W, b)
     assert (post[-1] == 0.5).all()
+
+
+def test_single_layer_helpers_match_torch():
+    from oracle.mlp_oracle import linear_bwd_data, linear_bwd_weight, linear_fwd, mse_loss_grad
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((33, 7))
+    W = rng.standard_normal((5, 7))
+    b = rng.standard_normal(5)
+    tX, tW, tb = (torch.tensor(a, requires_grad=True) for a in (X, W, b))
+    a = torch.nn.functional.linear(tX, tW, tb)
+    np.testing.assert_allclose(linear_fwd(X, W, b, False), a.detach().numpy(), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(linear_fwd(X, W, b, True), torch.relu(a).detach().numpy(), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(linear_fwd(X, W, None, False), (tX @ tW.T).detach().numpy(), rtol=1e-14, atol=1e-14)
+    dY = rng.standard_normal((33, 5))
+    a.backward(torch.tensor(dY))
+    np.testing.assert_allclose(linear_bwd_data(dY, W, None), tX.grad.numpy(), rtol=1e-13, atol=1e-14)
+    gW, gb = linear_bwd_weight(dY, X)
+    np.testing.assert_allclose(gW, tW.grad.numpy(), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(gb, tb.grad.numpy(), rtol=1e-13, atol=1e-14)
+    mask = rng.standard_normal((33, 7))
+    np.testing.assert_array_equal(linear_bwd_data(dY, W, mask)[mask <= 0], 0.0)
+    Y = rng.standard_normal((9, 4))
+    T = rng.standard_normal((9, 4))
+    tY = torch.tensor(Y, requires_grad=True)
+    l = torch.nn.functional.mse_loss(tY, torch.tensor(T))
+    l.backward()
+    loss, g = mse_loss_grad(Y, T)
+    assert abs(loss - l.item()) <= 1e-14 * l.item()
+    np.testing.assert_allclose(g, tY.grad.numpy(), rtol=1e-13, atol=1e-15)

@@ -98,3 +98,84 @@ def check_adamw(p, m, v, ref, p0, m0, g, lr, beta1, beta2, eps, step):
     return [_report("p", p, rp, 16 * U32 * (np.abs(p0) + step_size * mass_m / den)),
             _report("m", m, rm, 4 * U32 * mass_m),
             _report("v", v, rv, np.maximum(4 * U32 * rv, np.finfo(np.float32).tiny))]
+
+
+# ---------------------------------------------------------------- MLP step
+#
+# Probabilistic first-order error bounds (rounding errors of a long fp32
+# chain behave like independent draws, so they grow like sqrt(n) u, not the
+# worst-case n u; the forms follow that analysis), propagated layer by layer
+# from the fp64 oracle's values, with independent contributions added in
+# quadrature ("rss") and a safety factor KAPPA_MLP:
+#   local rounding of an n-term fp32 chain over terms of absolute sum m:
+#       KAPPA_MLP sqrt(n) u m;
+#   forward a_l = x W^T + b:  E_l = rss(E_{l-1} through |W_l|, local(dims[l] + 1));
+#     ReLU is 1-Lipschitz, so the post-ReLU bound is the same;
+#   output gradient g = 2 (y - t) / n:  G = rss((2/n) E_y, 3 u |g|);
+#   upstream dX = g W:  Gx = rss(G through |W|, local(dims[l+1]));
+#     through the previous ReLU: where |a_ref| <= E (the two sides may take
+#     different masks) add |dX_ref|; elsewhere Gx where a_ref > 0, else 0;
+#   weight gradient over the batch, splits of ks rows each an fp32 chain,
+#   the splits added in fp64: rss(G |x|, |g| E_x over the batch) +
+#     local(ks + 1) + u |gW|; bias gradient likewise with x = 1;
+#   loss: (2/n) sum |y - t| E_y + 4 u loss.
+# KAPPA_MLP = 4 leaves at least 2x over the worst ratio of two plain fp32
+# evaluations (torch's CPU GEMMs, and sequential chains in k order like the
+# matrix cores') at the tested shapes; a doubled or dropped gradient term
+# fails on nearly every element.
+KAPPA_MLP = 4.0
+
+
+def _rss_prop(E, aW2):
+    """sqrt(E^2 @ (W^2)^T): independent errors E carried through W."""
+    return np.sqrt((E * E) @ aW2.T)
+
+
+def mlp_bounds(X, Ws, bs, ref, k_split, kappa=KAPPA_MLP):
+    """Bounds for act[l], loss, gW[l], gb[l] of the GPU step against ref =
+    oracle.mlp_oracle.mlp_train_step(...) on the same fp32 inputs."""
+    X = np.asarray(X, np.float64)
+    L = len(Ws)
+    W64 = [np.asarray(W, np.float64) for W in Ws]
+    aW = [np.abs(W) for W in W64]
+    aW2 = [W * W for W in W64]
+    ab = [np.abs(np.asarray(b, np.float64)) for b in bs]
+    E, Ex, x = [], np.zeros_like(X), X
+    for l in range(L):
+        K = aW[l].shape[1]
+        local = kappa * np.sqrt(K + 1) * U32 * (np.abs(x) @ aW[l].T + ab[l])
+        El = np.sqrt(_rss_prop(Ex, aW2[l]) ** 2 + local ** 2)
+        E.append(El)
+        Ex, x = El, ref["post"][l]
+    y = ref["post"][-1]
+    n = y.size
+    G = [None] * L
+    g = ref["dA"][L - 1]
+    G[L - 1] = np.sqrt(((2.0 / n) * E[-1]) ** 2 + (3 * U32 * g) ** 2)
+    for l in range(L - 1, 0, -1):
+        Kd = aW[l].shape[0]
+        gl = ref["dA"][l]
+        local = kappa * np.sqrt(Kd) * U32 * (np.abs(gl) @ aW[l])
+        Gx = np.sqrt((G[l] * G[l]) @ aW2[l] + local ** 2)
+        dx_ref = gl @ W64[l]
+        a_prev = ref["pre"][l - 1]
+        amb = np.abs(a_prev) <= E[l - 1]
+        G[l - 1] = np.where(amb, np.abs(dx_ref) + Gx, np.where(a_prev > 0, Gx, 0.0))
+    gW, gb = [], []
+    for l in range(L):
+        xin = X if l == 0 else ref["post"][l - 1]
+        Ein = np.zeros_like(X) if l == 0 else E[l - 1]
+        gl = np.abs(ref["dA"][l])
+        prop = np.sqrt((G[l] ** 2).T @ (xin ** 2) + (gl ** 2).T @ (Ein ** 2))
+        bw = prop + kappa * np.sqrt(k_split + 1) * U32 * (gl.T @ np.abs(xin)) + U32 * np.abs(ref["gW"][l])
+        bb = np.sqrt((G[l] ** 2).sum(axis=0)) + kappa * np.sqrt(k_split + 1) * U32 * gl.sum(axis=0) + \
+            U32 * np.abs(ref["gb"][l])
+        gW.append(bw)
+        gb.append(bb)
+    return dict(act=E, gW=gW, gb=gb,
+                loss_fn=lambda T: (2.0 / n) * float(np.sum(np.abs(y - np.asarray(T, np.float64)) * E[-1])) +
+                4 * U32 * ref["loss"])
+
+
+def check_bound(name, x, ref, bound):
+    return _report(name, x, ref, np.maximum(np.asarray(bound, np.float64), np.finfo(np.float32).tiny))
