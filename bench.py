@@ -216,9 +216,10 @@ def deterministic_runs(torch, cfc, t, n=3):
     return True
 
 
-def time_steps(torch, cfc, t, out, steps, warmup, trials):
+def time_calls(torch, fn, steps, warmup, trials):
+    """Median over trials of the ms per call of fn, calls back to back."""
     for _ in range(warmup):
-        cfc.cfc_train_kloop(*t, out=out)
+        fn()
     torch.cuda.synchronize()
     res = []
     for _ in range(trials):
@@ -226,11 +227,15 @@ def time_steps(torch, cfc, t, out, steps, warmup, trials):
         torch.cuda.synchronize()
         a.record()
         for _ in range(steps):
-            cfc.cfc_train_kloop(*t, out=out)
+            fn()
         b.record()
         torch.cuda.synchronize()
         res.append(a.elapsed_time(b) / steps)
     return float(np.median(res)), res
+
+
+def time_steps(torch, cfc, t, out, steps, warmup, trials):
+    return time_calls(torch, lambda: cfc.cfc_train_kloop(*t, out=out), steps, warmup, trials)
 
 
 def bench_reduce(torch, cfc, timer, shapes):
@@ -432,6 +437,10 @@ def main():
         finally:
             cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
+    # the K-loop step with the GEMM-form weight gradient in place of scratch + reducer
+    og = cfc.cfc_train_kloop_gemm(*t)
+    ms_gemm, _ = time_calls(torch, lambda: cfc.cfc_train_kloop_gemm(*t, out=og), max(20, args.steps // 5), 5, 3)
+
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
     t_node = graph_node_latency(torch)
     kernels = {}
@@ -450,6 +459,10 @@ def main():
         kt["scratch_fill"] = timer(lambda: cfc.cfc_scratch_fill(dp, t[0], out.h_hist, out.gW_scratch,
                                                                 out.gb_scratch), 50)
         kt["reduce_axis0"] = timer(lambda: cfc.reduce_axis0(gW_flat, red_out), 50)
+        # the GEMM-form weight gradient (no scratch) on the same dp, against scratch fill + reduce
+        gws = torch.empty(cfc.lib().cfc_weight_grad_gemm_workspace_bytes(B, C, n_x, K) // 4 + 1, device="cuda")
+        gWg, gbg = torch.empty((3, C, n_in), device="cuda"), torch.empty((3, C), device="cuda")
+        kt["weight_grad_gemm"] = timer(lambda: cfc.cfc_weight_grad_gemm(dp, t[0], out.h_hist, gWg, gbg, gws), 50)
         # step kernels of the 2K-launch path
         S = torch.zeros((B, 3, C, n_in), device="cuda")
         Sb = torch.zeros((B, 3, C), device="cuda")
@@ -532,6 +545,7 @@ def main():
                  "flops": flops, "bytes_min": bytes_min,
                  "contrast_path": contrast,
                  "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None,
+                 "gemm_form_weight_grad_ms_per_step": round(ms_gemm, 5),
                  "critical_path": crit}
 
     result = {

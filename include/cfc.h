@@ -188,6 +188,38 @@ int cfc_adamw_step(float* const* params, const float* const* grads, float* const
                    const int64_t* n, int nseg, float lr, float beta1, float beta2, float eps,
                    float weight_decay, int step, void* stream);
 
+/* GEMM-form weight gradient, an alternative to the per-sample scratch and
+ * its reducer ("K-loop Parallelization", section Architecture Choice, "Why
+ * scratch+reducer", weighs the per-sample scratch against other ways of
+ * summing over the batch; "H100 Epoch Optimization Phase 2", Task 2, forms
+ * a weight gradient as dY^T X over the batch).  It writes no scratch:
+ *   gW[q, c, k] = sum over t = 1..K, b of dp_t[b, q C + c] z_t[b, k],
+ *   gb[q, c]    = sum over t, b of dp_t[b, q C + c],
+ * with z_t = [u_t ; h_{t-1}], as ONE contraction over the K*B (t, b) rows on
+ * the matrix cores, cut into fixed row splits whose fp32 partials are added
+ * in fp64 by the batch-axis reducer.  Same values as cfc_train_kloop's gW,
+ * gb to rounding (a different, equally fixed summation order: not the same
+ * bits).
+ *   dp     [K, B, 3C]  pre-activation gradients (cfc_kloop_fwd_bwd leaves
+ *                      them at the start of its workspace)
+ *   u      [K, B, n_x], h_hist [K+1, B, C] (rows 0 .. K-1 are read)
+ *   gW     [3, C, n_in], gb [3, C]   OVERWRITTEN
+ *   ws     cfc_weight_grad_gemm_workspace_bytes() bytes of device memory.
+ * K*B up to 2^30 rows (and K*B*3C below 2^31); K*B == 0 writes zeros. */
+int cfc_weight_grad_gemm(const float* dp, const float* u, const float* h_hist, float* gW, float* gb, int B, int C,
+                         int n_x, int K, void* ws, size_t ws_bytes, void* stream);
+size_t cfc_weight_grad_gemm_workspace_bytes(int B, int C, int n_x, int K);
+
+/* The K-loop training step with the GEMM-form weight gradient in place of
+ * the scratch and its reducer: cfc_kloop_fwd_bwd, then
+ * cfc_weight_grad_gemm on the dp it leaves in the workspace.  Arguments as
+ * cfc_train_kloop without the scratch; ws holds
+ * cfc_train_kloop_gemm_workspace_bytes() bytes. */
+int cfc_train_kloop_gemm(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                         float* h_hist, float* act, float* gW, float* gb, void* ws, size_t ws_bytes, int B, int C,
+                         int n_x, int K, void* stream);
+size_t cfc_train_kloop_gemm_workspace_bytes(int B, int C, int n_x, int K);
+
 /* The two launches of cfc_kloop_fwd_bwd's persistent path, callable on
  * their own (same kernels, same bits):
  * cfc_input_projection -- the input part of every step's pre-activations,

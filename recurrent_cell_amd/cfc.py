@@ -52,6 +52,12 @@ def lib():
         L.cfc_kloop_recurrence.argtypes = [_P] * 7 + [_I, _I, _I, _I, _P]
         _F = ctypes.c_float
         L.cfc_adamw_step.argtypes = [_P] * 5 + [_I, _F, _F, _F, _F, _F, _I, _P]
+        L.cfc_weight_grad_gemm.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P, ctypes.c_size_t, _P]
+        L.cfc_weight_grad_gemm_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.cfc_weight_grad_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.cfc_train_kloop_gemm.argtypes = [_P] * 9 + [_P, ctypes.c_size_t, _I, _I, _I, _I, _P]
+        L.cfc_train_kloop_gemm_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.cfc_train_kloop_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.cfc_train_kloop_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.cfc_train_kloop_workspace_bytes.restype = ctypes.c_size_t
         L.cfc_set_kloop_mode.argtypes = [_I]
@@ -62,7 +68,8 @@ def lib():
         L.cfc_clear_graph_cache.argtypes = []
         for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
                   L.cfc_kloop_fwd_bwd, L.cfc_scratch_fill, L.cfc_clear_graph_cache,
-                  L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence, L.cfc_adamw_step):
+                  L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence, L.cfc_adamw_step,
+                  L.cfc_weight_grad_gemm, L.cfc_train_kloop_gemm):
             f.restype = _I
         _LIB = L
     return _LIB
@@ -249,6 +256,57 @@ def cfc_adamw_step(params, grads, ms, vs, lr, beta1=0.9, beta2=0.999, eps=1e-8, 
                                                   arr(vs, "v"), counts, n, lr, beta1, beta2, eps,
                                                   weight_decay, int(step), stream))
     return params
+
+
+def cfc_weight_grad_gemm(dp, u, h_hist, gW=None, gb=None, ws=None):
+    """GEMM-form weight gradient from the saved dp [K, B, 3C] (no scratch)."""
+    K, B, n_x = u.shape
+    C = h_hist.shape[2]
+    n_in = n_x + C
+    dev = dp.device
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+    gW = e(3, C, n_in) if gW is None else gW
+    gb = e(3, C) if gb is None else gb
+    if ws is None:
+        ws = e(max(lib().cfc_weight_grad_gemm_workspace_bytes(B, C, n_x, K) // 4, 1))
+    args = (_dev(dp, "dp", (K, B, 3 * C)), _dev(u, "u", (K, B, n_x)), _dev(h_hist, "h_hist", (K + 1, B, C)),
+            _dev(gW, "gW", (3, C, n_in)), _dev(gb, "gb", (3, C)))
+    _check("cfc_weight_grad_gemm", lib().cfc_weight_grad_gemm(*args, B, C, n_x, K, _dev(ws, "ws"), ws.numel() * 4,
+                                                              _stream(dp)))
+    return gW, gb
+
+
+@dataclass
+class KloopGemmBuffers:
+    """Outputs and workspace of cfc_train_kloop_gemm (no scratch)."""
+    h_hist: torch.Tensor
+    act: torch.Tensor
+    ws: torch.Tensor
+    gW: torch.Tensor
+    gb: torch.Tensor
+
+    @staticmethod
+    def allocate(B, C, n_x, K, device):
+        e = lambda *s: torch.empty(s, dtype=torch.float32, device=device)  # noqa: E731
+        ws_floats = lib().cfc_train_kloop_gemm_workspace_bytes(B, C, n_x, K) // 4
+        return KloopGemmBuffers(h_hist=e(K + 1, B, C), act=e(K, 3, B, C), ws=e(max(ws_floats, 1)),
+                                gW=e(3, C, n_x + C), gb=e(3, C))
+
+
+def cfc_train_kloop_gemm(u, y, h0, W, bias, out=None):
+    """The K-loop step with the GEMM-form weight gradient (no scratch)."""
+    K, B, n_x = u.shape
+    C = h0.shape[1]
+    n_in = n_x + C
+    if out is None:
+        out = KloopGemmBuffers.allocate(B, C, n_x, K, h0.device)
+    args = (_dev(u, "u", (K, B, n_x)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
+            _dev(W, "W", (3, C, n_in)), _dev(bias, "bias", (3, C)),
+            _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
+            _dev(out.gW, "gW", (3, C, n_in)), _dev(out.gb, "gb", (3, C)))
+    _check("cfc_train_kloop_gemm", lib().cfc_train_kloop_gemm(*args, _dev(out.ws, "ws"), out.ws.numel() * 4,
+                                                              B, C, n_x, K, _stream(u)))
+    return out
 
 
 def cfc_scratch_fill(dp, u, h_hist, gW_scratch, gb_scratch):

@@ -18,6 +18,7 @@
 #include "api_common.h"
 #include "cfc_kernels.h"
 #include "cfc_math.h"
+#include "gemm_kernels.h"
 
 namespace {
 
@@ -530,6 +531,172 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
     }
     const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, nullptr, nullptr, nullptr, nullptr, B, C, n_x, K};
     return enqueue_fwd_bwd(k, path, make_plan(B, C, n_x, W, nullptr), s);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM-form weight gradient: gW_q = sum over the K*B (t, b) rows of
+// dp_t[b, q C + c] z_t[b, k], one matrix-core contraction over the rows
+// (input columns from u, recurrent columns from h_hist[0 .. K-1]), cut into
+// fixed row splits whose partials are added by the batch-axis reducer.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct WgPlan {
+    int k_split;   // rows per split (multiple of the GEMM chunk)
+    int S;         // splits
+    int64_t part_floats;
+};
+
+// Splits: enough for about 512 workgroups over the output tiles; a function
+// of the sizes only.
+WgPlan wg_plan(int B, int C, int n_x, int K)
+{
+    WgPlan p{};
+    const int64_t rows = (int64_t)K * B;
+    const int tiles = ((3 * C + gemm::kTile - 1) / gemm::kTile) *
+                      ((n_x + gemm::kTile - 1) / gemm::kTile + (C + gemm::kTile - 1) / gemm::kTile);
+    int64_t S = (512 + tiles - 1) / tiles;
+    S = S < 1 ? 1 : (S > 32 ? 32 : S);
+    int64_t per = rows > 0 ? (rows + S - 1) / S : 1;
+    per = (per + gemm::kBK - 1) / gemm::kBK * gemm::kBK;
+    p.k_split = (int)per;
+    p.S = rows > 0 ? (int)((rows + per - 1) / per) : 1;
+    const int64_t n_in = (int64_t)n_x + C;
+    p.part_floats = ((int64_t)p.S * 3 * C * n_in + 3) / 4 * 4 + ((int64_t)p.S * 3 * C + 3) / 4 * 4;
+    return p;
+}
+
+gemm::Operand wg_operand(const float* p, int64_t ld, int64_t extent)
+{
+    return gemm::Operand{p, ld, 0, (ld % 4 == 0 && extent % 4 == 0 && extent >= 4 && aligned16(p)) ? 1 : 0};
+}
+
+int enqueue_weight_grad_gemm(const float* dp, const float* u, const float* h_hist, float* gW, float* gb, int B,
+                             int C, int n_x, int K, float* part, hipStream_t s)
+{
+    const int64_t n_in = (int64_t)n_x + C, R3 = 3 * (int64_t)C;
+    const int64_t rows = (int64_t)K * B;
+    const WgPlan p = wg_plan(B, C, n_x, K);
+    float* wpart = part;
+    float* bpart = part + ((int64_t)p.S * R3 * n_in + 3) / 4 * 4;
+    gemm::GemmTask t[2] = {};
+    int nt = 0;
+    for (int half = 0; half < 2; ++half) {
+        const int N = half == 0 ? n_x : C;
+        if (N == 0) continue;
+        gemm::GemmTask& g = t[nt++];
+        g.A = wg_operand(dp, R3, R3);                              // A(m, row) = dp[row, m]
+        g.B = half == 0 ? wg_operand(u, n_x, n_x) : wg_operand(h_hist, C, C);   // B(n, row) = z[row, n]
+        g.M = (int)R3;
+        g.N = N;
+        g.K = (int)rows;
+        g.k_split = p.k_split;
+        g.epi = gemm::kEpiDw;
+        g.out = wpart + (half == 0 ? 0 : n_x);
+        g.ldo = n_in;
+        g.split_stride = R3 * n_in;
+        if (nt == 1) {   // the bias gradient once, from the first task's dp tiles
+            g.colsum = bpart;
+            g.colsum_stride = R3;
+        }
+    }
+    // one launch per group of tasks that take the same loads
+    for (int va = 0; va < 2; ++va)
+        for (int vb = 0; vb < 2; ++vb) {
+            gemm::GemmBatch b{};
+            for (int i = 0; i < nt; ++i)
+                if (t[i].A.vec == va && t[i].B.vec == vb) b.t[b.ntask++] = t[i];
+            if (b.ntask == 0) continue;
+            gemm::finish_batch(b);
+            CFC_HIP(gemm::launch_gemm(b, s), "weight-gradient GEMM launch");
+        }
+    cfc::ReduceSeg segs[2] = {{wpart, gW, R3 * n_in, 0}, {bpart, gb, R3, 0}};
+    bool vec = true;
+    for (const auto& g : segs) vec = vec && g.N % 4 == 0 && aligned16(g.in) && aligned16(g.out);
+    const int V = vec ? 4 : 1;
+    for (auto& g : segs) g.groups = (g.N + V - 1) / V;
+    CFC_HIP(cfc::launch_reduce(segs, 2, p.S, V, s), "weight-gradient reduce launch");
+    return CFC_OK;
+}
+
+}  // namespace
+
+size_t cfc_weight_grad_gemm_workspace_bytes(int B, int C, int n_x, int K)
+{
+    if (check_dims(B, C, n_x) || K < 0 || K > (1 << 20)) return 0;
+    return sizeof(float) * (size_t)wg_plan(B, C, n_x, K).part_floats;
+}
+
+int cfc_weight_grad_gemm(const float* dp, const float* u, const float* h_hist, float* gW, float* gb, int B, int C,
+                         int n_x, int K, void* ws, size_t ws_bytes, void* stream)
+{
+    cfc_host::last_error().clear();
+    const char* fn = "cfc_weight_grad_gemm";
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "%s: K=%d out of range", fn, K);
+    const int64_t n_in = (int64_t)n_x + C, R3 = 3 * (int64_t)C, rows = (int64_t)K * B;
+    if (rows * R3 > ((int64_t)1 << 31) || rows > ((int64_t)1 << 30))
+        return fail(CFC_EINVAL, "%s: K*B=%lld rows too many", fn, (long long)rows);
+    if (!gW || !gb) return fail(CFC_EINVAL, "%s: null pointer", fn);
+    hipStream_t s = (hipStream_t)stream;
+    if (rows == 0) {
+        CFC_HIP(cfc::launch_fill_zero(gW, R3 * n_in, s), "zero fill launch");
+        CFC_HIP(cfc::launch_fill_zero(gb, R3, s), "zero fill launch");
+        return CFC_OK;
+    }
+    const size_t need = cfc_weight_grad_gemm_workspace_bytes(B, C, n_x, K);
+    if (!dp || !h_hist || !ws || (n_x > 0 && !u)) return fail(CFC_EINVAL, "%s: null pointer", fn);
+    if (ws_bytes < need) return fail(CFC_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+    const Span outs[] = {span(gW, R3 * n_in), span(gb, R3), Span{ws, need}};
+    const Span ins[] = {span(dp, rows * R3), span(u, rows * n_x), span(h_hist, rows * C)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Span& in : ins)
+            if (overlap(outs[i], in)) return fail(CFC_EINVAL, "%s: an output overlaps an input", fn);
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "%s: outputs overlap", fn);
+    }
+    return enqueue_weight_grad_gemm(dp, u, h_hist, gW, gb, B, C, n_x, K, static_cast<float*>(ws), s);
+}
+
+size_t cfc_train_kloop_gemm_workspace_bytes(int B, int C, int n_x, int K)
+{
+    if (check_dims(B, C, n_x) || K < 0 || K > (1 << 20)) return 0;
+    return sizeof(float) * (size_t)(kloop_ws_floats(B, C, n_x, K) + wg_plan(B, C, n_x, K).part_floats);
+}
+
+int cfc_train_kloop_gemm(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                         float* h_hist, float* act, float* gW, float* gb, void* ws, size_t ws_bytes, int B, int C,
+                         int n_x, int K, void* stream)
+{
+    cfc_host::last_error().clear();
+    const char* fn = "cfc_train_kloop_gemm";
+    const size_t need = cfc_train_kloop_gemm_workspace_bytes(B, C, n_x, K);
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "%s: K=%d out of range", fn, K);
+    if (ws_bytes < need) return fail(CFC_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+    const int64_t n_in = (int64_t)n_x + C, R3 = 3 * (int64_t)C, rows = (int64_t)K * B;
+    if (rows * R3 > ((int64_t)1 << 31) || rows > ((int64_t)1 << 30))
+        return fail(CFC_EINVAL, "%s: K*B=%lld rows too many", fn, (long long)rows);
+    if (!gW || !gb) return fail(CFC_EINVAL, "%s: null pointer", fn);
+    const Span extra[] = {span(gW, R3 * n_in), span(gb, R3)};
+    const Span others[] = {span(u, rows * n_x), span(y, rows * C), span(h0, (int64_t)B * C), span(W, R3 * n_in),
+                           span(bias, R3), span(h_hist, (K + 1) * (int64_t)B * C), span(act, rows * R3),
+                           Span{ws, need}};
+    for (int i = 0; i < 2; ++i) {
+        for (const Span& o : others)
+            if (overlap(extra[i], o)) return fail(CFC_EINVAL, "%s: gW or gb overlaps another array", fn);
+    }
+    if (overlap(extra[0], extra[1])) return fail(CFC_EINVAL, "%s: outputs overlap", fn);
+    const size_t kws = (size_t)kloop_ws_floats(B, C, n_x, K) * sizeof(float);
+    float* wsf = static_cast<float*>(ws);
+    if (int rc = cfc_kloop_fwd_bwd(u, y, h0, W, bias, h_hist, act, wsf, kws, B, C, n_x, K, stream)) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (rows == 0) {
+        CFC_HIP(cfc::launch_fill_zero(gW, R3 * n_in, s), "zero fill launch");
+        CFC_HIP(cfc::launch_fill_zero(gb, R3, s), "zero fill launch");
+        return CFC_OK;
+    }
+    return enqueue_weight_grad_gemm(wsf, u, h_hist, gW, gb, B, C, n_x, K, wsf + kloop_ws_floats(B, C, n_x, K), s);
 }
 
 int cfc_adamw_step(float* const* params, const float* const* grads, float* const* m, float* const* v,

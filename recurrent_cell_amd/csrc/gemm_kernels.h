@@ -1,11 +1,12 @@
-// Internal interface between the MLP C-ABI layer (mlp_api.hip) and its gfx950
-// kernels (mlp_kernels.hip).  include/mlp.h is the public ABI.
+// Internal interface of the fp32 matrix-core GEMM kernel with epilogues and
+// the MSE kernel (gemm_kernels.hip), used by the MLP C-ABI layer
+// (mlp_api.hip) and by the GEMM-form CfC weight gradient (cfc_api.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace mlp {
+namespace gemm {
 
 constexpr int kGemmThreads = 512;   // 8 wave64: 4 (rows) x 2 (columns) over the tile
 constexpr int kTile = 64;           // output tile: 64 rows x 64 columns
@@ -69,4 +70,4 @@ void finish_batch(GemmBatch& g);
 hipError_t launch_gemm(const GemmBatch& g, hipStream_t s);
 hipError_t launch_mse(const MseArgs& a, hipStream_t s);
 
-}  // namespace mlp
+}  // namespace gemm

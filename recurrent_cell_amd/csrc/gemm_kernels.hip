@@ -1,13 +1,14 @@
-// gfx950 kernels of the batched MLP training step: one fp32 matrix-core
-// GEMM kernel with three epilogues (forward + bias + ReLU, upstream gradient
-// + ReLU mask, weight-gradient splits + bias column sums) and the
-// mean-squared-error kernel.  Page "H100 Epoch Optimization Phase 2: Kernel
-// Occupancy & cuBLAS", Implementation Tasks 1 and 2: the per-sample layer
-// products become one batched product per layer, and the weight gradient
-// becomes dY^T X summed over the batch.
-#include "mlp_kernels.h"
+// gfx950 kernels of the batched MLP training step, also used by the
+// GEMM-form CfC weight gradient: one fp32 matrix-core GEMM kernel with three
+// epilogues (forward + bias + ReLU, upstream gradient + ReLU mask,
+// weight-gradient splits + bias column sums) and the mean-squared-error
+// kernel.  Page "H100 Epoch Optimization Phase 2: Kernel Occupancy &
+// cuBLAS", Implementation Tasks 1 and 2: the per-sample layer products
+// become one batched product per layer, and the weight gradient becomes
+// dY^T X summed over the batch.
+#include "gemm_kernels.h"
 
-namespace mlp {
+namespace gemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -300,4 +301,4 @@ hipError_t launch_mse(const MseArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-}  // namespace mlp
+}  // namespace gemm

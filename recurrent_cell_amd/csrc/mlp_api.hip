@@ -7,7 +7,7 @@
 #include "../../include/mlp.h"
 #include "api_common.h"
 #include "cfc_kernels.h"
-#include "mlp_kernels.h"
+#include "gemm_kernels.h"
 
 namespace {
 
@@ -24,9 +24,9 @@ constexpr int kMseParts = 256;    // at most this many partial losses
 int64_t round4(int64_t n) { return (n + 3) & ~int64_t(3); }
 
 // extent: the length of the contiguous index (K when kc, else the rows).
-mlp::Operand operand(const float* p, int64_t ld, int kc, int64_t extent)
+gemm::Operand operand(const float* p, int64_t ld, int kc, int64_t extent)
 {
-    return mlp::Operand{p, ld, kc, (ld % 4 == 0 && extent % 4 == 0 && extent >= 4 && aligned16(p)) ? 1 : 0};
+    return gemm::Operand{p, ld, kc, (ld % 4 == 0 && extent % 4 == 0 && extent >= 4 && aligned16(p)) ? 1 : 0};
 }
 
 // Reduction length of one weight-gradient split (a multiple of 16); the
@@ -36,7 +36,7 @@ int k_split_for(int M)
     int S = M / kSplitRows;
     S = S < 1 ? 1 : (S > kMaxSplits ? kMaxSplits : S);
     const int per = (M + S - 1) / S;
-    return (per + mlp::kBK - 1) / mlp::kBK * mlp::kBK;
+    return (per + gemm::kBK - 1) / gemm::kBK * gemm::kBK;
 }
 
 int splits_for(int M) { return M > 0 ? (M + k_split_for(M) - 1) / k_split_for(M) : 1; }
@@ -63,17 +63,17 @@ int check_dims(const int* dims, int L, const char* fn)
     return CFC_OK;
 }
 
-mlp::GemmTask fwd_task(const float* X, const float* W, const float* b, float* Y, int M, int n_in, int n_out,
+gemm::GemmTask fwd_task(const float* X, const float* W, const float* b, float* Y, int M, int n_in, int n_out,
                        int relu)
 {
-    mlp::GemmTask t{};
+    gemm::GemmTask t{};
     t.A = operand(X, n_in, 1, n_in);     // A(m, k) = X[m, k]
     t.B = operand(W, n_in, 1, n_in);     // B(n, k) = W[n, k]
     t.M = M;
     t.N = n_out;
     t.K = n_in;
-    t.k_split = (n_in + mlp::kBK - 1) / mlp::kBK * mlp::kBK;
-    t.epi = mlp::kEpiFwd;
+    t.k_split = (n_in + gemm::kBK - 1) / gemm::kBK * gemm::kBK;
+    t.epi = gemm::kEpiFwd;
     t.relu = relu ? 1 : 0;
     t.bias = b;
     t.out = Y;
@@ -81,17 +81,17 @@ mlp::GemmTask fwd_task(const float* X, const float* W, const float* b, float* Y,
     return t;
 }
 
-mlp::GemmTask dx_task(const float* dY, int64_t lddy, const float* W, const float* mask, float* dX, int64_t lddx,
+gemm::GemmTask dx_task(const float* dY, int64_t lddy, const float* W, const float* mask, float* dX, int64_t lddx,
                       int M, int n_in, int n_out)
 {
-    mlp::GemmTask t{};
+    gemm::GemmTask t{};
     t.A = operand(dY, lddy, 1, n_out);   // A(m, k) = dY[m, k]
     t.B = operand(W, n_in, 0, n_in);     // B(n, k) = W[k, n]
     t.M = M;
     t.N = n_in;
     t.K = n_out;
-    t.k_split = (n_out + mlp::kBK - 1) / mlp::kBK * mlp::kBK;
-    t.epi = mlp::kEpiDx;
+    t.k_split = (n_out + gemm::kBK - 1) / gemm::kBK * gemm::kBK;
+    t.epi = gemm::kEpiDx;
     t.mask = mask;
     t.ldm = n_in;
     t.out = dX;
@@ -101,17 +101,17 @@ mlp::GemmTask dx_task(const float* dY, int64_t lddy, const float* W, const float
 
 // gW = dY^T X split over the M rows: split s of the weight part at
 // wpart + s * wstride, of the bias column sums at bpart + s * bstride.
-mlp::GemmTask dw_task(const float* dY, int64_t lddy, const float* X, int M, int n_in, int n_out, float* wpart,
+gemm::GemmTask dw_task(const float* dY, int64_t lddy, const float* X, int M, int n_in, int n_out, float* wpart,
                       int64_t wstride, float* bpart, int64_t bstride)
 {
-    mlp::GemmTask t{};
+    gemm::GemmTask t{};
     t.A = operand(dY, lddy, 0, n_out);   // A(m, k) = dY[k, m]
     t.B = operand(X, n_in, 0, n_in);     // B(n, k) = X[k, n]
     t.M = n_out;
     t.N = n_in;
     t.K = M;
     t.k_split = k_split_for(M);
-    t.epi = mlp::kEpiDw;
+    t.epi = gemm::kEpiDw;
     t.out = wpart;
     t.ldo = n_in;
     t.split_stride = wstride;
@@ -120,10 +120,10 @@ mlp::GemmTask dw_task(const float* dY, int64_t lddy, const float* X, int M, int 
     return t;
 }
 
-int run_batch(mlp::GemmBatch& g, hipStream_t s, const char* what)
+int run_batch(gemm::GemmBatch& g, hipStream_t s, const char* what)
 {
-    mlp::finish_batch(g);
-    CFC_HIP(mlp::launch_gemm(g, s), what);
+    gemm::finish_batch(g);
+    CFC_HIP(gemm::launch_gemm(g, s), what);
     return CFC_OK;
 }
 
@@ -170,7 +170,7 @@ StepWs step_ws(int B, const int* dims, int L)
 int enqueue_mse(const float* Y, const float* T, float* dY, int64_t lddy, float* loss, float* lossp, int M, int N,
                 hipStream_t s)
 {
-    mlp::MseArgs a{};
+    gemm::MseArgs a{};
     a.Y = Y;
     a.T = T;
     a.dY = dY;
@@ -183,7 +183,7 @@ int enqueue_mse(const float* Y, const float* T, float* dY, int64_t lddy, float* 
     a.lossp = lossp;
     a.rows_per = mse_rows_per(M);
     a.S = mse_parts(M);
-    CFC_HIP(mlp::launch_mse(a, s), "mse launch");
+    CFC_HIP(gemm::launch_mse(a, s), "mse launch");
     CFC_HIP(cfc::launch_reduce_with_sum(nullptr, 0, 1, 1, lossp, a.S, loss, s), "loss sum launch");
     return CFC_OK;
 }
@@ -212,7 +212,7 @@ int mlp_linear_fwd(const float* X, const float* W, const float* b, float* Y, int
     const Span ins[] = {span(X, (int64_t)M * n_in), span(W, (int64_t)n_out * n_in), span(b, b ? n_out : 0)};
     for (const Span& i : ins)
         if (overlap(out, i)) return fail(CFC_EINVAL, "mlp_linear_fwd: the output overlaps an input");
-    mlp::GemmBatch g{};
+    gemm::GemmBatch g{};
     g.t[0] = fwd_task(X, W, b, Y, M, n_in, n_out, relu);
     g.ntask = 1;
     return run_batch(g, (hipStream_t)stream, "mlp_linear_fwd launch");
@@ -230,7 +230,7 @@ int mlp_linear_bwd_data(const float* dY, const float* W, const float* mask, floa
                         span(mask, mask ? (int64_t)M * n_in : 0)};
     for (const Span& i : ins)
         if (overlap(out, i)) return fail(CFC_EINVAL, "mlp_linear_bwd_data: the output overlaps an input");
-    mlp::GemmBatch g{};
+    gemm::GemmBatch g{};
     g.t[0] = dx_task(dY, n_out, W, mask, dX, n_in, M, n_in, n_out);
     g.ntask = 1;
     return run_batch(g, (hipStream_t)stream, "mlp_linear_bwd_data launch");
@@ -271,7 +271,7 @@ int mlp_linear_bwd_weight(const float* dY, const float* X, float* gW, float* gb,
     const int S = splits_for(M);
     float* wpart = static_cast<float*>(ws);
     float* bpart = wpart + round4((int64_t)S * NW);
-    mlp::GemmBatch g{};
+    gemm::GemmBatch g{};
     g.t[0] = dw_task(dY, n_out, X, M, n_in, n_out, wpart, NW, gb ? bpart : nullptr, n_out);
     g.ntask = 1;
     if (int rc = run_batch(g, s, "mlp_linear_bwd_weight launch")) return rc;
@@ -357,14 +357,14 @@ int mlp_train_step(const float* X, const float* T, int B, const int* dims, int n
 
     // forward, one launch per layer
     for (int l = 0; l < L; ++l) {
-        mlp::GemmBatch g{};
+        gemm::GemmBatch g{};
         g.t[0] = fwd_task(input(l), params + w_off[l], params + b_off[l], act[l], B, dims[l], dims[l + 1], l < L - 1);
         g.ntask = 1;
         if (int rc = run_batch(g, s, "forward launch")) return rc;
     }
     // loss and the output layer's gradient
     {
-        mlp::MseArgs a{};
+        gemm::MseArgs a{};
         a.Y = act[L - 1];
         a.T = T;
         a.dY = dy(L - 1);
@@ -377,11 +377,11 @@ int mlp_train_step(const float* X, const float* T, int B, const int* dims, int n
         a.lossp = wsf + w.loss_off;
         a.rows_per = mse_rows_per(B);
         a.S = w.P;
-        CFC_HIP(mlp::launch_mse(a, s), "mse launch");
+        CFC_HIP(gemm::launch_mse(a, s), "mse launch");
     }
     // upstream gradients through the ReLUs, one launch per layer > 0
     for (int l = L - 1; l >= 1; --l) {
-        mlp::GemmBatch g{};
+        gemm::GemmBatch g{};
         g.t[0] = dx_task(dy(l), w.ldy[l], params + w_off[l], act[l - 1], dy(l - 1), w.ldy[l - 1], B, dims[l],
                          dims[l + 1]);
         g.ntask = 1;
@@ -390,20 +390,20 @@ int mlp_train_step(const float* X, const float* T, int B, const int* dims, int n
     // every layer's weight- and bias-gradient splits: one launch per group of
     // layers whose operands take the same loads (16-byte or not)
     {
-        mlp::GemmBatch groups[4] = {};
+        gemm::GemmBatch groups[4] = {};
         float* part = wsf + w.part_off;
         for (int l = 0; l < L; ++l) {
-            mlp::GemmTask t = dw_task(dy(l), w.ldy[l], input(l), B, dims[l], dims[l + 1], part + w_off[l], w.Ptot,
+            gemm::GemmTask t = dw_task(dy(l), w.ldy[l], input(l), B, dims[l], dims[l + 1], part + w_off[l], w.Ptot,
                                       part + b_off[l], w.Ptot);
             const int64_t next = l + 1 < L ? w_off[l + 1] : w.Ptot;
             t.zlo[0] = (int64_t)dims[l + 1] * dims[l];
             t.zhi[0] = b_off[l] - w_off[l];
             t.zlo[1] = b_off[l] - w_off[l] + dims[l + 1];
             t.zhi[1] = next - w_off[l];
-            mlp::GemmBatch& g = groups[2 * t.A.vec + t.B.vec];
+            gemm::GemmBatch& g = groups[2 * t.A.vec + t.B.vec];
             g.t[g.ntask++] = t;
         }
-        for (mlp::GemmBatch& g : groups)
+        for (gemm::GemmBatch& g : groups)
             if (g.ntask > 0)
                 if (int rc = run_batch(g, s, "weight-gradient launch")) return rc;
     }

@@ -173,7 +173,7 @@ def test_workspace_size_and_path_queries(L):
 def test_no_atomics_in_kernel_sources():
     """Device code (kernels and the shared device math) uses no atomics."""
     csrc = os.path.join(ROOT, "recurrent_cell_amd", "csrc")
-    for fn in ("cfc_kernels.hip", "cfc_math.h", "cfc_kernels.h", "mlp_kernels.hip", "mlp_kernels.h"):
+    for fn in ("cfc_kernels.hip", "cfc_math.h", "cfc_kernels.h", "gemm_kernels.hip", "gemm_kernels.h"):
         text = open(os.path.join(csrc, fn)).read()
         assert not re.search(r"\batomic\w*\s*\(|__hip_atomic|__atomic_|std::atomic", text), fn
 
@@ -320,3 +320,32 @@ def test_mlp_argument_errors(ML):
     bad = list(ok)
     bad[3] = (ctypes.c_int * 3)(8, 0, 4)
     assert ML.mlp_train_step(*bad) == -1
+
+
+def test_weight_grad_gemm_argument_errors(L):
+    a = [FAKE + i * (1 << 32) for i in range(10)]
+    need = L.cfc_weight_grad_gemm_workspace_bytes(32, 128, 64, 64)
+    assert need > 0 and need % 16 == 0
+    assert L.cfc_weight_grad_gemm_workspace_bytes(32, 0, 64, 64) == 0
+    ok = (a[0], a[1], a[2], a[3], a[4], 32, 128, 64, 64, a[5], need, None)
+    bad = list(ok)
+    bad[10] = need - 4
+    assert L.cfc_weight_grad_gemm(*bad) == -1 and b"workspace" in L.cfc_last_error()
+    bad = list(ok)
+    bad[4] = a[3] + 64                      # gb inside gW
+    assert L.cfc_weight_grad_gemm(*bad) == -1 and b"overlap" in L.cfc_last_error()
+    bad = list(ok)
+    bad[0] = None
+    assert L.cfc_weight_grad_gemm(*bad) == -1
+    bad = list(ok)
+    bad[8] = -1
+    assert L.cfc_weight_grad_gemm(*bad) == -1
+    kneed = L.cfc_train_kloop_gemm_workspace_bytes(32, 128, 64, 64)
+    assert kneed == L.cfc_train_kloop_workspace_bytes(32, 128, 64, 64) + need
+    kok = (a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], kneed, 32, 128, 64, 64, None)
+    bad = list(kok)
+    bad[10] = kneed - 4
+    assert L.cfc_train_kloop_gemm(*bad) == -1
+    bad = list(kok)
+    bad[7] = a[5]                            # gW on h_hist
+    assert L.cfc_train_kloop_gemm(*bad) == -1 and b"overlap" in L.cfc_last_error()

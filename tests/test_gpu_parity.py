@@ -571,3 +571,53 @@ def test_adamw_reads_only_post_reducer_gradients(cfc):
     cfc.cfc_adamw_step(pc, [stale_gW, stale_gb], mc, vc, *hp, 2)
     assert not np.array_equal(host(pa[0]), host(pc[0]))
     assert not torch.equal(gW, stale_gW)
+
+
+# ---------------------------------------------------------------- GEMM-form weight gradient
+
+@pytest.mark.parametrize("case", ["tiny", "pages", "wide", "ragged_scalar", "no_input", "odd_channels",
+                                  "three_blocks", "long_input48"])
+def test_kloop_gemm_matches_oracle(cfc, oracle_mod, case):
+    """cfc_train_kloop_gemm (no scratch): activations as the K-loop's, gW and
+    gb against the oracle at the gradient tolerance."""
+    d = CASES[case]
+    if cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"], d["K"]) < 0:
+        pytest.skip("no K-loop path takes this shape")
+    say("kloop gemm-form parity", case, d)
+    x = cfc_inputs(**d, seed=1, bias_scale=0.2)
+    t = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    out = cfc.cfc_train_kloop_gemm(*t)
+    r = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64", want_dp=True)
+    m = grad_mass(x.u, r["h_hist"], r["dp"])
+    reps = [check_act("h_hist", host(out.h_hist), r["h_hist"]), check_act("act", host(out.act), r["act"]),
+            check_grad("gW", host(out.gW), r["gW"], m["gW"]), check_grad("gb", host(out.gb), r["gb"], m["gb"])]
+    for rep in reps:
+        say("  ", rep["name"], "worst", "%.3g" % rep["worst_ratio"], "normwise", "%.3g" % rep["normwise"])
+    for rep in reps:
+        assert_ok(rep)
+
+
+def test_kloop_gemm_composes_and_is_deterministic(cfc):
+    """cfc_train_kloop_gemm == cfc_kloop_fwd_bwd then cfc_weight_grad_gemm on
+    its dp, bit for bit, and repeated calls give the same bits; the
+    activations equal cfc_train_kloop's."""
+    d = CASES["pages"]
+    say("kloop gemm-form composition", d)
+    x = cfc_inputs(**d, seed=2, bias_scale=0.2)
+    t = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    a = cfc.cfc_train_kloop_gemm(*t)
+    gW1, gb1 = host(a.gW).copy(), host(a.gb).copy()
+    a.gW.fill_(float("nan"))
+    cfc.cfc_train_kloop_gemm(*t, out=a)
+    np.testing.assert_array_equal(bits(host(a.gW)), bits(gW1))
+    np.testing.assert_array_equal(bits(host(a.gb)), bits(gb1))
+    b = cfc.KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
+    cfc.cfc_kloop_fwd_bwd(*t, out=b)
+    K, B, C = d["K"], d["B"], d["C"]
+    dp = b.ws[:K * B * 3 * C].view(K, B, 3 * C)
+    gW, gb = cfc.cfc_weight_grad_gemm(dp, t[0], b.h_hist)
+    np.testing.assert_array_equal(bits(host(gW)), bits(gW1))
+    np.testing.assert_array_equal(bits(host(gb)), bits(gb1))
+    ref = cfc.cfc_train_kloop(*t)
+    np.testing.assert_array_equal(bits(host(ref.h_hist)), bits(host(a.h_hist)))
+    np.testing.assert_array_equal(bits(host(ref.act)), bits(host(a.act)))
