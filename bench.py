@@ -341,15 +341,16 @@ def bench_mlp(torch, timer, steps, trials, cpu_seconds):
             "frac": round(big["TFLOPs"] * 1e12 / FP32_PEAK, 4), "traffic": None,
             "kernel": "gemm_mfma_kernel (layer 1 forward, [16384 x 256] x [256 x 256])",
             "flops_per_launch": big["flops"], "launch_us": big["us"]}
-    from oracle.mlp_oracle import mlp_train_step as oracle_step
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle_step(x.X, x.T, x.W, x.b)
-        n += 1
-        if time.perf_counter() - t0 >= min(cpu_seconds, 5.0):
-            break
-    el = time.perf_counter() - t0
+    n, el = 0, 0.0
+    if cpu_seconds > 0:
+        from oracle.mlp_oracle import mlp_train_step as oracle_step
+        t0 = time.perf_counter()
+        while True:
+            oracle_step(x.X, x.T, x.W, x.b)
+            n += 1
+            if time.perf_counter() - t0 >= min(cpu_seconds, 5.0):
+                break
+        el = time.perf_counter() - t0
     return {"workload": "batched MLP train step (forward, MSE loss, backward, every gradient), one mlp_train_step "
                         "call", "B": B, "dims": dims, "value": round(1000.0 / ms, 2), "unit": "train-steps/s",
             "ms_per_step": round(ms, 5), "trials_ms": [round(v, 5) for v in res], "flops_per_step": fl,
@@ -357,7 +358,7 @@ def bench_mlp(torch, timer, steps, trials, cpu_seconds):
                                                                                          FP32_PEAK, 4),
             "roofline": roof, "launches": kt,
             "cpu_oracle": {"value": round(n / el, 3), "unit": "train-steps/s", "cores": "numpy fp64 (BLAS threads)",
-                           "kind": "oracle", "sample": "%d whole steps, %.1f s" % (n, el)}}
+                           "kind": "oracle", "sample": "%d whole steps, %.1f s" % (n, el)} if n else None}
 
 
 def cpu_baseline(x, budget_s):
@@ -388,6 +389,8 @@ def main():
     ap.add_argument("--workload", default="pages", choices=["tiny", "pages", "wide"])
     ap.add_argument("--no-steps-path", action="store_true", help="skip the step-kernel path contrast")
     ap.add_argument("--no-mlp", action="store_true", help="skip the batched MLP step")
+    ap.add_argument("--no-gemm-form", action="store_true", help="skip the GEMM-form weight-gradient step")
+    ap.add_argument("--only-mlp", action="store_true", help="run and print only the batched MLP step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size reference for "
                          "hardware byte counters)")
@@ -400,6 +403,11 @@ def main():
     import torch
     from recurrent_cell_amd import cfc
     from recurrent_cell_amd.inputs import CONFIGS, REDUCE_B, REDUCE_N, cfc_inputs
+
+    if args.only_mlp:
+        print(json.dumps({"mlp": bench_mlp(torch, LaunchTimer(torch), args.steps, args.trials,
+                                           0.0 if args.no_cpu else args.cpu_seconds)}), flush=True)
+        return
 
     d = CONFIGS[args.workload]
     B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
@@ -438,8 +446,10 @@ def main():
             cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
 
     # the K-loop step with the GEMM-form weight gradient in place of scratch + reducer
-    og = cfc.cfc_train_kloop_gemm(*t)
-    ms_gemm, _ = time_calls(torch, lambda: cfc.cfc_train_kloop_gemm(*t, out=og), max(20, args.steps // 5), 5, 3)
+    ms_gemm = None
+    if not args.no_gemm_form:
+        og = cfc.cfc_train_kloop_gemm(*t)
+        ms_gemm, _ = time_calls(torch, lambda: cfc.cfc_train_kloop_gemm(*t, out=og), max(20, args.steps // 5), 5, 3)
 
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
     t_node = graph_node_latency(torch)
@@ -545,7 +555,7 @@ def main():
                  "flops": flops, "bytes_min": bytes_min,
                  "contrast_path": contrast,
                  "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None,
-                 "gemm_form_weight_grad_ms_per_step": round(ms_gemm, 5),
+                 "gemm_form_weight_grad_ms_per_step": round(ms_gemm, 5) if ms_gemm else None,
                  "critical_path": crit}
 
     result = {
@@ -581,7 +591,7 @@ def main():
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}
 
     if not args.no_mlp:
-        result["mlp"] = bench_mlp(torch, LaunchTimer(torch), 50, 5, args.cpu_seconds)
+        result["mlp"] = bench_mlp(torch, LaunchTimer(torch), 50, 5, 0.0 if args.no_cpu else args.cpu_seconds)
 
     if not args.no_kernels:
         # the optimizer step beside the path: W and bias of this cell, then large flat tensors

@@ -31,6 +31,8 @@ struct Operand {
 struct GemmTask {
     Operand A, B;
     int M, N, K;
+    int a_ext;             // > 0: A's contiguous index may be read up to a_ext (its entries past
+                           //      K or M are zero in memory), so 16-byte loads cover the tail
     int k_split;           // reduction length of one split (multiple of kBK)
     int n_mt, n_nt, n_s;   // row tiles, column tiles, splits
     int epi, relu;

@@ -125,6 +125,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
     const int wm = wave >> 1;   // 16-row block of the tile
     const int wn = wave & 1;    // 32-column half of the tile
     const bool do_colsum = EPI == kEpiDw && T.colsum != nullptr && nt == 0;
+    // A's load extent: its reduction end (K-contiguous A, one split) or its rows
+    const int a_lim = T.a_ext > 0 ? T.a_ext : (AKC ? ke : T.M);
 
     f32x4 acc[2];
     acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
 
     f32x4 va = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, vb = va;
     if (nch > 0) {
-        va = load_chunk<AKC, VA>(T.A.p, T.A.ld, T.M, m0, kb, ke);
+        va = load_chunk<AKC, VA>(T.A.p, T.A.ld, AKC ? T.M : a_lim, m0, kb, AKC ? a_lim : ke);
         vb = load_chunk<BKC, VB>(T.B.p, T.B.ld, T.N, n0, kb, ke);
         store_chunk<AKC>(As[0], va);
         store_chunk<BKC>(Bs[0], vb);
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
         const int buf = ch & 1;
         const bool more = ch + 1 < nch;
         if (more) {
-            va = load_chunk<AKC, VA>(T.A.p, T.A.ld, T.M, m0, kb + (ch + 1) * kBK, ke);
+            va = load_chunk<AKC, VA>(T.A.p, T.A.ld, AKC ? T.M : a_lim, m0, kb + (ch + 1) * kBK, AKC ? a_lim : ke);
             vb = load_chunk<BKC, VB>(T.B.p, T.B.ld, T.N, n0, kb + (ch + 1) * kBK, ke);
         }
 #pragma unroll
@@ -198,6 +200,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
                     float d = acc[j][r];
                     if (T.mask != nullptr && !(T.mask[(int64_t)m * T.ldm + n] > 0.0f)) d = 0.0f;
                     T.out[(int64_t)m * T.ldo + n] = d;
+                } else if (m < T.M && n < T.ldo) {
+                    T.out[(int64_t)m * T.ldo + n] = 0.0f;   // row padding of the output
                 }
             }
         }
@@ -238,6 +242,15 @@ __global__ __launch_bounds__(kMseThreads) void mse_kernel(MseArgs a)
         const float d = a.Y[i] - a.T[i];
         a.dY[row * a.ldd + col] = a.gscale * d;
         acc += (double)d * (double)d;
+    }
+    // zero the row padding of dY (columns N .. ldd - 1)
+    const int64_t pad = a.ldd - a.N;
+    if (pad > 0) {
+        const int64_t r0 = e0 / a.N, r1 = e1 / a.N;
+        for (int64_t i = threadIdx.x; i < (r1 - r0) * pad; i += kMseThreads) {
+            const int64_t row = r0 + i / pad;
+            a.dY[row * a.ldd + a.N + (i - (row - r0) * pad)] = 0.0f;
+        }
     }
     red[threadIdx.x] = acc;
     __syncthreads();

@@ -120,6 +120,15 @@ gemm::GemmTask dw_task(const float* dY, int64_t lddy, const float* X, int M, int
     return t;
 }
 
+// The train step's dY buffers have rows padded to ldy (a multiple of 4)
+// with zeros (written by the loss kernel and the upstream-gradient
+// epilogue), so A = dY may be read up to ldy with 16-byte loads.
+void pad_a(gemm::GemmTask& t, int64_t ldy)
+{
+    t.a_ext = (int)ldy;
+    t.A.vec = (ldy % 4 == 0 && aligned16(t.A.p)) ? 1 : 0;
+}
+
 int run_batch(gemm::GemmBatch& g, hipStream_t s, const char* what)
 {
     gemm::finish_batch(g);
@@ -384,6 +393,7 @@ int mlp_train_step(const float* X, const float* T, int B, const int* dims, int n
         gemm::GemmBatch g{};
         g.t[0] = dx_task(dy(l), w.ldy[l], params + w_off[l], act[l - 1], dy(l - 1), w.ldy[l - 1], B, dims[l],
                          dims[l + 1]);
+        pad_a(g.t[0], w.ldy[l]);
         g.ntask = 1;
         if (int rc = run_batch(g, s, "upstream-gradient launch")) return rc;
     }
@@ -395,6 +405,7 @@ int mlp_train_step(const float* X, const float* T, int B, const int* dims, int n
         for (int l = 0; l < L; ++l) {
             gemm::GemmTask t = dw_task(dy(l), w.ldy[l], input(l), B, dims[l], dims[l + 1], part + w_off[l], w.Ptot,
                                       part + b_off[l], w.Ptot);
+            pad_a(t, w.ldy[l]);
             const int64_t next = l + 1 < L ? w_off[l + 1] : w.Ptot;
             t.zlo[0] = (int64_t)dims[l + 1] * dims[l];
             t.zhi[0] = b_off[l] - w_off[l];

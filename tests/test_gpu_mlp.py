@@ -18,6 +18,7 @@ CASES = {
     "splits": (3000, (48, 256, 128, 51), 0.1),        # several weight-gradient splits, 2 column tiles
     "deep_narrow": (130, (1, 7, 1, 7, 1, 5, 1, 3, 2), 0.5),   # eight layers, width-1 layers
     "headline": (MLP_B, MLP_DIMS, 0.0),               # the 48-256-256-128-51 net at B = 16384
+    "max_width": (65, (4096, 33, 4096), 0.1),         # MLP_MAX_DIM-wide input and output layers
 }
 
 

@@ -13,7 +13,8 @@ import pytest
 import torch
 
 from recurrent_cell_amd.inputs import CONFIGS, adamw_inputs, cfc_inputs, normal, reduce_rows, small_int_rows
-from tests.tolerances import (assert_ok, check_act, check_adamw, check_grad, check_reduce, grad_mass)
+from tests.tolerances import (assert_ok, check_act, check_adamw, check_grad, check_reduce, check_vs_fp32,
+                              grad_mass)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +31,9 @@ CASES = {
     "two_channel_groups": dict(B=3, C=100, n_x=20, K=7),  # 2 channels per dz group, last groups partial
     "three_blocks": dict(B=3, C=72, n_x=36, K=5),      # 3 recurrent column blocks of 32, 2 channels per group
     "odd_channels": dict(B=2, C=37, n_x=3, K=4),       # C and n_x not multiples of 4: scalar moves
+    "mfma_max": dict(B=64, C=320, n_x=128, K=3),       # the largest shape the MFMA step kernels take
 }
+MAX_SIZE = dict(B=1, C=2048, n_x=6144, K=2)            # CFC_MAX_C channels, n_in = CFC_MAX_N_IN
 
 
 def need_path(cfc, d):
@@ -621,3 +624,30 @@ def test_kloop_gemm_composes_and_is_deterministic(cfc):
     ref = cfc.cfc_train_kloop(*t)
     np.testing.assert_array_equal(bits(host(ref.h_hist)), bits(host(a.h_hist)))
     np.testing.assert_array_equal(bits(host(ref.act)), bits(host(a.act)))
+
+
+def test_kloop_at_the_maximum_size(cfc, oracle_mod):
+    """C = CFC_MAX_C, n_in = CFC_MAX_N_IN: the scratch K-loop and the
+    GEMM-form step against the fp64 oracle, no worse than 4x the oracle's own
+    fp32 evaluation (the stated tolerances are out of reach of fp32 sums of
+    8,192 terms; see tests/tolerances.py)."""
+    d = MAX_SIZE
+    say("kloop at the maximum size", d)
+    x = cfc_inputs(**d, seed=1, bias_scale=0.2)
+    t = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    out = cfc.cfc_train_kloop(*t)
+    gem = cfc.cfc_train_kloop_gemm(*t)
+    r = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64", want_dp=True)
+    r32 = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f32", want_dp=True)
+    m = grad_mass(x.u, r["h_hist"], r["dp"])
+    act_b = {k: 1e-6 + 1e-5 * np.abs(r[k]) for k in ("h_hist", "act")}
+    grad_b = {k: 1e-6 + 1e-4 * np.abs(r[k]) + 16 * 2.0 ** -24 * m[k] for k in ("S", "Sb", "gW", "gb")}
+    reps = [check_vs_fp32(k, host(getattr(out, k)), r[k], r32[k], act_b[k]) for k in ("h_hist", "act")]
+    reps += [check_vs_fp32(k, host(getattr(out, a)), r[k], r32[k], grad_b[k])
+             for k, a in (("S", "gW_scratch"), ("Sb", "gb_scratch"), ("gW", "gW"), ("gb", "gb"))]
+    reps += [check_vs_fp32("gemm " + k, host(getattr(gem, k)), r[k], r32[k], grad_b[k]) for k in ("gW", "gb")]
+    for rep in reps:
+        say("  ", rep["name"], "worst", "%.3g" % rep["worst_ratio"], "fp32 oracle", "%.3g" % rep["worst_fp32"],
+            "normwise", "%.3g" % rep["normwise"], "fp32", "%.3g" % rep["normwise_fp32"])
+    for rep in reps:
+        assert_ok(rep)
