@@ -159,7 +159,8 @@ struct ReduceArgs {
     int64_t B;
     int R;                // row slices per column (a function of B only)
     int64_t rows_per_slice;
-    const float* xin;     // nullable: one more sum, xout[0] = sum of xin[0 .. xn) in fp64, in index order
+    const float* xin;     // nullable: one more sum, xout[0] = sum of xin[0 .. xn) in fp64 (lane l of the
+                          // first workgroup adds l, l + 256, .. in order, then a fixed pairwise tree)
     float* xout;
     int64_t xn;
 };
@@ -190,8 +191,8 @@ hipError_t launch_fill(const FillArgs& a, hipStream_t s);
 hipError_t launch_xproj(const XprojArgs& a, hipStream_t s);
 hipError_t launch_persist(const PersistArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceSeg* segs, int nseg, int64_t B, int V, hipStream_t s);
-// The same launch with one more serial fp64 sum (xn floats at xin) into xout[0],
-// done by the first workgroup.
+// The same launch with one more fp64 sum (xn floats at xin, fixed order) into
+// xout[0], done by the first workgroup.
 hipError_t launch_reduce_with_sum(const ReduceSeg* segs, int nseg, int64_t B, int V, const float* xin, int64_t xn,
                                   float* xout, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);

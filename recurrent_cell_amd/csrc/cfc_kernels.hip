@@ -1331,10 +1331,18 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
                 if (n0 + j < N) out[n0 + j] = (float)s[j];
         }
     }
-    if (a.xn > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+    if (a.xn > 0 && blockIdx.x == 0) {
+        // lane l adds elements l, l + 256, .. in order; then a fixed pairwise tree
+        __shared__ double xs[kThreads];
         double t = 0.0;
-        for (int64_t i = 0; i < a.xn; ++i) t += (double)a.xin[i];
-        a.xout[0] = (float)t;
+        for (int64_t i = threadIdx.x; i < a.xn; i += kThreads) t += (double)a.xin[i];
+        xs[threadIdx.x] = t;
+        __syncthreads();
+        for (int h = kThreads / 2; h > 0; h >>= 1) {
+            if ((int)threadIdx.x < h) xs[threadIdx.x] += xs[threadIdx.x + h];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) a.xout[0] = (float)xs[0];
     }
 }
 
