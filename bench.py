@@ -502,11 +502,18 @@ def main():
             fl = recurrence_flops(B, C, K)
             achieved = fl / dur
             traffic = measured_traffic() if args.workload == "pages" else None
+            # what the kernel can use: one CU per sample (B of 256), fp32 FMA
+            # without packed math (4 SIMDs x 16 lanes x 2 flop per clock;
+            # half the 256 flop per clock per CU of the published peak)
+            usable = min(B, 256) * 2.4e9 * 4 * 16 * 2
             roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
                         "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": traffic,
                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                         "kernel": "kloop_persist_kernel", "flops_per_launch": fl,
-                        "launch_us": round(dur * 1e6, 3)}
+                        "launch_us": round(dur * 1e6, 3),
+                        "usable_peak": round(usable / 1e12, 3),
+                        "frac_of_usable": round(achieved / usable, 4),
+                        "usable_note": "one CU per sample (a sample's steps are sequential), non-packed fp32 FMA"}
         elif path == "steps_mfma":
             # the 2K step launches of the K-loop (and the one W re-layout), per launch on average
             dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
