@@ -28,6 +28,18 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroups are dispatched round-robin over the 8 XCDs (block i to XCD
+// i mod 8), and each XCD has its own L2.  This maps block i to a logical
+// index such that each XCD receives one contiguous run of logical indices,
+// so tiles that share operands (consecutive logical indices) share an L2.
+// A bijection of [0, n); no arithmetic depends on it.
+__device__ __forceinline__ int64_t xcd_local_order(int64_t i, int64_t n)
+{
+    const int64_t q = n / 8, r = n % 8;
+    const int64_t x = i % 8, j = i / 8;
+    return x * q + min(x, r) + j;
+}
+
 // 16-byte load from an address the caller has clamped into bounds, issued
 // unconditionally; zero where !valid.  Branch-free, so a run of such loads
 // stays in flight together (a load under a branch is waited for where the
@@ -191,8 +203,10 @@ __global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int ntile = (int)(blockIdx.x % (unsigned)a.n_ntiles);
-    const int64_t mtile = blockIdx.x / (unsigned)a.n_ntiles;
+    // the column tiles of a row tile share its u rows: keep them on one XCD
+    const int64_t blk = xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
+    const int ntile = (int)(blk % a.n_ntiles);
+    const int64_t mtile = blk / a.n_ntiles;
     const int64_t m0 = mtile * 64 + (wave >> 1) * 32;
     const int n0 = ntile * 64 + (wave & 1) * 32;
     const int li = lane & 15;
@@ -772,8 +786,10 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
     const int n_in = a.n_x + a.C;
     const int R3 = 3 * a.C;
     const int tiles = a.n_rt * a.n_kt;
-    const int b = blockIdx.x / tiles;
-    const int rem = blockIdx.x - b * tiles;
+    // a sample's tiles share its dp rows and z columns: keep them on one XCD
+    const int blk = (int)xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
+    const int b = blk / tiles;
+    const int rem = blk - b * tiles;
     const int rt = rem / a.n_kt;
     const int kt = rem - rt * a.n_kt;
     const int r0 = rt * kFillTile;

@@ -14,6 +14,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
+// Workgroups are dispatched round-robin over the 8 XCDs (block i to XCD
+// i mod 8), each with its own L2.  Block i takes the logical index that
+// gives each XCD one contiguous run of logical indices, so the column tiles
+// of a row tile (consecutive indices, the same A rows) share one L2.  A
+// bijection of [0, n).
+__device__ __forceinline__ int64_t xcd_local_order(int64_t i, int64_t n)
+{
+    const int64_t q = n / 8, r = n % 8;
+    const int64_t x = i % 8, j = i / 8;
+    return x * q + min(x, r) + j;
+}
+
 // This thread's share of one staged chunk of an operand: rows [r0, r0 + 64)
 // of R, reduction indices [k0, k0 + 32) cut at kend; zero outside.  One
 // float4 per thread, with no branch: loads go to clamped (in-bounds)
@@ -101,12 +113,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
     constexpr int BKC = EPI == kEpiFwd ? 1 : 0;
     __shared__ __attribute__((aligned(16))) float As[2][kTile][kLdsPitch];
     __shared__ __attribute__((aligned(16))) float Bs[2][kTile][kLdsPitch];
+    const int64_t blk = xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
     int ti = 0;
 #pragma unroll
     for (int i = 1; i < kMaxTasks; ++i)
-        if (i < g.ntask && (int64_t)blockIdx.x >= g.start[i]) ti = i;
+        if (i < g.ntask && blk >= g.start[i]) ti = i;
     const GemmTask T = g.t[ti];
-    const int64_t w = (int64_t)blockIdx.x - g.start[ti];
+    const int64_t w = blk - g.start[ti];
     const int per_s = T.n_mt * T.n_nt;
     const int s = (int)(w / per_s);
     const int rem = (int)(w - (int64_t)s * per_s);
