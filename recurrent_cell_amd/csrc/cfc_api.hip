@@ -198,12 +198,30 @@ int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipSt
                                      k.B, k.C, k.n_x, nct, L};
             CFC_HIP(cfc::launch_fwd_mfma(a, s), "forward step launch");
         }
+        // The launch of step t forms the carry of its channel tile and, from it,
+        // dp of step t - 1 for those channels; the launch of step t - 1 then
+        // reads dp instead of forming it (only the first launch, t = K with
+        // zero carry, forms dp from h, y and act itself).
         for (int t = k.K; t >= 1; --t) {
-            const int step = k.K - t;  // 0 for t = K
-            const float* dh_in = (t == k.K) ? nullptr : dh_ws + ((step - 1) % 2) * BC;
-            const cfc::BwdMfmaArgs a{k.h_hist + t * BC, k.y + (t - 1) * BC, k.act + (int64_t)(t - 1) * 3 * BC,
-                                     dh_in, Wb, dh_ws + (step % 2) * BC, dp + (int64_t)(t - 1) * 3 * BC,
-                                     k.B, k.C, nct, L};
+            cfc::BwdMfmaArgs a{};
+            a.h_t = k.h_hist + t * BC;
+            a.y_t = k.y + (t - 1) * BC;
+            a.act_t = k.act + (int64_t)(t - 1) * 3 * BC;
+            a.dh_in = nullptr;
+            a.Wb = Wb;
+            a.dh_out = nullptr;
+            a.dp_out = dp + (int64_t)(t - 1) * 3 * BC;
+            a.B = k.B;
+            a.C = k.C;
+            a.n_ctiles = nct;
+            a.L = L;
+            a.dp_in = (t == k.K) ? nullptr : dp + (int64_t)(t - 1) * 3 * BC;
+            if (t > 1) {
+                a.h_prev = k.h_hist + (t - 1) * BC;
+                a.y_prev = k.y + (t - 2) * BC;
+                a.act_prev = k.act + (int64_t)(t - 2) * 3 * BC;
+                a.dp_prev_out = dp + (int64_t)(t - 2) * 3 * BC;
+            }
             CFC_HIP(cfc::launch_bwd_mfma(a, s), "backward step launch");
         }
         return CFC_OK;

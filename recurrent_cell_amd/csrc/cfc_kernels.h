@@ -91,15 +91,20 @@ struct FwdMfmaArgs {
 };
 
 struct BwdMfmaArgs {
-    const float* h_t;     // [B, C]
-    const float* y_t;     // [B, C]
-    const float* act_t;   // [3, B, C]
-    const float* dh_in;   // nullable [B, C]
+    const float* h_t;     // [B, C]      (read when dp_in is null)
+    const float* y_t;     // [B, C]      (read when dp_in is null)
+    const float* act_t;   // [3, B, C]   (read when dp_in is null)
+    const float* dh_in;   // nullable [B, C]: carry into this step (read when dp_in is null)
     const float* Wb;      // MFMA backward layout
-    float* dh_out;        // [B, C] carry to step t - 1
-    float* dp_out;        // [B, 3C] dp of this step
+    float* dh_out;        // nullable [B, C]: carry to step t - 1
+    float* dp_out;        // [B, 3C] dp of this step, the tile's channels (written when dp_in is null)
     int B, C, n_ctiles;
     MfmaLayout L;
+    const float* dp_in;   // nullable [B, 3C]: dp of this step, formed by the launch of step t + 1
+    const float* h_prev;  // [B, C] h_{t-1}       (when dp_prev_out is not null)
+    const float* y_prev;  // [B, C] y_{t-1}
+    const float* act_prev;  // [3, B, C] act_{t-1}
+    float* dp_prev_out;   // nullable [B, 3C]: dp of step t - 1 for the tile's channels
 };
 
 struct XprojArgs {

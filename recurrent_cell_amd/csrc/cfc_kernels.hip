@@ -504,7 +504,6 @@ constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
 __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a)
 {
     __shared__ __attribute__((aligned(16))) float zs[16 * (kMfmaMaxLdf + 4)];
-    __shared__ __attribute__((aligned(16))) float wsm[48 * (kMfmaMaxLdf + 4)];
     __shared__ float as[3 * 16 * 16];
     const MfmaLayout L = a.L;
     const int C = a.C;
@@ -522,30 +521,21 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     const int li = lane & 15;
     const int lk = lane >> 4;
 
-    // The tile's 48 W rows (head-major, channels c0 .. c0 + 15) from the
-    // forward layout into LDS: contiguous float4 loads, all in flight before
-    // the first LDS store (indices clamped; the extra loads are not stored).
-    {
-        const int w4 = L.ldf / 4;
-        constexpr int kWSlots = (48 * kMfmaMaxLdf / 4 + kFwdMfmaThreads - 1) / kFwdMfmaThreads;
-        f32x4 v[kWSlots];
+    // This lane's W operands straight from the forward layout into
+    // registers (each W value feeds exactly one lane's MFMAs, so it needs no
+    // LDS): row (head q, channel c0 + li), the four k-slots of every block,
+    // issued with the z loads below before any of them is waited for.
+    const float* wrow = a.Wf + ((int64_t)q * C + min(c0 + li, C - 1)) * L.ldf;
+    f32x4 wx[kMfmaMaxNxb], wh[kMfmaMaxNhb][2];
 #pragma unroll
-        for (int m = 0; m < kWSlots; ++m) {
-            const int i = min(tid + m * kFwdMfmaThreads, 48 * w4 - 1);
-            const int row = i / w4;
-            const int c = min(c0 + (row & 15), C - 1);
-            v[m] = *reinterpret_cast<const f32x4*>(a.Wf + ((int64_t)(row >> 4) * C + c) * L.ldf + 4 * (i - row * w4));
-        }
+    for (int p = 0; p < kMfmaMaxNxb; ++p)
+        wx[p] = *reinterpret_cast<const f32x4*>(wrow + 16 * min(p, nxb - 1) + 4 * lk);
 #pragma unroll
-        for (int m = 0; m < kWSlots; ++m) {
-            const int i = tid + m * kFwdMfmaThreads;
-            if (i < 48 * w4) {
-                const int row = i / w4;
-                *reinterpret_cast<f32x4*>(wsm + row * ldp + 4 * (i - row * w4)) = v[m];
-            }
-        }
+    for (int i = 0; i < kMfmaMaxNhb; ++i) {
+        const int o = L.nxp + 32 * min(i, nhb - 1) + 8 * lk;
+        wh[i][0] = *reinterpret_cast<const f32x4*>(wrow + o);
+        wh[i][1] = *reinterpret_cast<const f32x4*>(wrow + o + 4);
     }
-
     // z rows in float4 units: unit u of row s covers columns 4 u .. 4 u + 3
     // of [u ; h] in their natural order (zero past n_x, past C and for
     // absent samples); h goes to its permuted LDS place.
@@ -594,32 +584,33 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     __syncthreads();
 
     const float* zr = zs + li * ldp;                 // sample li
-    const float* wr = wsm + (q * 16 + li) * ldp;     // channel c0 + li, head q
     f32x4 ax[4], ah[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) ax[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 8; ++j) ah[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // Runtime trip counts keep the accumulators in place across iterations;
-    // unrolling by 2 lets the next iteration's LDS reads overlap the MFMAs.
-#pragma unroll 2
-    for (int p = 0; p < nxb; ++p) {
-        const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + 16 * p + 4 * lk);
+    // Unrolled over the register-held W blocks; the trip counts are uniform
+    // and the blocks past nxb / nhb are never used.
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ax[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wv[c], ax[c], 0, 0, 0);
+    for (int p = 0; p < kMfmaMaxNxb; ++p) {
+        if (p < nxb) {
+            const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                ax[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wx[p][c], ax[c], 0, 0, 0);
+        }
     }
-#pragma unroll 2
-    for (int i = 0; i < nhb; ++i) {
-        const int o = L.nxp + 32 * i + 8 * lk;
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + o);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + o + 4);
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wr + o);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wr + o + 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ah[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z0[j], w0[j], ah[j], 0, 0, 0);
-            ah[4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z1[j], w1[j], ah[4 + j], 0, 0, 0);
+    for (int i = 0; i < kMfmaMaxNhb; ++i) {
+        if (i < nhb) {
+            const int o = L.nxp + 32 * i + 8 * lk;
+            const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + o);
+            const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + o + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ah[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z0[j], wh[i][0][j], ah[j], 0, 0, 0);
+                ah[4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z1[j], wh[i][1][j], ah[4 + j], 0, 0, 0);
+            }
         }
     }
     const float bias = a.bias[q * C + min(c0 + li, C - 1)];
@@ -672,10 +663,61 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
     const int tid = threadIdx.x;
     const int64_t BC = (int64_t)a.B * C;
 
+    // inputs of the epilogue (dp of step t - 1 for (sample tid / 16, channel
+    // k0 + tid % 16)), loaded now so that their latency is hidden
+    float ep_h = 0.0f, ep_y = 0.0f, ep_g0 = 0.0f, ep_g1 = 0.0f, ep_g2 = 0.0f;
+    {
+        const int s = tid >> 4;
+        const int col = tid & 15;
+        const int64_t bk = (int64_t)min(s0 + s, a.B - 1) * C + min(k0 + col, C - 1);
+        // unconditional loads (a load under a branch is waited for where the
+        // branch joins); this step's arrays stand in when there is no step t - 1
+        const bool prev = a.dp_prev_out != nullptr;
+        const float* hp = prev ? a.h_prev : a.h_t;
+        const float* yp = prev ? a.y_prev : a.y_t;
+        const float* gp = prev ? a.act_prev : a.act_t;
+        ep_h = hp[bk];
+        ep_y = yp[bk];
+        ep_g0 = gp[bk];
+        ep_g1 = gp[BC + bk];
+        ep_g2 = gp[2 * BC + bk];
+    }
     for (int i = tid; i < 16 * kDzGroups * 16; i += kBwdMfmaThreads) dps[i] = 0.0f;
+    const int c4n = C / 4;
+    if (a.dp_in != nullptr) {
+        // dp of this step, formed at the end of the launch of step t + 1: the
+        // tile's samples, all heads and channels (float4 over 4 channels of
+        // one head), every load in flight before the LDS stores.
+        constexpr int kPSlots = (16 * 3 * 320 / 4 + kBwdMfmaThreads - 1) / kBwdMfmaThreads;
+        const int n4 = 16 * 3 * c4n;
+        f32x4 vp[kPSlots];
+#pragma unroll
+        for (int m = 0; m < kPSlots; ++m) {
+            const int i = min(tid + m * kBwdMfmaThreads, n4 - 1);
+            const int s = i / (3 * c4n);
+            const int r4 = i - s * 3 * c4n;   // float4 index within the sample's 3C
+            vp[m] = *reinterpret_cast<const f32x4*>(a.dp_in + (int64_t)min(s0 + s, a.B - 1) * 3 * C + 4 * r4);
+        }
+        __syncthreads();   // zeros of dps in place before the dp stores
+#pragma unroll
+        for (int m = 0; m < kPSlots; ++m) {
+            const int i = tid + m * kBwdMfmaThreads;
+            const int s = i / (3 * c4n);
+            if (i < n4 && s0 + s < a.B) {
+                const int r4 = i - s * 3 * c4n;
+                const int qq = r4 / c4n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 4 * (r4 - qq * c4n) + e;
+                    const int g = c / cpg;
+                    const int el = 3 * (c - g * cpg) + qq;
+                    dps[(s * kDzGroups + g) * 16 + 4 * (el & 3) + (el >> 2)] = vp[m][e];
+                }
+            }
+        }
+    } else {
     // dp of (sample s, channels 4 c4 .. 4 c4 + 3) for the tile's samples and
     // every channel: every load of the pass in flight before the arithmetic.
-    const int c4n = C / 4;
     constexpr int kDSlots = (16 * 320 / 4 + kBwdMfmaThreads - 1) / kBwdMfmaThreads;
     f32x4 vh[kDSlots], vy[kDSlots], vd[kDSlots], vg0[kDSlots], vg1[kDSlots], vg2[kDSlots];
 #pragma unroll
@@ -718,6 +760,7 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
             }
         }
     }
+    }
     __syncthreads();
 
     const int lane = tid & 63;
@@ -756,8 +799,21 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
         const int col = tid & 15;
         const int b = s0 + s;
         const int k = k0 + col;
-        if (b < a.B && k < C)
-            a.dh_out[(int64_t)b * C + k] = (ts[0][s][col] + ts[1][s][col]) + (ts[2][s][col] + ts[3][s][col]);
+        if (b < a.B && k < C) {
+            const float carry = (ts[0][s][col] + ts[1][s][col]) + (ts[2][s][col] + ts[3][s][col]);
+            const int64_t bk = (int64_t)b * C + k;
+            if (a.dh_out != nullptr) a.dh_out[bk] = carry;
+            if (a.dp_prev_out != nullptr) {
+                // dp of step t - 1 for channel k, from the carry just formed
+                float dh = ep_h - ep_y;
+                dh += carry;
+                float d[3];
+                cell_backward(dh, ep_g0, ep_g1, ep_g2, d[0], d[1], d[2]);
+                const int64_t row = (int64_t)b * 3 * C;
+#pragma unroll
+                for (int qq = 0; qq < 3; ++qq) a.dp_prev_out[row + qq * C + k] = d[qq];
+            }
+        }
     }
 }
 
