@@ -52,22 +52,36 @@ KERNEL_SOURCES = [os.path.join(ROOT, "recurrent_cell_amd", "csrc", f)
                   for f in ("cfc_kernels.hip", "cfc_kernels.h", "cfc_math.h")]
 
 
+def kernel_source_digest():
+    """sha256 of the persistent kernel's source: in each of KERNEL_SOURCES the
+    text between "[persistent kernel source: begin]" and "... end]" markers
+    (the whole file where it has none), in file order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        text = open(f, "rb").read()
+        parts = text.split(b"// [persistent kernel source: begin]\n")
+        if len(parts) == 1:
+            h.update(text)
+            continue
+        for p in parts[1:]:
+            h.update(p.split(b"// [persistent kernel source: end]\n")[0])
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the persistent kernel from the committed
     rocprofv3 counter summary, or None if the kernel sources changed since
     the counters were taken (or the summary is missing)."""
-    import hashlib
     import re
     try:
         text = open(TRAFFIC_SUMMARY).read()
-        h = hashlib.sha256()
-        for f in KERNEL_SOURCES:
-            h.update(open(f, "rb").read())
+        digest = kernel_source_digest()
     except OSError:
         return None
     m_hash = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != h.hexdigest():
+    if not m_hash or not m_bytes or m_hash.group(1) != digest:
         return None
     return int(m_bytes.group(1))
 

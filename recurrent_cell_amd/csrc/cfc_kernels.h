@@ -13,7 +13,9 @@ constexpr int kGroups = kThreads / kGroup;
 constexpr int kSlices = 16;            // backward W^T dp: 16 slices x 4 row groups = 64 groups
 constexpr int kCols = kThreads / kSlices;
 constexpr int kMaxReduceSegs = 2;
+// [persistent kernel source: begin]
 constexpr int kPersistThreads = 512;   // persistent K-loop kernel: 8 wave64, 64 groups of 8 lanes
+// [persistent kernel source: end]
 constexpr int kFillTile = 64;          // scratch fill: 64 rows x 64 columns per workgroup
 constexpr int kFillSteps = 64;         // time steps staged in LDS per pass
 
@@ -117,6 +119,7 @@ struct XprojArgs {
     int n_x, n_in, n_ntiles;
 };
 
+// [persistent kernel source: begin]
 struct PersistArgs {
     const float* X;       // [K, B, 3C] input projection (bias included)
     const float* y;       // [K, B, C]
@@ -128,6 +131,7 @@ struct PersistArgs {
     float* dp;            // [K, B, 3C]
     int B, C, n_x, K;
 };
+// [persistent kernel source: end]
 
 constexpr int kMaxAdamwSegs = 4;
 

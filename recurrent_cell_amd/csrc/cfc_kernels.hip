@@ -974,6 +974,7 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
     if (do_bias && r0 + (int)threadIdx.x < R3) a.gb_s[(int64_t)b * R3 + r0 + threadIdx.x] = sb;
 }
 
+// [persistent kernel source: begin]
 // ---------------------------------------------------------------------------
 // Persistent K-loop kernel: workgroup b runs sample b's whole step; the input
 // projection X = W_x u + bias of every step comes precomputed (xproj_kernel),
@@ -1318,6 +1319,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     lds_barrier();
     if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, c_vec, dp_row(prev_t1));
 }
+// [persistent kernel source: end]
 
 // ---------------------------------------------------------------------------
 // Batch-axis reduction out[n] = sum_b in[b, n] ("reduce_axis0").
@@ -1499,6 +1501,7 @@ hipError_t launch_bwd_bt(const BwdArgs& a, const StepPlan& p, hipStream_t s)
     return hipGetLastError();
 }
 
+// [persistent kernel source: begin]
 // Persistent-kernel instantiations: CPG = ceil(C / 64) channels per
 // canonical group, NH = ceil(C / 32) recurrent column blocks of 32;
 // 12 CPG NH W values per lane.
@@ -1519,6 +1522,7 @@ hipError_t launch_persist_t(const PersistArgs& a, hipStream_t s)
     hipLaunchKernelGGL((kloop_persist_kernel<CPG, NH>), dim3((unsigned)a.B), dim3(kPersistThreads), 0, s, a);
     return hipGetLastError();
 }
+// [persistent kernel source: end]
 
 }  // namespace
 
