@@ -199,6 +199,26 @@ def copy_peak(torch, mib=2048, reps=10):
     return 2 * n * 4 / float(np.median(ts))
 
 
+def fma_rate(torch, cfc, blocks, threads=512, iters=8192, reps=5):
+    """Measured non-packed fp32 FMA rate (flop/s) of `blocks` workgroups of
+    `threads` lanes, one workgroup per CU (the FMA-chain probe of
+    include/probe.h), median over reps launches."""
+    out = torch.empty(blocks * threads, device="cuda")
+    cfc.cfc_probe_fma(out, blocks, threads, 16)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cfc.cfc_probe_fma(out, blocks, threads, iters)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("FMA probe produced non-finite values")
+    return 2.0 * 64 * iters * blocks * threads / float(np.median(ts))
+
+
 def host_info():
     model = None
     try:
@@ -520,6 +540,10 @@ def main():
             # without packed math (4 SIMDs x 16 lanes x 2 flop per clock;
             # half the 256 flop per clock per CU of the published peak)
             usable = min(B, 256) * 2.4e9 * 4 * 16 * 2
+            # the same rate measured: the FMA-chain probe on B workgroups of
+            # the kernel's 512 lanes, one per CU, and on all 256 CUs
+            meas_b = fma_rate(torch, cfc, min(B, 256))
+            meas_chip = fma_rate(torch, cfc, 256)
             roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
                         "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": traffic,
                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
@@ -527,7 +551,13 @@ def main():
                         "launch_us": round(dur * 1e6, 3),
                         "usable_peak": round(usable / 1e12, 3),
                         "frac_of_usable": round(achieved / usable, 4),
-                        "usable_note": "one CU per sample (a sample's steps are sequential), non-packed fp32 FMA"}
+                        "usable_note": "one CU per sample (a sample's steps are sequential), non-packed fp32 FMA",
+                        "usable_peak_measured": round(meas_b / 1e12, 3),
+                        "frac_of_usable_measured": round(achieved / meas_b, 4),
+                        "fma_probe_chip_TFLOPs": round(meas_chip / 1e12, 2),
+                        "fma_probe_chip_GHz": round(meas_chip / (256 * 128) / 1e9, 3),
+                        "fma_probe_note": "v_fma_f32 chains, 512 lanes per workgroup, one workgroup per CU; "
+                                          "GHz = chip rate / (256 CUs x 128 flop/clk)"}
         elif path == "steps_mfma":
             # the 2K step launches of the K-loop (and the one W re-layout), per launch on average
             dur = kt["fwd_bwd"]["mean_s"] / (2 * K)

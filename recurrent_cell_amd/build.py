@@ -10,9 +10,9 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("cfc_kernels.hip", "cfc_api.hip", "gemm_kernels.hip",
-                                                    "mlp_api.hip")]
+                                                    "mlp_api.hip", "probe.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("cfc_kernels.h", "cfc_math.h", "api_common.h", "gemm_kernels.h")] + \
-    [os.path.join(ROOT, "include", f) for f in ("cfc.h", "mlp.h")]
+    [os.path.join(ROOT, "include", f) for f in ("cfc.h", "mlp.h", "probe.h")]
 LIB = os.path.join(HERE, "libcfc.so")
 ARCH = "gfx950"
 

@@ -66,10 +66,11 @@ def lib():
         L.cfc_last_error.argtypes = []
         L.cfc_last_error.restype = ctypes.c_char_p
         L.cfc_clear_graph_cache.argtypes = []
+        L.cfc_probe_fma.argtypes = [_I, _I, _I, _I, _P, _P]
         for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
                   L.cfc_kloop_fwd_bwd, L.cfc_scratch_fill, L.cfc_clear_graph_cache,
                   L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence, L.cfc_adamw_step,
-                  L.cfc_weight_grad_gemm, L.cfc_train_kloop_gemm):
+                  L.cfc_weight_grad_gemm, L.cfc_train_kloop_gemm, L.cfc_probe_fma):
             f.restype = _I
         _LIB = L
     return _LIB
@@ -256,6 +257,17 @@ def cfc_adamw_step(params, grads, ms, vs, lr, beta1=0.9, beta2=0.999, eps=1e-8, 
                                                   arr(vs, "v"), counts, n, lr, beta1, beta2, eps,
                                                   weight_decay, int(step), stream))
     return params
+
+
+def cfc_probe_fma(out, blocks, threads, iters, one_per_cu=True):
+    """FMA-rate probe (include/probe.h): 2 * 64 * iters * blocks * threads
+    flops of non-packed fp32 FMA; out [blocks * threads] receives each lane's
+    chain sum."""
+    if out.numel() < blocks * threads:
+        raise ValueError("out holds fewer than blocks * threads floats")
+    _check("cfc_probe_fma", lib().cfc_probe_fma(int(blocks), int(threads), int(bool(one_per_cu)), int(iters),
+                                                _dev(out, "out"), _stream(out)))
+    return out
 
 
 def cfc_weight_grad_gemm(dp, u, h_hist, gW=None, gb=None, ws=None):

@@ -14,7 +14,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("cfc.h", "mlp.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("cfc.h", "mlp.h", "probe.h")]
 
 
 def _declared():
@@ -349,3 +349,15 @@ def test_weight_grad_gemm_argument_errors(L):
     bad = list(kok)
     bad[7] = a[5]                            # gW on h_hist
     assert L.cfc_train_kloop_gemm(*bad) == -1 and b"overlap" in L.cfc_last_error()
+
+
+# ---------------------------------------------------------------- FMA-rate probe
+
+def test_probe_fma_argument_errors(L):
+    L.cfc_probe_fma.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    L.cfc_probe_fma.restype = ctypes.c_int
+    for blocks, threads, iters in ((0, 512, 1), (65537, 512, 1), (1, 0, 1), (1, 96, 1), (1, 1088, 1),
+                                   (1, 512, 0), (1, 512, (1 << 20) + 1)):
+        assert L.cfc_probe_fma(blocks, threads, 1, iters, FAKE, None) == -1
+    assert L.cfc_probe_fma(1, 512, 1, 1, None, None) == -1
+    assert b"NULL" in L.cfc_last_error()

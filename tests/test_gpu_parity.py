@@ -659,3 +659,15 @@ def test_kloop_at_the_maximum_size(cfc, oracle_mod):
             "normwise", "%.3g" % rep["normwise"], "fp32", "%.3g" % rep["normwise_fp32"])
     for rep in reps:
         assert_ok(rep)
+
+
+def test_fma_probe_runs_bounded_chains(cfc):
+    """The FMA-rate probe: every chain x <- fma(x, 0.999, 0.001) stays in
+    [0, 8] from its start and tends to 1, so each lane's sum of 8 chains lies
+    in (0, 64) and, after many links, near 8."""
+    out = torch.full((4 * 512,), float("nan"), device="cuda")
+    cfc.cfc_probe_fma(out, 4, 512, 4096)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    assert np.abs(o - 8.0).max() < 1e-2
