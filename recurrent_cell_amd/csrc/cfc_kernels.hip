@@ -1060,6 +1060,27 @@ __device__ __forceinline__ float group_bcast(float v)
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x18 | (SRC << 5)));
 }
 
+// tree_sum16 with all 16 LDS reads issued before the first add (the empty
+// asm takes every value as an operand, so no read can sink below it): one
+// LDS latency instead of two on the carry's path.  Same adds, same bits.
+__device__ __forceinline__ float tree_sum16_loads_first(const float* p, int s)
+{
+    float r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = p[i * s];
+    asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                 "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]),
+                 "+v"(r[14]), "+v"(r[15]));
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = r[2 * i] + r[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+    return a[0] + a[1];
+}
+
 template <int CPG, int NH>
 __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistArgs a)
 {
@@ -1094,12 +1115,15 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     const bool c_vec = (C % 4 == 0) && ((((uintptr_t)a.act) | ((uintptr_t)a.h_hist) | ((uintptr_t)a.y) |
                                           ((uintptr_t)a.dp) | ((uintptr_t)a.X)) & 15u) == 0;
 
+    // w[s]: the recurrent columns of channel g CPG + s; in the forward, with
+    // CPG == 2, quad 1 holds them swapped (w[s] of channel g CPG + (s ^ jq))
+    // so that the last level of sum8 can leave each quad its own channel.
     float w[CPG][3][NH][4];
 #pragma unroll
     for (int cl = 0; cl < CPG; ++cl)
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            const int c = g * CPG + cl;
+            const int c = g * CPG + (CPG == 2 ? (cl ^ jq) : cl);
             const bool ok = c < C;
             const float* wrow = a.W + (int64_t)(q * C + min(c, C - 1)) * n_in + n_x;
 #pragma unroll
@@ -1191,16 +1215,24 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                     for (int i = 0; i < NH; ++i)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) p = fmaf(w[cl][q][i][e], zv[i][e], p);
-                    hs[cl][q] = sum8(p);
+                    hs[cl][q] = (CPG == 2) ? quad_sum4(p) : sum8(p);
                 }
-            float hsel = hs[0][2];
+            float hsel;
+            if constexpr (CPG == 2) {
+                // sum8's last level, kept by the quad that owns the channel:
+                // slot 0 is the quad's own channel, and the mirrored lane of
+                // the other quad holds the same channel in its slot 1, so
+                // own + mirror(other) is sum8's own + partner, bit for bit.
+                float hq[3];
 #pragma unroll
-            for (int cl = 0; cl < CPG; ++cl)
-#pragma unroll
-                for (int q = 0; q < 3; ++q)
-                    if (jq == cl && fn == q) hsel = hs[cl][q];
+                for (int q = 0; q < 3; ++q) hq[q] = hs[0][q] + dpp_get<kDppRowHalfMirror>(hs[1][q]);
+                hsel = (fn == 0) ? hq[0] : (fn == 1) ? hq[1] : hq[2];
+            } else {
+                hsel = (fn == 0) ? hs[0][0] : (fn == 1) ? hs[0][1] : hs[0][2];
+            }
             const float v = cell_fn(fn, xv + hsel);
-            const float h = cell_h(quad_bcast<0>(v), quad_bcast<1>(v), quad_bcast<2>(v));
+            // lane 0 of the quad (the only one that uses h) holds the gate itself
+            const float h = cell_h(v, quad_bcast<1>(v), quad_bcast<2>(v));
             if (q_ok) {
                 float* ob = obuf + (tt * 4) * C + cq;
                 if (fn == 0) {
@@ -1216,6 +1248,20 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     }
     if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, c_vec, out_row(prev_t0));
     __syncthreads();   // every forward store is performed and visible to the whole workgroup
+
+    if constexpr (CPG == 2) {
+        // back to the canonical slots: w[s] of channel g CPG + s in every quad
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int i = 0; i < NH; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a0 = w[0][q][i][e], a1 = w[1][q][i][e];
+                    w[0][q][i][e] = jq ? a1 : a0;
+                    w[1][q][i][e] = jq ? a0 : a1;
+                }
+    }
 
     // ---------------- backward ----------------
     // Staged rows per step tt of a chunk: 5 tt + v, v = gate, g, hh (act), h_t,
@@ -1284,13 +1330,11 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 dp[0][q] = group_bcast<0>(mdp[q]);
                 if (CPG > 1) dp[CPG - 1][q] = group_bcast<4>(mdp[q]);
             }
-#pragma unroll
-            for (int cl = 0; cl < CPG; ++cl)
-                if (g * CPG + cl >= C) dp[cl][0] = dp[cl][1] = dp[cl][2] = 0.0f;
             if (q_ok && fn < 3) dbuf[tt * R3 + fn * C + cq] = (fn == 0) ? mdp[0] : (fn == 1) ? mdp[1] : mdp[2];
-            // Partial of the group over the carry columns.  Absent channels
-            // carry W = 0 and dp = 0, and fma(0, 0, P) == P exactly (P is
-            // never -0), so the chains need no per-channel branches.
+            // Partial of the group over the carry columns.  An absent
+            // channel carries W = 0 and the finite dp of the clamped channel
+            // C - 1; 0 * dp is +-0 and P is never -0, so fma(0, dp, P) == P
+            // exactly and the chains need no per-channel branches.
 #pragma unroll
             for (int i = 0; i < NH; ++i) {
                 float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1309,7 +1353,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             }
             lds_barrier();
             if (jq < CPG) {   // uniform over each quad
-                const float v = tree_sum16(&part[buf][fn][cqc], 4 * HWP);
+                const float v = tree_sum16_loads_first(&part[buf][fn][cqc], 4 * HWP);
                 carry_mine = quad_sum4(v);
             }
         }
