@@ -1024,10 +1024,11 @@ struct PersistLds {
     static_assert(HW <= 64 * CPG, "every channel belongs to a group");
 };
 
-// Coalesced move of `rows` rows of `len` floats between LDS (row pitch len)
-// and global memory (row rr at dst(rr)); 16-byte moves when vec.
+// Coalesced move of `rows` rows of `len` floats between LDS (row pitch
+// `pitch` >= len) and global memory (row rr at gptr(rr)); 16-byte moves when
+// vec.
 template <int THREADS, bool TO_GLOBAL, typename Ptr>
-__device__ __forceinline__ void move_rows(float* lds, int rows, int len, bool vec, Ptr gptr)
+__device__ __forceinline__ void move_rows(float* lds, int rows, int len, int pitch, bool vec, Ptr gptr)
 {
     if (vec) {
         const int w = len / 4;
@@ -1036,18 +1037,18 @@ __device__ __forceinline__ void move_rows(float* lds, int rows, int len, bool ve
             const int x = 4 * (i - rr * w);
             float* g = gptr(rr) + x;
             if (TO_GLOBAL)
-                *reinterpret_cast<f32x4*>(g) = *reinterpret_cast<const f32x4*>(lds + rr * len + x);
+                *reinterpret_cast<f32x4*>(g) = *reinterpret_cast<const f32x4*>(lds + rr * pitch + x);
             else
-                *reinterpret_cast<f32x4*>(lds + rr * len + x) = *reinterpret_cast<const f32x4*>(g);
+                *reinterpret_cast<f32x4*>(lds + rr * pitch + x) = *reinterpret_cast<const f32x4*>(g);
         }
     } else {
         for (int i = threadIdx.x; i < rows * len; i += THREADS) {
             const int rr = i / len;
             const int x = i - rr * len;
             if (TO_GLOBAL)
-                gptr(rr)[x] = lds[i];
+                gptr(rr)[x] = lds[rr * pitch + x];
             else
-                lds[i] = gptr(rr)[x];
+                lds[rr * pitch + x] = gptr(rr)[x];
         }
     }
 }
@@ -1152,8 +1153,11 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     // X prefetch into registers: a lane moves one float4 of one staged row
     // of 3C floats per pass, on a map computed once (16-byte path only).
     // A row is x_w <= 3 HW / 4 float4; the lanes cover x_rstep rows per pass.
+    // In LDS a row is staged per head at pitch HW ([tt][head][HW]), so that,
+    // in a whole chunk, every step's LDS offsets are constants.
     const int x_w = R3 / 4;
     const int x_col = x_w > 0 ? tid % x_w : 0;
+    const int x_lds = ((4 * x_col) / C) * HW + (4 * x_col) % C;   // C % 4 == 0 on this path
     const int x_row0 = x_w > 0 ? tid / x_w : kFwdChunk;
     const int x_rstep = x_w > 0 ? THREADS / x_w : 1;
     constexpr int XRS_MIN = THREADS / (3 * HW / 4);
@@ -1189,19 +1193,26 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             for (int m = 0; m < XPF; ++m) {
                 const int rr = x_row0 + m * x_rstep;
                 if (x_row0 < x_rstep && rr < nt)
-                    *reinterpret_cast<f32x4*>(stage + rr * R3 + 4 * x_col) = xpf[m];
+                    *reinterpret_cast<f32x4*>(stage + rr * 3 * HW + x_lds) = xpf[m];
             }
         } else {
-            move_rows<THREADS, false>(stage, nt, R3, false, x_row(t0));
+            const auto src = x_row(t0);
+            for (int i = tid; i < nt * R3; i += THREADS) {
+                const int rr = i / R3;
+                const int x = i - rr * R3;
+                const int hd = x / C;
+                stage[rr * 3 * HW + hd * HW + (x - hd * C)] = src(rr)[x];
+            }
         }
-        if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, c_vec, out_row(prev_t0));
+        if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, c_vec, out_row(prev_t0));
         if (c_vec && t0 + kFwdChunk <= K) load_x(t0 + kFwdChunk, min(kFwdChunk, K - t0 - kFwdChunk + 1));
         lds_barrier();
-        for (int tt = 0; tt < nt; ++tt) {
-            const int t = t0 + tt;
-            const float* zc = zs[(t - 1) & 1];
-            float* zn = zs[t & 1];
-            const float xv = stage[tt * R3 + min(fn, 2) * C + cqc];
+        // One step; t0 - 1 is even, so h_{t-1} sits in zs[tt & 1].
+        static_assert(kFwdChunk % 2 == 0, "chunks start on odd t");
+        auto fstep = [&](int tt) __attribute__((always_inline)) {
+            const float* zc = zs[tt & 1];
+            float* zn = zs[(tt + 1) & 1];
+            const float xv = stage[tt * 3 * HW + min(fn, 2) * HW + cqc];
             f32x4 zv[NH];
 #pragma unroll
             for (int i = 0; i < NH; ++i) zv[i] = *reinterpret_cast<const f32x4*>(zc + 32 * i + 4 * j);
@@ -1234,19 +1245,22 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             // lane 0 of the quad (the only one that uses h) holds the gate itself
             const float h = cell_h(v, quad_bcast<1>(v), quad_bcast<2>(v));
             if (q_ok) {
-                float* ob = obuf + (tt * 4) * C + cq;
+                float* ob = obuf + (tt * 4) * HW + cq;
                 if (fn == 0) {
                     zn[cq] = h;
                     ob[0] = h;
                 }
-                if (fn < 3) ob[(1 + fn) * C] = v;
+                if (fn < 3) ob[(1 + fn) * HW] = v;
             }
             lds_barrier();
-        }
+        };
+#pragma unroll
+        for (int tt = 0; tt < kFwdChunk; ++tt)
+            if (tt < nt) fstep(tt);
         prev_t0 = t0;
         prev_nt = nt;
     }
-    if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, c_vec, out_row(prev_t0));
+    if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, c_vec, out_row(prev_t0));
     __syncthreads();   // every forward store is performed and visible to the whole workgroup
 
     if constexpr (CPG == 2) {
@@ -1265,7 +1279,8 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
 
     // ---------------- backward ----------------
     // Staged rows per step tt of a chunk: 5 tt + v, v = gate, g, hh (act), h_t,
-    // y_t, each C floats; register prefetch on the 16-byte path.
+    // y_t, each C floats at row pitch HW (so that, in a whole chunk, every
+    // step's LDS offsets are constants); register prefetch on the 16-byte path.
     const int c_w = C / 4;
     const int c_col = c_w > 0 ? tid % c_w : 0;
     const int c_row0 = c_w > 0 ? tid / c_w : 5 * kBwdChunk;
@@ -1306,23 +1321,26 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
 #pragma unroll
             for (int m = 0; m < BPF; ++m) {
                 const int rr = c_row0 + m * c_rstep;
-                if (c_row0 < c_rstep && rr < 5 * nt) *reinterpret_cast<f32x4*>(stage + rr * C + 4 * c_col) = bpf[m];
+                if (c_row0 < c_rstep && rr < 5 * nt) *reinterpret_cast<f32x4*>(stage + rr * HW + 4 * c_col) = bpf[m];
             }
         } else {
-            move_rows<THREADS, false>(stage, 5 * nt, C, false, in_row(t1));
+            move_rows<THREADS, false>(stage, 5 * nt, C, HW, false, in_row(t1));
         }
-        if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, c_vec, dp_row(prev_t1));
+        if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, c_vec, dp_row(prev_t1));
         if (c_vec && t1 - kBwdChunk >= 1) load_b(t1 - kBwdChunk, min(kBwdChunk, t1 - kBwdChunk));
         lds_barrier();
-        for (int tt = 0; tt < nt; ++tt) {
-            const int t = t1 - tt;
-            const int buf = t & 1;
-            const float* st = stage + tt * 5 * C;
+        // One step.  The partial buffers alternate with tt (the barrier at
+        // a chunk boundary orders the last reads of one chunk before the
+        // first writes of the next).
+        auto bstep = [&](int tt) __attribute__((always_inline)) {
+            float* pb = &part[tt & 1][0][0];
+            const float* st = stage + tt * 5 * HW;
             float mdp[3];
             {
-                float dh = st[3 * C + cqc] - st[4 * C + cqc];
-                if (t < K) dh += carry_mine;
-                cell_backward(dh, st[cqc], st[C + cqc], st[2 * C + cqc], mdp[0], mdp[1], mdp[2]);
+                // carry_mine is +0 at t = K, and h_t - y_t is never -0 (h_t
+                // is not), so the add is exact there
+                const float dh = (st[3 * HW + cqc] - st[4 * HW + cqc]) + carry_mine;
+                cell_backward(dh, st[cqc], st[HW + cqc], st[2 * HW + cqc], mdp[0], mdp[1], mdp[2]);
             }
             float dp[CPG][3];
 #pragma unroll
@@ -1349,19 +1367,22 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 v.y = P[1];
                 v.z = P[2];
                 v.w = P[3];
-                *reinterpret_cast<f32x4*>(&part[buf][g][32 * i + 4 * j]) = v;
+                *reinterpret_cast<f32x4*>(pb + g * HWP + 32 * i + 4 * j) = v;
             }
             lds_barrier();
             if (jq < CPG) {   // uniform over each quad
-                const float v = tree_sum16_loads_first(&part[buf][fn][cqc], 4 * HWP);
+                const float v = tree_sum16_loads_first(pb + fn * HWP + cqc, 4 * HWP);
                 carry_mine = quad_sum4(v);
             }
-        }
+        };
+#pragma unroll
+        for (int tt = 0; tt < kBwdChunk; ++tt)
+            if (tt < nt) bstep(tt);
         prev_t1 = t1;
         prev_nt = nt;
     }
     lds_barrier();
-    if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, c_vec, dp_row(prev_t1));
+    if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, c_vec, dp_row(prev_t1));
 }
 // [persistent kernel source: end]
 
