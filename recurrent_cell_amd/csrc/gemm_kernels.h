@@ -11,7 +11,7 @@ namespace gemm {
 constexpr int kGemmThreads = 512;   // 8 wave64: 4 (rows) x 2 (columns) over the tile
 constexpr int kTile = 64;           // output tile: 64 rows x 64 columns
 constexpr int kBK = 32;             // reduction indices staged per chunk
-constexpr int kLdsPitch = 36;       // floats per staged row (32 + 4: spreads LDS banks)
+constexpr int kLdsPitch = 32;       // floats per staged row; its 8 float4 columns are XOR-swizzled by row
 constexpr int kMaxTasks = 8;
 constexpr int kMseThreads = 256;
 

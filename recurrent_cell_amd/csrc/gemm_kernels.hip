@@ -77,18 +77,26 @@ __device__ __forceinline__ f32x4 load_chunk(const float* p, int64_t ld, int R, i
     return v;
 }
 
-// The staged chunk in LDS as [row][k] (row pitch kLdsPitch floats).
+// Physical float4 column of logical float4 column c4 (k = 4 c4 .. 4 c4 + 3)
+// in staged row `row`: XOR-swizzled by bits 2-4 of the row, so that the
+// transposing scalar stores of a wave (16 rows 4 apart, 4 k) hit 32
+// different banks and the float4 reads stay 16-byte aligned.
+__device__ __forceinline__ int swz(int row, int c4) { return c4 ^ ((row >> 2) & 7); }
+
+// The staged chunk in LDS as [row][k] (row pitch kLdsPitch floats, float4
+// columns swizzled by swz).
 template <int KC>
 __device__ __forceinline__ void store_chunk(float (*dst)[kLdsPitch], f32x4 v)
 {
     const int t = threadIdx.x;
     if constexpr (KC) {
-        *reinterpret_cast<f32x4*>(&dst[t >> 3][4 * (t & 7)]) = v;
+        const int row = t >> 3;
+        *reinterpret_cast<f32x4*>(&dst[row][4 * swz(row, t & 7)]) = v;
     } else {
         const int k = t >> 4;
         const int r = 4 * (t & 15);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[r + e][k] = v[e];
+        for (int e = 0; e < 4; ++e) dst[r + e][4 * swz(r + e, k >> 2) + (k & 3)] = v[e];
     }
 }
 
@@ -163,11 +171,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
         }
 #pragma unroll
         for (int h = 0; h < kBK / 16; ++h) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&As[buf][wm * 16 + li][16 * h + 4 * lk]);
+            const int ra = wm * 16 + li;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&As[buf][ra][4 * swz(ra, 4 * h + lk)]);
             f32x4 b[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const f32x4*>(&Bs[buf][wn * 32 + 16 * j + li][16 * h + 4 * lk]);
+            for (int j = 0; j < 2; ++j) {
+                const int rb = wn * 32 + 16 * j + li;
+                b[j] = *reinterpret_cast<const f32x4*>(&Bs[buf][rb][4 * swz(rb, 4 * h + lk)]);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
         if (do_colsum && t < kTile) {
 #pragma unroll
             for (int q = 0; q < kBK / 4; ++q) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&As[buf][t][4 * q]);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&As[buf][t][4 * swz(t, q)]);
                 csum = (((csum + x[0]) + x[1]) + x[2]) + x[3];
             }
         }
