@@ -1395,79 +1395,116 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
 // bits of a column do not depend on N, V, the segment it sits in or the grid.
 // Up to two tensors (segments) with the same B are reduced by one launch.
 // ---------------------------------------------------------------------------
-template <int V>
+template <int V, int G>
 __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
 {
-    __shared__ double part[kThreads * V];
+    // G column groups per lane: group j of this lane is (blockIdx.x G + j)
+    // lanes + lane, so that every j is one coalesced row segment per slice;
+    // the loads of all G groups of a row are in flight together.
+    __shared__ double part[kThreads * V * G];
     const int lanes = kThreads / a.R;
     const int slice = threadIdx.x / lanes;
     const int lane = threadIdx.x - slice * lanes;
-    int64_t g = (int64_t)blockIdx.x * lanes + lane;
-    const bool second = g >= a.seg[0].groups;
-    if (second) g -= a.seg[0].groups;
-    const float* in = second ? a.seg[1].in : a.seg[0].in;
-    float* out = second ? a.seg[1].out : a.seg[0].out;
-    const int64_t N = second ? a.seg[1].N : a.seg[0].N;
-    const int64_t groups = second ? a.seg[1].groups : a.seg[0].groups;
-    const bool valid = (second ? a.nseg > 1 : true) && g < groups;
-
-    double acc[V];
+    const float* in[G];
+    float* out[G];
+    int64_t N[G], n0[G];
+    bool valid[G], whole[G];
 #pragma unroll
-    for (int j = 0; j < V; ++j) acc[j] = 0.0;
-    const int64_t n0 = g * V;
-    if (valid) {
-        const int64_t rb = (int64_t)slice * a.rows_per_slice;
-        const int64_t re = min(rb + a.rows_per_slice, a.B);
-        const float* __restrict__ p = in + rb * N + n0;
-        bool done = false;
-        if constexpr (V == 4) {
-            if (n0 + 4 <= N) {
+    for (int jg = 0; jg < G; ++jg) {
+        int64_t gi = ((int64_t)blockIdx.x * G + jg) * lanes + lane;
+        const bool second = gi >= a.seg[0].groups;
+        if (second) gi -= a.seg[0].groups;
+        in[jg] = second ? a.seg[1].in : a.seg[0].in;
+        out[jg] = second ? a.seg[1].out : a.seg[0].out;
+        N[jg] = second ? a.seg[1].N : a.seg[0].N;
+        const int64_t groups = second ? a.seg[1].groups : a.seg[0].groups;
+        valid[jg] = (second ? a.nseg > 1 : true) && gi < groups;
+        n0[jg] = gi * V;
+        whole[jg] = valid[jg] && n0[jg] + V <= N[jg];
+    }
+
+    double acc[G][V];
+#pragma unroll
+    for (int jg = 0; jg < G; ++jg)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[jg][e] = 0.0;
+    const int64_t rb = (int64_t)slice * a.rows_per_slice;
+    const int64_t re = min(rb + a.rows_per_slice, a.B);
+    bool vec_all = true, any = false;
+#pragma unroll
+    for (int jg = 0; jg < G; ++jg) {
+        vec_all = vec_all && (whole[jg] || !valid[jg]);
+        any = any || valid[jg];
+    }
+    if (V == 4 && vec_all) {
+        if (any) {
+            // every group of the lane is whole or absent: 16-byte loads; an
+            // absent group reads column 0 of the first segment's rows (in
+            // bounds: there is a valid group, so that segment has B rows of
+            // at least 4 columns) and is dropped
+            const float* p[G];
+            int64_t st[G];
+#pragma unroll
+            for (int jg = 0; jg < G; ++jg) {
+                st[jg] = valid[jg] ? N[jg] : a.seg[0].N;
+                p[jg] = valid[jg] ? in[jg] + rb * N[jg] + n0[jg] : a.seg[0].in + rb * a.seg[0].N;
+            }
 #pragma unroll 8
-                for (int64_t b = rb; b < re; ++b, p += N) {
-                    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-                    acc[0] += (double)v.x;
-                    acc[1] += (double)v.y;
-                    acc[2] += (double)v.z;
-                    acc[3] += (double)v.w;
+            for (int64_t b = rb; b < re; ++b) {
+                f32x4 v[G];
+#pragma unroll
+                for (int jg = 0; jg < G; ++jg)
+                    v[jg] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p[jg]));
+#pragma unroll
+                for (int jg = 0; jg < G; ++jg) {
+                    acc[jg][0] += (double)v[jg].x;
+                    acc[jg][1] += (double)v[jg].y;
+                    acc[jg][2] += (double)v[jg].z;
+                    acc[jg][3] += (double)v[jg].w;
+                    p[jg] += st[jg];
                 }
-                done = true;
             }
         }
-        if (!done) {
-            for (int64_t b = rb; b < re; ++b, p += N) {
+    } else {
 #pragma unroll
-                for (int j = 0; j < V; ++j)
-                    if (n0 + j < N) acc[j] += (double)p[j];
+        for (int jg = 0; jg < G; ++jg) {
+            if (!valid[jg]) continue;
+            const float* __restrict__ q = in[jg] + rb * N[jg] + n0[jg];
+            for (int64_t b = rb; b < re; ++b, q += N[jg]) {
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    if (n0[jg] + e < N[jg]) acc[jg][e] += (double)q[e];
             }
         }
     }
 #pragma unroll
-    for (int j = 0; j < V; ++j) part[(slice * lanes + lane) * V + j] = acc[j];
+    for (int jg = 0; jg < G; ++jg)
+#pragma unroll
+        for (int e = 0; e < V; ++e) part[((slice * lanes + lane) * G + jg) * V + e] = acc[jg][e];
     __syncthreads();
-    if (slice == 0 && valid) {
-        double s[V];
+    if (slice == 0) {
 #pragma unroll
-        for (int j = 0; j < V; ++j) s[j] = part[lane * V + j];
-        for (int i = 1; i < a.R; ++i) {
+        for (int jg = 0; jg < G; ++jg) {
+            if (!valid[jg]) continue;
+            double sm[V];
 #pragma unroll
-            for (int j = 0; j < V; ++j) s[j] += part[(i * lanes + lane) * V + j];
-        }
-        bool done = false;
-        if constexpr (V == 4) {
-            if (n0 + 4 <= N) {
-                f32x4 o;
-                o.x = (float)s[0];
-                o.y = (float)s[1];
-                o.z = (float)s[2];
-                o.w = (float)s[3];
-                *reinterpret_cast<f32x4*>(out + n0) = o;
-                done = true;
+            for (int e = 0; e < V; ++e) sm[e] = part[(lane * G + jg) * V + e];
+            for (int i = 1; i < a.R; ++i) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) sm[e] += part[((i * lanes + lane) * G + jg) * V + e];
             }
-        }
-        if (!done) {
+            if (V == 4 && whole[jg]) {
+                f32x4 o;
+                o.x = (float)sm[0];
+                o.y = (float)sm[1];
+                o.z = (float)sm[2];
+                o.w = (float)sm[3];
+                *reinterpret_cast<f32x4*>(out[jg] + n0[jg]) = o;
+            } else {
 #pragma unroll
-            for (int j = 0; j < V; ++j)
-                if (n0 + j < N) out[n0 + j] = (float)s[j];
+                for (int e = 0; e < V; ++e)
+                    if (n0[jg] + e < N[jg]) out[jg][n0[jg] + e] = (float)sm[e];
+            }
         }
     }
     if (a.xn > 0 && blockIdx.x == 0) {
@@ -1754,12 +1791,20 @@ hipError_t launch_reduce_with_sum(const ReduceSeg* segs, int nseg, int64_t B, in
     for (int i = nseg; i < kMaxReduceSegs; ++i) a.seg[i] = ReduceSeg{nullptr, nullptr, 0, 0};
     if (total == 0 && a.xn == 0) return hipSuccess;
     const int lanes = kThreads / a.R;
-    const int64_t blocks = total > 0 ? (total + lanes - 1) / lanes : 1;
+    // Two column groups per lane where a slice has few rows and the grid
+    // would be very large: more loads in flight per lane (measured: B = 32,
+    // N = 8M 0.69 -> 0.73 of the HBM datasheet rate; smaller grids lose by it).
+    // The bits of a column do not depend on this.
+    const int64_t blocks1 = (total + lanes - 1) / lanes;
+    const int G = (V == 4 && a.rows_per_slice <= 8 && blocks1 > 16384) ? 2 : 1;
+    const int64_t blocks = total > 0 ? (total + (int64_t)lanes * G - 1) / ((int64_t)lanes * G) : 1;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (V == 4)
-        hipLaunchKernelGGL(reduce_axis0_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    if (V == 4 && G == 2)
+        hipLaunchKernelGGL((reduce_axis0_kernel<4, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else if (V == 4)
+        hipLaunchKernelGGL((reduce_axis0_kernel<4, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(reduce_axis0_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((reduce_axis0_kernel<1, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

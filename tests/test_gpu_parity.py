@@ -521,6 +521,33 @@ def test_reduce_full_size_sampled(cfc, oracle_mod, B, N):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("B", [32, 128])
+def test_reduce_large_grid_ragged_and_column_bits(cfc, oracle_mod, B):
+    """The largest grids take two column groups per lane.  A ragged tail
+    (the last workgroup partly past N) is checked against the oracle, and
+    every column's bits equal those of the same column reduced in a small
+    launch (one group per lane): the bits depend on B alone."""
+    N = 4 * (8388608 // 4 + 4 * 64 * 2 + 3)   # multiple of 4, not of a workgroup's columns
+    say("reduce large grid", B, N)
+    gen = torch.Generator(device="cuda").manual_seed(77 + B)
+    x = torch.randn((B, N), device="cuda", generator=gen)
+    out = torch.full((N,), float("nan"), device="cuda")
+    cfc.reduce_axis0(x, out)
+    idx = np.unique(np.concatenate([np.arange(N - 3000, N), np.random.default_rng(B).integers(0, N, 2048)]))
+    cols = host(x[:, torch.from_numpy(idx).cuda()])
+    ref = oracle_mod.reduce_axis0_f64(np.ascontiguousarray(cols))
+    got = host(out)
+    assert np.isfinite(got).all()
+    assert_ok(check_reduce("reduce", got[idx], ref, np.abs(cols.astype(np.float64)).sum(0), B))
+    for lo, hi in ((0, 4096), (N - 4096, N)):
+        part = x[:, lo:hi].contiguous()
+        small = torch.full((hi - lo,), float("nan"), device="cuda")
+        cfc.reduce_axis0(part, small)
+        assert torch.equal(small.view(torch.int32), out[lo:hi].view(torch.int32))
+    del x
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- AdamW after the reducer
 
 def f32(x):
