@@ -963,7 +963,7 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
         if (r < R3 && k < n_in) {
             float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in + k;
             if (vec_out && k + 4 <= n_in) {
-                *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(&dps[row][c4]);
+                __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&dps[row][c4]), reinterpret_cast<f32x4*>(dst));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
