@@ -48,6 +48,7 @@ def step_bytes_flops(B, C, n_x, K):
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kloop_persist_pages_hbm_traffic.md")
+VALU_SUMMARY = os.path.join(ROOT, "profiles", "kloop_persist_pages_valu.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "recurrent_cell_amd", "csrc", f)
                   for f in ("cfc_kernels.hip", "cfc_kernels.h", "cfc_math.h")]
 
@@ -69,21 +70,34 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the persistent kernel from the committed
-    rocprofv3 counter summary, or None if the kernel sources changed since
-    the counters were taken (or the summary is missing)."""
+def profile_value(path, key):
+    """A value recorded in a committed rocprofv3 counter summary ("key: value"
+    under the kernel sources' sha256), or None if the summary is missing or
+    the persistent kernel's sources changed since the counters were taken."""
     import re
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(path).read()
         digest = kernel_source_digest()
     except OSError:
         return None
     m_hash = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
-    m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != digest:
+    m_val = re.search(r"%s:\s*([0-9.]+)" % re.escape(key), text)
+    if not m_hash or not m_val or m_hash.group(1) != digest:
         return None
-    return int(m_bytes.group(1))
+    return float(m_val.group(1))
+
+
+def measured_traffic():
+    """HBM bytes per launch of the persistent kernel (FETCH_SIZE + WRITE_SIZE,
+    calibrated), or None (see profile_value)."""
+    v = profile_value(TRAFFIC_SUMMARY, "traffic_bytes_per_launch")
+    return None if v is None else int(v)
+
+
+def measured_valu_busy():
+    """Fraction of time the VALU of the persistent kernel's CUs is busy
+    (SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES), or None (see profile_value)."""
+    return profile_value(VALU_SUMMARY, "valu_busy_fraction")
 
 
 def recurrence_flops(B, C, K):
@@ -536,6 +550,7 @@ def main():
             fl = recurrence_flops(B, C, K)
             achieved = fl / dur
             traffic = measured_traffic() if args.workload == "pages" else None
+            valu_busy = measured_valu_busy() if args.workload == "pages" else None
             # what the kernel can use: one CU per sample (B of 256), fp32 FMA
             # without packed math (4 SIMDs x 16 lanes x 2 flop per clock;
             # half the 256 flop per clock per CU of the published peak)
@@ -557,7 +572,12 @@ def main():
                         "fma_probe_chip_TFLOPs": round(meas_chip / 1e12, 2),
                         "fma_probe_chip_GHz": round(meas_chip / (256 * 128) / 1e9, 3),
                         "fma_probe_note": "v_fma_f32 chains, 512 lanes per workgroup, one workgroup per CU; "
-                                          "GHz = chip rate / (256 CUs x 128 flop/clk)"}
+                                          "GHz = chip rate / (256 CUs x 128 flop/clk)",
+                        "traffic_GBps": round(traffic / dur / 1e9, 1) if traffic else None,
+                        "traffic_frac_of_hbm_peak": round(traffic / dur / HBM_PEAK, 4) if traffic else None,
+                        "valu_busy_rocprof": valu_busy,
+                        "valu_busy_note": "SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES over the kernel's CUs "
+                                          "(profiles/kloop_persist_pages_valu.md)"}
         elif path == "steps_mfma":
             # the 2K step launches of the K-loop (and the one W re-layout), per launch on average
             dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
