@@ -486,25 +486,26 @@ __global__ __launch_bounds__(kThreads) void permute_w_kernel(PermuteArgs a)
     }
 }
 
-constexpr int kFwdMfmaThreads = 192;   // one wave per head
+constexpr int kFwdMfmaThreads = 576;   // three waves per head
 constexpr int kMfmaMaxNxb = 8;         // input column blocks of 16: n_x <= 128
 constexpr int kMfmaMaxNhb = 10;        // recurrent column blocks of 32: C <= 320
 constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
 
-// Forward step on MFMA.  Workgroup = 16 samples x 16 channels; wave q forms
-// head q's pre-activations: four input chains (x_r: k-slot kk of block p is
-// column 16 p + 4 kk + r) and eight recurrent partitions (P_j: k-slot e of
-// block i is column n_x + 32 i + 4 j + e), then bias + ((x0+x1)+(x2+x3)) and
-// sum8 -- the canonical order.  The tile's 48 W rows (forward layout) and z
-// (u as is, h permuted like Wf) are staged in LDS, every load in flight
-// before the first LDS store.  Then all 192 lanes apply the cell.  Needs n_x, C multiples of 4 and 16-byte
-// aligned rows.  Operand layout (16 x 16 x 4): A[sample l % 16][k-slot l /
+// Forward step on MFMA.  Workgroup = 16 samples x 16 channels; three waves
+// per head q: part 0 forms the four input chains (x_r: k-slot kk of block p
+// is column 16 p + 4 kk + r) and X = bias + ((x0+x1)+(x2+x3)); part 1 the
+// recurrent partitions P_0..P_3 and part 2 P_4..P_7 (P_j: k-slot e of block
+// i is column n_x + 32 i + 4 j + e), each with its half of sum8.  The cell
+// then takes X + (half 1 + half 2): the canonical order.  The lanes' W
+// operands come straight from the forward layout into registers; z (u as
+// is, h permuted like Wf) is staged in LDS, every load in flight before the
+// first LDS store.  Needs n_x, C multiples of 4 and 16-byte aligned rows.  Operand layout (16 x 16 x 4): A[sample l % 16][k-slot l /
 // 16], B[k-slot l / 16][channel l % 16]; D[sample i][channel j] in lane
 // j + 16 (i / 4), register i % 4.
 __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a)
 {
     __shared__ __attribute__((aligned(16))) float zs[16 * (kMfmaMaxLdf + 4)];
-    __shared__ float as[3 * 16 * 16];
+    __shared__ float as[3][3][16 * 16];   // [head][X, half 1, half 2][sample, channel]
     const MfmaLayout L = a.L;
     const int C = a.C;
     const int n_x = a.n_x;
@@ -517,24 +518,24 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     const int ldp = L.ldf + 4;              // row pitch: 4 banks between rows
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int q = tid >> 6;
+    const int q = (tid >> 6) / 3;       // head
+    const int part = (tid >> 6) % 3;    // 0: input chains, 1: P_0..P_3, 2: P_4..P_7 (uniform per wave)
     const int li = lane & 15;
     const int lk = lane >> 4;
 
     // This lane's W operands straight from the forward layout into
     // registers (each W value feeds exactly one lane's MFMAs, so it needs no
-    // LDS): row (head q, channel c0 + li), the four k-slots of every block,
-    // issued with the z loads below before any of them is waited for.
+    // LDS): row (head q, channel c0 + li), the four k-slots of every block of
+    // the wave's part, issued with the z loads below before any of them is
+    // waited for.  Blocks past nxb / nhb load a clamped block, never used.
     const float* wrow = a.Wf + ((int64_t)q * C + min(c0 + li, C - 1)) * L.ldf;
-    f32x4 wx[kMfmaMaxNxb], wh[kMfmaMaxNhb][2];
-#pragma unroll
-    for (int p = 0; p < kMfmaMaxNxb; ++p)
-        wx[p] = *reinterpret_cast<const f32x4*>(wrow + 16 * min(p, nxb - 1) + 4 * lk);
+    static_assert(kMfmaMaxNxb <= kMfmaMaxNhb, "one register block array serves both parts");
+    f32x4 wv[kMfmaMaxNhb];
 #pragma unroll
     for (int i = 0; i < kMfmaMaxNhb; ++i) {
-        const int o = L.nxp + 32 * min(i, nhb - 1) + 8 * lk;
-        wh[i][0] = *reinterpret_cast<const f32x4*>(wrow + o);
-        wh[i][1] = *reinterpret_cast<const f32x4*>(wrow + o + 4);
+        const int o = (part == 0) ? 16 * min(i, nxb - 1) + 4 * lk
+                                  : L.nxp + 32 * min(i, nhb - 1) + 8 * lk + 4 * (part - 1);
+        wv[i] = *reinterpret_cast<const f32x4*>(wrow + o);
     }
     // z rows in float4 units: unit u of row s covers columns 4 u .. 4 u + 3
     // of [u ; h] in their natural order (zero past n_x, past C and for
@@ -584,41 +585,40 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     __syncthreads();
 
     const float* zr = zs + li * ldp;                 // sample li
-    f32x4 ax[4], ah[8];
+    f32x4 acc[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ax[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ah[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     // Unrolled over the register-held W blocks; the trip counts are uniform
     // and the blocks past nxb / nhb are never used.
+    if (part == 0) {
 #pragma unroll
-    for (int p = 0; p < kMfmaMaxNxb; ++p) {
-        if (p < nxb) {
-            const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
+        for (int p = 0; p < kMfmaMaxNxb; ++p) {
+            if (p < nxb) {
+                const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + 16 * p + 4 * lk);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                ax[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wx[p][c], ax[c], 0, 0, 0);
+                for (int c = 0; c < 4; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[c], wv[p][c], acc[c], 0, 0, 0);
+            }
         }
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < kMfmaMaxNhb; ++i) {
-        if (i < nhb) {
-            const int o = L.nxp + 32 * i + 8 * lk;
-            const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + o);
-            const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + o + 4);
+        for (int i = 0; i < kMfmaMaxNhb; ++i) {
+            if (i < nhb) {
+                const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + L.nxp + 32 * i + 8 * lk + 4 * (part - 1));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ah[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z0[j], wh[i][0][j], ah[j], 0, 0, 0);
-                ah[4 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(z1[j], wh[i][1][j], ah[4 + j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[j], wv[i][j], acc[j], 0, 0, 0);
             }
         }
     }
     const float bias = a.bias[q * C + min(c0 + li, C - 1)];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float X = xproj_combine(bias, ax[0][e], ax[1][e], ax[2][e], ax[3][e]);
-        const float H = ((ah[0][e] + ah[1][e]) + (ah[2][e] + ah[3][e])) + ((ah[4][e] + ah[5][e]) + (ah[6][e] + ah[7][e]));
-        as[(q * 16 + 4 * lk + e) * 16 + li] = X + H;
+        // part 0: X = bias + ((x0 + x1) + (x2 + x3)); parts 1, 2: their half
+        // of sum8, (P0 + P1) + (P2 + P3) and (P4 + P5) + (P6 + P7)
+        const float v = (part == 0) ? xproj_combine(bias, acc[0][e], acc[1][e], acc[2][e], acc[3][e])
+                                    : (acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]);
+        as[q][part][(4 * lk + e) * 16 + li] = v;
     }
     __syncthreads();
 
@@ -629,7 +629,10 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
         const int b = s0 + s;
         const int c = c0 + cl;
         if (b < a.B && c < C) {
-            const CellOut o = cell_forward(as[s * 16 + cl], as[(16 + s) * 16 + cl], as[(32 + s) * 16 + cl]);
+            float pre[3];
+#pragma unroll
+            for (int h = 0; h < 3; ++h) pre[h] = as[h][0][i] + (as[h][1][i] + as[h][2][i]);   // X + H
+            const CellOut o = cell_forward(pre[0], pre[1], pre[2]);
             const int64_t bc = (int64_t)b * C + c;
             a.h_t[bc] = o.h;
             a.act_t[bc] = o.gate;
