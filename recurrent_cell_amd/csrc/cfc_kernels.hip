@@ -645,18 +645,19 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
 // Backward step (K-loop: dp out, carry) on MFMA.  Workgroup = 16 samples x
 // 16 carry columns.  dp of the tile's samples for every channel goes to LDS
 // in the MFMA layout dps[s][g][kk][p] (element 4 p + kk of group g's chain);
-// the workgroup stores dp of its own 16 channels.  Wave w forms the canonical
-// subtree T_w of dz over groups g = w + 4 m (m = 0..15): P_g is a chain of
-// PG MFMAs from +0 (the 16 chains independent, so their instructions
-// interleave), then the pairwise tree of tree_sum16.  Then
-// dz = (T0 + T1) + (T2 + T3).
-constexpr int kBwdMfmaThreads = 256;
+// the workgroup stores dp of its own 16 channels.  The canonical subtree T_w
+// of dz over groups g = w + 4 m (m = 0..15) is formed by two waves, one per
+// half m = 0..7 and m = 8..15: P_g is a chain of PG MFMAs from +0 (the 8
+// chains of a wave independent, so their instructions interleave), then
+// the first three levels of the pairwise tree of tree_sum16; its last level
+// adds the halves.  Then dz = (T0 + T1) + (T2 + T3).
+constexpr int kBwdMfmaThreads = 512;   // 4 subtrees x 2 halves of their 16 groups
 
 template <int PG>
 __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a)
 {
     __shared__ __attribute__((aligned(16))) float dps[16 * kDzGroups * 16];
-    __shared__ __attribute__((aligned(16))) float ts[4][16][17];
+    __shared__ __attribute__((aligned(16))) float ts[2][4][16][17];   // [half][subtree][sample][column]
     const int C = a.C;
     const int cpg = dz_group_channels(C);
     const int ctile = blockIdx.x % a.n_ctiles;
@@ -767,43 +768,46 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
     __syncthreads();
 
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = (tid >> 6) & 3;   // subtree
+    const int hf = tid >> 8;        // half of the subtree's 16 groups: m = 8 hf .. 8 hf + 7
     const int li = lane & 15;
     const int lk = lane >> 4;
     const float* wb = a.Wb + ((int64_t)min(k0 + li, C - 1) * kDzGroups) * 16 + 4 * lk;   // + 16 g
     const float* da = dps + li * kDzGroups * 16 + 4 * lk;                                 // + 16 g
-    f32x4 bv[16];
+    f32x4 bv[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) bv[m] = *reinterpret_cast<const f32x4*>(wb + 16 * (w + 4 * m));
-    __builtin_amdgcn_sched_barrier(0);   // the 16 loads ahead of the MFMAs
-    // The 16 group partials as independent MFMA chains (so that their
-    // instructions interleave), then the pairwise tree of tree_sum16.
-    f32x4 av[16], P[16];
+    for (int m = 0; m < 8; ++m) bv[m] = *reinterpret_cast<const f32x4*>(wb + 16 * (w + 4 * (8 * hf + m)));
+    __builtin_amdgcn_sched_barrier(0);   // the 8 loads ahead of the MFMAs
+    // The half's 8 group partials as independent MFMA chains (so that their
+    // instructions interleave), then the first three levels of the pairwise
+    // tree of tree_sum16; its last level adds the two halves below.
+    f32x4 av[8], P[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) av[m] = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * m));
+    for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * (8 * hf + m)));
 #pragma unroll
-    for (int m = 0; m < 16; ++m) P[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < 8; ++m) P[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int p = 0; p < PG; ++p)
 #pragma unroll
-        for (int m = 0; m < 16; ++m) P[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][p], bv[m][p], P[m], 0, 0, 0);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) P[m] = P[2 * m] + P[2 * m + 1];
+        for (int m = 0; m < 8; ++m) P[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][p], bv[m][p], P[m], 0, 0, 0);
 #pragma unroll
     for (int m = 0; m < 4; ++m) P[m] = P[2 * m] + P[2 * m + 1];
 #pragma unroll
     for (int m = 0; m < 2; ++m) P[m] = P[2 * m] + P[2 * m + 1];
     const f32x4 T = P[0] + P[1];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ts[w][4 * lk + e][li] = T[e];
+    for (int e = 0; e < 4; ++e) ts[hf][w][4 * lk + e][li] = T[e];
     __syncthreads();
-    {
+    if (tid < 256) {
         const int s = tid >> 4;
         const int col = tid & 15;
         const int b = s0 + s;
         const int k = k0 + col;
         if (b < a.B && k < C) {
-            const float carry = (ts[0][s][col] + ts[1][s][col]) + (ts[2][s][col] + ts[3][s][col]);
+            float T4[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) T4[v] = ts[0][v][s][col] + ts[1][v][s][col];   // tree_sum16's last level
+            const float carry = (T4[0] + T4[1]) + (T4[2] + T4[3]);
             const int64_t bk = (int64_t)b * C + k;
             if (a.dh_out != nullptr) a.dh_out[bk] = carry;
             if (a.dp_prev_out != nullptr) {
