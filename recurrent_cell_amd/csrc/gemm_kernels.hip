@@ -28,9 +28,11 @@ __device__ __forceinline__ int64_t xcd_local_order(int64_t i, int64_t n)
 
 // This thread's share of one staged chunk of an operand: rows [r0, r0 + 64)
 // of R, reduction indices [k0, k0 + 32) cut at kend; zero outside.  One
-// float4 per thread, with no branch: loads go to clamped (in-bounds)
-// addresses and are selected afterwards, so the prefetch of the next chunk
-// stays in flight until its LDS store.
+// float4 per thread, in two parts: load_chunk issues the loads on clamped
+// (in-bounds) addresses, with no branch and no use of the values, and
+// mask_chunk zeroes the out-of-range elements where the chunk goes to LDS.
+// A select right after the loads made the compiler wait for them there, so
+// the prefetch of the next chunk did not overlap the matrix-core work.
 //   KC: element (r, k) at p[r * ld + k] (else p[k * ld + r]);
 //   VEC: 16-byte loads along the contiguous index; the host sets it only
 //        when ld and that index's extent are multiples of 4 and p is
@@ -45,34 +47,46 @@ __device__ __forceinline__ f32x4 load_chunk(const float* p, int64_t ld, int R, i
         // 64 rows x 8 float4 along k: row t / 8, k0 + 4 (t % 8)
         const int r = r0 + (t >> 3);
         const int k = k0 + 4 * (t & 7);
-        const bool rok = r < R;
         const float* src = p + (int64_t)min(r, R - 1) * ld;
         if constexpr (VEC) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(src + min(k, kend - 4));
-            v = (rok && k < kend) ? x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            v = *reinterpret_cast<const f32x4*>(src + min(k, kend - 4));
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x = src[min(k + e, kend - 1)];
-                v[e] = (rok && k + e < kend) ? x : 0.0f;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = src[min(k + e, kend - 1)];
         }
     } else {
         // 32 reduction rows x 16 float4 along r: k0 + t / 16, r0 + 4 (t % 16)
         const int k = k0 + (t >> 4);
         const int r = r0 + 4 * (t & 15);
-        const bool kok = k < kend;
         const float* src = p + (int64_t)min(k, kend - 1) * ld;
         if constexpr (VEC) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(src + min(r, R - 4));
-            v = (kok && r < R) ? x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            v = *reinterpret_cast<const f32x4*>(src + min(r, R - 4));
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x = src[min(r + e, R - 1)];
-                v[e] = (kok && r + e < R) ? x : 0.0f;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = src[min(r + e, R - 1)];
         }
+    }
+    return v;
+}
+
+template <int KC, bool VEC>
+__device__ __forceinline__ f32x4 mask_chunk(f32x4 v, int R, int r0, int k0, int kend)
+{
+    const int t = threadIdx.x;
+    if constexpr (KC) {
+        const int r = r0 + (t >> 3);
+        const int k = k0 + 4 * (t & 7);
+        const bool rok = r < R;
+        if constexpr (VEC) return (rok && k < kend) ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (rok && k + e < kend) ? v[e] : 0.0f;
+    } else {
+        const int k = k0 + (t >> 4);
+        const int r = r0 + 4 * (t & 15);
+        const bool kok = k < kend;
+        if constexpr (VEC) return (kok && r < R) ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (kok && r + e < R) ? v[e] : 0.0f;
     }
     return v;
 }
@@ -154,21 +168,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
     acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float csum = 0.0f;
 
-    f32x4 va = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, vb = va;
+    // A: rows T.M (or a_lim) and reduction end a_lim (or ke); B: rows T.N, end ke
+    const int a_rows = AKC ? T.M : a_lim;
+    const int a_end = AKC ? a_lim : ke;
     if (nch > 0) {
-        va = load_chunk<AKC, VA>(T.A.p, T.A.ld, AKC ? T.M : a_lim, m0, kb, AKC ? a_lim : ke);
-        vb = load_chunk<BKC, VB>(T.B.p, T.B.ld, T.N, n0, kb, ke);
-        store_chunk<AKC>(As[0], va);
-        store_chunk<BKC>(Bs[0], vb);
+        const f32x4 va = load_chunk<AKC, VA>(T.A.p, T.A.ld, a_rows, m0, kb, a_end);
+        const f32x4 vb = load_chunk<BKC, VB>(T.B.p, T.B.ld, T.N, n0, kb, ke);
+        store_chunk<AKC>(As[0], mask_chunk<AKC, VA>(va, a_rows, m0, kb, a_end));
+        store_chunk<BKC>(Bs[0], mask_chunk<BKC, VB>(vb, T.N, n0, kb, ke));
     }
     __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
         const int buf = ch & 1;
-        const bool more = ch + 1 < nch;
-        if (more) {
-            va = load_chunk<AKC, VA>(T.A.p, T.A.ld, AKC ? T.M : a_lim, m0, kb + (ch + 1) * kBK, AKC ? a_lim : ke);
-            vb = load_chunk<BKC, VB>(T.B.p, T.B.ld, T.N, n0, kb + (ch + 1) * kBK, ke);
-        }
+        // The next chunk's loads, issued before this chunk's MFMAs and first
+        // used at the LDS store after them.  The last chunk loads itself
+        // again and stores it into the idle buffer, which no wave reads any
+        // more (every wave passed the previous barrier after its last read
+        // of it): no branch, so nothing forces an early wait.
+        const int kn = kb + min(ch + 1, nch - 1) * kBK;
+        const f32x4 va = load_chunk<AKC, VA>(T.A.p, T.A.ld, a_rows, m0, kn, a_end);
+        const f32x4 vb = load_chunk<BKC, VB>(T.B.p, T.B.ld, T.N, n0, kn, ke);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
 #pragma unroll
         for (int h = 0; h < kBK / 16; ++h) {
             const int ra = wm * 16 + li;
@@ -192,10 +212,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(GemmBatch g)
                 csum = (((csum + x[0]) + x[1]) + x[2]) + x[3];
             }
         }
-        if (more) {
-            store_chunk<AKC>(As[buf ^ 1], va);
-            store_chunk<BKC>(Bs[buf ^ 1], vb);
-        }
+        __builtin_amdgcn_sched_barrier(0);   // and their first use after them
+        store_chunk<AKC>(As[buf ^ 1], mask_chunk<AKC, VA>(va, a_rows, m0, kn, a_end));
+        store_chunk<BKC>(Bs[buf ^ 1], mask_chunk<BKC, VB>(vb, T.N, n0, kn, ke));
         __syncthreads();
     }
 
