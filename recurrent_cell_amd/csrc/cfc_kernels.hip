@@ -1020,6 +1020,13 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
 constexpr int kFwdChunk = 16;
 constexpr int kBwdChunk = 8;
 
+// 16-byte global load and store at a byte address (global address space:
+// a plain pointer made from an integer would be a flat access, which also
+// counts on the LDS wait counter).
+typedef __attribute__((address_space(1))) f32x4 global_f32x4;
+__device__ __forceinline__ f32x4 gload4(uint64_t addr) { return *(const global_f32x4*)addr; }
+__device__ __forceinline__ void gstore4(uint64_t addr, f32x4 v) { *(global_f32x4*)addr = v; }
+
 template <int CPG, int NH>
 struct PersistLds {
     static constexpr int HW = 32 * NH;           // recurrent columns held (>= C)
@@ -1173,7 +1180,52 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     auto x_row = [&](int t0) {
         return [=](int rr) { return const_cast<float*>(a.X) + ((int64_t)(t0 - 1 + rr) * B + b) * R3; };
     };
+    // Chunk-boundary moves on the 16-byte path use per-thread addresses
+    // computed once here, so that each move at a boundary is one 64-bit
+    // add of a uniform multiple of the chunk's first step (no division, no
+    // per-row choice of array; a per-lane choice between two pointer
+    // arguments made the compiler reload the pointer and wait for it at
+    // every move).  Unsigned byte addresses: the per-thread part may point
+    // before the array; the step's term brings it back in bounds.
+    //  - X rows of a whole chunk (row clamped as in load_x's general case);
+    //  - the forward outputs: float4 move m of this thread is element
+    //    i = tid + m THREADS of the chunk's [4 nt][C / 4] block, whose row
+    //    rr = 4 tt + v holds h_t (v = 0) or gate, g, hh (v = 1..3) of step
+    //    t0 + tt; its LDS offset is clamped into the block for rows past it.
+    constexpr int OM = (kFwdChunk * HW + THREADS - 1) / THREADS;
+    uint64_t x_addr[XPF];
+    uint64_t o_addr[OM];
+    int o_rr[OM], o_lds[OM];
+    bool o_act[OM];
+    if (c_vec) {
+#pragma unroll
+        for (int m = 0; m < XPF; ++m) {
+            const int rr = min(x_row0 + m * x_rstep, kFwdChunk - 1);
+            x_addr[m] = (uint64_t)a.X + 4 * (uint64_t)(((int64_t)(rr - 1) * B + b) * R3 + 4 * x_col);
+        }
+        const int w4 = C / 4;   // C % 4 == 0 on this path
+#pragma unroll
+        for (int m = 0; m < OM; ++m) {
+            const int i = tid + m * THREADS;
+            const int rr = i / w4;
+            const int xq = i - rr * w4;
+            const int v = rr & 3;
+            const int tq = rr >> 2;
+            o_rr[m] = rr;
+            o_lds[m] = min(rr, 4 * kFwdChunk - 1) * HW + 4 * xq;
+            o_act[m] = v != 0;
+            const int64_t off = (v == 0 ? (int64_t)tq * BC : (int64_t)(tq - 1) * 3 * BC + (int64_t)(v - 1) * BC) +
+                                (int64_t)b * C + 4 * xq;
+            o_addr[m] = (uint64_t)(v == 0 ? a.h_hist : a.act) + 4 * (uint64_t)off;
+        }
+    }
     auto load_x = [&](int t0, int nt) {
+        if (nt == kFwdChunk) {
+            const uint64_t t0o = 4 * (uint64_t)((int64_t)t0 * B * R3);
+#pragma unroll
+            for (int m = 0; m < XPF; ++m) xpf[m] = gload4(x_addr[m] + t0o);
+            return;
+        }
         const auto src = x_row(t0);
 #pragma unroll
         for (int m = 0; m < XPF; ++m) {
@@ -1181,6 +1233,18 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             // clamped into bounds; rows past the chunk are loaded but never staged
             xpf[m] = *reinterpret_cast<const f32x4*>(src(min(rr, nt - 1)) + 4 * x_col);
         }
+    };
+    // the chunk's outputs from LDS to h_hist and act (16-byte path): every
+    // LDS read first, then the stores of the rows inside the chunk
+    auto store_out = [&](int t0, int nt) {
+        const uint64_t sh = 4 * (uint64_t)((int64_t)t0 * BC);
+        const uint64_t sa = 3 * sh;
+        f32x4 v[OM];
+#pragma unroll
+        for (int m = 0; m < OM; ++m) v[m] = *reinterpret_cast<const f32x4*>(obuf + o_lds[m]);
+#pragma unroll
+        for (int m = 0; m < OM; ++m)
+            if (o_rr[m] < 4 * nt) gstore4(o_addr[m] + (o_act[m] ? sa : sh), v[m]);
     };
     auto out_row = [&](int t0) {
         return [=](int rr) {
@@ -1211,7 +1275,10 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 stage[rr * 3 * HW + hd * HW + (x - hd * C)] = src(rr)[x];
             }
         }
-        if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, c_vec, out_row(prev_t0));
+        if (prev_nt > 0) {
+            if (c_vec) store_out(prev_t0, prev_nt);
+            else move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, false, out_row(prev_t0));
+        }
         if (c_vec && t0 + kFwdChunk <= K) load_x(t0 + kFwdChunk, min(kFwdChunk, K - t0 - kFwdChunk + 1));
         lds_barrier();
         // One step; t0 - 1 is even, so h_{t-1} sits in zs[tt & 1].
@@ -1267,7 +1334,10 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         prev_t0 = t0;
         prev_nt = nt;
     }
-    if (prev_nt > 0) move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, c_vec, out_row(prev_t0));
+    if (prev_nt > 0) {
+        if (c_vec) store_out(prev_t0, prev_nt);
+        else move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, false, out_row(prev_t0));
+    }
     __syncthreads();   // every forward store is performed and visible to the whole workgroup
 
     if constexpr (CPG == 2) {
@@ -1308,7 +1378,57 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     auto dp_row = [&](int t1) {
         return [=](int tt) { return a.dp + ((int64_t)(t1 - tt - 1) * B + b) * R3; };
     };
+    // Per-thread addresses of the backward boundary moves (16-byte path),
+    // computed once as in the forward: the input rows of a whole chunk (row
+    // rr clamped to the chunk's last; act for v < 3, else h_hist or y;
+    // without the term of step t1), and dp, where float4 move m of this
+    // thread is element i = tid + m THREADS of the chunk's [nt][3C / 4] block.
+    constexpr int DM = (kBwdChunk * 3 * HW / 4 + THREADS - 1) / THREADS;
+    uint64_t i_addr[BPF];
+    bool i_act[BPF];
+    uint64_t d_addr[DM];
+    int d_tt[DM], d_lds[DM];
+    if (c_vec) {
+#pragma unroll
+        for (int m = 0; m < BPF; ++m) {
+            const int rr = min(c_row0 + m * c_rstep, 5 * kBwdChunk - 1);
+            const int tt = rr / 5;
+            const int v = rr - 5 * tt;
+            i_act[m] = v < 3;
+            const int64_t off = (v < 3 ? (int64_t)(-tt - 1) * 3 * BC + (int64_t)v * BC
+                                       : v == 3 ? (int64_t)(-tt) * BC : (int64_t)(-tt - 1) * BC) +
+                                (int64_t)b * C + 4 * c_col;
+            i_addr[m] = (uint64_t)(v < 3 ? a.act : v == 3 ? a.h_hist : a.y) + 4 * (uint64_t)off;
+        }
+        const int w4 = R3 / 4;
+#pragma unroll
+        for (int m = 0; m < DM; ++m) {
+            const int i = tid + m * THREADS;
+            const int tt = i / w4;
+            const int xq = i - tt * w4;
+            d_tt[m] = tt;
+            d_lds[m] = min(tt, kBwdChunk - 1) * R3 + 4 * xq;
+            d_addr[m] = (uint64_t)a.dp + 4 * (uint64_t)((int64_t)b * R3 + 4 * xq - (int64_t)(tt + 1) * B * R3);
+        }
+    }
+    // the chunk's dp from LDS to memory (16-byte path): LDS reads first
+    auto store_dp = [&](int t1, int nt) {
+        const uint64_t t1o = 4 * (uint64_t)((int64_t)t1 * B * R3);
+        f32x4 v[DM];
+#pragma unroll
+        for (int m = 0; m < DM; ++m) v[m] = *reinterpret_cast<const f32x4*>(dbuf + d_lds[m]);
+#pragma unroll
+        for (int m = 0; m < DM; ++m)
+            if (d_tt[m] < nt) gstore4(d_addr[m] + t1o, v[m]);
+    };
     auto load_b = [&](int t1, int nt) {
+        if (nt == kBwdChunk) {
+            const uint64_t sh = 4 * (uint64_t)((int64_t)t1 * BC);
+            const uint64_t sa = 3 * sh;
+#pragma unroll
+            for (int m = 0; m < BPF; ++m) bpf[m] = gload4(i_addr[m] + (i_act[m] ? sa : sh));
+            return;
+        }
         const auto src = in_row(t1);
 #pragma unroll
         for (int m = 0; m < BPF; ++m) {
@@ -1333,7 +1453,10 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         } else {
             move_rows<THREADS, false>(stage, 5 * nt, C, HW, false, in_row(t1));
         }
-        if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, c_vec, dp_row(prev_t1));
+        if (prev_nt > 0) {
+            if (c_vec) store_dp(prev_t1, prev_nt);
+            else move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, false, dp_row(prev_t1));
+        }
         if (c_vec && t1 - kBwdChunk >= 1) load_b(t1 - kBwdChunk, min(kBwdChunk, t1 - kBwdChunk));
         lds_barrier();
         // One step.  The partial buffers alternate with tt (the barrier at
@@ -1389,7 +1512,10 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         prev_nt = nt;
     }
     lds_barrier();
-    if (prev_nt > 0) move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, c_vec, dp_row(prev_t1));
+    if (prev_nt > 0) {
+        if (c_vec) store_dp(prev_t1, prev_nt);
+        else move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, false, dp_row(prev_t1));
+    }
 }
 // [persistent kernel source: end]
 

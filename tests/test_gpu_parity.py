@@ -32,6 +32,7 @@ CASES = {
     "three_blocks": dict(B=3, C=72, n_x=36, K=5),      # 3 recurrent column blocks of 32, 2 channels per group
     "odd_channels": dict(B=2, C=37, n_x=3, K=4),       # C and n_x not multiples of 4: scalar moves
     "mfma_max": dict(B=64, C=320, n_x=128, K=3),       # the largest shape the MFMA step kernels take
+    "long_ragged_k": dict(B=3, C=64, n_x=12, K=37),    # whole chunks, then a ragged one, in both directions
 }
 MAX_SIZE = dict(B=1, C=2048, n_x=6144, K=2)            # CFC_MAX_C channels, n_in = CFC_MAX_N_IN
 
@@ -276,7 +277,7 @@ def test_kloop_equals_eager_step_calls(cfc, case, path):
 
 @pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input",
                                   "long_input64", "long_input48", "two_channel_groups", "three_blocks",
-                                  "odd_channels"])
+                                  "odd_channels", "long_ragged_k"])
 def test_all_kloop_paths_agree_bitwise(cfc, case):
     """Persistent kernel, VALU step kernels and MFMA step kernels: the same bits."""
     d = CASES[case]
