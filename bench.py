@@ -409,6 +409,26 @@ def bench_mlp(torch, timer, steps, trials, cpu_seconds):
                            "kind": "oracle", "sample": "%d whole steps, %.1f s" % (n, el)} if n else None}
 
 
+def cpu_reduce_baseline(budget_s):
+    """The oracle's reduce_axis0 (fp64 column sums of fp32 rows in b order,
+    one thread) on a [32, 2^20] sample until budget_s has passed: GB/s of
+    the same algorithmic bytes as the GPU figure, (B + 1) N 4."""
+    import oracle
+    B, N = 32, 1 << 20
+    x = np.random.default_rng(0).standard_normal((B, N), dtype=np.float32)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.reduce_axis0_f64(x)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    by = (B + 1) * N * 4
+    return {"GBps": round(n * by / el / 1e9, 2), "cores": 1, "kind": "oracle",
+            "sample": "%d calls on B=%d, N=%d (fp64 accumulation, one thread), %.1f s" % (n, B, N, el)}
+
+
 def cpu_baseline(x, budget_s):
     """The fp64 oracle, single thread, on whole training steps of the same
     configuration until budget_s has passed."""
@@ -660,6 +680,8 @@ def main():
         gate = [r for r in red if r["B"] * r["N"] * 4 >= 512 * 2 ** 20]
         result["reduce_axis0"] = {"shapes": red,
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}
+        if not args.no_cpu:
+            result["reduce_axis0"]["cpu_oracle"] = cpu_reduce_baseline(2.0)
 
     if not args.no_mlp:
         result["mlp"] = bench_mlp(torch, LaunchTimer(torch), 50, 5, 0.0 if args.no_cpu else args.cpu_seconds)
