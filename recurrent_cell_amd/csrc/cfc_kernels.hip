@@ -215,6 +215,12 @@ __global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
     const int64_t M = a.M;
     const int N = a.N;
 
+    // the bias first: its load overlaps the operand loads instead of
+    // following the MFMAs with a round trip of its own
+    float bias[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) bias[nt] = a.bias[min(n0 + 16 * nt + li, N - 1)];
+
     f32x4 acc[2][2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -273,9 +279,6 @@ __global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
                             __builtin_amdgcn_mfma_f32_16x16x4f32(av[kb][mt][c], bv[kb][nt][c], acc[mt][nt][c], 0, 0, 0);
     }
 
-    float bias[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bias[nt] = a.bias[min(n0 + 16 * nt + li, N - 1)];
     wait_vmem_all();   // so that no store below waits behind another
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -962,7 +965,19 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
             for (int e = 0; e < 4; ++e) dps[wr + 16 * mt + 4 * lk + e][wc + 16 * nt + li] = acc[mt][nt][e];
     __syncthreads();
     const bool vec_out = (n_in % 4 == 0) && ((((uintptr_t)a.gW_s) & 15u) == 0);
-    for (int u = threadIdx.x; u < kFillTile * (kFillTile / 4); u += kThreads) {
+    // every LDS read of the tile first, then the stores (one LDS wait, not one per store)
+    constexpr int kOut = kFillTile * (kFillTile / 4) / kThreads;
+    static_assert(kFillTile * (kFillTile / 4) % kThreads == 0, "whole output passes");
+    f32x4 ov[kOut];
+#pragma unroll
+    for (int m = 0; m < kOut; ++m) {
+        const int u = threadIdx.x + m * kThreads;
+        const int row = u / (kFillTile / 4);
+        ov[m] = *reinterpret_cast<const f32x4*>(&dps[row][4 * (u - row * (kFillTile / 4))]);
+    }
+#pragma unroll
+    for (int m = 0; m < kOut; ++m) {
+        const int u = threadIdx.x + m * kThreads;
         const int row = u / (kFillTile / 4);
         const int c4 = 4 * (u - row * (kFillTile / 4));
         const int r = r0 + row;
@@ -970,11 +985,11 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
         if (r < R3 && k < n_in) {
             float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in + k;
             if (vec_out && k + 4 <= n_in) {
-                __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&dps[row][c4]), reinterpret_cast<f32x4*>(dst));
+                __builtin_nontemporal_store(ov[m], reinterpret_cast<f32x4*>(dst));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (k + e < n_in) dst[e] = dps[row][c4 + e];
+                    if (k + e < n_in) dst[e] = ov[m][e];
             }
         }
     }
