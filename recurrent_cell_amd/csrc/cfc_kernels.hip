@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
 //                   completes the carry.
 // ---------------------------------------------------------------------------
 constexpr int kFwdChunk = 16;
-constexpr int kBwdChunk = 8;
+constexpr int kBwdChunk = 16;
 
 // 16-byte global load and store at a byte address (global address space:
 // a plain pointer made from an integer would be a flat access, which also
