@@ -323,6 +323,35 @@ def test_kloop_equals_its_phases(cfc, case, path):
         np.testing.assert_array_equal(bits(host(getattr(ph, k))), bits(host(getattr(g, k))), err_msg=k)
 
 
+@pytest.mark.parametrize("B,C,n_x,K", [(256, 128, 64, 64), (420, 100, 20, 37), (1400, 64, 0, 4)])
+def test_scratch_fill_large_batch_equals_slices(cfc, B, C, n_x, K):
+    """A sample's scratch depends on that sample alone: on large batches
+    (thousands of tiles, ragged tiles, the fma tail, n_x = 0) the
+    full-batch call equals calls on slices of 16 samples bit for bit, and
+    both match fp64 sums."""
+    say("scratch fill, large batch against slices", B, C, n_x, K)
+    n_in = n_x + C
+    dp = normal((K, B, 3 * C), 19, 1)
+    u = normal((K, B, n_x), 19, 2)
+    h_hist = normal((K + 1, B, C), 19, 3)
+    S = torch.full((B, 3, C, n_in), float("nan"), device="cuda")
+    Sb = torch.full((B, 3, C), float("nan"), device="cuda")
+    cfc.cfc_scratch_fill(dev(dp), dev(u), dev(h_hist), S, Sb)
+    S_ref = torch.full_like(S, float("nan"))
+    Sb_ref = torch.full_like(Sb, float("nan"))
+    for b0 in range(0, B, 16):
+        b1 = min(B, b0 + 16)
+        cfc.cfc_scratch_fill(dev(dp[:, b0:b1]), dev(u[:, b0:b1]), dev(h_hist[:, b0:b1]), S_ref[b0:b1], Sb_ref[b0:b1])
+    np.testing.assert_array_equal(bits(host(S)), bits(host(S_ref)))
+    np.testing.assert_array_equal(bits(host(Sb)), bits(host(Sb_ref)))
+    z = np.concatenate([u, h_hist[:-1]], axis=2).astype(np.float64)              # [K,B,n_in]
+    A = np.ascontiguousarray(dp.astype(np.float64).transpose(1, 2, 0))          # [B,3C,K]
+    Z = np.ascontiguousarray(z.transpose(1, 0, 2))                              # [B,K,n_in]
+    ref = np.matmul(A, Z).reshape(B, 3, C, -1)
+    mass = np.matmul(np.abs(A), np.abs(Z)).reshape(B, 3, C, -1)
+    assert_ok(check_grad("S", host(S), ref, mass))
+
+
 @pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "no_input"])
 def test_scratch_fill_matches_its_definition(cfc, case):
     """S[b,r,k] = sum_t dp[t,b,r] z_t[b,k], Sb[b,r] = sum_t dp[t,b,r] on
