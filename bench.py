@@ -464,8 +464,10 @@ def main():
                          "hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the K-loop would shard over the batch; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path.  The K-loop "
+              "would shard over the batch (B/G samples per GPU, W replicated), each GPU reducing its "
+              "own scratch, then one all-gather of the G partial gradients and a fixed-order sum of "
+              "them on every GPU.", file=sys.stderr)
         sys.exit(2)
 
     import torch
