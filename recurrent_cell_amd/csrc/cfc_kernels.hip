@@ -532,6 +532,9 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     // the wave's part, issued with the z loads below before any of them is
     // waited for.  Blocks past nxb / nhb load a clamped block, never used.
     const float* wrow = a.Wf + ((int64_t)q * C + min(c0 + li, C - 1)) * L.ldf;
+    // the bias first, in flight with the operand loads (loaded after the
+    // MFMAs it was a round trip of its own before the epilogue)
+    const float bias = a.bias[q * C + min(c0 + li, C - 1)];
     static_assert(kMfmaMaxNxb <= kMfmaMaxNhb, "one register block array serves both parts");
     f32x4 wv[kMfmaMaxNhb];
 #pragma unroll
@@ -614,7 +617,6 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
             }
         }
     }
-    const float bias = a.bias[q * C + min(c0 + li, C - 1)];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         // part 0: X = bias + ((x0 + x1) + (x2 + x3)); parts 1, 2: their half
