@@ -33,6 +33,11 @@ CASES = {
     "odd_channels": dict(B=2, C=37, n_x=3, K=4),       # C and n_x not multiples of 4: scalar moves
     "mfma_max": dict(B=64, C=320, n_x=128, K=3),       # the largest shape the MFMA step kernels take
     "long_ragged_k": dict(B=3, C=64, n_x=12, K=37),    # whole chunks, then a ragged one, in both directions
+    "single_step": dict(B=1, C=16, n_x=8, K=1),        # K = 1, one sample
+    "single_step_max_c": dict(B=3, C=128, n_x=64, K=1),  # K = 1 at the persistent kernel's largest C
+    "one_channel": dict(B=2, C=1, n_x=3, K=2),         # C = 1
+    "valu_c129": dict(B=65, C=129, n_x=4, K=2),        # one channel past the persistent kernel: VALU steps
+    "mfma_long_k": dict(B=64, C=132, n_x=4, K=17),     # MFMA step kernels over more steps than a chunk
 }
 MAX_SIZE = dict(B=1, C=2048, n_x=6144, K=2)            # CFC_MAX_C channels, n_in = CFC_MAX_N_IN
 
@@ -277,7 +282,8 @@ def test_kloop_equals_eager_step_calls(cfc, case, path):
 
 @pytest.mark.parametrize("case", ["tiny", "pages", "ragged_scalar", "three_tiles", "sample_tiles", "no_input",
                                   "long_input64", "long_input48", "two_channel_groups", "three_blocks",
-                                  "odd_channels", "long_ragged_k"])
+                                  "odd_channels", "long_ragged_k", "single_step", "single_step_max_c",
+                                  "one_channel", "mfma_long_k"])
 def test_all_kloop_paths_agree_bitwise(cfc, case):
     """Persistent kernel, VALU step kernels and MFMA step kernels: the same bits."""
     d = CASES[case]
