@@ -7,6 +7,8 @@ The pages print no worked numeric example of the cell, so the oracle is pinned b
     RNN, which torch.nn.RNN computes (forward, and autograd gradients);
     with the gate driven to 0 or 1 by a large f-bias the cell follows one
     head alone, which pins the gate's sign and the head order;
+  * the closed form of a single step (K = 1: no carry; the gradients are
+    outer products of the written-out dp with z), computed here with numpy;
   * exact special cases (gate = 0.5 exactly when a_f = 0; gW_f = 0 exactly
     when the g and h heads coincide), invariants (gate in (0,1), |h_t| <= 1),
     descent of the loss along -grad, linearity over the batch;
@@ -159,6 +161,38 @@ def test_descent_along_negative_gradient(oracle_mod):
         # first-order prediction of the decrease holds to second order
         pred = eta * gnorm ** 2
         assert abs((r["loss"] - l1) - pred) <= 0.05 * pred
+
+
+def test_single_step_gradients_match_the_closed_form(oracle_mod):
+    """At K = 1 there is no carry.  With z = [u_1; h_0], a_q = W_q z + b_q,
+    gate = 1 / (1 + e^{a_f}), g = tanh a_g, hh = tanh a_h, h = gate g + (1 - gate) hh
+    and r = h - y, the per-sample pre-activation gradients are
+      dp_f = r (g - hh) (-gate (1 - gate)),  dp_g = r gate (1 - g^2),
+      dp_h = r (1 - gate) (1 - hh^2),
+    the weight gradients their outer products with z summed over the batch,
+    gb_q the sums of dp_q, dh0 the recurrent columns of sum_q W_q^T dp_q and
+    the loss 0.5 sum r^2 -- written out here with numpy, not the oracle's code."""
+    B, C, n_x = 5, 7, 3
+    x = cfc_inputs(B=B, C=C, n_x=n_x, K=1, seed=21, bias_scale=0.3)
+    u, y, h0, W, bias = (a.astype(np.float64) for a in (x.u, x.y, x.h0, x.W, x.bias))
+    z = np.concatenate([u[0], h0], axis=1)                         # [B, n_in]
+    a = np.einsum("qck,bk->qbc", W, z) + bias[:, None, :]          # [3, B, C]
+    gate, g, hh = 1.0 / (1.0 + np.exp(a[0])), np.tanh(a[1]), np.tanh(a[2])
+    h = gate * g + (1.0 - gate) * hh
+    r = h - y[0]
+    dp = np.stack([r * (g - hh) * (-gate * (1.0 - gate)),
+                   r * gate * (1.0 - g ** 2),
+                   r * (1.0 - gate) * (1.0 - hh ** 2)])            # [3, B, C]
+    gW = np.einsum("qbc,bk->qck", dp, z)
+    gb = dp.sum(axis=1)
+    dh0 = np.einsum("qck,qbc->bk", W, dp)[:, n_x:]
+    out = oracle_mod.train(x.u, x.y, x.h0, x.W, x.bias, "f64")
+    np.testing.assert_allclose(out["h_hist"][1], h, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(out["act"][0], np.stack([gate, g, hh]), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(out["gW"], gW, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["gb"], gb, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["dh0"], dh0, rtol=1e-12, atol=1e-14)
+    assert abs(out["loss"] - 0.5 * (r ** 2).sum()) <= 1e-12 * (r ** 2).sum()
 
 
 def test_batch_linearity_and_per_sample_scratch(oracle_mod):
