@@ -196,6 +196,21 @@ def test_input_projection_matches_oracle(cfc, oracle_mod, case):
     assert_ok(check_grad("X", X, ref, mass))
 
 
+@pytest.mark.parametrize("case,rows", [("wide", 37), ("wide", 256), ("wide", 4000), ("odd_channels", 5)])
+def test_input_projection_rows_do_not_depend_on_the_launch(cfc, case, rows):
+    """Each row of X has one canonical value: the first rows projected on
+    their own (a small grid, a ragged last row tile) equal the same rows of
+    the full call (the wide shape's 16,384 rows), bit for bit."""
+    d = CASES[case]
+    say("input projection rows", case, rows)
+    x = cfc_inputs(**d, seed=18, bias_scale=0.5)
+    u = dev(x.u).reshape(-1, d["n_x"])
+    W, bias = dev(x.W), dev(x.bias)
+    full = host(cfc.cfc_input_projection(u, W, bias))
+    part = host(cfc.cfc_input_projection(u[:rows].contiguous(), W, bias))
+    np.testing.assert_array_equal(bits(part), bits(full[:rows]))
+
+
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "three_blocks", "odd_channels"])
 def test_recurrence_composes_to_fwd_bwd(cfc, case):
     """cfc_input_projection then cfc_kloop_recurrence gives the bits of
