@@ -139,8 +139,10 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *  - step kernels (any C): 2K step launches, the fill and the reduction,
  *    captured once as a HIP graph per (device, pointers, sizes) and replayed
  *    on later calls with the same key.  Calls sharing a key must be issued
- *    on one stream at a time.
- * cfc_set_kloop_mode() can force either path.  K == 0 or B == 0 writes
+ *    on one stream at a time.  At most 64 graphs are cached; the least
+ *    recently used one is evicted and destroyed by a later call once its
+ *    last replay has completed (the call never waits for it).
+ * cfc_set_kloop_mode() can force either path for the calling thread.  K == 0 or B == 0 writes
  * h_hist[0] = h0 and zeros to the scratch and gradients.
  */
 int cfc_train_kloop(const float* u, const float* y, const float* h0,
@@ -253,7 +255,9 @@ int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist,
  * Returns 0 for invalid sizes. */
 size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K);
 
-/* Path selection of cfc_train_kloop for the whole process.
+/* Path selection of cfc_train_kloop, cfc_kloop_fwd_bwd and cfc_kloop_path
+ * for the CALLING THREAD (each thread starts in CFC_KLOOP_AUTO; a setting
+ * never affects the calls of another thread).
  * CFC_KLOOP_AUTO (default): the persistent kernel when C <= 128; otherwise
  *   the step kernels, on MFMA when B >= 64 and the shape fits them (C <= 320
  *   and n_x <= 128, both multiples of 4; 16-byte aligned arrays), else on
@@ -273,7 +277,8 @@ enum cfc_kloop_mode {
 };
 int cfc_set_kloop_mode(int mode);
 
-/* The path cfc_train_kloop takes for these sizes under the current mode:
+/* The path cfc_train_kloop takes for these sizes under the calling thread's
+ * mode:
  * CFC_KLOOP_PERSISTENT, CFC_KLOOP_STEPS_VALU or CFC_KLOOP_STEPS_MFMA (the
  * workspace is assumed 16-byte aligned); -1 for invalid sizes or a forced
  * path the sizes cannot take. */

@@ -3,7 +3,6 @@
 // K-loop training step.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -13,6 +12,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <vector>
 
 #include "../../include/cfc.h"
 #include "api_common.h"
@@ -136,7 +136,9 @@ struct KloopArgs {
 // K-loop paths: step kernels on VALU, step kernels on MFMA, persistent.
 enum class Path { Steps = 0, StepsMfma = 1, Persistent = 2 };
 
-std::atomic<int> g_kloop_mode{CFC_KLOOP_AUTO};
+// The path mode of the calling thread (cfc_set_kloop_mode): per thread, so
+// that one caller forcing a path never changes another thread's calls.
+thread_local int g_kloop_mode = CFC_KLOOP_AUTO;
 
 // Smallest batch for which the automatic choice takes the MFMA step kernels
 // (a 16-sample MFMA tile wastes most of its rows below this).
@@ -291,15 +293,38 @@ std::mutex g_mu;
 std::map<GraphKey, GraphEntry> g_graphs;
 std::map<int, hipStream_t> g_capture_streams;
 uint64_t g_clock = 0;
+// Evicted graphs whose last replay may still be running: destroyed by a later
+// call once their completion event reports done, so that no call of the
+// K-loop ever waits on the device.
+std::vector<GraphEntry> g_retired;
 
-void destroy_entry(GraphEntry& e)
+void release_entry(GraphEntry& e)
 {
-    if (e.done) {
-        (void)hipEventSynchronize(e.done);
-        (void)hipEventDestroy(e.done);
-    }
+    if (e.done) (void)hipEventDestroy(e.done);
     if (e.exec) (void)hipGraphExecDestroy(e.exec);
     e = GraphEntry{};
+}
+
+// Blocking destruction, for cfc_clear_graph_cache only.
+void destroy_entry(GraphEntry& e)
+{
+    if (e.done) (void)hipEventSynchronize(e.done);
+    release_entry(e);
+}
+
+// Destroy the retired graphs whose last replay has completed; the others
+// stay retired.  Never blocks (hipEventQuery only asks).
+void reap_retired()
+{
+    size_t keep = 0;
+    for (size_t i = 0; i < g_retired.size(); ++i) {
+        GraphEntry& e = g_retired[i];
+        if (!e.done || hipEventQuery(e.done) == hipSuccess)
+            release_entry(e);
+        else
+            g_retired[keep++] = e;
+    }
+    g_retired.resize(keep);
 }
 
 int build_graph(const KloopArgs& k, Path path, const cfc::StepPlan& p, int dev, GraphEntry& out)
@@ -418,7 +443,7 @@ int cfc_set_kloop_mode(int mode)
     cfc_host::last_error().clear();
     if (mode < CFC_KLOOP_AUTO || mode > CFC_KLOOP_STEPS_MFMA)
         return fail(CFC_EINVAL, "cfc_set_kloop_mode: unknown mode %d", mode);
-    g_kloop_mode.store(mode);
+    g_kloop_mode = mode;
     return CFC_OK;
 }
 
@@ -426,7 +451,7 @@ int cfc_kloop_path(int B, int C, int n_x, int K)
 {
     if (B < 0 || K < 0 || C < 1 || n_x < 0) return -1;
     Path path;
-    if (!choose_path(g_kloop_mode.load(), B, C, n_x, {}, &path)) return -1;
+    if (!choose_path(g_kloop_mode, B, C, n_x, {}, &path)) return -1;
     return path == Path::Persistent ? CFC_KLOOP_PERSISTENT
          : path == Path::StepsMfma  ? CFC_KLOOP_STEPS_MFMA : CFC_KLOOP_STEPS_VALU;
 }
@@ -465,7 +490,7 @@ static int check_kloop(const char* fn, const float* u, const float* y, const flo
     for (int i = 0; i < 7; ++i)
         for (int j = i + 1; j < 7; ++j)
             if (overlap(outs[i], outs[j])) return fail(CFC_EINVAL, "%s: outputs overlap", fn);
-    const int mode = g_kloop_mode.load();
+    const int mode = g_kloop_mode;
     if (!choose_path(mode, B, C, n_x, {ws, u, y, h0, h_hist, act}, path)) {
         if (mode == CFC_KLOOP_PERSISTENT)
             return fail(CFC_EINVAL, "%s: the persistent kernel holds C <= 128 channels (C=%d)", fn, C);
@@ -512,13 +537,16 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
     const GraphKey key{dev, (int)path, u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch,
                        gW, gb, B, C, n_x, K};
     std::lock_guard<std::mutex> lock(g_mu);
+    reap_retired();
     auto it = g_graphs.find(key);
     if (it == g_graphs.end()) {
         if (g_graphs.size() >= kMaxGraphs) {
+            // the least recently used graph leaves the cache; it is destroyed
+            // by a later call once its last replay has completed
             auto victim = g_graphs.begin();
             for (auto j = g_graphs.begin(); j != g_graphs.end(); ++j)
                 if (j->second.last_use < victim->second.last_use) victim = j;
-            destroy_entry(victim->second);
+            g_retired.push_back(victim->second);
             g_graphs.erase(victim);
         }
         GraphEntry e;
@@ -852,6 +880,8 @@ int cfc_clear_graph_cache(void)
     std::lock_guard<std::mutex> lock(g_mu);
     for (auto& kv : g_graphs) destroy_entry(kv.second);
     g_graphs.clear();
+    for (auto& e : g_retired) destroy_entry(e);
+    g_retired.clear();
     return CFC_OK;
 }
 

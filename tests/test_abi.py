@@ -170,6 +170,55 @@ def test_workspace_size_and_path_queries(L):
     assert L.cfc_kloop_path(32, 128, 64, 64) == P
 
 
+def test_path_mode_is_per_thread(L):
+    """A mode set on one thread leaves every other thread's path alone: each
+    thread starts in the automatic mode, and the setting of one thread is not
+    seen by calls made on another (no process-wide path state)."""
+    import threading
+    P, VALU = 2, 3
+    seen = {}
+    go = threading.Event()
+    done = threading.Event()
+
+    def other():
+        seen["before"] = L.cfc_kloop_path(32, 128, 64, 64)
+        go.wait(10)
+        seen["after"] = L.cfc_kloop_path(32, 128, 64, 64)
+        assert L.cfc_set_kloop_mode(2) == 0          # forces persistent on this thread only
+        seen["own"] = L.cfc_kloop_path(4, 129, 0, 4)
+        done.set()
+
+    th = threading.Thread(target=other)
+    th.start()
+    try:
+        assert L.cfc_set_kloop_mode(3) == 0              # VALU forced on the main thread
+        assert L.cfc_kloop_path(32, 128, 64, 64) == VALU
+        go.set()
+        assert done.wait(10)
+        th.join(10)
+        assert seen == {"before": P, "after": P, "own": -1}
+        assert L.cfc_kloop_path(4, 129, 0, 4) == VALU     # the other thread's setting is not seen here
+    finally:
+        assert L.cfc_set_kloop_mode(0) == 0
+
+
+def test_graph_cache_never_waits_on_the_device():
+    """The K-loop's graph cache evicts without blocking: destruction of an
+    evicted graph is deferred until its completion event reports done, so no
+    call path of cfc_train_kloop reaches a host synchronisation."""
+    text = open(os.path.join(ROOT, "recurrent_cell_amd", "csrc", "cfc_api.hip")).read()
+    body = text[text.index("int cfc_train_kloop("):]
+    body = body[:body.index("\n}\n")]
+    assert "Synchronize" not in body and "destroy_entry" not in body
+    reap = text[text.index("void reap_retired()"):]
+    reap = reap[:reap.index("\n}\n")]
+    assert "hipEventQuery" in reap and "Synchronize" not in reap
+    # the one blocking destruction is reachable only from cfc_clear_graph_cache
+    callers = [m.start() for m in re.finditer(r"destroy_entry\(", text)]
+    clear = text.index("int cfc_clear_graph_cache(")
+    assert all(c > clear for c in callers[1:]), "destroy_entry called outside cfc_clear_graph_cache"
+
+
 def test_no_atomics_in_kernel_sources():
     """Device code (kernels and the shared device math) uses no atomics."""
     csrc = os.path.join(ROOT, "recurrent_cell_amd", "csrc")
