@@ -15,8 +15,14 @@ Also measured in the same run:
   * the same step on the 2K-launch step-kernel path, for contrast;
   * graph-node latency (a graph of dependent one-element kernels), which
     gives the step's latency roofline;
+  * the other two K-loop configurations (tiny B=4 C=16 n_x=8 K=4, and wide
+    B=256 C=256 n_x=128 K=64) with their own rooflines, under "workloads";
   * reduce_axis0 GB/s on the standalone [B, N] shapes;
-  * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
+  * the batched MLP step and AdamW;
+  * the CPU oracle on the host (cpu_baseline): fp64 and fp32 on one thread
+    and fp32 on every usable host thread, for each K-loop configuration (the
+    wide one on a bounded sample of its samples), and the reduction's column
+    sums on one and on every thread.
 """
 import argparse
 import json
@@ -397,59 +403,309 @@ def bench_mlp(torch, timer, steps, trials, cpu_seconds):
             "frac": round(big["TFLOPs"] * 1e12 / FP32_PEAK, 4), "traffic": None,
             "kernel": "gemm_mfma_kernel (layer 1 forward, [16384 x 256] x [256 x 256])",
             "flops_per_launch": big["flops"], "launch_us": big["us"]}
-    n, el = 0, 0.0
+    cpu = None
     if cpu_seconds > 0:
+        # the numpy fp64 oracle with its BLAS on one thread, then on every
+        # usable thread (threadpoolctl sets the BLAS pool)
+        from threadpoolctl import threadpool_limits
         from oracle.mlp_oracle import mlp_train_step as oracle_step
-        t0 = time.perf_counter()
-        while True:
-            oracle_step(x.X, x.T, x.W, x.b)
-            n += 1
-            if time.perf_counter() - t0 >= min(cpu_seconds, 5.0):
-                break
-        el = time.perf_counter() - t0
+        cpu = {}
+        for key, th in (("fp64_1t", 1), ("fp64_all", host_threads())):
+            with threadpool_limits(limits=th):
+                n = 0
+                t0 = time.perf_counter()
+                while True:
+                    oracle_step(x.X, x.T, x.W, x.b)
+                    n += 1
+                    if time.perf_counter() - t0 >= min(cpu_seconds, 4.0):
+                        break
+                el = time.perf_counter() - t0
+            cpu[key] = {"value": round(n / el, 3), "unit": "train-steps/s", "cores": th, "kind": "oracle",
+                        "sample": "%d whole steps, numpy fp64, BLAS on %d thread(s), %.1f s" % (n, th, el)}
     return {"workload": "batched MLP train step (forward, MSE loss, backward, every gradient), one mlp_train_step "
                         "call", "B": B, "dims": dims, "value": round(1000.0 / ms, 2), "unit": "train-steps/s",
             "ms_per_step": round(ms, 5), "trials_ms": [round(v, 5) for v in res], "flops_per_step": fl,
             "step_TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2), "step_frac_fp32_peak": round(fl / (ms * 1e-3) /
                                                                                          FP32_PEAK, 4),
-            "roofline": roof, "launches": kt,
-            "cpu_oracle": {"value": round(n / el, 3), "unit": "train-steps/s", "cores": "numpy fp64 (BLAS threads)",
-                           "kind": "oracle", "sample": "%d whole steps, %.1f s" % (n, el)} if n else None}
+            "roofline": roof, "launches": kt, "cpu_oracle": cpu}
 
 
-def cpu_reduce_baseline(budget_s):
-    """The oracle's reduce_axis0 (fp64 column sums of fp32 rows in b order,
-    one thread) on a [32, 2^20] sample until budget_s has passed: GB/s of
-    the same algorithmic bytes as the GPU figure, (B + 1) N 4."""
-    import oracle
-    B, N = 32, 1 << 20
-    x = np.random.default_rng(0).standard_normal((B, N), dtype=np.float32)
+def _oracle_steps_per_s(oracle, x, precision, threads, budget_s, batch=None):
+    """Whole training steps of the oracle per second on `threads` host threads
+    (at least one call, then until budget_s has passed).  With batch=b', the
+    first b' samples of the workload stand in for all B (samples are
+    independent, so the per-step work is linear in B) and the rate is scaled
+    by b'/B.  Returns (steps/s of the full workload, calls, seconds, threads used)."""
+    B = x.h0.shape[0]
+    u, y, h0 = x.u, x.y, x.h0
+    if batch is not None and batch < B:
+        u, y, h0 = (np.ascontiguousarray(a) for a in (x.u[:, :batch], x.y[:, :batch], x.h0[:batch]))
+    else:
+        batch = B
+    args = (u, y, h0, x.W, x.bias)
+    oracle.set_threads(threads)
+    used = oracle.threads()
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.reduce_axis0_f64(x)
+        oracle.train(*args, precision)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    by = (B + 1) * N * 4
-    return {"GBps": round(n * by / el / 1e9, 2), "cores": 1, "kind": "oracle",
-            "sample": "%d calls on B=%d, N=%d (fp64 accumulation, one thread), %.1f s" % (n, B, N, el)}
+    return n / el * batch / B, n, el, used
 
 
-def cpu_baseline(x, budget_s):
-    """The fp64 oracle, single thread, on whole training steps of the same
-    configuration until budget_s has passed."""
+def host_threads():
+    """Host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS where that is set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baselines(configs, budget_s):
+    """The oracle as it stands (plain C, gcc -O2, OpenMP over samples only),
+    timed on the host beside the GPU: fp64 and fp32 on one thread and fp32 on
+    every usable thread, for the tiny, pages and wide configurations (the wide
+    one on a bounded sample of its samples), plus the batch-axis reduction's
+    fp64 column sums on one thread and split over columns on every thread."""
     import oracle
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.train(x.u, x.y, x.h0, x.W, x.bias, "f64")
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return n, el
+    from recurrent_cell_amd.inputs import cfc_inputs
+    allt = host_threads()
+    before = oracle.threads()
+    out = {"host_threads": allt}
+    try:
+        for name, plan in (("pages", [("fp64_1t", "f64", 1, None), ("fp32_1t", "f32", 1, None),
+                                      ("fp32_all", "f32", allt, None)]),
+                           ("tiny", [("fp32_1t", "f32", 1, None), ("fp32_all", "f32", allt, None)]),
+                           ("wide", [("fp32_1t", "f32", 1, 8), ("fp32_all", "f32", allt, 8 * allt)])):
+            d = configs[name]
+            x = cfc_inputs(**d, seed=0)
+            rows = {}
+            for key, prec, th, batch in plan:
+                v, n, el, used = _oracle_steps_per_s(oracle, x, prec, th, budget_s, batch)
+                b = d["B"] if batch is None or batch >= d["B"] else batch
+                rows[key] = {"value": round(v, 4), "unit": "train-steps/s", "cores": used, "kind": "oracle",
+                             "sample": "%d whole train steps (B=%d C=%d n_x=%d K=%d), %s oracle, %d thread(s), "
+                                       "%.1f s%s" % (n, b, d["C"], d["n_x"], d["K"], prec, used, el,
+                                                     "" if b == d["B"] else
+                                                     "; %d of the %d samples, rate scaled by %d/%d" %
+                                                     (b, d["B"], b, d["B"]))}
+            out[name] = rows
+        B, N = 32, 1 << 20
+        xr = np.random.default_rng(0).standard_normal((B, N), dtype=np.float32)
+        by = (B + 1) * N * 4
+        red = {}
+        for key, th in (("fp64_1t", 1), ("fp64_all", allt)):
+            oracle.set_threads(th)
+            used = oracle.threads()
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                oracle.reduce_axis0_f64(xr)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= min(budget_s, 2.0):
+                    break
+            red[key] = {"GBps": round(n * by / el / 1e9, 2), "cores": used, "kind": "oracle",
+                        "sample": "%d calls on B=%d, N=%d (fp64 column sums in b order, columns split over %d "
+                                  "thread(s)), %.1f s" % (n, B, N, used, el)}
+        out["reduce_axis0"] = red
+    finally:
+        oracle.set_threads(before)
+    return out
+
+
+PATH_NAMES = {2: "persistent", 3: "steps_valu", 4: "steps_mfma"}
+
+
+def step_roofline(path, B, C, n_x, K, ms_per_step, t_node):
+    """The step against its bounds.  The persistent path's headline ratio is
+    the critical path at the non-packed fp32 rate: the 2K recurrence steps of
+    a sample run in order on one CU, so they are bounded by one CU's rate, not
+    the chip's; the parallel kernels by their whole-chip floors; plus one node
+    latency per launch.  SURVEY's formula (node latencies plus the whole-chip
+    floor of the flops or bytes) is given beside it, over this path's launches
+    and, as context only, over the pages' 2K + 3 dependent launches."""
+    bytes_min, flops = step_bytes_flops(B, C, n_x, K)
+    nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3}[path]
+    t_formula = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
+    pages_nodes = 2 * K + 3
+    t_pages = pages_nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
+    r = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3), "flops": flops, "bytes_min": bytes_min}
+    if path == "persistent":
+        cu_clk = 2.4e9
+        t_rec = recurrence_flops(B, C, K) / B / (256 * cu_clk)
+        par_flops = projection_flops(B, C, n_x, K) + 2 * K * B * 3 * C * (n_x + C)
+        par_bytes = fill_bytes(B, C, n_x, K) + 4 * (B + 1) * 3 * C * (n_x + C) + 4 * K * B * (n_x + 3 * C)
+        t_par = max(par_flops / FP32_PEAK, par_bytes / HBM_PEAK)
+        t_np = nodes * t_node + 2 * t_rec + t_par
+        t_pk = nodes * t_node + t_rec + t_par
+        r.update({"roof": "critical path: per-CU recurrence at the non-packed fp32 rate (128 flop/clk/CU at "
+                          "2.4 GHz) + parallel kernels at whole-chip floors + one node latency per launch",
+                  "t_roof_ms": round(t_np * 1e3, 4), "step_over_roof": round(ms_per_step / (t_np * 1e3), 3),
+                  "recurrence_floor_nonpacked_us": round(2 * t_rec * 1e6, 2),
+                  "parallel_floor_us": round(t_par * 1e6, 2),
+                  "packed_rate_roof_ms": round(t_pk * 1e3, 4),
+                  "step_over_packed_rate_roof": round(ms_per_step / (t_pk * 1e3), 3)})
+    else:
+        r.update({"roof": "node latencies of this path's launches + whole-chip floor of the step's flops or bytes",
+                  "t_roof_ms": round(t_formula * 1e3, 4), "step_over_roof": round(ms_per_step / (t_formula * 1e3), 3)})
+    r["context"] = {"whole_chip_formula_ms": round(t_formula * 1e3, 4),
+                    "step_over_whole_chip_formula": round(ms_per_step / (t_formula * 1e3), 3),
+                    "pages_graph_nodes": pages_nodes, "pages_graph_roof_ms": round(t_pages * 1e3, 4),
+                    "step_over_pages_graph_roof": round(ms_per_step / (t_pages * 1e3), 3),
+                    "note": "the pages-graph figure charges the pages' 2K + 3 dependent launches, which this "
+                            "path does not run when it is the persistent one: context only"}
+    return r
+
+
+def kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload):
+    """Roofline object of the K-loop's dominant kernel from live timings kt."""
+    n_in = n_x + C
+    if path == "persistent":
+        dur = kt["recurrence"]["mean_s"]
+        fl = recurrence_flops(B, C, K)
+        achieved = fl / dur
+        traffic = measured_traffic() if workload == "pages" else None
+        valu_busy = measured_valu_busy() if workload == "pages" else None
+        # what the kernel can use: one CU per sample (B of 256), fp32 FMA
+        # without packed math (4 SIMDs x 16 lanes x 2 flop per clock; half
+        # the 256 flop per clock per CU of the published peak)
+        usable = min(B, 256) * 2.4e9 * 4 * 16 * 2
+        # the same rate measured: the FMA-chain probe on B workgroups of the
+        # kernel's 512 lanes, one per CU, and on all 256 CUs
+        meas_b = fma_rate(torch, cfc, min(B, 256))
+        meas_chip = fma_rate(torch, cfc, 256)
+        return {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+                "kernel": "kloop_persist_kernel", "flops_per_launch": fl,
+                "launch_us": round(dur * 1e6, 3),
+                "usable_peak": round(usable / 1e12, 3),
+                "frac_of_usable": round(achieved / usable, 4),
+                "usable_note": "one CU per sample (a sample's steps are sequential), non-packed fp32 FMA",
+                "usable_peak_measured": round(meas_b / 1e12, 3),
+                "frac_of_usable_measured": round(achieved / meas_b, 4),
+                "fma_probe_chip_TFLOPs": round(meas_chip / 1e12, 2),
+                "fma_probe_chip_GHz": round(meas_chip / (256 * 128) / 1e9, 3),
+                "fma_probe_note": "v_fma_f32 chains, 512 lanes per workgroup, one workgroup per CU; "
+                                  "GHz = chip rate / (256 CUs x 128 flop/clk)",
+                "traffic_GBps": round(traffic / dur / 1e9, 1) if traffic else None,
+                "traffic_frac_of_hbm_peak": round(traffic / dur / HBM_PEAK, 4) if traffic else None,
+                "valu_busy_rocprof": valu_busy,
+                "valu_busy_note": "SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES over the kernel's CUs "
+                                  "(profiles/kloop_persist_pages_valu.md)"}
+    if path == "steps_mfma":
+        # the 2K step launches of the K-loop (and the one W re-layout), per launch on average
+        dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
+        fl = K * B * 3 * C * (n_in + C) * 2 // (2 * K)
+        achieved = fl / dur
+        return {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
+                "kernel": "fwd_mfma_kernel + bwd_mfma_kernel (average over the 2K step launches)",
+                "flops_per_launch": fl, "launch_us": round(dur * 1e6, 3)}
+    dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
+    fl = K * B * 3 * C * (n_in + C) * 2 // (2 * K)
+    achieved = fl / dur
+    return {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
+            "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
+            "kernel": "fwd_step_kernel + bwd_step_kernel (average over the 2K step launches)",
+            "flops_per_launch": fl, "launch_us": round(dur * 1e6, 3)}
+
+
+def bench_kloop(torch, cfc, workload, steps, warmup, trials, t_node, detail):
+    """One configuration of the K-loop: train steps/s of cfc_train_kloop, the
+    live per-kernel timings and the roofline objects.  detail=True adds the
+    contrast path, the GEMM-form step and the single-step kernels."""
+    from recurrent_cell_amd.inputs import CONFIGS, cfc_inputs
+    d = CONFIGS[workload]
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    n_in = n_x + C
+    x = cfc_inputs(**d, seed=0)
+    t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    path = PATH_NAMES[cfc.cfc_kloop_path(B, C, n_x, K)]
+    out = cfc.cfc_train_kloop(*t)
+    ms_per_step, trials_ms = time_steps(torch, cfc, t, out, steps, warmup, trials)
+    res = {"workload": workload, "B": B, "C": C, "n_x": n_x, "n_in": n_in, "K": K, "path": path,
+           "value": round(1000.0 / ms_per_step, 2), "unit": "train-steps/s", "ms_per_step": round(ms_per_step, 5),
+           "trials_ms": [round(v, 5) for v in trials_ms]}
+
+    timer = LaunchTimer(torch)
+    kt = {}
+    n_rep = 20 if K * B * C * n_in < (1 << 26) else 5
+    kt["fwd_bwd"] = timer(lambda: cfc.cfc_kloop_fwd_bwd(*t, out=out), n_rep)
+    if path == "persistent":
+        X = torch.empty((K, B, 3 * C), device="cuda")
+        kt["input_projection"] = timer(lambda: cfc.cfc_input_projection(t[0], t[3], t[4], X), 50)
+        kt["recurrence"] = timer(lambda: cfc.cfc_kloop_recurrence(X, t[1], t[2], t[3], out=out), 20)
+    dp = out.ws[:K * B * 3 * C].view(K, B, 3 * C)
+    kt["scratch_fill"] = timer(lambda: cfc.cfc_scratch_fill(dp, t[0], out.h_hist, out.gW_scratch,
+                                                            out.gb_scratch), 20)
+    gW_flat = out.gW_scratch.view(B, -1)
+    red_out = torch.empty(3 * C * n_in, device="cuda")
+    kt["reduce_axis0"] = timer(lambda: cfc.reduce_axis0(gW_flat, red_out), 20)
+
+    if detail:
+        # another path on the same inputs, for contrast: the step kernels after
+        # the persistent path; the other step-kernel variant after a step path
+        modes = {"persistent": cfc.KLOOP_STEPS, "steps_mfma": cfc.KLOOP_STEPS_VALU,
+                 "steps_valu": cfc.KLOOP_STEPS_MFMA}
+        cfc.cfc_set_kloop_mode(modes[path])
+        try:
+            taken = cfc.cfc_kloop_path(B, C, n_x, K)
+            if taken >= 0:
+                out_c = cfc.cfc_train_kloop(*t)
+                ms_c, _ = time_steps(torch, cfc, t, out_c, max(20, steps // 10), 5, 3)
+                res["contrast"] = {"path": PATH_NAMES[taken], "ms_per_step": round(ms_c, 5)}
+                del out_c
+        finally:
+            cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+        # the K-loop step with the GEMM-form weight gradient in place of scratch + reducer
+        og = cfc.cfc_train_kloop_gemm(*t)
+        ms_g, _ = time_calls(torch, lambda: cfc.cfc_train_kloop_gemm(*t, out=og), max(20, steps // 5), 5, 3)
+        res["gemm_form_weight_grad_ms_per_step"] = round(ms_g, 5)
+        gws = torch.empty(cfc.lib().cfc_weight_grad_gemm_workspace_bytes(B, C, n_x, K) // 4 + 1, device="cuda")
+        gWg, gbg = torch.empty((3, C, n_in), device="cuda"), torch.empty((3, C), device="cuda")
+        kt["weight_grad_gemm"] = timer(lambda: cfc.cfc_weight_grad_gemm(dp, t[0], out.h_hist, gWg, gbg, gws), 50)
+        # single-step kernels (the ABI calls, per-step += into the scratch)
+        S = torch.zeros((B, 3, C, n_in), device="cuda")
+        Sb = torch.zeros((B, 3, C), device="cuda")
+        dh = [torch.zeros((B, C), device="cuda") for _ in range(2)]
+        h_hist, act = out.h_hist, out.act
+        it = [0]
+
+        def fwd():
+            k = it[0] % K
+            cfc.cfc_fwd_step(t[0][k], h_hist[k], t[3], t[4], h_t=h_hist[k + 1], act_t=act[k])
+            it[0] += 1
+
+        def bwd():
+            k = K - 1 - it[0] % K
+            cfc.cfc_bwd_step(t[0][k], h_hist[k], h_hist[k + 1], t[1][k], t[3], act[k], dh[it[0] % 2], S, Sb,
+                             dh_out=dh[(it[0] + 1) % 2])
+            it[0] += 1
+        kt["fwd_step"] = timer(fwd, 2 * K)
+        it[0] = 0
+        kt["bwd_step"] = timer(bwd, 2 * K)
+        del S, Sb
+    cfc.cfc_train_kloop(*t, out=out)   # restore the step's own state
+    torch.cuda.synchronize()
+    res["kernels"] = {k: dict(mean_us=round(v["mean_s"] * 1e6, 3), median_us=round(v["median_s"] * 1e6, 3),
+                              gap_median_us=round(v["gap_median_us"], 3)) for k, v in kt.items()}
+    res["roofline"] = kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload)
+    res["step_roofline"] = step_roofline(path, B, C, n_x, K, ms_per_step, t_node)
+    if detail:
+        res["deterministic_3_runs"] = deterministic_runs(torch, cfc, t)
+    del out
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -458,15 +714,20 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--trials", type=int, default=7)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.5, help="seconds per CPU-oracle measurement")
     ap.add_argument("--no-reduce", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
-    ap.add_argument("--workload", default="pages", choices=["tiny", "pages", "wide"])
-    ap.add_argument("--no-steps-path", action="store_true", help="skip the step-kernel path contrast")
+    ap.add_argument("--workload", default="pages", choices=["tiny", "pages", "wide"],
+                    help="the configuration of the headline line")
+    ap.add_argument("--no-other-workloads", action="store_true", help="skip the tiny and wide legs")
     ap.add_argument("--no-mlp", action="store_true", help="skip the batched MLP step")
-    ap.add_argument("--no-gemm-form", action="store_true", help="skip the GEMM-form weight-gradient step")
+    ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW timings")
     ap.add_argument("--only-mlp", action="store_true", help="run and print only the batched MLP step")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the headline workload's train step only (for profiling runs)")
+    ap.add_argument("--no-kernels", action="store_true", help="same as --only-step")
+    ap.add_argument("--no-steps-path", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-gemm-form", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size reference for "
                          "hardware byte counters)")
@@ -498,215 +759,83 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    x = cfc_inputs(**d, seed=0)
-    t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]
-    names = {cfc.KLOOP_PERSISTENT: "persistent", cfc.KLOOP_STEPS_VALU: "steps_valu",
-             cfc.KLOOP_STEPS_MFMA: "steps_mfma"}
-    path = names[cfc.cfc_kloop_path(B, C, n_x, K)]
-    out = cfc.cfc_train_kloop(*t)
-    ms_per_step, trials = time_steps(torch, cfc, t, out, args.steps, args.warmup, args.trials)
-    value = 1000.0 / ms_per_step
+    if args.only_step or args.no_kernels:
+        x = cfc_inputs(**d, seed=0)
+        t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]
+        out = cfc.cfc_train_kloop(*t)
+        ms, tr = time_steps(torch, cfc, t, out, args.steps, args.warmup, args.trials)
+        print(json.dumps({"workload": args.workload, "ms_per_step": round(ms, 5),
+                          "value": round(1000.0 / ms, 2), "trials_ms": [round(v, 5) for v in tr]}), flush=True)
+        return
 
-    # Another path on the same inputs, for contrast: the step kernels after
-    # the persistent path; the other step-kernel variant after a step path.
-    ms_steps, contrast = None, None
-    if not args.no_steps_path:
-        modes = {"persistent": cfc.KLOOP_STEPS, "steps_mfma": cfc.KLOOP_STEPS_VALU,
-                 "steps_valu": cfc.KLOOP_STEPS_MFMA}
-        cfc.cfc_set_kloop_mode(modes[path])
-        try:
-            taken = cfc.cfc_kloop_path(B, C, n_x, K)
-            if taken >= 0:
-                contrast = names[taken]
-                out_steps = cfc.cfc_train_kloop(*t)
-                ms_steps, _ = time_steps(torch, cfc, t, out_steps, max(20, args.steps // 10), 5, 3)
-        finally:
-            cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
-
-    # the K-loop step with the GEMM-form weight gradient in place of scratch + reducer
-    ms_gemm = None
-    if not args.no_gemm_form:
-        og = cfc.cfc_train_kloop_gemm(*t)
-        ms_gemm, _ = time_calls(torch, lambda: cfc.cfc_train_kloop_gemm(*t, out=og), max(20, args.steps // 5), 5, 3)
-
-    bytes_min, flops = step_bytes_flops(B, C, n_x, K)
     t_node = graph_node_latency(torch)
-    kernels = {}
-    roofline = None
-    if not args.no_kernels:
-        timer = LaunchTimer(torch)
-        gW_flat = out.gW_scratch.view(B, -1)
-        red_out = torch.empty(3 * C * n_in, device="cuda")
-        dp = out.ws[:K * B * 3 * C].view(K, B, 3 * C)
-        kt = {}
-        kt["fwd_bwd"] = timer(lambda: cfc.cfc_kloop_fwd_bwd(*t, out=out), 20)
-        if path == "persistent":
-            X = torch.empty((K, B, 3 * C), device="cuda")
-            kt["input_projection"] = timer(lambda: cfc.cfc_input_projection(t[0], t[3], t[4], X), 50)
-            kt["recurrence"] = timer(lambda: cfc.cfc_kloop_recurrence(X, t[1], t[2], t[3], out=out), 20)
-        kt["scratch_fill"] = timer(lambda: cfc.cfc_scratch_fill(dp, t[0], out.h_hist, out.gW_scratch,
-                                                                out.gb_scratch), 50)
-        kt["reduce_axis0"] = timer(lambda: cfc.reduce_axis0(gW_flat, red_out), 50)
-        # the GEMM-form weight gradient (no scratch) on the same dp, against scratch fill + reduce
-        gws = torch.empty(cfc.lib().cfc_weight_grad_gemm_workspace_bytes(B, C, n_x, K) // 4 + 1, device="cuda")
-        gWg, gbg = torch.empty((3, C, n_in), device="cuda"), torch.empty((3, C), device="cuda")
-        kt["weight_grad_gemm"] = timer(lambda: cfc.cfc_weight_grad_gemm(dp, t[0], out.h_hist, gWg, gbg, gws), 50)
-        # step kernels of the 2K-launch path
-        S = torch.zeros((B, 3, C, n_in), device="cuda")
-        Sb = torch.zeros((B, 3, C), device="cuda")
-        dh = [torch.zeros((B, C), device="cuda") for _ in range(2)]
-        h_hist, act = out.h_hist, out.act
-        it = [0]
-
-        def fwd():
-            k = it[0] % K
-            cfc.cfc_fwd_step(t[0][k], h_hist[k], t[3], t[4], h_t=h_hist[k + 1], act_t=act[k])
-            it[0] += 1
-
-        def bwd():
-            k = K - 1 - it[0] % K
-            cfc.cfc_bwd_step(t[0][k], h_hist[k], h_hist[k + 1], t[1][k], t[3], act[k], dh[it[0] % 2], S, Sb,
-                             dh_out=dh[(it[0] + 1) % 2])
-            it[0] += 1
-        kt["fwd_step"] = timer(fwd, 2 * K)
-        it[0] = 0
-        kt["bwd_step"] = timer(bwd, 2 * K)
-        cfc.cfc_train_kloop(*t, out=out)   # restore the step's own state
-        torch.cuda.synchronize()
-        kernels = {k: dict(mean_us=round(v["mean_s"] * 1e6, 3), median_us=round(v["median_s"] * 1e6, 3),
-                           gap_median_us=round(v["gap_median_us"], 3)) for k, v in kt.items()}
-        if path == "persistent":
-            dur = kt["recurrence"]["mean_s"]
-            fl = recurrence_flops(B, C, K)
-            achieved = fl / dur
-            traffic = measured_traffic() if args.workload == "pages" else None
-            valu_busy = measured_valu_busy() if args.workload == "pages" else None
-            # what the kernel can use: one CU per sample (B of 256), fp32 FMA
-            # without packed math (4 SIMDs x 16 lanes x 2 flop per clock;
-            # half the 256 flop per clock per CU of the published peak)
-            usable = min(B, 256) * 2.4e9 * 4 * 16 * 2
-            # the same rate measured: the FMA-chain probe on B workgroups of
-            # the kernel's 512 lanes, one per CU, and on all 256 CUs
-            meas_b = fma_rate(torch, cfc, min(B, 256))
-            meas_chip = fma_rate(torch, cfc, 256)
-            roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
-                        "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": traffic,
-                        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
-                        "kernel": "kloop_persist_kernel", "flops_per_launch": fl,
-                        "launch_us": round(dur * 1e6, 3),
-                        "usable_peak": round(usable / 1e12, 3),
-                        "frac_of_usable": round(achieved / usable, 4),
-                        "usable_note": "one CU per sample (a sample's steps are sequential), non-packed fp32 FMA",
-                        "usable_peak_measured": round(meas_b / 1e12, 3),
-                        "frac_of_usable_measured": round(achieved / meas_b, 4),
-                        "fma_probe_chip_TFLOPs": round(meas_chip / 1e12, 2),
-                        "fma_probe_chip_GHz": round(meas_chip / (256 * 128) / 1e9, 3),
-                        "fma_probe_note": "v_fma_f32 chains, 512 lanes per workgroup, one workgroup per CU; "
-                                          "GHz = chip rate / (256 CUs x 128 flop/clk)",
-                        "traffic_GBps": round(traffic / dur / 1e9, 1) if traffic else None,
-                        "traffic_frac_of_hbm_peak": round(traffic / dur / HBM_PEAK, 4) if traffic else None,
-                        "valu_busy_rocprof": valu_busy,
-                        "valu_busy_note": "SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES over the kernel's CUs "
-                                          "(profiles/kloop_persist_pages_valu.md)"}
-        elif path == "steps_mfma":
-            # the 2K step launches of the K-loop (and the one W re-layout), per launch on average
-            dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
-            fl = K * B * 3 * C * (n_in + C) * 2 // (2 * K)
-            achieved = fl / dur
-            roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
-                        "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
-                        "kernel": "fwd_mfma_kernel + bwd_mfma_kernel (average over the 2K step launches)",
-                        "flops_per_launch": fl, "launch_us": round(dur * 1e6, 3)}
-        else:
-            dur = kt["bwd_step"]["mean_s"]
-            by = bwd_launch_bytes(B, C, n_x)
-            roofline = {"bound": "hbm", "achieved": round(by / dur / 1e9, 1), "peak": HBM_PEAK / 1e9,
-                        "unit": "GB/s", "frac": round(by / dur / HBM_PEAK, 4), "traffic": None,
-                        "kernel": "bwd_step_kernel", "bytes_per_launch": by, "launch_us": round(dur * 1e6, 3)}
-
-    nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3}[path]
-    t_roof = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
-    # the same formula over the pages' own K-loop structure: one memset, K
-    # forward and K backward launches and two reductions as dependent nodes
-    pages_nodes = 2 * K + 3
-    t_roof_pages = pages_nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
-    # Critical-path roofline of the persistent path: the 2K recurrence steps
-    # of a sample run in order on one CU, so they are bounded by one CU's
-    # fp32 rate (the published peak per CU: 256 flop/clk at 2.4 GHz; half
-    # that without packed fp32), not by the chip's; the parallel kernels by
-    # their own whole-chip bounds; plus one node latency per launch.
-    crit = None
-    if path == "persistent":
-        cu_clk = 2.4e9
-        t_rec = recurrence_flops(B, C, K) / B / (256 * cu_clk)
-        par_flops = projection_flops(B, C, n_x, K) + 2 * K * B * 3 * C * n_in
-        par_bytes = fill_bytes(B, C, n_x, K) + 4 * (B + 1) * 3 * C * n_in + 4 * K * B * (n_x + 3 * C)
-        t_par = max(par_flops / FP32_PEAK, par_bytes / HBM_PEAK)
-        t_crit = nodes * t_node + t_rec + t_par
-        t_crit_np = nodes * t_node + 2 * t_rec + t_par
-        crit = {"recurrence_floor_us": round(t_rec * 1e6, 2), "parallel_floor_us": round(t_par * 1e6, 2),
-                "critical_path_roof_ms": round(t_crit * 1e3, 4),
-                "step_over_critical_path_roof": round(ms_per_step / (t_crit * 1e3), 3),
-                "critical_path_roof_nonpacked_ms": round(t_crit_np * 1e3, 4),
-                "step_over_critical_path_roof_nonpacked": round(ms_per_step / (t_crit_np * 1e3), 3)}
-    step_roof = {"path": path, "nodes": nodes, "t_node_us": round(t_node * 1e6, 3),
-                 "t_roof_ms": round(t_roof * 1e3, 4), "step_over_roof": round(ms_per_step / (t_roof * 1e3), 3),
-                 "pages_graph_nodes": pages_nodes, "t_roof_pages_graph_ms": round(t_roof_pages * 1e3, 4),
-                 "step_over_roof_pages_graph": round(ms_per_step / (t_roof_pages * 1e3), 3),
-                 "flops": flops, "bytes_min": bytes_min,
-                 "contrast_path": contrast,
-                 "contrast_ms_per_step": round(ms_steps, 5) if ms_steps else None,
-                 "gemm_form_weight_grad_ms_per_step": round(ms_gemm, 5) if ms_gemm else None,
-                 "critical_path": crit}
+    head = bench_kloop(torch, cfc, args.workload, args.steps, args.warmup, args.trials, t_node, detail=True)
+    print("[bench] %s step: %.5f ms" % (args.workload, head["ms_per_step"]), file=sys.stderr, flush=True)
 
     result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "train-steps/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": head["value"], "unit": "train-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "CfC K-loop train step (fwd + BPTT + scratch + reduce_axis0), one cfc_train_kloop call",
-                   "B": B, "C": C, "n_x": n_x, "n_in": n_in, "K": K, "seed": 0, "path": path},
-        "roofline": roofline,
-        "step_roofline": step_roof,
-        "kernels": kernels,
-        "trials_ms": [round(v, 5) for v in trials],
+                   "B": B, "C": C, "n_x": n_x, "n_in": n_in, "K": K, "seed": 0, "path": head["path"]},
+        "roofline": head["roofline"],
+        "step_roofline": head["step_roofline"],
+        "kernels": head["kernels"],
+        "trials_ms": head["trials_ms"],
+        "contrast": head.get("contrast"),
+        "gemm_form_weight_grad_ms_per_step": head.get("gemm_form_weight_grad_ms_per_step"),
+        "deterministic_3_runs": head.get("deterministic_3_runs"),
     }
-
-    if not args.no_kernels:
-        result["deterministic_3_runs"] = deterministic_runs(torch, cfc, t)
     result["host"] = host_info()
-    if not (args.no_kernels and args.no_reduce):
+
+    if not args.no_other_workloads:
+        legs = {}
+        for w in ("tiny", "pages", "wide"):
+            if w == args.workload:
+                continue
+            legs[w] = bench_kloop(torch, cfc, w, 200 if w == "tiny" else 50, 10, 5, t_node, detail=False)
+            print("[bench] %s step: %.5f ms" % (w, legs[w]["ms_per_step"]), file=sys.stderr, flush=True)
+        result["workloads"] = legs
+
+    if not args.no_reduce:
         peak = copy_peak(torch)
         result["hbm_copy_peak"] = {"GBps": round(peak / 1e9, 1), "frac_of_datasheet": round(peak / HBM_PEAK, 4),
                                    "what": "torch fp32 device copy, 2 GiB read + 2 GiB written, median of 10"}
-
-    if not args.no_reduce:
         timer = LaunchTimer(torch)
         shapes = [(b, n) for b in REDUCE_B for n in REDUCE_N]
         red = bench_reduce(torch, cfc, timer, shapes)
-        if "hbm_copy_peak" in result:
-            for r in red:
-                r["frac_copy"] = round(r["GBps"] / result["hbm_copy_peak"]["GBps"], 3)
+        for r in red:
+            r["frac_copy"] = round(r["GBps"] / result["hbm_copy_peak"]["GBps"], 3)
         gate = [r for r in red if r["B"] * r["N"] * 4 >= 512 * 2 ** 20]
         result["reduce_axis0"] = {"shapes": red,
                                   "min_frac_large": min(r["frac"] for r in gate) if gate else None}
-        if not args.no_cpu:
-            result["reduce_axis0"]["cpu_oracle"] = cpu_reduce_baseline(2.0)
+        print("[bench] reduce_axis0 done", file=sys.stderr, flush=True)
 
     if not args.no_mlp:
         result["mlp"] = bench_mlp(torch, LaunchTimer(torch), 50, 5, 0.0 if args.no_cpu else args.cpu_seconds)
+        print("[bench] mlp done", file=sys.stderr, flush=True)
 
-    if not args.no_kernels:
+    if not args.no_adamw:
         # the optimizer step beside the path: W and bias of this cell, then large flat tensors
         result["adamw"] = bench_adamw(torch, cfc, LaunchTimer(torch),
                                       [(3 * C * n_in, 3 * C), (1 << 24,), (1 << 26,)])
 
     if not args.no_cpu:
-        n, el = cpu_baseline(x, args.cpu_seconds)
-        result["cpu_baseline"] = {"value": round(n / el, 4), "unit": "train-steps/s", "cores": 1,
-                                  "kind": "oracle",
-                                  "sample": "%d whole train steps of the same workload (B=%d C=%d n_x=%d K=%d), "
-                                            "fp64 oracle, one thread, %.1f s" % (n, B, C, n_x, K, el)}
+        cb = cpu_baselines(CONFIGS, args.cpu_seconds)
+        main_leg = cb[args.workload]
+        best = main_leg["fp32_all"]
+        result["cpu_baseline"] = dict(best)
+        result["cpu_baseline"]["variants"] = {args.workload: main_leg}
+        result["cpu_baseline"]["host_threads"] = cb["host_threads"]
+        result["cpu_baseline"]["gpu_over_cpu"] = round(result["value"] / best["value"], 1)
+        for w in ("tiny", "pages", "wide"):
+            if w != args.workload:
+                result["cpu_baseline"]["variants"][w] = cb[w]
+                if "workloads" in result and w in result["workloads"]:
+                    result["workloads"][w]["cpu_baseline"] = cb[w]
+        if "reduce_axis0" in result:
+            result["reduce_axis0"]["cpu_oracle"] = cb["reduce_axis0"]
     print(json.dumps(result), flush=True)
 
 

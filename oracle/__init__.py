@@ -7,4 +7,5 @@ nothing from it.
 """
 from .oracle import (  # noqa: F401
     fwd_step, bwd_step, forward, train, reduce_axis0_f64, sum_axis0, input_projection, adamw_step, lib_path,
+    set_threads, threads,
 )

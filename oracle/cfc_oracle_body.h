@@ -38,14 +38,18 @@
 #define FN(name) CAT(name, SUF)
 
 /* One forward step for every sample: h_t and the saved activations.
- * Loop order b -> c -> q -> k; the dot product runs k = 0 .. n_in-1. */
+ * Loop order b -> c -> q -> k; the dot product runs k = 0 .. n_in-1.
+ * Samples are independent (each writes only its own rows), so the b loop
+ * may run on several host threads; every value is computed by the same
+ * statements in the same order whatever the thread count. */
 void FN(oracle_fwd_step)(const REAL* u_t, const REAL* h_prev, const REAL* W,
                          const REAL* bias, long B, long C, long n_x,
                          REAL* h_t, REAL* act_t)
 {
     const long n_in = n_x + C;
-    REAL* z = (REAL*)malloc(sizeof(REAL) * (size_t)(n_in > 0 ? n_in : 1));
+#pragma omp parallel for schedule(static)
     for (long b = 0; b < B; ++b) {
+        REAL* z = (REAL*)malloc(sizeof(REAL) * (size_t)(n_in > 0 ? n_in : 1));
         /* z = [u_t[b] ; h_prev[b]] */
         for (long k = 0; k < n_x; ++k) z[k] = u_t[b * n_x + k];
         for (long k = 0; k < C; ++k) z[n_x + k] = h_prev[b * C + k];
@@ -65,8 +69,8 @@ void FN(oracle_fwd_step)(const REAL* u_t, const REAL* h_prev, const REAL* W,
             act_t[(1 * B + b) * C + c] = g;
             act_t[(2 * B + b) * C + c] = hh;
         }
+        free(z);
     }
-    free(z);
 }
 
 /* The input part of the pre-activations for M rows of inputs at once:
@@ -86,7 +90,8 @@ void FN(oracle_input_projection)(const REAL* u, const REAL* W, const REAL* bias,
         }
 }
 
-/* One backward step for every sample.
+/* One backward step for every sample (the b loop may run on several host
+ * threads, as in oracle_fwd_step: sample b writes only its own rows).
  *   dh    = (h_t - y_t) + dh_in                       (loss residual + carry)
  *   dp_f  = dh * (g - hh) * (-gate * (1 - gate))       (d/da_f; dgate/da_f = -gate(1-gate))
  *   dp_g  = dh * gate * (1 - g^2)
@@ -103,9 +108,10 @@ void FN(oracle_bwd_step)(const REAL* u_t, const REAL* h_prev, const REAL* h_t,
                          REAL* dp_out)
 {
     const long n_in = n_x + C;
-    REAL* z = (REAL*)malloc(sizeof(REAL) * (size_t)(n_in > 0 ? n_in : 1));
-    REAL* dp = (REAL*)malloc(sizeof(REAL) * (size_t)(3 * C > 0 ? 3 * C : 1));
+#pragma omp parallel for schedule(static)
     for (long b = 0; b < B; ++b) {
+        REAL* z = (REAL*)malloc(sizeof(REAL) * (size_t)(n_in > 0 ? n_in : 1));
+        REAL* dp = (REAL*)malloc(sizeof(REAL) * (size_t)(3 * C > 0 ? 3 * C : 1));
         for (long k = 0; k < n_x; ++k) z[k] = u_t[b * n_x + k];
         for (long k = 0; k < C; ++k) z[n_x + k] = h_prev[b * C + k];
         for (long c = 0; c < C; ++c) {
@@ -134,9 +140,9 @@ void FN(oracle_bwd_step)(const REAL* u_t, const REAL* h_prev, const REAL* h_t,
             else if (du_t)
                 du_t[b * n_x + k] = acc;
         }
+        free(dp);
+        free(z);
     }
-    free(dp);
-    free(z);
 }
 
 /* Column sum over the batch axis, in increasing b, in REAL:

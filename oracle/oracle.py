@@ -53,8 +53,23 @@ def _lib():
             f.restype = None
         lib.oracle_reduce_axis0_f64.argtypes = [_P, _I64, _I64, _P]
         lib.oracle_reduce_axis0_f64.restype = None
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         _LIB = lib
     return _LIB
+
+
+def set_threads(n):
+    """Host threads of the oracle's per-sample and per-column loops (n >= 1).
+    Results are bitwise the same for any count."""
+    _lib().oracle_set_threads(int(n))
+
+
+def threads():
+    """Threads the oracle's parallel loops use now."""
+    return int(_lib().oracle_threads())
 
 
 def _dt(precision):

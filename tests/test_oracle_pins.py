@@ -323,3 +323,28 @@ def test_adamw_oracle_special_cases(oracle_mod):
     p, _, _ = oracle_mod.adamw_step(p0, g, np.zeros(33), np.zeros(33), lr=1e-2, beta1=0.9, beta2=0.999,
                                     eps=1e-30, weight_decay=0.0, step=1)
     np.testing.assert_allclose(p, p0 - 1e-2 * np.sign(g), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+def test_thread_count_does_not_change_the_oracle(oracle_mod, precision):
+    """The oracle's per-sample loops on several host threads give the bits of
+    one thread: samples write disjoint rows and the batch-axis sums stay serial
+    in increasing b (this is what makes the all-core CPU baseline the same
+    computation as the single-thread one)."""
+    x = cfc_inputs(B=9, C=24, n_x=7, K=5, seed=3, bias_scale=0.2)
+    u, y, h0, W, bias = (a if precision == "f32" else a.astype(np.float64) for a in (x.u, x.y, x.h0, x.W, x.bias))
+    before = oracle_mod.threads()
+    try:
+        oracle_mod.set_threads(1)
+        one = oracle_mod.train(u, y, h0, W, bias, precision, want_du=True, want_dp=True)
+        r1 = oracle_mod.reduce_axis0_f64(x.u.reshape(-1, 7 * 9)[:, :50].copy())
+        oracle_mod.set_threads(4)
+        assert oracle_mod.threads() == 4
+        many = oracle_mod.train(u, y, h0, W, bias, precision, want_du=True, want_dp=True)
+        r4 = oracle_mod.reduce_axis0_f64(x.u.reshape(-1, 7 * 9)[:, :50].copy())
+    finally:
+        oracle_mod.set_threads(before)
+    for k in one:
+        a, b = np.asarray(one[k]), np.asarray(many[k])
+        assert a.tobytes() == b.tobytes(), k
+    assert r1.tobytes() == r4.tobytes()

@@ -48,28 +48,46 @@ U64 = 2.0 ** -53
 KAPPA = 16.0
 
 
-def _report(name, x, ref, bound):
+def _report(name, x, ref, bound, plain=None):
+    """Pass/fail report of x against ref under `bound`; with `plain` (the
+    stated tolerance without any added term) also the fraction of elements
+    that meet the stated tolerance alone."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
     err = np.abs(x - ref)
     ratio = err / bound
     bad = ~(err <= bound)  # NaN fails
     norm = np.linalg.norm(ref)
-    return dict(name=name, n=int(x.size), fails=int(bad.sum()),
-                worst_ratio=float(np.nanmax(ratio)) if x.size else 0.0,
-                max_err=float(err.max()) if x.size else 0.0,
-                normwise=float(np.linalg.norm(x - ref) / norm) if norm > 0 else float(np.linalg.norm(x - ref)),
-                first_bad=np.argwhere(bad)[:5].tolist())
+    rep = dict(name=name, n=int(x.size), fails=int(bad.sum()),
+               worst_ratio=float(np.nanmax(ratio)) if x.size else 0.0,
+               max_err=float(err.max()) if x.size else 0.0,
+               normwise=float(np.linalg.norm(x - ref) / norm) if norm > 0 else float(np.linalg.norm(x - ref)),
+               first_bad=np.argwhere(bad)[:5].tolist())
+    if plain is not None:
+        rep["plain_ok_frac"] = float((err <= plain).mean()) if x.size else 1.0
+    return rep
 
 
 def check_act(name, x, ref, rtol=1e-5, atol=1e-6):
     ref = np.asarray(ref, np.float64)
-    return _report(name, x, ref, atol + rtol * np.abs(ref))
+    b = atol + rtol * np.abs(ref)
+    return _report(name, x, ref, b, plain=b)
 
 
 def check_grad(name, x, ref, mass, rtol=1e-4, atol=1e-6, kappa=KAPPA):
+    """The gradient criterion; the report's plain_ok_frac is the fraction of
+    elements within the stated rel 1e-4 / abs 1e-6 alone (no mass term)."""
     ref = np.asarray(ref, np.float64)
-    return _report(name, x, ref, atol + rtol * np.abs(ref) + kappa * U32 * np.asarray(mass))
+    plain = atol + rtol * np.abs(ref)
+    return _report(name, x, ref, plain + kappa * U32 * np.asarray(mass), plain=plain)
+
+
+def describe(rep):
+    """One line of a report for the test log."""
+    s = "%s: worst %.3g of the bound, normwise %.3g" % (rep["name"], rep["worst_ratio"], rep["normwise"])
+    if "plain_ok_frac" in rep:
+        s += ", %.6f within the stated tolerance alone" % rep["plain_ok_frac"]
+    return s
 
 
 def check_reduce(name, x, ref, absmass, B, rtol=1e-6):
