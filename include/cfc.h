@@ -284,6 +284,29 @@ int cfc_set_kloop_mode(int mode);
  * path the sizes cannot take. */
 int cfc_kloop_path(int B, int C, int n_x, int K);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * K-loop training step of cfc_train_kloop, same arguments without ws and
+ * ws_bytes, same kernels and the same bits, with its workspace in a fixed
+ * array that the library holds on each device until the process ends
+ * (CFC_NOALLOC_MAX_WS_BYTES; sizes whose cfc_train_kloop_workspace_bytes
+ * exceed it give CFC_EINVAL before anything is enqueued).  The call
+ * allocates and frees nothing, builds no graph (every launch is enqueued
+ * directly on `stream`, on either path, honouring the calling thread's
+ * cfc_set_kloop_mode) and never waits on the device.  Every call on one
+ * device shares that device's array: calls whose work overlaps on one device
+ * (several streams or threads at once) race and give undefined results;
+ * calls issued one after another on a stream are safe.  Each call writes
+ * every part of the array it reads, so no state carries over between calls.
+ */
+#define CFC_NOALLOC_MAX_WS_BYTES (32u << 20)
+int cfc_train_kloop_noalloc(const float* u, const float* y, const float* h0,
+                            const float* W, const float* bias,
+                            float* h_hist, float* act,
+                            float* gW_scratch, float* gb_scratch,
+                            float* gW, float* gb,
+                            int B, int C, int n_x, int K, void* stream);
+
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* cfc_last_error(void);
 

@@ -47,6 +47,7 @@ def lib():
         L.reduce_axis0.argtypes = [_P, _I64, _I64, _P, _P]
         L.cfc_train_kloop.argtypes = [_P] * 8 + [ctypes.c_size_t] + [_P] * 4 + [_I, _I, _I, _I, _P]
         L.cfc_kloop_fwd_bwd.argtypes = [_P] * 8 + [ctypes.c_size_t, _I, _I, _I, _I, _P]
+        L.cfc_train_kloop_noalloc.argtypes = [_P] * 11 + [_I, _I, _I, _I, _P]
         L.cfc_scratch_fill.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
         L.cfc_input_projection.argtypes = [_P] * 4 + [_I64, _I, _I, _P]
         L.cfc_kloop_recurrence.argtypes = [_P] * 7 + [_I, _I, _I, _I, _P]
@@ -70,7 +71,7 @@ def lib():
         for f in (L.cfc_fwd_step, L.cfc_bwd_step, L.reduce_axis0, L.cfc_train_kloop,
                   L.cfc_kloop_fwd_bwd, L.cfc_scratch_fill, L.cfc_clear_graph_cache,
                   L.cfc_set_kloop_mode, L.cfc_input_projection, L.cfc_kloop_recurrence, L.cfc_adamw_step,
-                  L.cfc_weight_grad_gemm, L.cfc_train_kloop_gemm, L.cfc_probe_fma):
+                  L.cfc_weight_grad_gemm, L.cfc_train_kloop_gemm, L.cfc_probe_fma, L.cfc_train_kloop_noalloc):
             f.restype = _I
         _LIB = L
     return _LIB
@@ -194,6 +195,23 @@ def cfc_train_kloop(u, y, h0, W, bias, out=None):
             _dev(out.gb_scratch, "gb_scratch", (B, 3, C)), _dev(out.gW, "gW", (3, C, n_in)),
             _dev(out.gb, "gb", (3, C)))
     _check("cfc_train_kloop", lib().cfc_train_kloop(*args, B, C, n_x, K, _stream(h0)))
+    return out
+
+
+def cfc_train_kloop_noalloc(u, y, h0, W, bias, out):
+    """cfc_train_kloop with the library's fixed workspace (no allocation in
+    the call, no graph; see include/cfc.h): out supplies h_hist, act, the
+    scratch, gW and gb (its ws is not used).  Returns out."""
+    K, B, n_x = u.shape
+    C = h0.shape[1]
+    n_in = n_x + C
+    args = (_dev(u, "u", (K, B, n_x)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
+            _dev(W, "W", (3, C, n_in)), _dev(bias, "bias", (3, C)),
+            _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
+            _dev(out.gW_scratch, "gW_scratch", (B, 3, C, n_in)),
+            _dev(out.gb_scratch, "gb_scratch", (B, 3, C)), _dev(out.gW, "gW", (3, C, n_in)),
+            _dev(out.gb, "gb", (3, C)))
+    _check("cfc_train_kloop_noalloc", lib().cfc_train_kloop_noalloc(*args, B, C, n_x, K, _stream(h0)))
     return out
 
 

@@ -875,6 +875,81 @@ int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist, float
     return enqueue_fill(dp, u, h_hist, gW_scratch, gb_scratch, B, C, n_x, K, s);
 }
 
+// ---------------------------------------------------------------------------
+// The K-loop step without a caller workspace, for callers that cannot
+// allocate device memory: its workspace is a fixed array of the library on
+// each device, and every launch is enqueued directly (no graph, whose
+// instantiation would allocate).
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// The workspace of cfc_train_kloop_noalloc: one copy per device, held until
+// the process ends.  Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) float scratch[CFC_NOALLOC_MAX_WS_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device dev (the current device),
+// looked up on the first call on that device.
+int scratch_on_device(int dev, float** out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        CFC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "workspace symbol address");
+        if (p == nullptr) return cfc_host::fail(CFC_EHIP, "workspace symbol address: null");
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return CFC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cfc_train_kloop_noalloc(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                            float* h_hist, float* act, float* gW_scratch, float* gb_scratch, float* gW, float* gb,
+                            int B, int C, int n_x, int K, void* stream)
+{
+    cfc_host::last_error().clear();
+    const char* fn = "cfc_train_kloop_noalloc";
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "%s: K=%d out of range", fn, K);
+    const size_t need = (size_t)kloop_ws_floats(B, C, n_x, K) * sizeof(float);
+    if (need > (size_t)CFC_NOALLOC_MAX_WS_BYTES)
+        return fail(CFC_EINVAL, "%s: these sizes need %zu bytes of workspace; the fixed workspace holds %zu",
+                    fn, need, (size_t)CFC_NOALLOC_MAX_WS_BYTES);
+    int dev = 0;
+    CFC_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CFC_EINVAL, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    float* ws = nullptr;
+    if (int rc = scratch_on_device(dev, &ws)) return rc;
+    Path path = Path::Steps;
+    if (int rc = check_kloop(fn, u, y, h0, W, bias, h_hist, act, ws, need, gW_scratch, gb_scratch, gW, gb, B, C,
+                             n_x, K, true, &path))
+        return rc;
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0 || B == 0) {
+        if (BC > 0) CFC_HIP(hipMemcpyAsync(h_hist, h0, BC * 4, hipMemcpyDeviceToDevice, s), "h0 copy");
+        CFC_HIP(cfc::launch_fill_zero(gW_scratch, BC * 3 * n_in, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gb_scratch, 3 * BC, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gW, 3 * C * n_in, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gb, 3 * C, s), "zero fill");
+        return CFC_OK;
+    }
+    // every part of the workspace is written before it is read within the
+    // call (dp, X, the carry, the re-laid W), so nothing needs clearing
+    const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
+    return enqueue_kloop(k, path, make_plan(B, C, n_x, W, gW_scratch), s);
+}
+
 int cfc_clear_graph_cache(void)
 {
     std::lock_guard<std::mutex> lock(g_mu);

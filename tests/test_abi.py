@@ -410,3 +410,15 @@ def test_probe_fma_argument_errors(L):
         assert L.cfc_probe_fma(blocks, threads, 1, iters, FAKE, None) == -1
     assert L.cfc_probe_fma(1, 512, 1, 1, None, None) == -1
     assert b"NULL" in L.cfc_last_error()
+
+
+def test_noalloc_size_check_comes_first(L):
+    """cfc_train_kloop_noalloc refuses sizes whose workspace exceeds its fixed
+    array before any HIP call (so this runs without a GPU)."""
+    a = [FAKE + i * (1 << 32) for i in range(11)]
+    limit = 32 << 20
+    assert L.cfc_train_kloop_workspace_bytes(256, 256, 128, 64) > limit
+    assert L.cfc_train_kloop_noalloc(*a, 256, 256, 128, 64, None) == -1
+    assert b"fixed workspace" in L.cfc_last_error()
+    assert L.cfc_train_kloop_noalloc(*a, 4, 0, 8, 4, None) == -1          # C = 0
+    assert L.cfc_train_kloop_noalloc(*a, 4, 16, 8, -1, None) == -1        # K < 0
