@@ -1539,11 +1539,15 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
 // ---------------------------------------------------------------------------
 // Batch-axis reduction out[n] = sum_b in[b, n] ("reduce_axis0").
 // Workgroup = R row slices x (256 / R) column lanes; a lane owns V adjacent
-// columns.  Slice i sums rows [i*rps, (i+1)*rps) in ascending b, in fp64;
-// slices are then added in ascending order through LDS by slice 0, and the
-// fp64 total is rounded to fp32 once.  R and rps depend on B alone, so the
-// bits of a column do not depend on N, V, the segment it sits in or the grid.
-// Up to two tensors (segments) with the same B are reduced by one launch.
+// columns.  Slice i sums rows [i*rps, (i+1)*rps) in ascending b, in fp64.
+// The R slice partials of a column are then added by a block tree: while the
+// partner slice sits in another wavefront, through LDS (stride halving:
+// slice i < s adds slice i + s, s = R/2, R/4, ..), and the last levels, once
+// both partners are lanes of one wavefront, by a wavefront exchange; so
+// R = 4 gives (p0 + p2) + (p1 + p3).  The fp64 total is rounded to fp32
+// once.  R and rps depend on B alone, so the bits of a column do not depend
+// on N, V, the segment it sits in or the grid.  Up to two tensors (segments)
+// with the same B are reduced by one launch.
 // ---------------------------------------------------------------------------
 template <int V, int G>
 __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
@@ -1551,7 +1555,7 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
     // G column groups per lane: group j of this lane is (blockIdx.x G + j)
     // lanes + lane, so that every j is one coalesced row segment per slice;
     // the loads of all G groups of a row are in flight together.
-    __shared__ double part[kThreads * V * G];
+    __shared__ double part[V * G][kThreads];   // component-major: lanes read and write consecutive doubles
     const int lanes = kThreads / a.R;
     const int slice = threadIdx.x / lanes;
     const int lane = threadIdx.x - slice * lanes;
@@ -1627,33 +1631,59 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
             }
         }
     }
+    // Block tree over the R slices.  LDS levels while the partner slice is in
+    // another wavefront (sh * lanes >= 64, so `slice < sh` is uniform over
+    // each wavefront): slice i < sh adds the partial that slice i + sh holds
+    // after the previous level.  A level reads slices [sh, 2 sh) and writes
+    // slices [0, sh), so one barrier per level orders it.
+    int sh = a.R / 2;
+    if (sh * lanes >= 64) {
 #pragma unroll
-    for (int jg = 0; jg < G; ++jg)
+        for (int jg = 0; jg < G; ++jg)
 #pragma unroll
-        for (int e = 0; e < V; ++e) part[((slice * lanes + lane) * G + jg) * V + e] = acc[jg][e];
-    __syncthreads();
-    if (slice == 0) {
+            for (int e = 0; e < V; ++e) part[jg * V + e][threadIdx.x] = acc[jg][e];
+    }
+    for (; sh > 0 && sh * lanes >= 64; sh >>= 1) {
+        __syncthreads();
+        if (slice < sh) {
 #pragma unroll
-        for (int jg = 0; jg < G; ++jg) {
-            if (!valid[jg]) continue;
-            double sm[V];
+            for (int jg = 0; jg < G; ++jg)
 #pragma unroll
-            for (int e = 0; e < V; ++e) sm[e] = part[(lane * G + jg) * V + e];
-            for (int i = 1; i < a.R; ++i) {
+                for (int e = 0; e < V; ++e) acc[jg][e] += part[jg * V + e][threadIdx.x + sh * lanes];
+            if ((sh >> 1) * lanes >= 64) {
 #pragma unroll
-                for (int e = 0; e < V; ++e) sm[e] += part[((i * lanes + lane) * G + jg) * V + e];
+                for (int jg = 0; jg < G; ++jg)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) part[jg * V + e][threadIdx.x] = acc[jg][e];
             }
-            if (V == 4 && whole[jg]) {
-                f32x4 o;
-                o.x = (float)sm[0];
-                o.y = (float)sm[1];
-                o.z = (float)sm[2];
-                o.w = (float)sm[3];
-                *reinterpret_cast<f32x4*>(out[jg] + n0[jg]) = o;
-            } else {
+        }
+    }
+    if (threadIdx.x < 64 || slice == 0) {
+        // Levels left only when a slice is narrower than a wavefront: then
+        // wavefront 0 holds slice 0 and every partner of those levels, and
+        // lane l adds lane l ^ (sh lanes) (both partners keep the same bits).
+        for (; sh > 0; sh >>= 1) {
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    if (n0[jg] + e < N[jg]) out[jg][n0[jg] + e] = (float)sm[e];
+            for (int jg = 0; jg < G; ++jg)
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[jg][e] += __shfl_xor(acc[jg][e], sh * lanes);
+        }
+        if (slice == 0) {
+#pragma unroll
+            for (int jg = 0; jg < G; ++jg) {
+                if (!valid[jg]) continue;
+                if (V == 4 && whole[jg]) {
+                    f32x4 o;
+                    o.x = (float)acc[jg][0];
+                    o.y = (float)acc[jg][1];
+                    o.z = (float)acc[jg][2];
+                    o.w = (float)acc[jg][3];
+                    *reinterpret_cast<f32x4*>(out[jg] + n0[jg]) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        if (n0[jg] + e < N[jg]) out[jg][n0[jg] + e] = (float)acc[jg][e];
+                }
             }
         }
     }
