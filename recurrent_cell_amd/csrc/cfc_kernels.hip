@@ -1092,25 +1092,46 @@ __device__ __forceinline__ float group_bcast(float v)
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x18 | (SRC << 5)));
 }
 
-// tree_sum16 with all 16 LDS reads issued before the first add (the empty
-// asm takes every value as an operand, so no read can sink below it): one
-// LDS latency instead of two on the carry's path.  Same adds, same bits.
-__device__ __forceinline__ float tree_sum16_loads_first(const float* p, int s)
+// The last three levels of tree_sum16 over p[0], p[s], .., p[7 s] (the level-1
+// pair sums of the canonical dz subtree), with all 8 LDS reads issued before
+// the first add (the empty asm takes every value as an operand, so no read
+// can sink below it): ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)).
+__device__ __forceinline__ float tree_sum8_loads_first(const float* p, int s)
 {
-    float r[16];
+    float r[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = p[i * s];
+    for (int i = 0; i < 8; ++i) r[i] = p[i * s];
     asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
-                 "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]),
-                 "+v"(r[14]), "+v"(r[15]));
-    float a[8];
+                 "+v"(r[7]));
+    float a[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = r[2 * i] + r[2 * i + 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
-    return a[0] + a[1];
+    for (int i = 0; i < 4; ++i) a[i] = r[2 * i] + r[2 * i + 1];
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// The backward cell's factors that do not depend on the carry, for one
+// channel at one staged step (rows gate, g, hh, h_t, y_t at pitch HW):
+// cell_backward's operations, split so that only
+//   dh = r + carry;  df = (dh A) Bf;  dg = (dh G) Fg;  dhh = (dh H) Fh
+// remain once the carry is known (the same operations in the same order,
+// hence the same bits).
+struct BwdFactors {
+    float r, A, Bf, G, Fg, H, Fh;
+};
+
+template <int HW>
+__device__ __forceinline__ BwdFactors bwd_factors(const float* st, int c)
+{
+    const float gate = st[c], g = st[HW + c], hh = st[2 * HW + c];
+    BwdFactors f;
+    f.r = st[3 * HW + c] - st[4 * HW + c];
+    f.A = g - hh;
+    f.Bf = -gate * (1.0f - gate);
+    f.G = gate;
+    f.Fg = fmaf(-g, g, 1.0f);
+    f.H = 1.0f - gate;
+    f.Fh = fmaf(-hh, hh, 1.0f);
+    return f;
 }
 
 template <int CPG, int NH>
@@ -1479,15 +1500,17 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         // One step.  The partial buffers alternate with tt (the barrier at
         // a chunk boundary orders the last reads of one chunk before the
         // first writes of the next).
+        BwdFactors fb = bwd_factors<HW>(stage, cqc);   // step t1 (staged step 0)
         auto bstep = [&](int tt) __attribute__((always_inline)) {
             float* pb = &part[tt & 1][0][0];
-            const float* st = stage + tt * 5 * HW;
             float mdp[3];
             {
                 // carry_mine is +0 at t = K, and h_t - y_t is never -0 (h_t
                 // is not), so the add is exact there
-                const float dh = (st[3 * HW + cqc] - st[4 * HW + cqc]) + carry_mine;
-                cell_backward(dh, st[cqc], st[HW + cqc], st[2 * HW + cqc], mdp[0], mdp[1], mdp[2]);
+                const float dh = fb.r + carry_mine;
+                mdp[0] = (dh * fb.A) * fb.Bf;
+                mdp[1] = (dh * fb.G) * fb.Fg;
+                mdp[2] = (dh * fb.H) * fb.Fh;
             }
             float dp[CPG][3];
 #pragma unroll
@@ -1500,25 +1523,65 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             // channel carries W = 0 and the finite dp of the clamped channel
             // C - 1; 0 * dp is +-0 and P is never -0, so fma(0, dp, P) == P
             // exactly and the chains need no per-channel branches.
+            // P[n], n = 4 i + e: column 32 i + 4 j + e.
+            float P[4 * NH];
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int i = 0; i < NH; ++i)
 #pragma unroll
-                for (int cl = 0; cl < CPG; ++cl)
+                for (int e = 0; e < 4; ++e) {
+                    float acc = 0.0f;
 #pragma unroll
-                    for (int q = 0; q < 3; ++q)
+                    for (int cl = 0; cl < CPG; ++cl)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) P[e] = fmaf(w[cl][q][i][e], dp[cl][q], P[e]);
-                f32x4 v;
-                v.x = P[0];
-                v.y = P[1];
-                v.z = P[2];
-                v.w = P[3];
-                *reinterpret_cast<f32x4*>(pb + g * HWP + 32 * i + 4 * j) = v;
+                        for (int q = 0; q < 3; ++q) acc = fmaf(w[cl][q][i][e], dp[cl][q], acc);
+                    P[4 * i + e] = acc;
+                }
+            // Level 1 of the canonical dz subtrees: group g + group g + 4,
+            // which are lanes l and l + 32 of one wavefront.  One swap of
+            // the wavefront halves pairs P[n] with P[n + 2 NH]: lanes < 32
+            // then hold the level-1 sums of columns n < 2 NH, lanes >= 32
+            // those of the rest, each as (lower group) + (upper group).
+            // They go to the lower group's row.
+            constexpr int HALF = 2 * NH;
+            float S1[HALF];
+#pragma unroll
+            for (int n = 0; n < HALF; ++n) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(P[n]), __float_as_uint(P[n + HALF]),
+                                                                 false, false);
+                S1[n] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            const bool upper = (tid & 32) != 0;
+            float* prow = pb + (upper ? g - 4 : g) * HWP + 4 * j;
+            if constexpr (NH == 1) {
+                float2 v2;
+                v2.x = S1[0];
+                v2.y = S1[1];
+                *reinterpret_cast<float2*>(prow + (upper ? 2 : 0)) = v2;
+            } else if constexpr (NH == 3) {
+#pragma unroll
+                for (int n = 0; n < HALF; ++n) {
+                    const int nn = n + (upper ? HALF : 0);
+                    prow[32 * (nn >> 2) + (nn & 3)] = S1[n];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NH / 2; ++i) {
+                    f32x4 v;
+                    v.x = S1[4 * i];
+                    v.y = S1[4 * i + 1];
+                    v.z = S1[4 * i + 2];
+                    v.w = S1[4 * i + 3];
+                    *reinterpret_cast<f32x4*>(prow + 32 * (i + (upper ? NH / 2 : 0))) = v;
+                }
             }
             lds_barrier();
+            // the next step's carry-independent factors: their LDS reads go
+            // out ahead of the tree's, off the carry's path (unconditionally,
+            // from a staged row inside the buffer: after a chunk's last step
+            // they are unused, and the next chunk reloads them)
+            fb = bwd_factors<HW>(stage + (tt + 1 < kBwdChunk ? tt + 1 : tt) * 5 * HW, cqc);
             if (jq < CPG) {   // uniform over each quad
-                const float v = tree_sum16_loads_first(pb + fn * HWP + cqc, 4 * HWP);
+                const float v = tree_sum8_loads_first(pb + fn * HWP + cqc, 8 * HWP);
                 carry_mine = quad_sum4(v);
             }
         };
