@@ -725,6 +725,8 @@ def main():
     ap.add_argument("--only-mlp", action="store_true", help="run and print only the batched MLP step")
     ap.add_argument("--only-step", action="store_true",
                     help="time the headline workload's train step only (for profiling runs)")
+    ap.add_argument("--only-reduce", action="store_true",
+                    help="run and print only the reduce_axis0 shapes (for profiling runs)")
     ap.add_argument("--no-kernels", action="store_true", help="same as --only-step")
     ap.add_argument("--no-steps-path", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--no-gemm-form", action="store_true", help=argparse.SUPPRESS)
@@ -759,6 +761,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only_reduce:
+        shapes = [(b, n) for b in REDUCE_B for n in REDUCE_N]
+        print(json.dumps({"reduce_axis0": bench_reduce(torch, cfc, LaunchTimer(torch), shapes)}), flush=True)
+        return
     if args.only_step or args.no_kernels:
         x = cfc_inputs(**d, seed=0)
         t = [torch.from_numpy(a).cuda() for a in (x.u, x.y, x.h0, x.W, x.bias)]

@@ -1694,32 +1694,62 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(ReduceArgs a)
             }
         }
     }
-    // Block tree over the R slices.  LDS levels while the partner slice is in
-    // another wavefront (sh * lanes >= 64, so `slice < sh` is uniform over
-    // each wavefront): slice i < sh adds the partial that slice i + sh holds
-    // after the previous level.  A level reads slices [sh, 2 sh) and writes
-    // slices [0, sh), so one barrier per level orders it.
+    // Block tree over the R slices, stride halving: slice i < sh adds slice
+    // i + sh, sh = R/2, R/4, ..  The levels whose partner slice is in
+    // another wavefront go through LDS in one exchange: every slice writes
+    // its partial, and after one barrier each lane of the W0 slices of
+    // wavefront 0 (W0 = 64 / lanes when a slice is narrower than a
+    // wavefront, else slice 0 alone) reads the partials p[i + m W0] of the
+    // slices it gathers and adds them in the tree's order.
+    const int W0 = lanes < 64 ? 64 / lanes : 1;
+    const int M = a.R / W0 > 0 ? a.R / W0 : 1;   // partials per gathering lane
     int sh = a.R / 2;
-    if (sh * lanes >= 64) {
+    if (M > 1) {
 #pragma unroll
         for (int jg = 0; jg < G; ++jg)
 #pragma unroll
             for (int e = 0; e < V; ++e) part[jg * V + e][threadIdx.x] = acc[jg][e];
-    }
-    for (; sh > 0 && sh * lanes >= 64; sh >>= 1) {
         __syncthreads();
-        if (slice < sh) {
+        if (slice < W0) {
+            // The stride-halving tree over v[0 .. M) is the pairwise tree of
+            // adjacent values over v in bit-reversed index order: take
+            // u_k = v[bitrev(k)] in turn and fold it into the pending level
+            // sums (lv[l] holds the sum of the last 2^l values), left + right.
+            const int L = 31 - __clz(M);
 #pragma unroll
             for (int jg = 0; jg < G; ++jg)
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[jg][e] += part[jg * V + e][threadIdx.x + sh * lanes];
-            if ((sh >> 1) * lanes >= 64) {
+                for (int e = 0; e < V; ++e) {
+                    double lv[5];
 #pragma unroll
-                for (int jg = 0; jg < G; ++jg)
+                    for (int l = 0; l < 5; ++l) lv[l] = 0.0;
 #pragma unroll
-                    for (int e = 0; e < V; ++e) part[jg * V + e][threadIdx.x] = acc[jg][e];
-            }
+                    for (int k = 0; k < 16; ++k) {
+                        if (k >= M) break;
+                        const int idx = L > 0 ? (int)(__brev((unsigned)k) >> (32 - L)) : 0;
+                        double x = idx == 0 ? acc[jg][e]
+                                            : part[jg * V + e][min((int)threadIdx.x + idx * W0 * lanes, kThreads - 1)];
+#pragma unroll
+                        for (int l = 0; l < 5; ++l) {
+                            if ((k >> l) & 1) {
+                                x = lv[l] + x;
+                            } else {
+                                lv[l] = x;
+                                break;
+                            }
+                        }
+                    }
+                    double r = lv[0];
+#pragma unroll
+                    for (int l = 1; l < 5; ++l)
+                        if (l == L) r = lv[l];
+                    acc[jg][e] = r;
+                    // one tree at a time: keeps the register count (and the
+                    // occupancy of the streaming phase) down
+                    __builtin_amdgcn_sched_barrier(0);
+                }
         }
+        sh = W0 / 2;
     }
     if (threadIdx.x < 64 || slice == 0) {
         // Levels left only when a slice is narrower than a wavefront: then
