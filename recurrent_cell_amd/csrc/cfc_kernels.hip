@@ -1192,6 +1192,71 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 }
             }
         }
+    // Backward: staged rows per step tt of a chunk: 5 tt + v, v = gate, g, hh (act), h_t,
+    // y_t, each C floats at row pitch HW (so that, in a whole chunk, every
+    // step's LDS offsets are constants); register prefetch on the 16-byte path.
+    const int c_w = C / 4;
+    const int c_col = c_w > 0 ? tid % c_w : 0;
+    const int c_row0 = c_w > 0 ? tid / c_w : 5 * kBwdChunk;
+    const int c_rstep = c_w > 0 ? THREADS / c_w : 1;
+    constexpr int CRS_MIN = THREADS / (HW / 4);
+    constexpr int BPF = (5 * kBwdChunk + CRS_MIN - 1) / CRS_MIN;
+    f32x4 bpf[BPF];
+    auto in_row = [&](int t1) {
+        return [=](int rr) {
+            const int tt = rr / 5;
+            const int v = rr - 5 * tt;
+            const int t = t1 - tt;
+            const float* src = (v < 3) ? a.act + (int64_t)(t - 1) * 3 * BC + v * BC
+                             : (v == 3) ? a.h_hist + (int64_t)t * BC : a.y + (int64_t)(t - 1) * BC;
+            return const_cast<float*>(src) + (int64_t)b * C;
+        };
+    };
+    auto dp_row = [&](int t1) {
+        return [=](int tt) { return a.dp + ((int64_t)(t1 - tt - 1) * B + b) * R3; };
+    };
+    // Per-thread addresses of the backward boundary moves (16-byte path),
+    // computed once as in the forward: the input rows of a whole chunk (row
+    // rr clamped to the chunk's last; act for v < 3, else h_hist or y;
+    // without the term of step t1), and dp, where float4 move m of this
+    // thread is element i = tid + m THREADS of the chunk's [nt][3C / 4] block.
+    constexpr int DM = (kBwdChunk * 3 * HW / 4 + THREADS - 1) / THREADS;
+    uint64_t i_addr[BPF];
+    int i_act[BPF];
+    uint64_t d_addr[DM];
+    int d_tt[DM], d_lds[DM];
+    if (c_vec) {
+#pragma unroll
+        for (int m = 0; m < BPF; ++m) {
+            const int rr = min(c_row0 + m * c_rstep, 5 * kBwdChunk - 1);
+            const int tt = rr / 5;
+            const int v = rr - 5 * tt;
+            i_act[m] = v < 3;
+            const int64_t off = (v < 3 ? (int64_t)(-tt - 1) * 3 * BC + (int64_t)v * BC
+                                       : v == 3 ? (int64_t)(-tt) * BC : (int64_t)(-tt - 1) * BC) +
+                                (int64_t)b * C + 4 * c_col;
+            i_addr[m] = (uint64_t)(v < 3 ? a.act : v == 3 ? a.h_hist : a.y) + 4 * (uint64_t)off;
+        }
+        const int w4 = R3 / 4;
+#pragma unroll
+        for (int m = 0; m < DM; ++m) {
+            const int i = tid + m * THREADS;
+            const int tt = i / w4;
+            const int xq = i - tt * w4;
+            d_tt[m] = tt;
+            d_lds[m] = min(tt, kBwdChunk - 1) * R3 + 4 * xq;
+            d_addr[m] = (uint64_t)a.dp + 4 * (uint64_t)((int64_t)b * R3 + 4 * xq - (int64_t)(tt + 1) * B * R3);
+        }
+    }
+    // the backward's per-thread map is computed here, while W is in flight
+    // (it is integer work the step loops never repeat), and pinned so that
+    // it is not moved to the backward
+    if (c_vec) {
+#pragma unroll
+        for (int m = 0; m < BPF; ++m) asm volatile("" : "+v"(i_addr[m]), "+v"(i_act[m]));
+#pragma unroll
+        for (int m = 0; m < DM; ++m) asm volatile("" : "+v"(d_addr[m]), "+v"(d_tt[m]), "+v"(d_lds[m]));
+    }
     for (int i = tid; i < 2 * HW; i += THREADS) (&zs[0][0])[i] = 0.0f;
     __syncthreads();
     for (int c = tid; c < C; c += THREADS) {
@@ -1294,6 +1359,13 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     };
     if (c_vec && K >= 1) load_x(1, min(kFwdChunk, K));
     int prev_t0 = 0, prev_nt = 0;
+    // With K a whole number of chunks the backward's first chunk (steps K ..
+    // K - 15) is the forward's last: it is handed over in LDS from the
+    // forward's output buffer, with y_t loaded during that chunk, instead of
+    // being stored and loaded back after the forward.
+    static_assert(kBwdChunk == kFwdChunk, "the last forward chunk is the first backward chunk");
+    const bool first_from_lds = (K >= kBwdChunk) && (K % kBwdChunk == 0);
+    f32x4 ypf = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int t0 = 1; t0 <= K; t0 += kFwdChunk) {
         const int nt = min(kFwdChunk, K - t0 + 1);
         wait_vmem_all();   // loads and stores issued a whole chunk ago; none waits below
@@ -1318,6 +1390,9 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             else move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, false, out_row(prev_t0));
         }
         if (c_vec && t0 + kFwdChunk <= K) load_x(t0 + kFwdChunk, min(kFwdChunk, K - t0 - kFwdChunk + 1));
+        // y of backward row c_row0 (step K - c_row0) during the last chunk
+        if (c_vec && first_from_lds && t0 + kFwdChunk > K && c_row0 < kBwdChunk)
+            ypf = *reinterpret_cast<const f32x4*>(a.y + ((int64_t)(K - c_row0 - 1) * B + b) * C + 4 * c_col);
         lds_barrier();
         // One step; t0 - 1 is even, so h_{t-1} sits in zs[tt & 1].
         static_assert(kFwdChunk % 2 == 0, "chunks start on odd t");
@@ -1372,11 +1447,47 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         prev_t0 = t0;
         prev_nt = nt;
     }
+    // the stores of the chunks before the last (issued a chunk ago) have
+    // landed: after the barrier below the backward may load those rows
+    wait_vmem_all();
+    if (first_from_lds) {
+        // backward row tt (step K - tt): gate, g, hh, h_t from forward row
+        // 15 - tt of the output buffer (h_t, gate, g, hh), y_t from ypf
+        if (c_vec) {
+            if (c_row0 < kBwdChunk) {
+                const float* o = obuf + (kBwdChunk - 1 - c_row0) * 4 * HW + 4 * c_col;
+                float* st = stage + c_row0 * 5 * HW + 4 * c_col;
+                const f32x4 oh = *reinterpret_cast<const f32x4*>(o);
+                const f32x4 og = *reinterpret_cast<const f32x4*>(o + HW);
+                const f32x4 o2 = *reinterpret_cast<const f32x4*>(o + 2 * HW);
+                const f32x4 o3 = *reinterpret_cast<const f32x4*>(o + 3 * HW);
+                *reinterpret_cast<f32x4*>(st) = og;
+                *reinterpret_cast<f32x4*>(st + HW) = o2;
+                *reinterpret_cast<f32x4*>(st + 2 * HW) = o3;
+                *reinterpret_cast<f32x4*>(st + 3 * HW) = oh;
+                *reinterpret_cast<f32x4*>(st + 4 * HW) = ypf;
+            }
+        } else {
+            for (int tt = 0; tt < kBwdChunk; ++tt)
+                for (int c = tid; c < C; c += THREADS) {
+                    const float* o = obuf + (kBwdChunk - 1 - tt) * 4 * HW + c;
+                    float* st = stage + tt * 5 * HW + c;
+                    st[0] = o[HW];
+                    st[HW] = o[2 * HW];
+                    st[2 * HW] = o[3 * HW];
+                    st[3 * HW] = o[0];
+                    st[4 * HW] = a.y[((int64_t)(K - tt - 1) * B + b) * C + c];
+                }
+        }
+    }
     if (prev_nt > 0) {
         if (c_vec) store_out(prev_t0, prev_nt);
         else move_rows<THREADS, true>(obuf, 4 * prev_nt, C, HW, false, out_row(prev_t0));
     }
-    __syncthreads();   // every forward store is performed and visible to the whole workgroup
+    // otherwise the backward's first loads read the rows just stored, some
+    // by other waves: each wave's stores land before the barrier
+    if (!first_from_lds) wait_vmem_all();
+    __syncthreads();   // the handed-over chunk is visible; obuf is free
 
     if constexpr (CPG == 2) {
         // back to the canonical slots: w[s] of channel g CPG + s in every quad
@@ -1393,62 +1504,6 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     }
 
     // ---------------- backward ----------------
-    // Staged rows per step tt of a chunk: 5 tt + v, v = gate, g, hh (act), h_t,
-    // y_t, each C floats at row pitch HW (so that, in a whole chunk, every
-    // step's LDS offsets are constants); register prefetch on the 16-byte path.
-    const int c_w = C / 4;
-    const int c_col = c_w > 0 ? tid % c_w : 0;
-    const int c_row0 = c_w > 0 ? tid / c_w : 5 * kBwdChunk;
-    const int c_rstep = c_w > 0 ? THREADS / c_w : 1;
-    constexpr int CRS_MIN = THREADS / (HW / 4);
-    constexpr int BPF = (5 * kBwdChunk + CRS_MIN - 1) / CRS_MIN;
-    f32x4 bpf[BPF];
-    auto in_row = [&](int t1) {
-        return [=](int rr) {
-            const int tt = rr / 5;
-            const int v = rr - 5 * tt;
-            const int t = t1 - tt;
-            const float* src = (v < 3) ? a.act + (int64_t)(t - 1) * 3 * BC + v * BC
-                             : (v == 3) ? a.h_hist + (int64_t)t * BC : a.y + (int64_t)(t - 1) * BC;
-            return const_cast<float*>(src) + (int64_t)b * C;
-        };
-    };
-    auto dp_row = [&](int t1) {
-        return [=](int tt) { return a.dp + ((int64_t)(t1 - tt - 1) * B + b) * R3; };
-    };
-    // Per-thread addresses of the backward boundary moves (16-byte path),
-    // computed once as in the forward: the input rows of a whole chunk (row
-    // rr clamped to the chunk's last; act for v < 3, else h_hist or y;
-    // without the term of step t1), and dp, where float4 move m of this
-    // thread is element i = tid + m THREADS of the chunk's [nt][3C / 4] block.
-    constexpr int DM = (kBwdChunk * 3 * HW / 4 + THREADS - 1) / THREADS;
-    uint64_t i_addr[BPF];
-    bool i_act[BPF];
-    uint64_t d_addr[DM];
-    int d_tt[DM], d_lds[DM];
-    if (c_vec) {
-#pragma unroll
-        for (int m = 0; m < BPF; ++m) {
-            const int rr = min(c_row0 + m * c_rstep, 5 * kBwdChunk - 1);
-            const int tt = rr / 5;
-            const int v = rr - 5 * tt;
-            i_act[m] = v < 3;
-            const int64_t off = (v < 3 ? (int64_t)(-tt - 1) * 3 * BC + (int64_t)v * BC
-                                       : v == 3 ? (int64_t)(-tt) * BC : (int64_t)(-tt - 1) * BC) +
-                                (int64_t)b * C + 4 * c_col;
-            i_addr[m] = (uint64_t)(v < 3 ? a.act : v == 3 ? a.h_hist : a.y) + 4 * (uint64_t)off;
-        }
-        const int w4 = R3 / 4;
-#pragma unroll
-        for (int m = 0; m < DM; ++m) {
-            const int i = tid + m * THREADS;
-            const int tt = i / w4;
-            const int xq = i - tt * w4;
-            d_tt[m] = tt;
-            d_lds[m] = min(tt, kBwdChunk - 1) * R3 + 4 * xq;
-            d_addr[m] = (uint64_t)a.dp + 4 * (uint64_t)((int64_t)b * R3 + 4 * xq - (int64_t)(tt + 1) * B * R3);
-        }
-    }
     // the chunk's dp from LDS to memory (16-byte path): LDS reads first
     auto store_dp = [&](int t1, int nt) {
         const uint64_t t1o = 4 * (uint64_t)((int64_t)t1 * B * R3);
@@ -1475,21 +1530,24 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
             bpf[m] = *reinterpret_cast<const f32x4*>(src(min(rr, 5 * nt - 1)) + 4 * c_col);
         }
     };
-    if (c_vec && K >= 1) load_b(K, min(kBwdChunk, K));
+    if (c_vec && K >= 1 && !first_from_lds) load_b(K, min(kBwdChunk, K));
     float carry_mine = 0.0f;   // the carry of the quad's channel
     int prev_t1 = 0;
     prev_nt = 0;
     for (int t1 = K; t1 >= 1; t1 -= kBwdChunk) {
         const int nt = min(kBwdChunk, t1);   // steps t1, t1 - 1, .., t1 - nt + 1
-        wait_vmem_all();   // loads and stores issued a whole chunk ago; none waits below
-        if (c_vec) {
+        if (!first_from_lds || t1 != K) {
+            wait_vmem_all();   // loads and stores issued a whole chunk ago; none waits below
+            if (c_vec) {
 #pragma unroll
-            for (int m = 0; m < BPF; ++m) {
-                const int rr = c_row0 + m * c_rstep;
-                if (c_row0 < c_rstep && rr < 5 * nt) *reinterpret_cast<f32x4*>(stage + rr * HW + 4 * c_col) = bpf[m];
+                for (int m = 0; m < BPF; ++m) {
+                    const int rr = c_row0 + m * c_rstep;
+                    if (c_row0 < c_rstep && rr < 5 * nt)
+                        *reinterpret_cast<f32x4*>(stage + rr * HW + 4 * c_col) = bpf[m];
+                }
+            } else {
+                move_rows<THREADS, false>(stage, 5 * nt, C, HW, false, in_row(t1));
             }
-        } else {
-            move_rows<THREADS, false>(stage, 5 * nt, C, HW, false, in_row(t1));
         }
         if (prev_nt > 0) {
             if (c_vec) store_dp(prev_t1, prev_nt);

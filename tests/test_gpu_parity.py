@@ -38,6 +38,8 @@ CASES = {
     "one_channel": dict(B=2, C=1, n_x=3, K=2),         # C = 1
     "valu_c129": dict(B=65, C=129, n_x=4, K=2),        # one channel past the persistent kernel: VALU steps
     "mfma_long_k": dict(B=64, C=132, n_x=4, K=17),     # MFMA step kernels over more steps than a chunk
+    "whole_chunks": dict(B=3, C=100, n_x=20, K=32),    # K a multiple of the chunk: backward's first chunk from LDS
+    "whole_chunks_odd": dict(B=2, C=37, n_x=3, K=16),  # the same with scalar moves (C % 4 != 0)
 }
 MAX_SIZE = dict(B=1, C=2048, n_x=6144, K=2)            # CFC_MAX_C channels, n_in = CFC_MAX_N_IN
 
