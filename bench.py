@@ -8,9 +8,11 @@ the pages-shaped configuration B=32, C=128, n_x=64 (n_in=192), K=64, fp32,
 inputs seeded and already resident in HBM.  Prints ONE JSON line.
 
 Also measured in the same run:
-  * the duration of each kernel of the step, live: HIP event pairs around
-    eager launches of each phase on the launch stream, with the stream
-    pre-loaded by a spin kernel so the events time the GPU, not the host;
+  * the duration of each kernel of the step, live: one HIP event pair
+    around back-to-back eager launches of each phase on the launch stream,
+    pre-loaded by a spin kernel so the events time the GPU, not the host
+    (pair_median_us: the median of per-launch event pairs, which also hold
+    the event records' own cost);
     the kernel with the largest share of the step gives the roofline object;
   * the same step on the 2K-launch step-kernel path, for contrast;
   * graph-node latency (a graph of dependent one-element kernels), which
@@ -132,9 +134,14 @@ def bwd_launch_bytes(B, C, n_x):
 
 
 class LaunchTimer:
-    """Average GPU duration of one launch of fn: an event pair around each of
-    n launches, with the stream first kept busy by a spin kernel long enough
-    for the host to enqueue them all (so no pair waits on the host)."""
+    """Average GPU duration of one launch of fn: one event pair around n
+    back-to-back launches, with the stream first kept busy by a spin kernel
+    long enough for the host to enqueue them all (so the GPU never waits on
+    the host and the pair times only the launches).  Per-launch event pairs
+    are taken too, for context: each such pair also holds the event records'
+    own cost (about 2 us on this GPU), so their figures run above the kernel
+    durations a kernel trace reports, while the back-to-back mean agrees with
+    them."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -146,7 +153,7 @@ class LaunchTimer:
             torch.cuda.synchronize()
             self.cycles_per_s = 1_000_000 / max(a.elapsed_time(b) * 1e-3, 1e-6)
         except (AttributeError, RuntimeError):
-            self.cycles_per_s = None   # no spin kernel: pairs may include host time
+            self.cycles_per_s = None   # no spin kernel: the pairs may include host time
 
     def _preload(self, seconds):
         if self.cycles_per_s is not None:
@@ -156,20 +163,32 @@ class LaunchTimer:
         torch = self.torch
         fn()
         torch.cuda.synchronize()
-        for _ in range(3):
+        ev = mean_s = None
+        for _ in range(4):
+            # back to back: the launch duration
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            self._preload(n * host_us * 1e-6)
+            h0 = time.perf_counter()
+            s.record()
+            for _ in range(n):
+                fn()
+            e.record()
+            host_s = time.perf_counter() - h0
+            # per-launch pairs (context)
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
             self._preload(n * host_us * 1e-6)
-            for s, e in ev:
-                s.record()
+            for a, b in ev:
+                a.record()
                 fn()
-                e.record()
+                b.record()
             torch.cuda.synchronize()
-            ms = np.array([s.elapsed_time(e) for s, e in ev])
-            gaps = np.array([ev[i][1].elapsed_time(ev[i + 1][0]) for i in range(n - 1)]) if n > 1 else np.zeros(1)
-            if np.median(gaps) < 0.002:
+            mean_s = s.elapsed_time(e) * 1e-3 / n
+            if self.cycles_per_s is None or host_s < 0.5 * n * host_us * 1e-6:
                 break
-            host_us *= 3
-        return dict(mean_s=float(ms.mean()) * 1e-3, median_s=float(np.median(ms)) * 1e-3,
+            host_us *= 3   # the enqueue took longer than the spin covered: spin longer
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        gaps = np.array([ev[i][1].elapsed_time(ev[i + 1][0]) for i in range(n - 1)]) if n > 1 else np.zeros(1)
+        return dict(mean_s=mean_s, pair_mean_s=float(ms.mean()) * 1e-3, pair_median_s=float(np.median(ms)) * 1e-3,
                     gap_median_us=float(np.median(gaps)) * 1e3, n=n)
 
 
@@ -309,12 +328,12 @@ def bench_reduce(torch, cfc, timer, shapes):
             cfc.reduce_axis0(xs[i[0] % copies], out)
             i[0] += 1
         r = timer(run, max(10, copies))
-        t_s = r["median_s"]
+        t_s = r["mean_s"]
         row = dict(B=B, N=N, bytes=nbytes, us=round(t_s * 1e6, 2), GBps=round(nbytes / t_s / 1e9, 1),
                    frac=round(nbytes / t_s / HBM_PEAK, 3), cold=copies * in_bytes >= 512 * 2 ** 20)
         if copies > 1:
             # the same buffer every launch: its reads can come from the Infinity Cache
-            w = timer(lambda: cfc.reduce_axis0(xs[0], out), 20)["median_s"]
+            w = timer(lambda: cfc.reduce_axis0(xs[0], out), 20)["mean_s"]
             row["warm_us"] = round(w * 1e6, 2)
             row["warm_GBps"] = round(nbytes / w / 1e9, 1)
         res.append(row)
@@ -697,8 +716,8 @@ def bench_kloop(torch, cfc, workload, steps, warmup, trials, t_node, detail):
         del S, Sb
     cfc.cfc_train_kloop(*t, out=out)   # restore the step's own state
     torch.cuda.synchronize()
-    res["kernels"] = {k: dict(mean_us=round(v["mean_s"] * 1e6, 3), median_us=round(v["median_s"] * 1e6, 3),
-                              gap_median_us=round(v["gap_median_us"], 3)) for k, v in kt.items()}
+    res["kernels"] = {k: dict(mean_us=round(v["mean_s"] * 1e6, 3), pair_median_us=round(v["pair_median_s"] * 1e6, 3),
+                              n=v["n"]) for k, v in kt.items()}
     res["roofline"] = kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload)
     res["step_roofline"] = step_roofline(path, B, C, n_x, K, ms_per_step, t_node)
     if detail:
