@@ -1,6 +1,7 @@
-// gfx950 kernels of the CfC K-loop: forward and backward (BPTT) step
-// kernels, the persistent per-sample K-loop kernel, the deferred fill of the
-// per-sample gradient scratch, and the batch-axis reduction.
+// gfx950 kernels of the CfC K-loop: the input projection of all steps
+// (MFMA), forward and backward (BPTT) step kernels on VALU and on MFMA, the
+// persistent per-sample K-loop kernel, the deferred fill of the per-sample
+// gradient scratch (MFMA), the batch-axis reduction and AdamW.
 //
 // Parallel structure ("K-loop Parallelization -- Block-per-Batch Kernel
 // Refactor", section Architecture Choice): samples are independent, so no
@@ -10,9 +11,10 @@
 //    still fill the chip.  Channel tile j is the fastest-varying part of the
 //    workgroup id, so it always runs on XCD (j mod 8) and its W rows and
 //    scratch rows stay in that XCD's L2 from one K-step to the next.
-//  * Persistent kernel: one 1024-lane workgroup per sample runs all K forward
-//    and all K backward steps with the sample's W held in registers (when W
-//    fits: 3C x n_in <= 64 DPP rows x 16 lanes x 72 values).
+//  * Persistent kernel: one 512-lane workgroup (8 wave64) per sample runs all
+//    K forward and all K backward steps of the recurrence with the recurrent
+//    columns of W (3C x C, C <= 128) held in registers, 96 values per lane at
+//    C = 128; the input part of every step comes from the input projection.
 // Every (sample, channel) scratch row has exactly one writer.  No atomics.
 //
 // Determinism: every output follows the canonical order of cfc_math.h, which
