@@ -541,7 +541,7 @@ def cpu_baselines(configs, budget_s):
     return out
 
 
-PATH_NAMES = {2: "persistent", 3: "steps_valu", 4: "steps_mfma"}
+PATH_NAMES = {2: "persistent", 3: "steps_valu", 4: "steps_mfma", 5: "resident_mfma"}
 
 
 def step_roofline(path, B, C, n_x, K, ms_per_step, t_node):
@@ -553,7 +553,7 @@ def step_roofline(path, B, C, n_x, K, ms_per_step, t_node):
     floor of the flops or bytes) is given beside it, over this path's launches
     and, as context only, over the pages' 2K + 3 dependent launches."""
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
-    nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3}[path]
+    nodes = {"persistent": 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3, "resident_mfma": 5}[path]
     t_formula = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
     pages_nodes = 2 * K + 3
     t_pages = pages_nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
@@ -630,6 +630,17 @@ def kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload):
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
                 "kernel": "fwd_mfma_kernel + bwd_mfma_kernel (average over the 2K step launches)",
                 "flops_per_launch": fl, "launch_us": round(dur * 1e6, 3)}
+    if path == "resident_mfma":
+        # one launch for all 2K steps (with the W re-layout and the exchange
+        # clear before it, in the timed call)
+        dur = kt["fwd_bwd"]["mean_s"]
+        fl = K * B * 3 * C * (n_in + C) * 2
+        achieved = fl / dur
+        return {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": None,
+                "kernel": "kloop_resident_kernel (all 2K steps; the call also holds the W re-layout)",
+                "flops_per_launch": fl, "launch_us": round(dur * 1e6, 3),
+                "us_per_step": round(dur * 1e6 / (2 * K), 3)}
     dur = kt["fwd_bwd"]["mean_s"] / (2 * K)
     fl = K * B * 3 * C * (n_in + C) * 2 // (2 * K)
     achieved = fl / dur
@@ -671,11 +682,12 @@ def bench_kloop(torch, cfc, workload, steps, warmup, trials, t_node, detail):
     red_out = torch.empty(3 * C * n_in, device="cuda")
     kt["reduce_axis0"] = timer(lambda: cfc.reduce_axis0(gW_flat, red_out), 20)
 
-    if detail:
+    if detail or path == "resident_mfma":
         # another path on the same inputs, for contrast: the step kernels after
-        # the persistent path; the other step-kernel variant after a step path
+        # the persistent path; the other step-kernel variant after a step
+        # path; the MFMA step kernels (2K launches) after the resident kernel
         modes = {"persistent": cfc.KLOOP_STEPS, "steps_mfma": cfc.KLOOP_STEPS_VALU,
-                 "steps_valu": cfc.KLOOP_STEPS_MFMA}
+                 "steps_valu": cfc.KLOOP_STEPS_MFMA, "resident_mfma": cfc.KLOOP_STEPS_MFMA}
         cfc.cfc_set_kloop_mode(modes[path])
         try:
             taken = cfc.cfc_kloop_path(B, C, n_x, K)
@@ -686,6 +698,7 @@ def bench_kloop(torch, cfc, workload, steps, warmup, trials, t_node, detail):
                 del out_c
         finally:
             cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+    if detail:
         # the K-loop step with the GEMM-form weight gradient in place of scratch + reducer
         og = cfc.cfc_train_kloop_gemm(*t)
         ms_g, _ = time_calls(torch, lambda: cfc.cfc_train_kloop_gemm(*t, out=og), max(20, steps // 5), 5, 3)

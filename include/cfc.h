@@ -131,18 +131,23 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *                        S[b,q,c,:] = sum_t dp_q[t,b,c] z_t[b,:] (t = K..1)
  *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
  *                        call's work on `stream` has completed
- * Two paths give the same bits:
+ * The paths give the same bits:
  *  - persistent (C <= 128): an input-projection launch for all steps, one
  *    workgroup per sample running every K step with the recurrent W in
  *    registers, the scratch fill and the reduction -- four launches,
  *    enqueued directly on `stream`;
+ *  - resident MFMA (B >= 64, C > 128, shapes of the MFMA step kernels whose
+ *    grid fits the device at once): a W re-layout, one cooperative launch
+ *    running all 2K steps, the fill and the reduction, enqueued directly (a
+ *    cooperative launch is not captured into graphs: on a stream under
+ *    capture the call takes the MFMA step kernels instead);
  *  - step kernels (any C): 2K step launches, the fill and the reduction,
  *    captured once as a HIP graph per (device, pointers, sizes) and replayed
  *    on later calls with the same key.  Calls sharing a key must be issued
  *    on one stream at a time.  At most 64 graphs are cached; the least
  *    recently used one is evicted and destroyed by a later call once its
  *    last replay has completed (the call never waits for it).
- * cfc_set_kloop_mode() can force either path for the calling thread.  K == 0 or B == 0 writes
+ * cfc_set_kloop_mode() can force a path for the calling thread.  K == 0 or B == 0 writes
  * h_hist[0] = h0 and zeros to the scratch and gradients.
  */
 int cfc_train_kloop(const float* u, const float* y, const float* h0,
@@ -251,21 +256,29 @@ int cfc_scratch_fill(const float* dp, const float* u, const float* h_hist,
                      int B, int C, int n_x, int K, void* stream);
 
 /* Bytes of workspace cfc_train_kloop needs: 4 * (round_up(6 K B C + 2 B C, 64)
- *   + 3 C ldf + 1024 C), ldf = round_up(n_x, 16) + round_up(C, 32).
+ *   + 3 C ldf + 1024 C + 32 ceil(B / 16) (round_up(C, 32) + 1024)
+ *   + round_up(32 (ceil(B / 16) ceil(C / 16) + 1), 64)),
+ *   ldf = round_up(n_x, 16) + round_up(C, 32).
  * Returns 0 for invalid sizes. */
 size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K);
 
 /* Path selection of cfc_train_kloop, cfc_kloop_fwd_bwd and cfc_kloop_path
  * for the CALLING THREAD (each thread starts in CFC_KLOOP_AUTO; a setting
  * never affects the calls of another thread).
- * CFC_KLOOP_AUTO (default): the persistent kernel when C <= 128; otherwise
- *   the step kernels, on MFMA when B >= 64 and the shape fits them (C <= 320
- *   and n_x <= 128, both multiples of 4; 16-byte aligned arrays), else on
- *   VALU;
+ * CFC_KLOOP_AUTO (default): the persistent kernel when C <= 128; otherwise,
+ *   when B >= 64 and the shape fits the MFMA step kernels (C <= 320 and
+ *   n_x <= 128, both multiples of 4; 16-byte aligned arrays), the resident
+ *   MFMA kernel if its ceil(B / 16) ceil(C / 16) workgroups can all be
+ *   resident on the device at once, else the MFMA step kernels; otherwise
+ *   the step kernels on VALU;
  * CFC_KLOOP_STEPS: the step kernels, MFMA or VALU as in AUTO;
  * CFC_KLOOP_PERSISTENT: the persistent kernel;
  * CFC_KLOOP_STEPS_VALU / CFC_KLOOP_STEPS_MFMA: the step kernels on VALU / on
- *   MFMA.
+ *   MFMA;
+ * CFC_KLOOP_RESIDENT: the resident MFMA kernel (the MFMA step kernels' steps,
+ *   all 2K of them in one cooperative launch, each workgroup holding its W
+ *   operands in registers and the workgroups of a sample tile handing one
+ *   another h_t and dp_t through memory, every wait bounded).
  * A mode that forces a path the sizes cannot take makes cfc_train_kloop and
  * cfc_kloop_fwd_bwd return CFC_EINVAL.  All paths give the same bits. */
 enum cfc_kloop_mode {
@@ -273,15 +286,17 @@ enum cfc_kloop_mode {
     CFC_KLOOP_STEPS = 1,
     CFC_KLOOP_PERSISTENT = 2,
     CFC_KLOOP_STEPS_VALU = 3,
-    CFC_KLOOP_STEPS_MFMA = 4
+    CFC_KLOOP_STEPS_MFMA = 4,
+    CFC_KLOOP_RESIDENT = 5
 };
 int cfc_set_kloop_mode(int mode);
 
 /* The path cfc_train_kloop takes for these sizes under the calling thread's
  * mode:
- * CFC_KLOOP_PERSISTENT, CFC_KLOOP_STEPS_VALU or CFC_KLOOP_STEPS_MFMA (the
- * workspace is assumed 16-byte aligned); -1 for invalid sizes or a forced
- * path the sizes cannot take. */
+ * CFC_KLOOP_PERSISTENT, CFC_KLOOP_STEPS_VALU, CFC_KLOOP_STEPS_MFMA or
+ * CFC_KLOOP_RESIDENT (the workspace is assumed 16-byte aligned; the
+ * resident kernel's fit is that of the current device); -1 for invalid
+ * sizes or a forced path the sizes cannot take. */
 int cfc_kloop_path(int B, int C, int n_x, int K);
 
 /* For callers that cannot allocate device memory (code under HIP graph
@@ -292,7 +307,7 @@ int cfc_kloop_path(int B, int C, int n_x, int K);
  * (CFC_NOALLOC_MAX_WS_BYTES; sizes whose cfc_train_kloop_workspace_bytes
  * exceed it give CFC_EINVAL before anything is enqueued).  The call
  * allocates and frees nothing, builds no graph (every launch is enqueued
- * directly on `stream`, on either path, honouring the calling thread's
+ * directly on `stream`, on every path, honouring the calling thread's
  * cfc_set_kloop_mode) and never waits on the device.  Every call on one
  * device shares that device's array: calls whose work overlaps on one device
  * (several streams or threads at once) race and give undefined results;

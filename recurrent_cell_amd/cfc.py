@@ -22,6 +22,7 @@ KLOOP_STEPS = 1
 KLOOP_PERSISTENT = 2
 KLOOP_STEPS_VALU = 3
 KLOOP_STEPS_MFMA = 4
+KLOOP_RESIDENT = 5
 
 _LIB = None
 _P = ctypes.c_void_p
@@ -352,14 +353,16 @@ def cfc_scratch_fill(dp, u, h_hist, gW_scratch, gb_scratch):
 
 
 def cfc_set_kloop_mode(mode):
-    """KLOOP_AUTO, KLOOP_STEPS, KLOOP_PERSISTENT, KLOOP_STEPS_VALU or
-    KLOOP_STEPS_MFMA for the calling thread (other threads keep their own)."""
+    """KLOOP_AUTO, KLOOP_STEPS, KLOOP_PERSISTENT, KLOOP_STEPS_VALU,
+    KLOOP_STEPS_MFMA or KLOOP_RESIDENT for the calling thread (other threads
+    keep their own)."""
     _check("cfc_set_kloop_mode", lib().cfc_set_kloop_mode(int(mode)))
 
 
 def cfc_kloop_path(B, C, n_x, K):
-    """KLOOP_PERSISTENT, KLOOP_STEPS_VALU or KLOOP_STEPS_MFMA: the path
-    cfc_train_kloop takes now on this thread (-1 if its mode cannot take these sizes)."""
+    """KLOOP_PERSISTENT, KLOOP_STEPS_VALU, KLOOP_STEPS_MFMA or KLOOP_RESIDENT:
+    the path cfc_train_kloop takes now on this thread (-1 if its mode cannot
+    take these sizes)."""
     return int(lib().cfc_kloop_path(B, C, n_x, K))
 
 

@@ -125,7 +125,17 @@ int enqueue_reduce(const cfc::ReduceSeg* segs_in, int nseg, int64_t B, hipStream
 // path) | dh ping-pong [2, B, C] (step path) | padding to 256 bytes | the
 // MFMA step path's re-laid W (forward layout, then backward layout).
 int64_t kloop_ws_wofs(int B, int C, int K) { return ((int64_t)2 * K * B * 3 * C + (int64_t)2 * B * C + 63) & ~(int64_t)63; }
-int64_t kloop_ws_floats(int B, int C, int n_x, int K) { return kloop_ws_wofs(B, C, K) + cfc::mfma_w_floats(C, n_x); }
+// After the re-laid W: the resident kernel's exchange blocks, then its step
+// counters (one per workgroup) and error word; all zeroed before its launch.
+int64_t kloop_ws_flags(int B, int C)
+{
+    return ((((int64_t)(B + 15) / 16) * ((C + 15) / 16) + 1) * cfc::kResFlagStride + 63) & ~(int64_t)63;
+}
+int64_t kloop_ws_resident(int B, int C) { return cfc::resident_exchange_floats(B, C) + kloop_ws_flags(B, C); }
+int64_t kloop_ws_floats(int B, int C, int n_x, int K)
+{
+    return kloop_ws_wofs(B, C, K) + cfc::mfma_w_floats(C, n_x) + kloop_ws_resident(B, C);
+}
 
 struct KloopArgs {
     const float *u, *y, *h0, *W, *bias;
@@ -133,8 +143,9 @@ struct KloopArgs {
     int B, C, n_x, K;
 };
 
-// K-loop paths: step kernels on VALU, step kernels on MFMA, persistent.
-enum class Path { Steps = 0, StepsMfma = 1, Persistent = 2 };
+// K-loop paths: step kernels on VALU, step kernels on MFMA, persistent,
+// resident MFMA.
+enum class Path { Steps = 0, StepsMfma = 1, Persistent = 2, Resident = 3 };
 
 // The path mode of the calling thread (cfc_set_kloop_mode): per thread, so
 // that one caller forcing a path never changes another thread's calls.
@@ -143,6 +154,21 @@ thread_local int g_kloop_mode = CFC_KLOOP_AUTO;
 // Smallest batch for which the automatic choice takes the MFMA step kernels
 // (a 16-sample MFMA tile wastes most of its rows below this).
 constexpr int kMfmaMinB = 64;
+
+// Polls of one wait of the resident kernel before it gives up (each poll is
+// one load of the counters and a short sleep, about a microsecond): far
+// beyond any step, so that it only ends a wait that cannot end.
+constexpr int kResidentSpinLimit = 1 << 20;
+
+// A cooperative launch cannot be captured into a graph: a stream under
+// capture takes the MFMA step kernels instead of the resident kernel.
+Path uncaptured(Path path, hipStream_t s)
+{
+    if (path != Path::Resident) return path;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusNone) return path;
+    return Path::StepsMfma;
+}
 
 // The path a K-loop call of these sizes takes in `mode`; false if the mode
 // forces a path the sizes cannot take.
@@ -154,13 +180,19 @@ bool choose_path(int mode, int B, int C, int n_x, std::initializer_list<const vo
     bool aligned = true;
     for (const void* p : ptrs) aligned = aligned && (p == nullptr || aligned16(p));
     const bool mfma_ok = cfc::mfma_fits(C, n_x) && aligned;
+    // the resident kernel: the MFMA step kernels' shapes, with every
+    // workgroup of its grid resident on the current device at once
+    const bool res_ok = mfma_ok && (int64_t)((B + 15) / 16) * ((C + 15) / 16) <=
+                                       cfc::resident_capacity(cfc::mfma_layout(C, n_x));
     switch (mode) {
     case CFC_KLOOP_PERSISTENT: *out = Path::Persistent; return pers_ok;
     case CFC_KLOOP_STEPS_VALU: *out = Path::Steps; return true;
     case CFC_KLOOP_STEPS_MFMA: *out = Path::StepsMfma; return mfma_ok;
+    case CFC_KLOOP_RESIDENT: *out = Path::Resident; return res_ok;
     case CFC_KLOOP_STEPS: *out = (mfma_ok && B >= kMfmaMinB) ? Path::StepsMfma : Path::Steps; return true;
     default:
-        *out = pers_ok ? Path::Persistent : (mfma_ok && B >= kMfmaMinB) ? Path::StepsMfma : Path::Steps;
+        *out = pers_ok ? Path::Persistent
+             : (mfma_ok && B >= kMfmaMinB) ? (res_ok ? Path::Resident : Path::StepsMfma) : Path::Steps;
         return true;
     }
 }
@@ -185,6 +217,37 @@ int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipSt
         CFC_HIP(cfc::launch_xproj(x, s), "input projection launch");
         const cfc::PersistArgs a{X, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
         CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch");
+        return CFC_OK;
+    }
+    if (path == Path::Resident) {
+        const cfc::MfmaLayout L = cfc::mfma_layout(k.C, k.n_x);
+        float* Wf = k.ws + kloop_ws_wofs(k.B, k.C, k.K);
+        float* Wb = Wf + (int64_t)3 * k.C * L.ldf;
+        float* xch = k.ws + kloop_ws_wofs(k.B, k.C, k.K) + cfc::mfma_w_floats(k.C, k.n_x);
+        float* flags = xch + cfc::resident_exchange_floats(k.B, k.C);
+        CFC_HIP(cfc::launch_permute_w(cfc::PermuteArgs{k.W, Wf, Wb, k.C, k.n_x, L}, s), "W re-layout launch");
+        CFC_HIP(cfc::launch_fill_zero(xch, kloop_ws_resident(k.B, k.C), s), "exchange and counter zero fill");
+        cfc::ResidentArgs a{};
+        a.u = k.u;
+        a.y = k.y;
+        a.h0 = k.h0;
+        a.Wf = Wf;
+        a.Wb = Wb;
+        a.bias = k.bias;
+        a.h_hist = k.h_hist;
+        a.act = k.act;
+        a.dp = dp;
+        a.hx = xch;
+        a.dpx = xch + 2 * (((int64_t)k.B + 15) / 16) * 16 * ((k.C + 31) & ~31);
+        a.flags = reinterpret_cast<int*>(flags);
+        a.B = k.B;
+        a.C = k.C;
+        a.n_x = k.n_x;
+        a.K = k.K;
+        a.n_ctiles = (k.C + 15) / 16;
+        a.L = L;
+        a.spin_limit = kResidentSpinLimit;
+        CFC_HIP(cfc::launch_resident(a, s), "resident K-loop launch");
         return CFC_OK;
     }
     if (path == Path::StepsMfma) {
@@ -441,7 +504,7 @@ size_t cfc_train_kloop_workspace_bytes(int B, int C, int n_x, int K)
 int cfc_set_kloop_mode(int mode)
 {
     cfc_host::last_error().clear();
-    if (mode < CFC_KLOOP_AUTO || mode > CFC_KLOOP_STEPS_MFMA)
+    if (mode < CFC_KLOOP_AUTO || mode > CFC_KLOOP_RESIDENT)
         return fail(CFC_EINVAL, "cfc_set_kloop_mode: unknown mode %d", mode);
     g_kloop_mode = mode;
     return CFC_OK;
@@ -453,6 +516,7 @@ int cfc_kloop_path(int B, int C, int n_x, int K)
     Path path;
     if (!choose_path(g_kloop_mode, B, C, n_x, {}, &path)) return -1;
     return path == Path::Persistent ? CFC_KLOOP_PERSISTENT
+         : path == Path::Resident   ? CFC_KLOOP_RESIDENT
          : path == Path::StepsMfma  ? CFC_KLOOP_STEPS_MFMA : CFC_KLOOP_STEPS_VALU;
 }
 
@@ -494,6 +558,10 @@ static int check_kloop(const char* fn, const float* u, const float* y, const flo
     if (!choose_path(mode, B, C, n_x, {ws, u, y, h0, h_hist, act}, path)) {
         if (mode == CFC_KLOOP_PERSISTENT)
             return fail(CFC_EINVAL, "%s: the persistent kernel holds C <= 128 channels (C=%d)", fn, C);
+        if (mode == CFC_KLOOP_RESIDENT && cfc::mfma_fits(C, n_x))
+            return fail(CFC_EINVAL, "%s: the resident kernel's %lld workgroups do not fit the device at once, "
+                        "or an array is not 16-byte aligned (B=%d C=%d)", fn,
+                        (long long)(((int64_t)B + 15) / 16 * ((C + 15) / 16)), B, C);
         return fail(CFC_EINVAL, "%s: the MFMA step kernels take C <= 320 and n_x <= 128, both multiples of 4, "
                     "and 16-byte aligned arrays (C=%d n_x=%d)", fn, C, n_x);
     }
@@ -530,7 +598,8 @@ int cfc_train_kloop(const float* u, const float* y, const float* h0, const float
     // scratch fill, reduction), enqueued directly: replaying them as a graph
     // measured about 5 us slower per step.  The step path's 2K + 2 launches
     // go through the cached graph.
-    if (path == Path::Persistent) return enqueue_kloop(k, path, p, s);
+    path = uncaptured(path, s);
+    if (path == Path::Persistent || path == Path::Resident) return enqueue_kloop(k, path, p, s);
 
     int dev = 0;
     CFC_HIP(hipGetDevice(&dev), "hipGetDevice");
@@ -576,7 +645,7 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
         return CFC_OK;
     }
     const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, nullptr, nullptr, nullptr, nullptr, B, C, n_x, K};
-    return enqueue_fwd_bwd(k, path, make_plan(B, C, n_x, W, nullptr), s);
+    return enqueue_fwd_bwd(k, uncaptured(path, s), make_plan(B, C, n_x, W, nullptr), s);
 }
 
 // ---------------------------------------------------------------------------
@@ -945,9 +1014,10 @@ int cfc_train_kloop_noalloc(const float* u, const float* y, const float* h0, con
         return CFC_OK;
     }
     // every part of the workspace is written before it is read within the
-    // call (dp, X, the carry, the re-laid W), so nothing needs clearing
+    // call (dp, X, the carry, the re-laid W, the resident kernel's counters,
+    // which it zeroes first), so nothing needs clearing
     const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch, gW, gb, B, C, n_x, K};
-    return enqueue_kloop(k, path, make_plan(B, C, n_x, W, gW_scratch), s);
+    return enqueue_kloop(k, uncaptured(path, s), make_plan(B, C, n_x, W, gW_scratch), s);
 }
 
 int cfc_clear_graph_cache(void)

@@ -90,6 +90,10 @@ struct FwdMfmaArgs {
     float* h_prev_copy;   // nullable [B, C]
     int B, C, n_x, n_ctiles;
     MfmaLayout L;
+    // resident kernel only: h_{t-1} and h_t of the sample tile in the staged
+    // layout ([16][cp], recurrent columns permuted like Wf), at agent scope
+    const float* hx;
+    float* hx_out;
 };
 
 struct BwdMfmaArgs {
@@ -107,6 +111,35 @@ struct BwdMfmaArgs {
     const float* y_prev;  // [B, C] y_{t-1}
     const float* act_prev;  // [3, B, C] act_{t-1}
     float* dp_prev_out;   // nullable [B, 3C]: dp of step t - 1 for the tile's channels
+    // resident kernel only: dp_t and dp_{t-1} of the sample tile in the
+    // staged layout ([16][64 groups][16]), at agent scope
+    const float* dpx;
+    float* dpx_out;
+};
+
+// Resident MFMA K-loop (one cooperative launch): workgroup (btile, ctile)
+// runs the forward step and then the backward step of its tile for every t,
+// its W operands held in registers throughout; the workgroups of a sample
+// tile hand h_t, act_t and dp_t to one another through memory, each step
+// gated by their step counters in `flags`.
+constexpr int kResFlagStride = 32;   // ints between the resident kernel's counters
+struct ResidentArgs {
+    const float* u;       // [K, B, n_x]
+    const float* y;       // [K, B, C]
+    const float* h0;      // [B, C]
+    const float* Wf;      // MFMA forward layout
+    const float* Wb;      // MFMA backward layout
+    const float* bias;    // [3, C]
+    float* h_hist;        // [K+1, B, C]
+    float* act;           // [K, 3, B, C]
+    float* dp;            // [K, B, 3C]
+    float* hx;            // [2][n_btiles][16][cp], zero at launch: h_t by step parity, staged layout
+    float* dpx;           // [2][n_btiles][16][64][16], zero at launch: dp_t by step parity, staged layout
+    int* flags;           // [(n_btiles * n_ctiles + 1) * kResFlagStride], zero at launch: steps done per
+                          // workgroup, then an error word, each at the start of its own 128-byte line
+    int B, C, n_x, K, n_ctiles;
+    MfmaLayout L;
+    int spin_limit;       // polls of a wait before it gives up and sets the error word
 };
 
 struct XprojArgs {
@@ -213,6 +246,13 @@ MfmaLayout mfma_layout(int C, int n_x);
 int64_t mfma_w_floats(int C, int n_x);
 bool mfma_fits(int C, int n_x);   // both MFMA step kernels can take this shape
 hipError_t launch_permute_w(const PermuteArgs& a, hipStream_t s);
+// Workgroups of the resident kernel that can run at once on the current
+// device for this layout (0 without cooperative launch); its grid is
+// ceil(B / 16) * ceil(C / 16).
+int64_t resident_capacity(const MfmaLayout& L);
+// Floats of the resident kernel's exchange blocks (hx, then dpx) for B, C.
+int64_t resident_exchange_floats(int B, int C);
+hipError_t launch_resident(const ResidentArgs& a, hipStream_t s);
 hipError_t launch_fwd_mfma(const FwdMfmaArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const BwdMfmaArgs& a, hipStream_t s);
 

@@ -22,6 +22,7 @@
 // persistent kernel and a B = 1 run of any single sample all produce the
 // same bits.
 #include "cfc_kernels.h"
+#include <climits>
 #include "cfc_math.h"
 
 namespace cfc {
@@ -491,11 +492,45 @@ __global__ __launch_bounds__(kThreads) void permute_w_kernel(PermuteArgs a)
     }
 }
 
-constexpr int kFwdMfmaThreads = 576;   // three waves per head
-constexpr int kMfmaMaxNxb = 8;         // input column blocks of 16: n_x <= 128
-constexpr int kMfmaMaxNhb = 10;        // recurrent column blocks of 32: C <= 320
-constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
-
+// Moves of the resident kernel (kloop_resident_kernel): its workgroups hand
+// h_t, act_t and dp_t to one another through memory while they run, so those
+// arrays are written and read at agent scope (write-through stores, loads
+// that do not hit stale cache lines); the step kernels, whose launches are
+// ordered by the stream, use plain moves.  RES selects.
+__device__ __forceinline__ float ld_agent(const float* p)
+{
+    return __int_as_float(__hip_atomic_load(reinterpret_cast<int*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_agent(float* p, float v)
+{
+    __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool RES>
+__device__ __forceinline__ float ld1(const float* p)
+{
+    if constexpr (RES) return ld_agent(p);
+    else return *p;
+}
+template <bool RES>
+__device__ __forceinline__ f32x4 ld4(const float* p)
+{
+    if constexpr (RES) {
+        unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float*>(p));
+        const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return f32x4{__int_as_float((int)(unsigned)lo), __int_as_float((int)(unsigned)(lo >> 32)),
+                     __int_as_float((int)(unsigned)hi), __int_as_float((int)(unsigned)(hi >> 32))};
+    } else {
+        return *reinterpret_cast<const f32x4*>(p);
+    }
+}
+template <bool RES>
+__device__ __forceinline__ void st1(float* p, float v)
+{
+    if constexpr (RES) st_agent(p, v);
+    else *p = v;
+}
 // Forward step on MFMA.  Workgroup = 16 samples x 16 channels; three waves
 // per head q: part 0 forms the four input chains (x_r: k-slot kk of block p
 // is column 16 p + 4 kk + r) and X = bias + ((x0+x1)+(x2+x3)); part 1 the
@@ -507,44 +542,76 @@ constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
 // first LDS store.  Needs n_x, C multiples of 4 and 16-byte aligned rows.  Operand layout (16 x 16 x 4): A[sample l % 16][k-slot l /
 // 16], B[k-slot l / 16][channel l % 16]; D[sample i][channel j] in lane
 // j + 16 (i / 4), register i % 4.
-__global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a)
+constexpr int kFwdMfmaThreads = 576;   // three waves per head
+constexpr int kMfmaMaxNxb = 8;         // input column blocks of 16: n_x <= 128
+constexpr int kMfmaMaxNhb = 10;        // recurrent column blocks of 32: C <= 320
+constexpr int kMfmaMaxLdf = 16 * kMfmaMaxNxb + 32 * kMfmaMaxNhb;
+constexpr int kFwdMfmaZs = 16 * (kMfmaMaxLdf + 4);   // staged z rows (floats)
+
+// This lane's W operands straight from the forward layout into registers
+// (each W value feeds exactly one lane's MFMAs, so it needs no LDS): row
+// (head q, channel c0 + li), the four k-slots of every block of the wave's
+// part.  Blocks past nxb / nhb load a clamped block, never used.  The bias
+// first, in flight with the operand loads (loaded after the MFMAs it was a
+// round trip of its own before the epilogue).
+__device__ __forceinline__ void fwd_mfma_operands(const FwdMfmaArgs& a, int c0, f32x4 (&wv)[kMfmaMaxNhb],
+                                                  float& bias)
 {
-    __shared__ __attribute__((aligned(16))) float zs[16 * (kMfmaMaxLdf + 4)];
-    __shared__ float as[3][3][16 * 16];   // [head][X, half 1, half 2][sample, channel]
     const MfmaLayout L = a.L;
     const int C = a.C;
-    const int n_x = a.n_x;
     const int nxb = L.nxp / 16;
     const int nhb = L.cp / 32;
-    const int ctile = blockIdx.x % a.n_ctiles;
-    const int btile = blockIdx.x / a.n_ctiles;
-    const int s0 = btile * 16;
-    const int c0 = ctile * 16;
-    const int ldp = L.ldf + 4;              // row pitch: 4 banks between rows
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int q = (tid >> 6) / 3;       // head
-    const int part = (tid >> 6) % 3;    // 0: input chains, 1: P_0..P_3, 2: P_4..P_7 (uniform per wave)
+    const int q = (tid >> 6) / 3;
+    const int part = (tid >> 6) % 3;
     const int li = lane & 15;
     const int lk = lane >> 4;
-
-    // This lane's W operands straight from the forward layout into
-    // registers (each W value feeds exactly one lane's MFMAs, so it needs no
-    // LDS): row (head q, channel c0 + li), the four k-slots of every block of
-    // the wave's part, issued with the z loads below before any of them is
-    // waited for.  Blocks past nxb / nhb load a clamped block, never used.
     const float* wrow = a.Wf + ((int64_t)q * C + min(c0 + li, C - 1)) * L.ldf;
-    // the bias first, in flight with the operand loads (loaded after the
-    // MFMAs it was a round trip of its own before the epilogue)
-    const float bias = a.bias[q * C + min(c0 + li, C - 1)];
+    bias = a.bias[q * C + min(c0 + li, C - 1)];
     static_assert(kMfmaMaxNxb <= kMfmaMaxNhb, "one register block array serves both parts");
-    f32x4 wv[kMfmaMaxNhb];
 #pragma unroll
     for (int i = 0; i < kMfmaMaxNhb; ++i) {
         const int o = (part == 0) ? 16 * min(i, nxb - 1) + 4 * lk
                                   : L.nxp + 32 * min(i, nhb - 1) + 8 * lk + 4 * (part - 1);
         wv[i] = *reinterpret_cast<const f32x4*>(wrow + o);
     }
+}
+
+// Place of recurrent column m in a staged z row past the input columns
+// (the Wf permutation): 32 (m / 32) + 8 (m % 4) + (m % 32) / 4.
+__device__ __forceinline__ int staged_h_col(int m) { return 32 * (m >> 5) + 8 * (m & 3) + ((m & 31) >> 2); }
+
+// One forward step of the workgroup's tile (btile, ctile) given its W
+// operands; zs and as are the step's LDS (kFwdMfmaZs and 3 x 3 x 256 floats).
+// RES (resident kernel): z is read and h_t, act_t written at agent scope,
+// and h_t also goes to the sample tile's exchange rows hx_out in the staged
+// layout; HX: h_{t-1} comes from the exchange rows hx (copied as they are)
+// instead of h_prev.
+template <bool RES, bool HX>
+__device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, int ctile,
+                                              const f32x4 (&wv)[kMfmaMaxNhb], float bias, float* zs,
+                                              float (*as)[3][16 * 16])
+{
+    const MfmaLayout L = a.L;
+    const int C = a.C;
+    const int n_x = a.n_x;
+    const int nxb = L.nxp / 16;
+    const int nhb = L.cp / 32;
+    const int s0 = btile * 16;
+    const int c0 = ctile * 16;
+    const int ldp = L.ldf + 4;              // row pitch: 4 banks between rows
+    int tid = threadIdx.x;
+    // the resident kernel runs this body once per step: the per-lane index
+    // arithmetic is recomputed each time rather than held in registers
+    // across the K steps
+    if constexpr (RES) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int q = (tid >> 6) / 3;       // head
+    const int part = (tid >> 6) % 3;    // 0: input chains, 1: P_0..P_3, 2: P_4..P_7 (uniform per wave)
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+
     // z rows in float4 units: unit u of row s covers columns 4 u .. 4 u + 3
     // of [u ; h] in their natural order (zero past n_x, past C and for
     // absent samples); h goes to its permuted LDS place.
@@ -559,8 +626,9 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
             const int u4 = i - s * w4;
             const int64_t b = min(s0 + s, a.B - 1);
             const float* src = (4 * u4 < L.nxp) ? a.u_t + b * n_x + min(4 * u4, max(n_x - 4, 0))
-                                                : a.h_prev + b * C + min(4 * u4 - L.nxp, C - 4);
-            v[m] = *reinterpret_cast<const f32x4*>(src);
+                             : HX ? a.hx + s * L.cp + (4 * u4 - L.nxp)
+                                  : a.h_prev + b * C + min(4 * u4 - L.nxp, C - 4);
+            v[m] = ld4<RES>(src);
         }
 #pragma unroll
         for (int m = 0; m < kZSlots; ++m) {
@@ -573,6 +641,9 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
                 if (4 * u4 < L.nxp) {
                     const bool ok = live && 4 * u4 < n_x;
                     *reinterpret_cast<f32x4*>(row + 4 * u4) = ok ? v[m] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                } else if (HX) {
+                    // staged already: zero for absent samples and past C (never written)
+                    *reinterpret_cast<f32x4*>(row + 4 * u4) = v[m];
                 } else {
                     const int m0 = 4 * u4 - L.nxp;              // recurrent columns m0 .. m0 + 3
                     const bool ok = live && m0 < C;
@@ -587,7 +658,7 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
         const int nb = min(16, a.B - s0);
         for (int i = tid; i < nb * C; i += kFwdMfmaThreads) {
             const int64_t idx = (int64_t)s0 * C + i;
-            a.h_prev_copy[idx] = a.h_prev[idx];
+            st1<RES>(a.h_prev_copy + idx, a.h_prev[idx]);
         }
     }
     __syncthreads();
@@ -641,12 +712,25 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
             for (int h = 0; h < 3; ++h) pre[h] = as[h][0][i] + (as[h][1][i] + as[h][2][i]);   // X + H
             const CellOut o = cell_forward(pre[0], pre[1], pre[2]);
             const int64_t bc = (int64_t)b * C + c;
-            a.h_t[bc] = o.h;
-            a.act_t[bc] = o.gate;
-            a.act_t[BC + bc] = o.g;
-            a.act_t[2 * BC + bc] = o.hh;
+            st1<RES>(a.h_t + bc, o.h);
+            st1<RES>(a.act_t + bc, o.gate);
+            st1<RES>(a.act_t + BC + bc, o.g);
+            st1<RES>(a.act_t + 2 * BC + bc, o.hh);
+            if constexpr (RES) st_agent(a.hx_out + s * L.cp + staged_h_col(c), o.h);
         }
     }
+}
+
+__global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float zs[kFwdMfmaZs];
+    __shared__ float as[3][3][16 * 16];   // [head][X, half 1, half 2][sample, channel]
+    const int ctile = blockIdx.x % a.n_ctiles;
+    const int btile = blockIdx.x / a.n_ctiles;
+    f32x4 wv[kMfmaMaxNhb];
+    float bias;
+    fwd_mfma_operands(a, ctile * 16, wv, bias);
+    fwd_mfma_step<false, false>(a, btile, ctile, wv, bias, zs, as);
 }
 
 // Backward step (K-loop: dp out, carry) on MFMA.  Workgroup = 16 samples x
@@ -659,26 +743,54 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
 // the first three levels of the pairwise tree of tree_sum16; its last level
 // adds the halves.  Then dz = (T0 + T1) + (T2 + T3).
 constexpr int kBwdMfmaThreads = 512;   // 4 subtrees x 2 halves of their 16 groups
+constexpr int kBwdMfmaDps = 16 * kDzGroups * 16;
 
-template <int PG>
-__global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a)
+// This lane's W operands of the carry: the 8 groups g = w + 4 (8 hf + m)
+// of its half of subtree w, carry column k0 + li.  Lanes past the 512 that
+// form the carry (the resident kernel runs 576) load half 1's, never used.
+__device__ __forceinline__ void bwd_mfma_operands(const BwdMfmaArgs& a, int k0, f32x4 (&bv)[8])
 {
-    __shared__ __attribute__((aligned(16))) float dps[16 * kDzGroups * 16];
-    __shared__ __attribute__((aligned(16))) float ts[2][4][16][17];   // [half][subtree][sample][column]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = (tid >> 6) & 3;           // subtree
+    const int hf = min(tid >> 8, 1);        // half of the subtree's 16 groups: m = 8 hf .. 8 hf + 7
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const float* wb = a.Wb + ((int64_t)min(k0 + li, a.C - 1) * kDzGroups) * 16 + 4 * lk;   // + 16 g
+#pragma unroll
+    for (int m = 0; m < 8; ++m) bv[m] = *reinterpret_cast<const f32x4*>(wb + 16 * (w + 4 * (8 * hf + m)));
+}
+
+// One backward step of the workgroup's tile (btile, ctile); dps and ts are
+// its LDS (kBwdMfmaDps and 2 x 4 x 16 x 17 floats).  The step kernel loads
+// the W operands after the dp staging (bv is its own); the resident kernel
+// (RES) holds them for every step and reads h, act and dp written by other
+// workgroups at agent scope, and also writes dp_{t-1} of its channels to
+// the sample tile's exchange block dpx_out in the staged layout, at agent
+// scope.  DP: where the step's dp comes from -- kDpRuntime: from dp_in when
+// it is not null, else formed from h_t, y_t and act_t (the step kernel);
+// kDpIn: the resident kernel's exchange block dpx, copied as it is (the
+// positions no channel writes stay zero from the launch); kDpFormed: formed
+// (the resident kernel's step K).
+constexpr int kDpRuntime = 0, kDpIn = 1, kDpFormed = 2;
+template <int PG, bool RES, int DP>
+__device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, int ctile, f32x4 (&bv)[8],
+                                              float* dps, float (*ts)[4][16][17])
+{
     const int C = a.C;
     const int cpg = dz_group_channels(C);
-    const int ctile = blockIdx.x % a.n_ctiles;
-    const int btile = blockIdx.x / a.n_ctiles;
     const int s0 = btile * 16;
     const int k0 = ctile * 16;
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    if constexpr (RES) asm volatile("" : "+v"(tid));   // as in fwd_mfma_step
+    const bool active = !RES || tid < kBwdMfmaThreads;   // uniform per wave
     const int64_t BC = (int64_t)a.B * C;
 
     // inputs of the epilogue (dp of step t - 1 for (sample tid / 16, channel
     // k0 + tid % 16)), loaded now so that their latency is hidden
     float ep_h = 0.0f, ep_y = 0.0f, ep_g0 = 0.0f, ep_g1 = 0.0f, ep_g2 = 0.0f;
     {
-        const int s = tid >> 4;
+        const int s = (tid >> 4) & 31;
         const int col = tid & 15;
         const int64_t bk = (int64_t)min(s0 + s, a.B - 1) * C + min(k0 + col, C - 1);
         // unconditional loads (a load under a branch is waited for where the
@@ -687,15 +799,27 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
         const float* hp = prev ? a.h_prev : a.h_t;
         const float* yp = prev ? a.y_prev : a.y_t;
         const float* gp = prev ? a.act_prev : a.act_t;
-        ep_h = hp[bk];
+        ep_h = ld1<RES>(hp + bk);
         ep_y = yp[bk];
-        ep_g0 = gp[bk];
-        ep_g1 = gp[BC + bk];
-        ep_g2 = gp[2 * BC + bk];
+        ep_g0 = ld1<RES>(gp + bk);
+        ep_g1 = ld1<RES>(gp + BC + bk);
+        ep_g2 = ld1<RES>(gp + 2 * BC + bk);
     }
-    for (int i = tid; i < 16 * kDzGroups * 16; i += kBwdMfmaThreads) dps[i] = 0.0f;
+    if (DP != kDpIn && active)
+        for (int i = tid; i < kBwdMfmaDps; i += kBwdMfmaThreads) dps[i] = 0.0f;
     const int c4n = C / 4;
-    if (a.dp_in != nullptr) {
+    if constexpr (DP == kDpIn) {
+        constexpr int kXSlots = kBwdMfmaDps / 4 / kBwdMfmaThreads;
+        static_assert(kXSlots * 4 * kBwdMfmaThreads == kBwdMfmaDps, "whole passes");
+        f32x4 vx[kXSlots];
+        if (active) {
+#pragma unroll
+            for (int m = 0; m < kXSlots; ++m) vx[m] = ld4<true>(a.dpx + 4 * (tid + m * kBwdMfmaThreads));
+#pragma unroll
+            for (int m = 0; m < kXSlots; ++m)
+                *reinterpret_cast<f32x4*>(dps + 4 * (tid + m * kBwdMfmaThreads)) = vx[m];
+        }
+    } else if (DP == kDpRuntime && a.dp_in != nullptr) {
         // dp of this step, formed at the end of the launch of step t + 1: the
         // tile's samples, all heads and channels (float4 over 4 channels of
         // one head), every load in flight before the LDS stores.
@@ -707,14 +831,14 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
             const int i = min(tid + m * kBwdMfmaThreads, n4 - 1);
             const int s = i / (3 * c4n);
             const int r4 = i - s * 3 * c4n;   // float4 index within the sample's 3C
-            vp[m] = *reinterpret_cast<const f32x4*>(a.dp_in + (int64_t)min(s0 + s, a.B - 1) * 3 * C + 4 * r4);
+            vp[m] = ld4<RES>(a.dp_in + (int64_t)min(s0 + s, a.B - 1) * 3 * C + 4 * r4);
         }
         __syncthreads();   // zeros of dps in place before the dp stores
 #pragma unroll
         for (int m = 0; m < kPSlots; ++m) {
             const int i = tid + m * kBwdMfmaThreads;
             const int s = i / (3 * c4n);
-            if (i < n4 && s0 + s < a.B) {
+            if (active && i < n4 && s0 + s < a.B) {
                 const int r4 = i - s * 3 * c4n;
                 const int qq = r4 / c4n;
 #pragma unroll
@@ -736,19 +860,19 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
         const int i = min(tid + m * kBwdMfmaThreads, 16 * c4n - 1);
         const int s = i / c4n;
         const int64_t bc = (int64_t)min(s0 + s, a.B - 1) * C + 4 * (i - s * c4n);
-        vh[m] = *reinterpret_cast<const f32x4*>(a.h_t + bc);
+        vh[m] = ld4<RES>(a.h_t + bc);
         vy[m] = *reinterpret_cast<const f32x4*>(a.y_t + bc);
         vd[m] = (a.dh_in != nullptr) ? *reinterpret_cast<const f32x4*>(a.dh_in + bc) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        vg0[m] = *reinterpret_cast<const f32x4*>(a.act_t + bc);
-        vg1[m] = *reinterpret_cast<const f32x4*>(a.act_t + BC + bc);
-        vg2[m] = *reinterpret_cast<const f32x4*>(a.act_t + 2 * BC + bc);
+        vg0[m] = ld4<RES>(a.act_t + bc);
+        vg1[m] = ld4<RES>(a.act_t + BC + bc);
+        vg2[m] = ld4<RES>(a.act_t + 2 * BC + bc);
     }
     __syncthreads();   // zeros of dps in place before the dp stores
 #pragma unroll
     for (int m = 0; m < kDSlots; ++m) {
         const int i = tid + m * kBwdMfmaThreads;
         const int s = i / c4n;
-        if (i < 16 * c4n && s0 + s < a.B) {
+        if (active && i < 16 * c4n && s0 + s < a.B) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 4 * (i - s * c4n) + e;
@@ -774,36 +898,37 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
     }
     __syncthreads();
 
-    const int lane = tid & 63;
-    const int w = (tid >> 6) & 3;   // subtree
-    const int hf = tid >> 8;        // half of the subtree's 16 groups: m = 8 hf .. 8 hf + 7
-    const int li = lane & 15;
-    const int lk = lane >> 4;
-    const float* wb = a.Wb + ((int64_t)min(k0 + li, C - 1) * kDzGroups) * 16 + 4 * lk;   // + 16 g
-    const float* da = dps + li * kDzGroups * 16 + 4 * lk;                                 // + 16 g
-    f32x4 bv[8];
+    if (active) {
+        const int lane = tid & 63;
+        const int w = (tid >> 6) & 3;   // subtree
+        const int hf = (tid >> 8) & 1;  // half of the subtree's 16 groups: m = 8 hf .. 8 hf + 7
+        const int li = lane & 15;
+        const int lk = lane >> 4;
+        if constexpr (!RES || DP == kDpFormed) {
+            bwd_mfma_operands(a, k0, bv);
+            __builtin_amdgcn_sched_barrier(0);   // the 8 loads ahead of the MFMAs
+        }
+        const float* da = dps + li * kDzGroups * 16 + 4 * lk;   // + 16 g
+        // The half's 8 group partials as independent MFMA chains (so that their
+        // instructions interleave), then the first three levels of the pairwise
+        // tree of tree_sum16; its last level adds the two halves below.
+        f32x4 av[8], P[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) bv[m] = *reinterpret_cast<const f32x4*>(wb + 16 * (w + 4 * (8 * hf + m)));
-    __builtin_amdgcn_sched_barrier(0);   // the 8 loads ahead of the MFMAs
-    // The half's 8 group partials as independent MFMA chains (so that their
-    // instructions interleave), then the first three levels of the pairwise
-    // tree of tree_sum16; its last level adds the two halves below.
-    f32x4 av[8], P[8];
+        for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * (8 * hf + m)));
 #pragma unroll
-    for (int m = 0; m < 8; ++m) av[m] = *reinterpret_cast<const f32x4*>(da + 16 * (w + 4 * (8 * hf + m)));
+        for (int m = 0; m < 8; ++m) P[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) P[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int p = 0; p < PG; ++p)
 #pragma unroll
-    for (int p = 0; p < PG; ++p)
+            for (int m = 0; m < 8; ++m) P[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][p], bv[m][p], P[m], 0, 0, 0);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) P[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][p], bv[m][p], P[m], 0, 0, 0);
+        for (int m = 0; m < 4; ++m) P[m] = P[2 * m] + P[2 * m + 1];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) P[m] = P[2 * m] + P[2 * m + 1];
+        for (int m = 0; m < 2; ++m) P[m] = P[2 * m] + P[2 * m + 1];
+        const f32x4 T = P[0] + P[1];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) P[m] = P[2 * m] + P[2 * m + 1];
-    const f32x4 T = P[0] + P[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ts[hf][w][4 * lk + e][li] = T[e];
+        for (int e = 0; e < 4; ++e) ts[hf][w][4 * lk + e][li] = T[e];
+    }
     __syncthreads();
     if (tid < 256) {
         const int s = tid >> 4;
@@ -826,7 +951,170 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
                 const int64_t row = (int64_t)b * 3 * C;
 #pragma unroll
                 for (int qq = 0; qq < 3; ++qq) a.dp_prev_out[row + qq * C + k] = d[qq];
+                if constexpr (RES) {
+                    const int g = k / cpg;
+#pragma unroll
+                    for (int qq = 0; qq < 3; ++qq) {
+                        const int el = 3 * (k - g * cpg) + qq;
+                        st_agent(a.dpx_out + (s * kDzGroups + g) * 16 + 4 * (el & 3) + (el >> 2), d[qq]);
+                    }
+                }
             }
+        }
+    }
+}
+
+template <int PG>
+__global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float dps[kBwdMfmaDps];
+    __shared__ __attribute__((aligned(16))) float ts[2][4][16][17];   // [half][subtree][sample][column]
+    f32x4 bv[8];
+    bwd_mfma_step<PG, false, kDpRuntime>(a, blockIdx.x / a.n_ctiles, blockIdx.x % a.n_ctiles, bv, dps, ts);
+}
+
+// ---------------------------------------------------------------------------
+// Resident MFMA K-loop: the step kernels' bodies, each workgroup running all
+// 2K steps of its (sample tile, channel tile) in one cooperative launch with
+// its W operands in registers.  Step t of a tile needs h_{t-1} (forward) or
+// dp_t (backward) of every channel tile of its samples, so the workgroups of
+// a sample tile count their finished steps in `flags` (forward step t: t;
+// backward step t: 2K - t + 1) and a step waits until all of them have
+// reached the one it needs.  The exchanged arrays move at agent scope (see
+// ld_agent), and a counter is written only after every wave's stores of the
+// step are performed, so a workgroup that sees a counter also sees the data
+// behind it; no atomics, no cache maintenance.  The arithmetic of every step
+// is the step kernels', so the bits are theirs.  The launch is cooperative:
+// every workgroup is resident, so every wait ends; a wait also gives up after
+// spin_limit polls (or once another workgroup has given up), setting the
+// error word, so that no failure can keep the kernel running.
+// ---------------------------------------------------------------------------
+constexpr int kResThreads = kFwdMfmaThreads;   // the backward's 512 lanes and one more wave
+constexpr int kResFwdLds = kFwdMfmaZs + 3 * 3 * 16 * 16;
+constexpr int kResBwdLds = kBwdMfmaDps + 2 * 4 * 16 * 17;
+constexpr int kResLds = kResFwdLds > kResBwdLds ? kResFwdLds : kResBwdLds;
+
+// Wave 0 polls the counters of the sample tile's nct workgroups (one lane
+// each; the other lanes read the error word, in the same round trip) until
+// all reach `need`, or a workgroup has given up; the other waves wait at the
+// barrier.  Each counter has a cache line of its own (kResFlagStride ints
+// apart), so that the tile's writers do not contend for one line; one poll
+// in flight at a time (more slowed the counters' stores).
+__device__ __forceinline__ void resident_wait(int* flags, int base, int nct, int err, int need, int spin_limit)
+{
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const bool counter = lane < nct;
+        int* p = flags + kResFlagStride * (counter ? base + lane : err);
+        for (int it = 0;; ++it) {
+            const int v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__all(!counter || v >= need) || __any(!counter && v != 0)) break;
+            if (it >= spin_limit) {
+                if (lane == 0) __hip_atomic_store(flags + kResFlagStride * err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    lds_barrier();
+}
+
+// Every wave's stores of the step performed, then the workgroup's counter.
+__device__ __forceinline__ void resident_report(int* flags, int pos, int steps)
+{
+    wait_vmem_all();
+    lds_barrier();
+    if (threadIdx.x == 0) __hip_atomic_store(flags + kResFlagStride * pos, steps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int PG>
+__global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArgs a)
+{
+    // the forward's and the backward's LDS share one buffer (the wait before
+    // the first backward step orders the last forward reads before it)
+    __shared__ __attribute__((aligned(16))) float lds[kResLds];
+    const int nct = a.n_ctiles;
+    const int ctile = blockIdx.x % nct;
+    const int btile = blockIdx.x / nct;
+    const int base = btile * nct;
+    const int err = gridDim.x;
+    const int K = a.K;
+    const int64_t BC = (int64_t)a.B * a.C;
+    const int64_t BX = (int64_t)a.B * a.n_x;
+    {
+        float* zs = lds;
+        float (*as)[3][16 * 16] = reinterpret_cast<float (*)[3][16 * 16]>(lds + kFwdMfmaZs);
+        FwdMfmaArgs f{};
+        f.Wf = a.Wf;
+        f.bias = a.bias;
+        f.B = a.B;
+        f.C = a.C;
+        f.n_x = a.n_x;
+        f.n_ctiles = nct;
+        f.L = a.L;
+        f32x4 wv[kMfmaMaxNhb];
+        float bias;
+        fwd_mfma_operands(f, ctile * 16, wv, bias);
+        // h_t of the sample tile in the staged layout, by the parity of t
+        const int64_t hx_tile = (int64_t)16 * a.L.cp;
+        const int64_t hx_par = (int64_t)gridDim.x / nct * hx_tile;
+        float* hx = a.hx + btile * hx_tile;
+        auto set_step = [&](int t) {
+            f.u_t = a.u + (int64_t)(t - 1) * BX;
+            f.h_prev = (t == 1) ? a.h0 : a.h_hist + (int64_t)(t - 1) * BC;
+            f.h_t = a.h_hist + (int64_t)t * BC;
+            f.act_t = a.act + (int64_t)(t - 1) * 3 * BC;
+            f.h_prev_copy = (t == 1) ? a.h_hist : nullptr;
+            f.hx = hx + ((t - 1) & 1) * hx_par;
+            f.hx_out = hx + (t & 1) * hx_par;
+        };
+        set_step(1);   // h_0 from h0, staged as the step kernel does
+        fwd_mfma_step<true, false>(f, btile, ctile, wv, bias, zs, as);
+        for (int t = 2; t <= K; ++t) {
+            resident_report(a.flags, base + ctile, t - 1);
+            resident_wait(a.flags, base, nct, err, t - 1, a.spin_limit);
+            set_step(t);
+            fwd_mfma_step<true, true>(f, btile, ctile, wv, bias, zs, as);
+        }
+        resident_report(a.flags, base + ctile, K);
+    }
+    {
+        float* dps = lds;
+        float (*ts)[4][16][17] = reinterpret_cast<float (*)[4][16][17]>(lds + kBwdMfmaDps);
+        BwdMfmaArgs g{};
+        g.Wb = a.Wb;
+        g.B = a.B;
+        g.C = a.C;
+        g.n_ctiles = nct;
+        g.L = a.L;
+        // dp_t of the sample tile in the staged layout, by the parity of t
+        const int64_t dpx_par = (int64_t)gridDim.x / nct * kBwdMfmaDps;
+        float* dpx = a.dpx + btile * (int64_t)kBwdMfmaDps;
+        auto set_step = [&](int t) {
+            g.dpx = dpx + (t & 1) * dpx_par;
+            g.dpx_out = dpx + ((t - 1) & 1) * dpx_par;
+            g.h_t = a.h_hist + (int64_t)t * BC;
+            g.y_t = a.y + (int64_t)(t - 1) * BC;
+            g.act_t = a.act + (int64_t)(t - 1) * 3 * BC;
+            g.dp_out = a.dp + (int64_t)(t - 1) * 3 * BC;
+            g.dp_in = (t == K) ? nullptr : a.dp + (int64_t)(t - 1) * 3 * BC;
+            g.h_prev = (t > 1) ? a.h_hist + (int64_t)(t - 1) * BC : nullptr;
+            g.y_prev = (t > 1) ? a.y + (int64_t)(t - 2) * BC : nullptr;
+            g.act_prev = (t > 1) ? a.act + (int64_t)(t - 2) * 3 * BC : nullptr;
+            g.dp_prev_out = (t > 1) ? a.dp + (int64_t)(t - 2) * 3 * BC : nullptr;
+        };
+        // t = K: every forward step done; dp formed from h, y and act, the W
+        // operands loaded after that staging (as the step kernel does) and
+        // then kept for the steps that read dp_t of every channel tile
+        f32x4 bv[8];
+        resident_wait(a.flags, base, nct, err, K, a.spin_limit);
+        set_step(K);
+        bwd_mfma_step<PG, true, kDpFormed>(g, btile, ctile, bv, dps, ts);
+        for (int t = K - 1; t >= 1; --t) {
+            resident_report(a.flags, base + ctile, 2 * K - t);   // step t + 1 done
+            resident_wait(a.flags, base, nct, err, 2 * K - t, a.spin_limit);
+            set_step(t);
+            bwd_mfma_step<PG, true, kDpIn>(g, btile, ctile, bv, dps, ts);
         }
     }
 }
@@ -2069,6 +2357,56 @@ hipError_t launch_bwd_mfma(const BwdMfmaArgs& a, hipStream_t s)
     default: hipLaunchKernelGGL((bwd_mfma_kernel<4>), dim3((unsigned)blocks), dim3(kBwdMfmaThreads), 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+namespace {
+const void* resident_fn(int pg)
+{
+    switch (pg) {
+    case 1: return (const void*)kloop_resident_kernel<1>;
+    case 2: return (const void*)kloop_resident_kernel<2>;
+    case 3: return (const void*)kloop_resident_kernel<3>;
+    default: return (const void*)kloop_resident_kernel<4>;
+    }
+}
+}  // namespace
+
+int64_t resident_capacity(const MfmaLayout& L)
+{
+    constexpr int kMaxDev = 64;
+    static int64_t cap[kMaxDev][5];
+    static bool known[kMaxDev][5];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev || L.pg < 1 || L.pg > 4) return 0;
+    if (!known[dev][L.pg]) {
+        int coop = 0, cus = 0, per_cu = 0;
+        int64_t c = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, resident_fn(L.pg), kResThreads, 0) == hipSuccess)
+            c = (int64_t)cus * per_cu;
+        cap[dev][L.pg] = c;
+        known[dev][L.pg] = true;
+    }
+    return cap[dev][L.pg];
+}
+
+int64_t resident_exchange_floats(int B, int C)
+{
+    const int64_t nbt = ((int64_t)B + 15) / 16;
+    return 2 * nbt * ((int64_t)16 * ((C + 31) & ~31) + kBwdMfmaDps);
+}
+
+hipError_t launch_resident(const ResidentArgs& a, hipStream_t s)
+{
+    if (a.L.pg < 1 || a.L.pg > 4 || !mfma_fits(a.C, a.n_x) || a.n_ctiles != (a.C + 15) / 16 || a.K < 1)
+        return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)((a.B + 15) / 16) * a.n_ctiles;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > resident_capacity(a.L)) return hipErrorCooperativeLaunchTooLarge;
+    ResidentArgs arg = a;
+    void* params[] = {&arg};
+    return hipLaunchCooperativeKernel(resident_fn(a.L.pg), dim3((unsigned)blocks), dim3(kResThreads), params, 0, s);
 }
 
 hipError_t launch_xproj(const XprojArgs& a, hipStream_t s)

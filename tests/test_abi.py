@@ -134,7 +134,10 @@ def test_projection_and_recurrence_argument_errors(L):
 
 def ws_bytes(B, C, n_x, K):
     ldf = (n_x + 15) // 16 * 16 + (C + 31) // 32 * 32
-    return 4 * (((6 * K * B * C + 2 * B * C + 63) // 64) * 64 + 3 * C * ldf + 1024 * C)
+    nbt = (B + 15) // 16
+    flags = (32 * (nbt * ((C + 15) // 16) + 1) + 63) // 64 * 64
+    xch = 32 * nbt * ((C + 31) // 32 * 32 + 1024)
+    return 4 * (((6 * K * B * C + 2 * B * C + 63) // 64) * 64 + 3 * C * ldf + 1024 * C + xch + flags)
 
 
 def test_workspace_size_and_path_queries(L):
@@ -142,8 +145,11 @@ def test_workspace_size_and_path_queries(L):
     assert L.cfc_train_kloop_workspace_bytes(3, 37, 5, 7) == ws_bytes(3, 37, 5, 7)
     assert L.cfc_train_kloop_workspace_bytes(-1, 128, 64, 64) == 0
     # persistent kernel for C <= 128 (any n_x: X is precomputed); step kernels otherwise,
-    # on MFMA from B = 64 where the shape fits them (C <= 320, n_x + C up to ~540)
-    P, VALU, MFMA = 2, 3, 4
+    # on MFMA from B = 64 where the shape fits them (C <= 320, n_x + C up to ~540).  The
+    # resident MFMA kernel needs a device that holds its whole grid at once: without a
+    # GPU (here) it fits nowhere, so its shapes take the MFMA step kernels and forcing it
+    # is refused
+    P, VALU, MFMA, RES = 2, 3, 4, 5
     assert L.cfc_kloop_path(32, 128, 64, 64) == P
     assert L.cfc_kloop_path(256, 256, 128, 64) == MFMA
     assert L.cfc_kloop_path(32, 256, 128, 64) == VALU      # B below the MFMA threshold
@@ -156,6 +162,10 @@ def test_workspace_size_and_path_queries(L):
     assert L.cfc_kloop_path(4, 128, 4000, 4) == P
     assert L.cfc_kloop_path(4, 129, 0, 4) == VALU
     assert L.cfc_set_kloop_mode(7) == -1
+    assert L.cfc_set_kloop_mode(6) == -1
+    assert L.cfc_set_kloop_mode(RES) == 0
+    assert L.cfc_kloop_path(256, 256, 128, 64) == -1
+    assert L.cfc_set_kloop_mode(0) == 0
     assert L.cfc_set_kloop_mode(1) == 0                      # steps: MFMA or VALU by shape
     assert L.cfc_kloop_path(32, 128, 64, 64) == VALU
     assert L.cfc_kloop_path(64, 128, 64, 64) == MFMA
@@ -220,11 +230,16 @@ def test_graph_cache_never_waits_on_the_device():
 
 
 def test_no_atomics_in_kernel_sources():
-    """Device code (kernels and the shared device math) uses no atomics."""
+    """Device code (kernels and the shared device math) uses no read-modify-write
+    atomics.  The only atomic builtins allowed are plain loads and stores with an
+    agent coherence scope (__hip_atomic_load / __hip_atomic_store), by which the
+    resident kernel's workgroups read one another's step counters and outputs."""
     csrc = os.path.join(ROOT, "recurrent_cell_amd", "csrc")
     for fn in ("cfc_kernels.hip", "cfc_math.h", "cfc_kernels.h", "gemm_kernels.hip", "gemm_kernels.h"):
         text = open(os.path.join(csrc, fn)).read()
-        assert not re.search(r"\batomic\w*\s*\(|__hip_atomic|__atomic_|std::atomic", text), fn
+        assert not re.search(r"\batomic\w*\s*\(|__atomic_|std::atomic", text), fn
+        for m in re.finditer(r"__hip_atomic_\w+", text):
+            assert m.group(0) in ("__hip_atomic_load", "__hip_atomic_store"), (fn, m.group(0))
 
 
 def test_product_never_imports_the_oracle():

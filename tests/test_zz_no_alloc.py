@@ -49,12 +49,16 @@ def run_both(cfc, d, seed):
     ("auto", dict(B=32, C=128, n_x=64, K=64), dict(B=4, C=16, n_x=8, K=4)),           # persistent kernel
     ("steps", dict(B=64, C=132, n_x=4, K=5), dict(B=3, C=129, n_x=0, K=2)),           # MFMA, then VALU steps
     ("steps_valu", dict(B=33, C=40, n_x=12, K=6), dict(B=2, C=20, n_x=5, K=3)),       # VALU steps, ragged
+    ("resident", dict(B=64, C=132, n_x=4, K=5), dict(B=32, C=128, n_x=64, K=8)),      # resident MFMA kernel
 ])
 def test_noalloc_equals_train_kloop_on_two_calls(cfc, mode, first, second):
-    m = {"auto": cfc.KLOOP_AUTO, "steps": cfc.KLOOP_STEPS, "steps_valu": cfc.KLOOP_STEPS_VALU}[mode]
+    m = {"auto": cfc.KLOOP_AUTO, "steps": cfc.KLOOP_STEPS, "steps_valu": cfc.KLOOP_STEPS_VALU,
+         "resident": cfc.KLOOP_RESIDENT}[mode]
     cfc.cfc_set_kloop_mode(m)
     try:
         for i, d in enumerate((first, second)):
+            if cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"], d["K"]) < 0:
+                pytest.skip("the forced path cannot take this shape on this device")
             say("no-alloc K-loop", mode, "call", i + 1, d, "path", cfc.cfc_kloop_path(d["B"], d["C"], d["n_x"],
                                                                                     d["K"]))
             run_both(cfc, d, seed=31 + i)
