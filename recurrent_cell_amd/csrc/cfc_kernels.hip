@@ -5,12 +5,16 @@
 //
 // Parallel structure ("K-loop Parallelization -- Block-per-Batch Kernel
 // Refactor", section Architecture Choice): samples are independent, so no
-// workgroup ever waits for another.
+// workgroup waits for another -- except inside the resident MFMA kernel,
+// where the channel tiles of one sample tile hand each step's h_t and dp_t
+// to one another under bounded waits.
 //  * Step kernels: a workgroup owns (a tile of samples) x (16 channels).  A
 //    sample is split over ceil(C / 16) workgroups so that B = 32 samples
 //    still fill the chip.  Channel tile j is the fastest-varying part of the
 //    workgroup id, so it always runs on XCD (j mod 8) and its W rows and
 //    scratch rows stay in that XCD's L2 from one K-step to the next.
+//  * Resident MFMA kernel (wide shapes): the MFMA step kernels' steps, all 2K
+//    of them in one cooperative launch, W operands held in registers.
 //  * Persistent kernel: one 512-lane workgroup (8 wave64) per sample runs all
 //    K forward and all K backward steps of the recurrence with the recurrent
 //    columns of W (3C x C, C <= 128) held in registers, 96 values per lane at
