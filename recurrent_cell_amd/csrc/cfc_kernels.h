@@ -90,10 +90,6 @@ struct FwdMfmaArgs {
     float* h_prev_copy;   // nullable [B, C]
     int B, C, n_x, n_ctiles;
     MfmaLayout L;
-    // resident kernel only: h_{t-1} and h_t of the sample tile in the staged
-    // layout ([16][cp], recurrent columns permuted like Wf), at agent scope
-    const float* hx;
-    float* hx_out;
 };
 
 struct BwdMfmaArgs {
@@ -133,8 +129,10 @@ struct ResidentArgs {
     float* h_hist;        // [K+1, B, C]
     float* act;           // [K, 3, B, C]
     float* dp;            // [K, B, 3C]
-    float* hx;            // [2][n_btiles][16][cp], zero at launch: h_t by step parity, staged layout
-    float* dpx;           // [2][n_btiles][16][64][16], zero at launch: dp_t by step parity, staged layout
+    float* hx;            // [2][n_btiles][16][cp], zero at launch: h_t by step parity, column
+                          // c = 32 i + 4 m + e of a sample at 4 (m cp / 32 + i) + e
+    float* dpx;           // [2][n_btiles][16][64][16], zero at launch: dp_t by step parity, the backward
+                          // step's LDS layout
     int* flags;           // [(n_btiles * n_ctiles + 1) * kResFlagStride], zero at launch: steps done per
                           // workgroup, then an error word, each at the start of its own 128-byte line
     int B, C, n_x, K, n_ctiles;

@@ -13,13 +13,16 @@
 //    still fill the chip.  Channel tile j is the fastest-varying part of the
 //    workgroup id, so it always runs on XCD (j mod 8) and its W rows and
 //    scratch rows stay in that XCD's L2 from one K-step to the next.
-//  * Resident MFMA kernel (wide shapes): the MFMA step kernels' steps, all 2K
-//    of them in one cooperative launch, W operands held in registers.
+//  * Resident MFMA kernel (wide shapes): all 2K steps of the MFMA step
+//    kernels' arithmetic in one cooperative launch, W operands held in
+//    registers; the channel tiles of a sample tile sit on one XCD, and each
+//    step's input projection is formed while the tile waits for the others.
 //  * Persistent kernel: one 512-lane workgroup (8 wave64) per sample runs all
 //    K forward and all K backward steps of the recurrence with the recurrent
 //    columns of W (3C x C, C <= 128) held in registers, 96 values per lane at
 //    C = 128; the input part of every step comes from the input projection.
-// Every (sample, channel) scratch row has exactly one writer.  No atomics.
+// Every (sample, channel) scratch row has exactly one writer.  No atomic
+// read-modify-write.
 //
 // Determinism: every output follows the canonical order of cfc_math.h, which
 // depends only on the sizes, so repeated runs, the step-kernel graph, the
@@ -510,6 +513,16 @@ __device__ __forceinline__ void st_agent(float* p, float v)
 {
     __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte load with the cache policy of ld_agent's loads (sc1), through a
+// raw buffer resource over [base, base + bytes): one request per 16 bytes,
+// where two 8-byte agent-scope loads make two (neither is served by the
+// vector L1).  Offsets at or past `bytes` read zero.
+__device__ __forceinline__ f32x4 ld4_dev(const float* base, int bytes, int byte_off)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
+}
 template <bool RES>
 __device__ __forceinline__ float ld1(const float* p)
 {
@@ -576,23 +589,14 @@ __device__ __forceinline__ void fwd_mfma_operands(const FwdMfmaArgs& a, int c0, 
     static_assert(kMfmaMaxNxb <= kMfmaMaxNhb, "one register block array serves both parts");
 #pragma unroll
     for (int i = 0; i < kMfmaMaxNhb; ++i) {
-        const int o = (part == 0) ? 16 * min(i, nxb - 1) + 4 * lk
+        const int o = (part == 0) ? 16 * max(min(i, nxb - 1), 0) + 4 * lk
                                   : L.nxp + 32 * min(i, nhb - 1) + 8 * lk + 4 * (part - 1);
         wv[i] = *reinterpret_cast<const f32x4*>(wrow + o);
     }
 }
 
-// Place of recurrent column m in a staged z row past the input columns
-// (the Wf permutation): 32 (m / 32) + 8 (m % 4) + (m % 32) / 4.
-__device__ __forceinline__ int staged_h_col(int m) { return 32 * (m >> 5) + 8 * (m & 3) + ((m & 31) >> 2); }
-
 // One forward step of the workgroup's tile (btile, ctile) given its W
 // operands; zs and as are the step's LDS (kFwdMfmaZs and 3 x 3 x 256 floats).
-// RES (resident kernel): z is read and h_t, act_t written at agent scope,
-// and h_t also goes to the sample tile's exchange rows hx_out in the staged
-// layout; HX: h_{t-1} comes from the exchange rows hx (copied as they are)
-// instead of h_prev.
-template <bool RES, bool HX>
 __device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, int ctile,
                                               const f32x4 (&wv)[kMfmaMaxNhb], float bias, float* zs,
                                               float (*as)[3][16 * 16])
@@ -605,11 +609,7 @@ __device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, i
     const int s0 = btile * 16;
     const int c0 = ctile * 16;
     const int ldp = L.ldf + 4;              // row pitch: 4 banks between rows
-    int tid = threadIdx.x;
-    // the resident kernel runs this body once per step: the per-lane index
-    // arithmetic is recomputed each time rather than held in registers
-    // across the K steps
-    if constexpr (RES) asm volatile("" : "+v"(tid));
+    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int q = (tid >> 6) / 3;       // head
     const int part = (tid >> 6) % 3;    // 0: input chains, 1: P_0..P_3, 2: P_4..P_7 (uniform per wave)
@@ -630,9 +630,8 @@ __device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, i
             const int u4 = i - s * w4;
             const int64_t b = min(s0 + s, a.B - 1);
             const float* src = (4 * u4 < L.nxp) ? a.u_t + b * n_x + min(4 * u4, max(n_x - 4, 0))
-                             : HX ? a.hx + s * L.cp + (4 * u4 - L.nxp)
-                                  : a.h_prev + b * C + min(4 * u4 - L.nxp, C - 4);
-            v[m] = ld4<RES>(src);
+                                                : a.h_prev + b * C + min(4 * u4 - L.nxp, C - 4);
+            v[m] = *reinterpret_cast<const f32x4*>(src);
         }
 #pragma unroll
         for (int m = 0; m < kZSlots; ++m) {
@@ -645,9 +644,6 @@ __device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, i
                 if (4 * u4 < L.nxp) {
                     const bool ok = live && 4 * u4 < n_x;
                     *reinterpret_cast<f32x4*>(row + 4 * u4) = ok ? v[m] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                } else if (HX) {
-                    // staged already: zero for absent samples and past C (never written)
-                    *reinterpret_cast<f32x4*>(row + 4 * u4) = v[m];
                 } else {
                     const int m0 = 4 * u4 - L.nxp;              // recurrent columns m0 .. m0 + 3
                     const bool ok = live && m0 < C;
@@ -662,7 +658,7 @@ __device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, i
         const int nb = min(16, a.B - s0);
         for (int i = tid; i < nb * C; i += kFwdMfmaThreads) {
             const int64_t idx = (int64_t)s0 * C + i;
-            st1<RES>(a.h_prev_copy + idx, a.h_prev[idx]);
+            a.h_prev_copy[idx] = a.h_prev[idx];
         }
     }
     __syncthreads();
@@ -716,11 +712,10 @@ __device__ __forceinline__ void fwd_mfma_step(const FwdMfmaArgs& a, int btile, i
             for (int h = 0; h < 3; ++h) pre[h] = as[h][0][i] + (as[h][1][i] + as[h][2][i]);   // X + H
             const CellOut o = cell_forward(pre[0], pre[1], pre[2]);
             const int64_t bc = (int64_t)b * C + c;
-            st1<RES>(a.h_t + bc, o.h);
-            st1<RES>(a.act_t + bc, o.gate);
-            st1<RES>(a.act_t + BC + bc, o.g);
-            st1<RES>(a.act_t + 2 * BC + bc, o.hh);
-            if constexpr (RES) st_agent(a.hx_out + s * L.cp + staged_h_col(c), o.h);
+            a.h_t[bc] = o.h;
+            a.act_t[bc] = o.gate;
+            a.act_t[BC + bc] = o.g;
+            a.act_t[2 * BC + bc] = o.hh;
         }
     }
 }
@@ -734,7 +729,7 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
     f32x4 wv[kMfmaMaxNhb];
     float bias;
     fwd_mfma_operands(a, ctile * 16, wv, bias);
-    fwd_mfma_step<false, false>(a, btile, ctile, wv, bias, zs, as);
+    fwd_mfma_step(a, btile, ctile, wv, bias, zs, as);
 }
 
 // Backward step (K-loop: dp out, carry) on MFMA.  Workgroup = 16 samples x
@@ -786,7 +781,10 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
     const int s0 = btile * 16;
     const int k0 = ctile * 16;
     int tid = threadIdx.x;
-    if constexpr (RES) asm volatile("" : "+v"(tid));   // as in fwd_mfma_step
+    // the resident kernel runs this body once per step: the per-lane index
+    // arithmetic is recomputed each time rather than held in registers
+    // across the K steps
+    if constexpr (RES) asm volatile("" : "+v"(tid));
     const bool active = !RES || tid < kBwdMfmaThreads;   // uniform per wave
     const int64_t BC = (int64_t)a.B * C;
 
@@ -818,7 +816,8 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
         f32x4 vx[kXSlots];
         if (active) {
 #pragma unroll
-            for (int m = 0; m < kXSlots; ++m) vx[m] = ld4<true>(a.dpx + 4 * (tid + m * kBwdMfmaThreads));
+            for (int m = 0; m < kXSlots; ++m)
+                vx[m] = ld4_dev(a.dpx, 4 * kBwdMfmaDps, 16 * (tid + m * kBwdMfmaThreads));
 #pragma unroll
             for (int m = 0; m < kXSlots; ++m)
                 *reinterpret_cast<f32x4*>(dps + 4 * (tid + m * kBwdMfmaThreads)) = vx[m];
@@ -978,25 +977,250 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Resident MFMA K-loop: the step kernels' bodies, each workgroup running all
-// 2K steps of its (sample tile, channel tile) in one cooperative launch with
-// its W operands in registers.  Step t of a tile needs h_{t-1} (forward) or
-// dp_t (backward) of every channel tile of its samples, so the workgroups of
-// a sample tile count their finished steps in `flags` (forward step t: t;
-// backward step t: 2K - t + 1) and a step waits until all of them have
-// reached the one it needs.  The exchanged arrays move at agent scope (see
-// ld_agent), and a counter is written only after every wave's stores of the
-// step are performed, so a workgroup that sees a counter also sees the data
-// behind it; no atomics, no cache maintenance.  The arithmetic of every step
-// is the step kernels', so the bits are theirs.  The launch is cooperative:
-// every workgroup is resident, so every wait ends; a wait also gives up after
+// Resident MFMA K-loop: each workgroup runs all 2K steps of its (sample
+// tile, channel tile) in one cooperative launch with its W operands in
+// registers.  Step t of a tile needs h_{t-1} (forward) or dp_t (backward) of
+// every channel tile of its samples, so the workgroups of a sample tile
+// count their finished steps in `flags` (forward step t: t; backward step t:
+// 2K - t + 1) and a step waits until all of them have reached the one it
+// needs.  The exchanged arrays move at agent scope (see ld_agent), and a
+// counter is written only after every wave's stores of the step are
+// performed, so a workgroup that sees a counter also sees the data behind
+// it; no atomics, no cache maintenance.  The backward steps are the
+// backward step kernel's body; the forward steps take the input projection
+// X (bias included) from xproj_kernel's output and form only the recurrent
+// part, one wave per partition (below).  Every sum is the step kernels'
+// canonical one, so the bits are theirs.  The launch is cooperative: every
+// workgroup is resident, so every wait ends; a wait also gives up after
 // spin_limit polls (or once another workgroup has given up), setting the
 // error word, so that no failure can keep the kernel running.
 // ---------------------------------------------------------------------------
-constexpr int kResThreads = kFwdMfmaThreads;   // the backward's 512 lanes and one more wave
-constexpr int kResFwdLds = kFwdMfmaZs + 3 * 3 * 16 * 16;
+constexpr int kResThreads = kBwdMfmaThreads;   // eight waves
+// Forward LDS: h_{t-1} rows [16][cp + 4], u rows [16][nxp + 4], the
+// recurrent partials [3][8][256] and X [3][256];
+// backward LDS: the step kernel's.  At least 81 KB, so that one workgroup
+// sits on each CU (two would share one CU's matrix cores and leave another
+// idle).
+constexpr int kResHp = 32 * kMfmaMaxNhb + 4;
+constexpr int kResUp = 16 * kMfmaMaxNxb + 4;
+constexpr int kResZh = 0, kResZu = 16 * kResHp, kResAs = kResZu + 16 * kResUp, kResXs = kResAs + 3 * 8 * 256;
+constexpr int kResFwdLds = kResXs + 3 * 256;
 constexpr int kResBwdLds = kBwdMfmaDps + 2 * 4 * 16 * 17;
-constexpr int kResLds = kResFwdLds > kResBwdLds ? kResFwdLds : kResBwdLds;
+constexpr int kResLdsMin = 81 * 1024 / 4;
+constexpr int kResLds = kResFwdLds > kResBwdLds ? (kResFwdLds > kResLdsMin ? kResFwdLds : kResLdsMin)
+                                                : (kResBwdLds > kResLdsMin ? kResBwdLds : kResLdsMin);
+
+// Forward h exchange rows (and their LDS copy): recurrent column c = 32 i +
+// 4 m + e of a sample sits at 4 (m nhb + i) + e, so that partition m's k-slot
+// e at block i, for the 16 samples, is one conflict-free LDS read (row pitch
+// cp + 4) and a row's float4 groups are the natural ones, permuted.
+__device__ __forceinline__ int res_hx_pos(int c, int nhb) { return 4 * (((c & 31) >> 2) * nhb + (c >> 5)) + (c & 3); }
+
+// The lane's W operands of the resident forward.  Wave m (0..7) holds, for
+// each head q, the B operand of recurrent partition P_m at every block i
+// (k-slot lk of block i is recurrent column 32 i + 4 m + lk of channel
+// c0 + li, found in the forward layout at the n_x padding + 32 i + 8 lk + m).
+// Waves 4..6 form head m - 4's input chains and hold the forward step
+// kernel's part-0 operands of that head (wx) and its bias.  Blocks past nhb
+// / nxb load a clamped block, never used.
+__device__ __forceinline__ void fwd_res_operands(const ResidentArgs& a, int c0, float (&wq)[3][kMfmaMaxNhb],
+                                                 f32x4 (&wx)[kMfmaMaxNxb], float& xbias)
+{
+    const MfmaLayout L = a.L;
+    const int C = a.C;
+    const int nhb = L.cp / 32;
+    const int nxb = L.nxp / 16;
+    const int lane = threadIdx.x & 63;
+    const int m = threadIdx.x >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int cl = min(c0 + li, C - 1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const float* wrow = a.Wf + ((int64_t)q * C + cl) * L.ldf;
+#pragma unroll
+        for (int i = 0; i < kMfmaMaxNhb; ++i) wq[q][i] = wrow[L.nxp + 32 * min(i, nhb - 1) + 8 * lk + m];
+    }
+    const int qx = min(max(m - 4, 0), 2);
+    const float* xrow = a.Wf + ((int64_t)qx * C + cl) * L.ldf;
+#pragma unroll
+    for (int p = 0; p < kMfmaMaxNxb; ++p)
+        wx[p] = *reinterpret_cast<const f32x4*>(xrow + 16 * max(min(p, nxb - 1), 0) + 4 * lk);
+    xbias = a.bias[qx * C + cl];
+}
+
+// u_t rows of the tile's samples, one float4 per lane (zero past n_x and
+// for absent samples), loaded unconditionally from a clamped address.
+// With n_x = 0 nothing is read (u may hold no element).
+__device__ __forceinline__ f32x4 res_load_u(const ResidentArgs& a, int t, int s0)
+{
+    const int w4 = a.L.nxp / 4;
+    if (w4 == 0) return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int i = min((int)threadIdx.x, 16 * w4 - 1);
+    const int s = i / w4;
+    const int k = 4 * (i - s * w4);
+    const int b = s0 + s;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.u + ((int64_t)(t - 1) * a.B + min(b, a.B - 1)) * a.n_x +
+                                                    min(k, a.n_x - 4));
+    return ((int)threadIdx.x < 16 * w4 && b < a.B && k < a.n_x) ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+__device__ __forceinline__ void res_store_u(const ResidentArgs& a, f32x4 v, float* zu)
+{
+    const int w4 = a.L.nxp / 4;
+    if ((int)threadIdx.x < 16 * w4) {
+        const int s = threadIdx.x / w4;
+        *reinterpret_cast<f32x4*>(zu + s * kResUp + 4 * (threadIdx.x - s * w4)) = v;
+    }
+}
+
+// Input projection of one step, wave 4 + q for head q (q < 3): the forward
+// step kernel's part-0 chains x_r (k-slot kk of block p is input column 16 p
+// + 4 kk + r) from the u rows in LDS, then X = bias + ((x0 + x1) + (x2 + x3))
+// into xs[q].
+__device__ __forceinline__ void res_xproj(const f32x4 (&wx)[kMfmaMaxNxb], float xbias, int nxb, const float* zu,
+                                          float (*xs)[256])
+{
+    const int lane = threadIdx.x & 63;
+    const int q = (threadIdx.x >> 6) - 4;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const float* ur = zu + li * kResUp + 4 * lk;
+    f32x4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < kMfmaMaxNxb; ++p) {
+        if (p < nxb) {
+            const f32x4 uv = *reinterpret_cast<const f32x4*>(ur + 16 * p);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(uv[c], wx[p][c], acc[c], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        xs[q][(4 * lk + e) * 16 + li] = xproj_combine(xbias, acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+}
+
+// One resident forward step t of tile (btile, ctile); X_t is in LDS on
+// entry (formed by waves 4..6 from u_t's rows while the workgroup waited for
+// the other tiles, or before step 1) and u_{t+1}'s rows on return.  h_{t-1}
+// is copied into LDS from the exchange rows hx (HX) or, at t = 1, from h0,
+// its loads issued before u_{t+1}'s.  Wave m forms recurrent partition P_m
+// of the three heads (the forward step kernel's chains, with their A and B
+// operands) into as[q][m].  Then waves 0..3 run the epilogue, pre_q = X_q +
+// (((P0 + P1) + (P2 + P3)) + ((P4 + P5) + (P6 + P7))), the step kernel's
+// order, writing h_t and act_t at agent scope and h_t also to the exchange
+// rows hx_out; every lane stores its part of u_{t+1}'s rows.
+template <bool HX>
+__device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int btile, int ctile,
+                                             const float (&wq)[3][kMfmaMaxNhb], float* lds, const float* hx,
+                                             float* hx_out)
+{
+    const int C = a.C;
+    const int B = a.B;
+    const int cp = a.L.cp;
+    const int nhb = cp / 32;
+    const int hp = cp + 4;
+    const int s0 = btile * 16;
+    const int c0 = ctile * 16;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // per-step index arithmetic, not held across steps
+    const int lane = tid & 63;
+    const int m = tid >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int64_t BC = (int64_t)B * C;
+    float* zh = lds + kResZh;
+    float* zu = lds + kResZu;
+    float (*as)[8][256] = reinterpret_cast<float (*)[8][256]>(lds + kResAs);
+    float (*xs)[256] = reinterpret_cast<float (*)[256]>(lds + kResXs);
+
+    // h_{t-1} rows into LDS, every load in flight before the LDS stores
+    const int c4 = cp / 4;
+    constexpr int kHSlots = (16 * 32 * kMfmaMaxNhb / 4 + kResThreads - 1) / kResThreads;
+    f32x4 hv4[kHSlots];
+#pragma unroll
+    for (int k = 0; k < kHSlots; ++k) {
+        const int idx = min(tid + k * kResThreads, 16 * c4 - 1);
+        const int s = idx / c4;
+        const int g = idx - s * c4;
+        if constexpr (HX) {
+            hv4[k] = ld4_dev(hx, 4 * 16 * cp, 16 * idx);
+        } else {
+            const int b = s0 + s;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(a.h0 + (int64_t)min(b, B - 1) * C + min(4 * g, C - 4));
+            hv4[k] = (b < B && 4 * g < C) ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+    // u_{t+1}'s load, issued after the h loads so that their wait does not
+    // include it
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4 uq = res_load_u(a, min(t + 1, a.K), s0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kHSlots; ++k) {
+        const int idx = tid + k * kResThreads;
+        if (idx < 16 * c4) {
+            const int s = idx / c4;
+            const int g = idx - s * c4;
+            // exchange rows hold the LDS order already; h0 rows are natural
+            const int pos = HX ? 4 * g : res_hx_pos(4 * g, nhb);
+            *reinterpret_cast<f32x4*>(zh + s * hp + pos) = hv4[k];
+        }
+    }
+    if (!HX && ctile == 0) {
+        const int nb = min(16, B - s0);
+        for (int i = tid; i < nb * C; i += kResThreads) {
+            const int64_t idx = (int64_t)s0 * C + i;
+            st_agent(a.h_hist + idx, a.h0[idx]);
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float* zr = zh + li * hp + 4 * (m * nhb) + lk;
+#pragma unroll
+    for (int i = 0; i < kMfmaMaxNhb; ++i) {
+        if (i < nhb) {
+            const float hv = zr[4 * i];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(hv, wq[q][i], acc[q], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) as[q][m][(4 * lk + e) * 16 + li] = acc[q][e];
+    __syncthreads();
+
+    if (tid < 256) {
+        const int es = tid >> 4;
+        const int b = s0 + es;
+        const int c = c0 + (tid & 15);
+        if (b < B && c < C) {
+            float pre[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const float* P = &as[q][0][tid];
+                const float h1 = (P[0 * 256] + P[1 * 256]) + (P[2 * 256] + P[3 * 256]);
+                const float h2 = (P[4 * 256] + P[5 * 256]) + (P[6 * 256] + P[7 * 256]);
+                pre[q] = xs[q][tid] + (h1 + h2);
+            }
+            const CellOut o = cell_forward(pre[0], pre[1], pre[2]);
+            const int64_t bc = (int64_t)b * C + c;
+            st_agent(a.h_hist + (int64_t)t * BC + bc, o.h);
+            float* act_t = a.act + (int64_t)(t - 1) * 3 * BC;
+            st_agent(act_t + bc, o.gate);
+            st_agent(act_t + BC + bc, o.g);
+            st_agent(act_t + 2 * BC + bc, o.hh);
+            st_agent(hx_out + es * cp + res_hx_pos(c, nhb), o.h);
+        }
+    }
+    res_store_u(a, uq, zu);   // X_t's reads of u_t ended before this step began
+}
 
 // Wave 0 polls the counters of the sample tile's nct workgroups (one lane
 // each; the other lanes read the error word, in the same round trip) until
@@ -1038,47 +1262,37 @@ __global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArg
     // the first backward step orders the last forward reads before it)
     __shared__ __attribute__((aligned(16))) float lds[kResLds];
     const int nct = a.n_ctiles;
-    const int ctile = blockIdx.x % nct;
-    const int btile = blockIdx.x / nct;
+    // the channel tiles of a sample tile hand one another h_t and dp_t: keep
+    // them on one XCD where the grid allows
+    const int v = (int)xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
+    const int ctile = v % nct;
+    const int btile = v / nct;
     const int base = btile * nct;
     const int err = gridDim.x;
     const int K = a.K;
     const int64_t BC = (int64_t)a.B * a.C;
-    const int64_t BX = (int64_t)a.B * a.n_x;
     {
-        float* zs = lds;
-        float (*as)[3][16 * 16] = reinterpret_cast<float (*)[3][16 * 16]>(lds + kFwdMfmaZs);
-        FwdMfmaArgs f{};
-        f.Wf = a.Wf;
-        f.bias = a.bias;
-        f.B = a.B;
-        f.C = a.C;
-        f.n_x = a.n_x;
-        f.n_ctiles = nct;
-        f.L = a.L;
-        f32x4 wv[kMfmaMaxNhb];
-        float bias;
-        fwd_mfma_operands(f, ctile * 16, wv, bias);
-        // h_t of the sample tile in the staged layout, by the parity of t
+        float wq[3][kMfmaMaxNhb];
+        f32x4 wx[kMfmaMaxNxb];
+        float xbias;
+        fwd_res_operands(a, ctile * 16, wq, wx, xbias);
+        float (*xs)[256] = reinterpret_cast<float (*)[256]>(lds + kResXs);
+        const bool xw = threadIdx.x >= 256 && threadIdx.x < 448;   // waves 4..6
+        // X_1 (the barriers of step 1 order it before its reads)
+        res_store_u(a, res_load_u(a, 1, btile * 16), lds + kResZu);
+        __syncthreads();
+        if (xw) res_xproj(wx, xbias, a.L.nxp / 16, lds + kResZu, xs);
+        // h_t of the sample tile in the exchange rows, by the parity of t
         const int64_t hx_tile = (int64_t)16 * a.L.cp;
         const int64_t hx_par = (int64_t)gridDim.x / nct * hx_tile;
         float* hx = a.hx + btile * hx_tile;
-        auto set_step = [&](int t) {
-            f.u_t = a.u + (int64_t)(t - 1) * BX;
-            f.h_prev = (t == 1) ? a.h0 : a.h_hist + (int64_t)(t - 1) * BC;
-            f.h_t = a.h_hist + (int64_t)t * BC;
-            f.act_t = a.act + (int64_t)(t - 1) * 3 * BC;
-            f.h_prev_copy = (t == 1) ? a.h_hist : nullptr;
-            f.hx = hx + ((t - 1) & 1) * hx_par;
-            f.hx_out = hx + (t & 1) * hx_par;
-        };
-        set_step(1);   // h_0 from h0, staged as the step kernel does
-        fwd_mfma_step<true, false>(f, btile, ctile, wv, bias, zs, as);
+        fwd_res_step<false>(a, 1, btile, ctile, wq, lds, nullptr, hx + hx_par);
         for (int t = 2; t <= K; ++t) {
             resident_report(a.flags, base + ctile, t - 1);
+            // X_t from the u rows step t - 1 stored, while wave 0 waits
+            if (xw) res_xproj(wx, xbias, a.L.nxp / 16, lds + kResZu, xs);
             resident_wait(a.flags, base, nct, err, t - 1, a.spin_limit);
-            set_step(t);
-            fwd_mfma_step<true, true>(f, btile, ctile, wv, bias, zs, as);
+            fwd_res_step<true>(a, t, btile, ctile, wq, lds, hx + ((t - 1) & 1) * hx_par, hx + (t & 1) * hx_par);
         }
         resident_report(a.flags, base + ctile, K);
     }
