@@ -500,35 +500,25 @@ __global__ __launch_bounds__(kThreads) void permute_w_kernel(PermuteArgs a)
 }
 
 // Moves of the resident kernel (kloop_resident_kernel): its workgroups hand
-// h_t, act_t and dp_t to one another through memory while they run, so those
-// arrays are written and read at agent scope (write-through stores, loads
-// that do not hit stale cache lines); the step kernels, whose launches are
-// ordered by the stream, use plain moves.  RES selects.
-__device__ __forceinline__ float ld_agent(const float* p)
-{
-    return __int_as_float(__hip_atomic_load(reinterpret_cast<int*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT));
-}
+// h_t, dp_t and the step-K activations to one another through memory while
+// they run, so those moves are made at device scope (sc1): write-through
+// stores, and loads that the vector L1 does not serve; the step kernels,
+// whose launches are ordered by the stream, and the resident kernel's moves
+// of a workgroup's own data use plain moves.
 __device__ __forceinline__ void st_agent(float* p, float v)
 {
     __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16-byte load with the cache policy of ld_agent's loads (sc1), through a
-// raw buffer resource over [base, base + bytes): one request per 16 bytes,
-// where two 8-byte agent-scope loads make two (neither is served by the
-// vector L1).  Offsets at or past `bytes` read zero.
+// 16-byte device-scope load through a raw buffer resource over [base, base
+// + bytes): one request per 16 bytes, where two 8-byte agent-scope atomic
+// loads make two.  Offsets at or past `bytes` read zero.
 __device__ __forceinline__ f32x4 ld4_dev(const float* base, int bytes, int byte_off)
 {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
 }
-template <bool RES>
-__device__ __forceinline__ float ld1(const float* p)
-{
-    if constexpr (RES) return ld_agent(p);
-    else return *p;
-}
+// RES: a 16-byte device-scope load (two 8-byte agent-scope loads).
 template <bool RES>
 __device__ __forceinline__ f32x4 ld4(const float* p)
 {
@@ -541,12 +531,6 @@ __device__ __forceinline__ f32x4 ld4(const float* p)
     } else {
         return *reinterpret_cast<const f32x4*>(p);
     }
-}
-template <bool RES>
-__device__ __forceinline__ void st1(float* p, float v)
-{
-    if constexpr (RES) st_agent(p, v);
-    else *p = v;
 }
 // Forward step on MFMA.  Workgroup = 16 samples x 16 channels; three waves
 // per head q: part 0 forms the four input chains (x_r: k-slot kk of block p
@@ -801,11 +785,13 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
         const float* hp = prev ? a.h_prev : a.h_t;
         const float* yp = prev ? a.y_prev : a.y_t;
         const float* gp = prev ? a.act_prev : a.act_t;
-        ep_h = ld1<RES>(hp + bk);
+        // (sample, channel) of this workgroup's own tile: in the resident
+        // kernel its own forward wrote them, so plain loads see them
+        ep_h = hp[bk];
         ep_y = yp[bk];
-        ep_g0 = ld1<RES>(gp + bk);
-        ep_g1 = ld1<RES>(gp + BC + bk);
-        ep_g2 = ld1<RES>(gp + 2 * BC + bk);
+        ep_g0 = gp[bk];
+        ep_g1 = gp[BC + bk];
+        ep_g2 = gp[2 * BC + bk];
     }
     if (DP != kDpIn && active)
         for (int i = tid; i < kBwdMfmaDps; i += kBwdMfmaThreads) dps[i] = 0.0f;
@@ -983,7 +969,7 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
 // every channel tile of its samples, so the workgroups of a sample tile
 // count their finished steps in `flags` (forward step t: t; backward step t:
 // 2K - t + 1) and a step waits until all of them have reached the one it
-// needs.  The exchanged arrays move at agent scope (see ld_agent), and a
+// needs.  The exchanged arrays move at device scope (see st_agent), and a
 // counter is written only after every wave's stores of the step are
 // performed, so a workgroup that sees a counter also sees the data behind
 // it; no atomics, no cache maintenance.  The backward steps are the
@@ -1104,18 +1090,21 @@ __device__ __forceinline__ void res_xproj(const f32x4 (&wx)[kMfmaMaxNxb], float 
 
 // One resident forward step t of tile (btile, ctile); X_t is in LDS on
 // entry (formed by waves 4..6 from u_t's rows while the workgroup waited for
-// the other tiles, or before step 1) and u_{t+1}'s rows on return.  h_{t-1}
-// is copied into LDS from the exchange rows hx (HX) or, at t = 1, from h0,
-// its loads issued before u_{t+1}'s.  Wave m forms recurrent partition P_m
-// of the three heads (the forward step kernel's chains, with their A and B
-// operands) into as[q][m].  Then waves 0..3 run the epilogue, pre_q = X_q +
-// (((P0 + P1) + (P2 + P3)) + ((P4 + P5) + (P6 + P7))), the step kernel's
-// order, writing h_t and act_t at agent scope and h_t also to the exchange
-// rows hx_out; every lane stores its part of u_{t+1}'s rows.
+// the other tiles, or before step 1) and u_{t+1}'s rows on return; uq holds
+// this lane's part of u_{t+1} on entry (loaded a step ago) and of u_{t+2} on
+// return.  h_{t-1} is copied into LDS from the exchange rows hx (HX) or, at
+// t = 1, from h0, its loads issued before u_{t+2}'s.  Wave m forms recurrent
+// partition P_m of the three heads (the forward step kernel's chains, with
+// their A and B operands) into as[q][m].  Then waves 0..3 run the epilogue,
+// pre_q = X_q + (((P0 + P1) + (P2 + P3)) + ((P4 + P5) + (P6 + P7))), the step
+// kernel's order, writing h_t to the exchange rows hx_out at device scope and
+// h_t, act_t to h_hist and act (at device scope at step K, whose values
+// every channel tile reads; plainly before, read again only by this
+// workgroup); every lane stores its part of u_{t+1}'s rows.
 template <bool HX>
 __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int btile, int ctile,
-                                             const float (&wq)[3][kMfmaMaxNhb], float* lds, const float* hx,
-                                             float* hx_out)
+                                             const float (&wq)[3][kMfmaMaxNhb], f32x4& uq, float* lds,
+                                             const float* hx, float* hx_out)
 {
     const int C = a.C;
     const int B = a.B;
@@ -1153,10 +1142,10 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
             hv4[k] = (b < B && 4 * g < C) ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     }
-    // u_{t+1}'s load, issued after the h loads so that their wait does not
+    // u_{t+2}'s load, issued after the h loads so that their wait does not
     // include it
     __builtin_amdgcn_sched_barrier(0);
-    const f32x4 uq = res_load_u(a, min(t + 1, a.K), s0);
+    const f32x4 uq_next = res_load_u(a, min(t + 2, a.K), s0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kHSlots; ++k) {
@@ -1211,15 +1200,26 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
             }
             const CellOut o = cell_forward(pre[0], pre[1], pre[2]);
             const int64_t bc = (int64_t)b * C + c;
-            st_agent(a.h_hist + (int64_t)t * BC + bc, o.h);
+            float* h_t = a.h_hist + (int64_t)t * BC;
             float* act_t = a.act + (int64_t)(t - 1) * 3 * BC;
-            st_agent(act_t + bc, o.gate);
-            st_agent(act_t + BC + bc, o.g);
-            st_agent(act_t + 2 * BC + bc, o.hh);
             st_agent(hx_out + es * cp + res_hx_pos(c, nhb), o.h);
+            if (t < a.K) {
+                // read again only by this workgroup (its backward epilogue)
+                h_t[bc] = o.h;
+                act_t[bc] = o.gate;
+                act_t[BC + bc] = o.g;
+                act_t[2 * BC + bc] = o.hh;
+            } else {
+                // step K: every channel tile of the sample tile forms dp_K from them
+                st_agent(h_t + bc, o.h);
+                st_agent(act_t + bc, o.gate);
+                st_agent(act_t + BC + bc, o.g);
+                st_agent(act_t + 2 * BC + bc, o.hh);
+            }
         }
     }
     res_store_u(a, uq, zu);   // X_t's reads of u_t ended before this step began
+    uq = uq_next;
 }
 
 // Wave 0 polls the counters of the sample tile's nct workgroups (one lane
@@ -1280,19 +1280,21 @@ __global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArg
         const bool xw = threadIdx.x >= 256 && threadIdx.x < 448;   // waves 4..6
         // X_1 (the barriers of step 1 order it before its reads)
         res_store_u(a, res_load_u(a, 1, btile * 16), lds + kResZu);
+        f32x4 uq = res_load_u(a, min(2, K), btile * 16);
         __syncthreads();
         if (xw) res_xproj(wx, xbias, a.L.nxp / 16, lds + kResZu, xs);
         // h_t of the sample tile in the exchange rows, by the parity of t
         const int64_t hx_tile = (int64_t)16 * a.L.cp;
         const int64_t hx_par = (int64_t)gridDim.x / nct * hx_tile;
         float* hx = a.hx + btile * hx_tile;
-        fwd_res_step<false>(a, 1, btile, ctile, wq, lds, nullptr, hx + hx_par);
+        fwd_res_step<false>(a, 1, btile, ctile, wq, uq, lds, nullptr, hx + hx_par);
         for (int t = 2; t <= K; ++t) {
             resident_report(a.flags, base + ctile, t - 1);
             // X_t from the u rows step t - 1 stored, while wave 0 waits
             if (xw) res_xproj(wx, xbias, a.L.nxp / 16, lds + kResZu, xs);
             resident_wait(a.flags, base, nct, err, t - 1, a.spin_limit);
-            fwd_res_step<true>(a, t, btile, ctile, wq, lds, hx + ((t - 1) & 1) * hx_par, hx + (t & 1) * hx_par);
+            fwd_res_step<true>(a, t, btile, ctile, wq, uq, lds, hx + ((t - 1) & 1) * hx_par,
+                               hx + (t & 1) * hx_par);
         }
         resident_report(a.flags, base + ctile, K);
     }
