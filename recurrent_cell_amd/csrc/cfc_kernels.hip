@@ -726,7 +726,15 @@ __global__ __launch_bounds__(kFwdMfmaThreads) void fwd_mfma_kernel(FwdMfmaArgs a
 // the first three levels of the pairwise tree of tree_sum16; its last level
 // adds the halves.  Then dz = (T0 + T1) + (T2 + T3).
 constexpr int kBwdMfmaThreads = 512;   // 4 subtrees x 2 halves of their 16 groups
-constexpr int kBwdMfmaDps = 16 * kDzGroups * 16;
+constexpr int kBwdMfmaDps = 16 * kDzGroups * 16;   // dp of a sample tile in the staged layout
+// In LDS a sample's staged dp starts 4 banks after the previous one's, so
+// that the 16 samples of a 16-byte operand read fall on distinct banks.
+constexpr int kDpsStride = kDzGroups * 16 + 4;
+constexpr int kBwdMfmaDpsLds = 16 * kDpsStride;
+// The subtree partials [half][subtree][sample][column] at row pitch 20: the
+// MFMA tile's stores (samples 4 lk + e, lanes lk = 0..3) fall on distinct
+// banks.
+constexpr int kTsP = 20;
 
 // This lane's W operands of the carry: the 8 groups g = w + 4 (8 hf + m)
 // of its half of subtree w, carry column k0 + li.  Lanes past the 512 that
@@ -745,7 +753,7 @@ __device__ __forceinline__ void bwd_mfma_operands(const BwdMfmaArgs& a, int k0, 
 }
 
 // One backward step of the workgroup's tile (btile, ctile); dps and ts are
-// its LDS (kBwdMfmaDps and 2 x 4 x 16 x 17 floats).  The step kernel loads
+// its LDS (kBwdMfmaDpsLds and 2 x 4 x 16 x kTsP floats).  The step kernel loads
 // the W operands after the dp staging (bv is its own); the resident kernel
 // (RES) holds them for every step and reads h, act and dp written by other
 // workgroups at agent scope, and also writes dp_{t-1} of its channels to
@@ -758,7 +766,7 @@ __device__ __forceinline__ void bwd_mfma_operands(const BwdMfmaArgs& a, int k0, 
 constexpr int kDpRuntime = 0, kDpIn = 1, kDpFormed = 2;
 template <int PG, bool RES, int DP>
 __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, int ctile, f32x4 (&bv)[8],
-                                              float* dps, float (*ts)[4][16][17])
+                                              float* dps, float (*ts)[4][16][kTsP])
 {
     const int C = a.C;
     const int cpg = dz_group_channels(C);
@@ -794,7 +802,7 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
         ep_g2 = gp[2 * BC + bk];
     }
     if (DP != kDpIn && active)
-        for (int i = tid; i < kBwdMfmaDps; i += kBwdMfmaThreads) dps[i] = 0.0f;
+        for (int i = tid; i < kBwdMfmaDpsLds; i += kBwdMfmaThreads) dps[i] = 0.0f;
     const int c4n = C / 4;
     if constexpr (DP == kDpIn) {
         constexpr int kXSlots = kBwdMfmaDps / 4 / kBwdMfmaThreads;
@@ -805,8 +813,10 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
             for (int m = 0; m < kXSlots; ++m)
                 vx[m] = ld4_dev(a.dpx, 4 * kBwdMfmaDps, 16 * (tid + m * kBwdMfmaThreads));
 #pragma unroll
-            for (int m = 0; m < kXSlots; ++m)
-                *reinterpret_cast<f32x4*>(dps + 4 * (tid + m * kBwdMfmaThreads)) = vx[m];
+            for (int m = 0; m < kXSlots; ++m) {
+                const int i = tid + m * kBwdMfmaThreads;   // float4 i of the block: sample i / 256
+                *reinterpret_cast<f32x4*>(dps + (i >> 8) * kDpsStride + 4 * (i & 255)) = vx[m];
+            }
         }
     } else if (DP == kDpRuntime && a.dp_in != nullptr) {
         // dp of this step, formed at the end of the launch of step t + 1: the
@@ -835,7 +845,7 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
                     const int c = 4 * (r4 - qq * c4n) + e;
                     const int g = c / cpg;
                     const int el = 3 * (c - g * cpg) + qq;
-                    dps[(s * kDzGroups + g) * 16 + 4 * (el & 3) + (el >> 2)] = vp[m][e];
+                    dps[s * kDpsStride + g * 16 + 4 * (el & 3) + (el >> 2)] = vp[m][e];
                 }
             }
         }
@@ -874,7 +884,7 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
 #pragma unroll
                 for (int qq = 0; qq < 3; ++qq) {
                     const int el = 3 * cl + qq;
-                    dps[(s * kDzGroups + g) * 16 + 4 * (el & 3) + (el >> 2)] = d[qq];
+                    dps[s * kDpsStride + g * 16 + 4 * (el & 3) + (el >> 2)] = d[qq];
                 }
                 if (c >= k0 && c < k0 + 16) {
                     const int64_t row = (int64_t)(s0 + s) * 3 * C;
@@ -897,7 +907,7 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
             bwd_mfma_operands(a, k0, bv);
             __builtin_amdgcn_sched_barrier(0);   // the 8 loads ahead of the MFMAs
         }
-        const float* da = dps + li * kDzGroups * 16 + 4 * lk;   // + 16 g
+        const float* da = dps + li * kDpsStride + 4 * lk;   // + 16 g
         // The half's 8 group partials as independent MFMA chains (so that their
         // instructions interleave), then the first three levels of the pairwise
         // tree of tree_sum16; its last level adds the two halves below.
@@ -956,8 +966,8 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
 template <int PG>
 __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float dps[kBwdMfmaDps];
-    __shared__ __attribute__((aligned(16))) float ts[2][4][16][17];   // [half][subtree][sample][column]
+    __shared__ __attribute__((aligned(16))) float dps[kBwdMfmaDpsLds];
+    __shared__ __attribute__((aligned(16))) float ts[2][4][16][kTsP];   // [half][subtree][sample][column]
     f32x4 bv[8];
     bwd_mfma_step<PG, false, kDpRuntime>(a, blockIdx.x / a.n_ctiles, blockIdx.x % a.n_ctiles, bv, dps, ts);
 }
@@ -983,15 +993,19 @@ __global__ __launch_bounds__(kBwdMfmaThreads) void bwd_mfma_kernel(BwdMfmaArgs a
 // ---------------------------------------------------------------------------
 constexpr int kResThreads = kBwdMfmaThreads;   // eight waves
 // Forward LDS: h_{t-1} rows [16][cp + 4], u rows [16][nxp + 4], the
-// recurrent partials [3][8][256] and X [3][256];
+// recurrent partials [3][8][16][kResAsP] and X [3][16][kResAsP];
 // backward LDS: the step kernel's.  At least 81 KB, so that one workgroup
 // sits on each CU (two would share one CU's matrix cores and leave another
 // idle).
 constexpr int kResHp = 32 * kMfmaMaxNhb + 4;
 constexpr int kResUp = 16 * kMfmaMaxNxb + 4;
-constexpr int kResZh = 0, kResZu = 16 * kResHp, kResAs = kResZu + 16 * kResUp, kResXs = kResAs + 3 * 8 * 256;
-constexpr int kResFwdLds = kResXs + 3 * 256;
-constexpr int kResBwdLds = kBwdMfmaDps + 2 * 4 * 16 * 17;
+// partial rows of 16 channels at pitch 20: the MFMA tile's stores (samples
+// 4 lk + e, lanes lk = 0..3) fall on distinct banks
+constexpr int kResAsP = 20;
+constexpr int kResZh = 0, kResZu = 16 * kResHp, kResAs = kResZu + 16 * kResUp,
+              kResXs = kResAs + 3 * 8 * 16 * kResAsP;
+constexpr int kResFwdLds = kResXs + 3 * 16 * kResAsP;
+constexpr int kResBwdLds = kBwdMfmaDpsLds + 2 * 4 * 16 * kTsP;
 constexpr int kResLdsMin = 81 * 1024 / 4;
 constexpr int kResLds = kResFwdLds > kResBwdLds ? (kResFwdLds > kResLdsMin ? kResFwdLds : kResLdsMin)
                                                 : (kResBwdLds > kResLdsMin ? kResBwdLds : kResLdsMin);
@@ -1065,7 +1079,7 @@ __device__ __forceinline__ void res_store_u(const ResidentArgs& a, f32x4 v, floa
 // + 4 kk + r) from the u rows in LDS, then X = bias + ((x0 + x1) + (x2 + x3))
 // into xs[q].
 __device__ __forceinline__ void res_xproj(const f32x4 (&wx)[kMfmaMaxNxb], float xbias, int nxb, const float* zu,
-                                          float (*xs)[256])
+                                          float (*xs)[16 * kResAsP])
 {
     const int lane = threadIdx.x & 63;
     const int q = (threadIdx.x >> 6) - 4;
@@ -1085,7 +1099,7 @@ __device__ __forceinline__ void res_xproj(const f32x4 (&wx)[kMfmaMaxNxb], float 
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        xs[q][(4 * lk + e) * 16 + li] = xproj_combine(xbias, acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+        xs[q][(4 * lk + e) * kResAsP + li] = xproj_combine(xbias, acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
 }
 
 // One resident forward step t of tile (btile, ctile); X_t is in LDS on
@@ -1122,8 +1136,8 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
     const int64_t BC = (int64_t)B * C;
     float* zh = lds + kResZh;
     float* zu = lds + kResZu;
-    float (*as)[8][256] = reinterpret_cast<float (*)[8][256]>(lds + kResAs);
-    float (*xs)[256] = reinterpret_cast<float (*)[256]>(lds + kResXs);
+    float (*as)[8][16 * kResAsP] = reinterpret_cast<float (*)[8][16 * kResAsP]>(lds + kResAs);
+    float (*xs)[16 * kResAsP] = reinterpret_cast<float (*)[16 * kResAsP]>(lds + kResXs);
 
     // h_{t-1} rows into LDS, every load in flight before the LDS stores
     const int c4 = cp / 4;
@@ -1182,7 +1196,7 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) as[q][m][(4 * lk + e) * 16 + li] = acc[q][e];
+        for (int e = 0; e < 4; ++e) as[q][m][(4 * lk + e) * kResAsP + li] = acc[q][e];
     __syncthreads();
 
     if (tid < 256) {
@@ -1193,10 +1207,11 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
             float pre[3];
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
-                const float* P = &as[q][0][tid];
-                const float h1 = (P[0 * 256] + P[1 * 256]) + (P[2 * 256] + P[3 * 256]);
-                const float h2 = (P[4 * 256] + P[5 * 256]) + (P[6 * 256] + P[7 * 256]);
-                pre[q] = xs[q][tid] + (h1 + h2);
+                const float* P = &as[q][0][es * kResAsP + (tid & 15)];
+                constexpr int M = 16 * kResAsP;   // one partition's rows
+                const float h1 = (P[0 * M] + P[1 * M]) + (P[2 * M] + P[3 * M]);
+                const float h2 = (P[4 * M] + P[5 * M]) + (P[6 * M] + P[7 * M]);
+                pre[q] = xs[q][es * kResAsP + (tid & 15)] + (h1 + h2);
             }
             const CellOut o = cell_forward(pre[0], pre[1], pre[2]);
             const int64_t bc = (int64_t)b * C + c;
@@ -1276,7 +1291,7 @@ __global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArg
         f32x4 wx[kMfmaMaxNxb];
         float xbias;
         fwd_res_operands(a, ctile * 16, wq, wx, xbias);
-        float (*xs)[256] = reinterpret_cast<float (*)[256]>(lds + kResXs);
+        float (*xs)[16 * kResAsP] = reinterpret_cast<float (*)[16 * kResAsP]>(lds + kResXs);
         const bool xw = threadIdx.x >= 256 && threadIdx.x < 448;   // waves 4..6
         // X_1 (the barriers of step 1 order it before its reads)
         res_store_u(a, res_load_u(a, 1, btile * 16), lds + kResZu);
@@ -1300,7 +1315,7 @@ __global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArg
     }
     {
         float* dps = lds;
-        float (*ts)[4][16][17] = reinterpret_cast<float (*)[4][16][17]>(lds + kBwdMfmaDps);
+        float (*ts)[4][16][kTsP] = reinterpret_cast<float (*)[4][16][kTsP]>(lds + kBwdMfmaDpsLds);
         BwdMfmaArgs g{};
         g.Wb = a.Wb;
         g.B = a.B;
@@ -1442,18 +1457,36 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
         }
         __syncthreads();
         const int nst4 = nst & ~3;
-        for (int tt = 0; tt < nst4; tt += 4) {
-            float av[2], bv[2];
+        // operands of the next 4 steps read while the current MFMAs run
+        // (two operand sets in turn, so that no copy waits for a read)
+        float a0[2], b0[2], a1[2], b1[2];
+        auto rd = [&](int tt, float (&av)[2], float (&bv)[2]) __attribute__((always_inline)) {
+            const int r = min(tt, kFillSteps - 4) + lk;   // in bounds; unused past nst4
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) av[mt] = dps[tt + lk][wr + 16 * mt + li];
+            for (int mt = 0; mt < 2; ++mt) av[mt] = dps[r][wr + 16 * mt + li];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) bv[nt] = zs[tt + lk][wc + 16 * nt + li];
+            for (int nt = 0; nt < 2; ++nt) bv[nt] = zs[r][wc + 16 * nt + li];
+        };
+        auto mma = [&](const float (&av)[2], const float (&bv)[2]) __attribute__((always_inline)) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+        };
+        rd(0, a0, b0);
+        int tt = 0;
+        for (; tt + 8 <= nst4; tt += 8) {
+            rd(tt + 4, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            rd(tt + 8, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (tt < nst4) mma(a0, b0);   // nst4 % 8 == 4
         for (int tt = nst4; tt < nst; ++tt) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
