@@ -129,8 +129,8 @@ struct ResidentArgs {
     float* h_hist;        // [K+1, B, C]
     float* act;           // [K, 3, B, C]
     float* dp;            // [K, B, 3C]
-    float* hx;            // [2][n_btiles][16][cp], zero at launch: h_t by step parity, column
-                          // c = 32 i + 4 m + e of a sample at 4 (m cp / 32 + i) + e
+    float* hx;            // [2][n_btiles][16 cp], zero at launch: h_t by step parity, each sample
+                          // tile's channel tiles' [16 samples][16 channels] blocks in turn
     float* dpx;           // [2][n_btiles][16][64][16], zero at launch: dp_t by step parity, the backward
                           // step's LDS layout
     int* flags;           // [(n_btiles * n_ctiles + 1) * kResFlagStride], zero at launch: steps done per

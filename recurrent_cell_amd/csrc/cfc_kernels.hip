@@ -518,6 +518,14 @@ __device__ __forceinline__ f32x4 ld4_dev(const float* base, int bytes, int byte_
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
 }
+// 16-byte device-scope (write-through) store through a raw buffer resource
+// over [base, base + bytes); offsets at or past `bytes` write nothing.
+__device__ __forceinline__ void st4_dev(float* base, int bytes, int byte_off, f32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                           byte_off, 0, 16 /* sc1 */);
+}
 // RES: a 16-byte device-scope load (two 8-byte agent-scope loads).
 template <bool RES>
 __device__ __forceinline__ f32x4 ld4(const float* p)
@@ -766,7 +774,7 @@ __device__ __forceinline__ void bwd_mfma_operands(const BwdMfmaArgs& a, int k0, 
 constexpr int kDpRuntime = 0, kDpIn = 1, kDpFormed = 2;
 template <int PG, bool RES, int DP>
 __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, int ctile, f32x4 (&bv)[8],
-                                              float* dps, float (*ts)[4][16][kTsP])
+                                              float* dps, float (*ts)[4][16][kTsP], float* wstage = nullptr)
 {
     const int C = a.C;
     const int cpg = dz_group_channels(C);
@@ -955,8 +963,28 @@ __device__ __forceinline__ void bwd_mfma_step(const BwdMfmaArgs& a, int btile, i
 #pragma unroll
                     for (int qq = 0; qq < 3; ++qq) {
                         const int el = 3 * (k - g * cpg) + qq;
-                        st_agent(a.dpx_out + (s * kDzGroups + g) * 16 + 4 * (el & 3) + (el >> 2), d[qq]);
+                        const int pos = 4 * (el & 3) + (el >> 2);
+                        if (wstage != nullptr)
+                            wstage[(s & 3) * 256 + (g - k0 / cpg) * 16 + pos] = d[qq];
+                        else
+                            st_agent(a.dpx_out + (s * kDzGroups + g) * 16 + pos, d[qq]);
                     }
+                }
+            }
+        }
+        if constexpr (RES) {
+            if (wstage != nullptr && a.dp_prev_out != nullptr) {
+                // this wave's 4 samples of the tile's whole dz groups, read
+                // back from its own staging (the wave's LDS moves are ordered)
+                // and stored as 16-byte device-scope stores
+                const int ng4 = 4 * (16 / cpg);   // float4 per sample
+                const int lane = tid & 63;
+                for (int i = lane; i < 4 * ng4; i += 64) {
+                    const int sl = i / ng4;
+                    const int f = i - sl * ng4;
+                    const int sg = (tid >> 6) * 4 + sl;   // the sample of the tile
+                    st4_dev(a.dpx_out, 4 * kBwdMfmaDps, 4 * ((sg * kDzGroups + k0 / cpg) * 16 + 4 * f),
+                            *reinterpret_cast<const f32x4*>(wstage + sl * 256 + 4 * f));
                 }
             }
         }
@@ -1005,15 +1033,18 @@ constexpr int kResAsP = 20;
 constexpr int kResZh = 0, kResZu = 16 * kResHp, kResAs = kResZu + 16 * kResUp,
               kResXs = kResAs + 3 * 8 * 16 * kResAsP;
 constexpr int kResFwdLds = kResXs + 3 * 16 * kResAsP;
-constexpr int kResBwdLds = kBwdMfmaDpsLds + 2 * 4 * 16 * kTsP;
+// + per-wave staging of the dp hand-over: 4 epilogue waves x 4 samples x
+// 256 slots
+constexpr int kResWs = kBwdMfmaDpsLds + 2 * 4 * 16 * kTsP;
+constexpr int kResBwdLds = kResWs + 4 * 4 * 256;
 constexpr int kResLdsMin = 81 * 1024 / 4;
 constexpr int kResLds = kResFwdLds > kResBwdLds ? (kResFwdLds > kResLdsMin ? kResFwdLds : kResLdsMin)
                                                 : (kResBwdLds > kResLdsMin ? kResBwdLds : kResLdsMin);
 
-// Forward h exchange rows (and their LDS copy): recurrent column c = 32 i +
-// 4 m + e of a sample sits at 4 (m nhb + i) + e, so that partition m's k-slot
-// e at block i, for the 16 samples, is one conflict-free LDS read (row pitch
-// cp + 4) and a row's float4 groups are the natural ones, permuted.
+// The LDS copy of h_{t-1}: recurrent column c = 32 i + 4 m + e of a sample
+// sits at 4 (m nhb + i) + e, so that partition m's k-slot e at block i, for
+// the 16 samples, is one conflict-free LDS read (row pitch cp + 4) and 4
+// consecutive channels (c % 4 = 0..3) land in one float4.
 __device__ __forceinline__ int res_hx_pos(int c, int nhb) { return 4 * (((c & 31) >> 2) * nhb + (c >> 5)) + (c & 3); }
 
 // The lane's W operands of the resident forward.  Wave m (0..7) holds, for
@@ -1139,13 +1170,18 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
     float (*as)[8][16 * kResAsP] = reinterpret_cast<float (*)[8][16 * kResAsP]>(lds + kResAs);
     float (*xs)[16 * kResAsP] = reinterpret_cast<float (*)[16 * kResAsP]>(lds + kResXs);
 
-    // h_{t-1} rows into LDS, every load in flight before the LDS stores
+    // h_{t-1} rows into LDS, every load in flight before the LDS stores.  The
+    // exchange rows hold each channel tile's [16 samples][16 channels] block
+    // in turn; h0 rows are natural.  Either way float4 idx goes to its
+    // partition-major place (res_hx_pos), 4 channels at once.
     const int c4 = cp / 4;
+    const int n4 = HX ? 64 * a.n_ctiles : 16 * c4;
     constexpr int kHSlots = (16 * 32 * kMfmaMaxNhb / 4 + kResThreads - 1) / kResThreads;
+    static_assert(64 * ((32 * kMfmaMaxNhb + 15) / 16) <= kHSlots * kResThreads, "one pass of slots");
     f32x4 hv4[kHSlots];
 #pragma unroll
     for (int k = 0; k < kHSlots; ++k) {
-        const int idx = min(tid + k * kResThreads, 16 * c4 - 1);
+        const int idx = min(tid + k * kResThreads, n4 - 1);
         const int s = idx / c4;
         const int g = idx - s * c4;
         if constexpr (HX) {
@@ -1164,12 +1200,16 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
 #pragma unroll
     for (int k = 0; k < kHSlots; ++k) {
         const int idx = tid + k * kResThreads;
-        if (idx < 16 * c4) {
-            const int s = idx / c4;
-            const int g = idx - s * c4;
-            // exchange rows hold the LDS order already; h0 rows are natural
-            const int pos = HX ? 4 * g : res_hx_pos(4 * g, nhb);
-            *reinterpret_cast<f32x4*>(zh + s * hp + pos) = hv4[k];
+        if (idx < n4) {
+            int s, c;
+            if constexpr (HX) {
+                s = (idx >> 2) & 15;                    // block idx / 64: channels 16 (idx / 64) ..
+                c = 16 * (idx >> 6) + 4 * (idx & 3);
+            } else {
+                s = idx / c4;
+                c = 4 * (idx - s * c4);
+            }
+            *reinterpret_cast<f32x4*>(zh + s * hp + res_hx_pos(c, nhb)) = hv4[k];
         }
     }
     if (!HX && ctile == 0) {
@@ -1217,7 +1257,7 @@ __device__ __forceinline__ void fwd_res_step(const ResidentArgs& a, int t, int b
             const int64_t bc = (int64_t)b * C + c;
             float* h_t = a.h_hist + (int64_t)t * BC;
             float* act_t = a.act + (int64_t)(t - 1) * 3 * BC;
-            st_agent(hx_out + es * cp + res_hx_pos(c, nhb), o.h);
+            st_agent(hx_out + ctile * 256 + tid, o.h);   // the tile's block: sample es, channel c
             if (t < a.K) {
                 // read again only by this workgroup (its backward epilogue)
                 h_t[bc] = o.h;
@@ -1342,14 +1382,23 @@ __global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArg
         // operands loaded after that staging (as the step kernel does) and
         // then kept for the steps that read dp_t of every channel tile
         f32x4 bv[8];
+        // the dp hand-over goes through per-wave LDS staging and 16-byte
+        // stores when every dz group lies in one channel tile (its channel
+        // count divides 16); staging slots that no channel writes stay zero
+        const int cpg = dz_group_channels(a.C);
+        float* wstage = nullptr;
+        if (16 % cpg == 0) {
+            for (int i = threadIdx.x; i < 4 * 4 * 256; i += kResThreads) lds[kResWs + i] = 0.0f;
+            wstage = lds + kResWs + (threadIdx.x >> 6) * 4 * 256;   // used by waves 0..3
+        }
         resident_wait(a.flags, base, nct, err, K, a.spin_limit);
         set_step(K);
-        bwd_mfma_step<PG, true, kDpFormed>(g, btile, ctile, bv, dps, ts);
+        bwd_mfma_step<PG, true, kDpFormed>(g, btile, ctile, bv, dps, ts, wstage);
         for (int t = K - 1; t >= 1; --t) {
             resident_report(a.flags, base + ctile, 2 * K - t);   // step t + 1 done
             resident_wait(a.flags, base, nct, err, 2 * K - t, a.spin_limit);
             set_step(t);
-            bwd_mfma_step<PG, true, kDpIn>(g, btile, ctile, bv, dps, ts);
+            bwd_mfma_step<PG, true, kDpIn>(g, btile, ctile, bv, dps, ts, wstage);
         }
     }
 }
