@@ -53,6 +53,7 @@ struct FillArgs {
     float* gW_s;          // [B, 3C, n_in] overwritten
     float* gb_s;          // [B, 3C]       overwritten
     int B, C, n_x, K, n_rt, n_kt;
+    int kt_per;           // column tiles per workgroup (chosen by launch_fill)
 };
 
 // MFMA step path (the K-loop's step kernels at large B).  W is re-laid once

@@ -1407,86 +1407,109 @@ __global__ __launch_bounds__(kResThreads) void kloop_resident_kernel(ResidentArg
 // Deferred scratch fill (K-loop): S[b, r, k] = fma chain over t = K .. 1 of
 // dp_t[b, r] * z_t[b, k] from +0 -- the same bits as K per-step "+=" updates
 // of a zeroed scratch -- and Sb[b, r] = add chain of dp_t[b, r].  Per sample
-// this is the product dp_b^T z_b over the K steps; each workgroup writes one
-// 64 x 64 tile of one sample's scratch once.  It stages up to kFillSteps
-// steps of dp (64 rows) and z (64 columns) in LDS, t descending, and each
-// wave accumulates a 32 x 32 block with v_mfma_f32_16x16x4f32, whose four
-// k-slots are taken in order as an fma chain: slot kk of the instruction at
-// staged step tt is step t0 - tt - kk.  Steps past the last multiple of 4
-// go through VALU fma on the same accumulators.  Operand layout (16 x 16 x
-// 4): lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; D[i][j] sits in
-// lane j + 16 (i / 4), register i % 4.  The tile leaves through LDS as
-// coalesced rows.
+// this is the product dp_b^T z_b over the K steps, written once in 64 x 64
+// tiles.  A workgroup takes one sample's row tile (64 rows of dp) and
+// kt_per of its column tiles (64 columns of z each), one after the other.
+// Steps are staged in LDS kFillSteps at a time, t descending.  The next
+// pass's operands are loaded into registers while the current pass's
+// MFMAs run, so a tile's load latency hides behind the previous tile's
+// work.  Each wave accumulates a 32 x 32 block with v_mfma_f32_16x16x4f32,
+// whose four k-slots are taken in order as an fma chain: slot kk of the
+// instruction at staged step tt is step t0 - tt - kk.  Steps past the last multiple of 4 go through VALU fma on
+// the same accumulators.  Operand layout (16 x 16 x 4): lane l holds
+// A[l % 16][l / 16] and B[l / 16][l % 16]; D[i][j] sits in lane
+// j + 16 (i / 4), register i % 4.  The tile leaves through LDS (the z
+// buffer) as coalesced rows.
 // ---------------------------------------------------------------------------
 constexpr int kFillPitch = kFillTile + 16;   // staged row pitch: the 4 k-slots of a read hit distinct banks
+constexpr int kFillSeg = kFillSteps * 32 / kThreads;   // 16-byte dp and z segments per thread and pass
 static_assert(kFillSteps * 32 % kThreads == 0, "whole staging passes");
 
-__global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
+__global__ __launch_bounds__(kThreads, 4) void scratch_fill_kernel(FillArgs a)
 {
     __shared__ __attribute__((aligned(16))) float dps[kFillSteps][kFillPitch];
     __shared__ __attribute__((aligned(16))) float zs[kFillSteps][kFillPitch];
     const int n_in = a.n_x + a.C;
     const int R3 = 3 * a.C;
-    const int tiles = a.n_rt * a.n_kt;
+    const int n_kg = (a.n_kt + a.kt_per - 1) / a.kt_per;   // column-tile groups per row tile
+    const int groups = a.n_rt * n_kg;
     // a sample's tiles share its dp rows and z columns: keep them on one XCD
     const int blk = (int)xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
-    const int b = blk / tiles;
-    const int rem = blk - b * tiles;
-    const int rt = rem / a.n_kt;
-    const int kt = rem - rt * a.n_kt;
+    const int b = blk / groups;
+    const int rem = blk - b * groups;
+    const int rt = rem / n_kg;
+    const int kt0 = (rem - rt * n_kg) * a.kt_per;
+    const int npass = (a.K + kFillSteps - 1) / kFillSteps;
+    const int items = min(a.kt_per, a.n_kt - kt0) * npass;   // (column tile, pass) pairs in order
     const int r0 = rt * kFillTile;
-    const int k0 = kt * kFillTile;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int wr = 32 * (wave >> 1);   // the wave's 32 x 32 block of the tile
     const int wc = 32 * (wave & 1);
-    const bool do_bias = (kt == 0) && (threadIdx.x < kFillTile);
     // 16-byte staging needs every 4-float segment to lie inside one row of one tensor
     const bool vec = (R3 % 4 == 0) && (a.n_x % 4 == 0) && (a.C % 4 == 0) &&
                      ((((uintptr_t)a.dp) | ((uintptr_t)a.u) | ((uintptr_t)a.h_hist)) & 15u) == 0;
 
-    f32x4 acc[2][2];
+    // Item it's dp rows and z columns, kFillSeg 16-byte segments per thread
+    // (32 per staged step: 16 of dp, 16 of z), all in flight at once,
+    // clamped into bounds; vok[m] false outside the tile's rows, columns
+    // and steps.  The zero select waits until the values go to LDS, so the
+    // loads of the next item stay in flight through the current MFMAs.
+    f32x4 v[kFillSeg];
+    bool vok[kFillSeg];
+    // A thread's segments share their column (sgi = threadIdx.x % 32) and
+    // differ in the staged step only: one base address per item, one
+    // step stride.
+    const int sgi = threadIdx.x & 31;
+    const bool is_dp = sgi < 16;
+    const int x = 4 * (sgi & 15);
+    auto issue = [&](int it) __attribute__((always_inline)) {
+        const int k0 = (kt0 + it / npass) * kFillTile;
+        const int t0 = a.K - (it % npass) * kFillSteps;
+        const int nst = min(kFillSteps, t0);
+        // base, row length and column picked by selects, not branches: the
+        // loads issue back to back
+        const int r = r0 + x;
+        const int k = min(k0 + x, n_in - 4);
+        const bool is_u = k < a.n_x;
+        const float* base = is_dp ? a.dp : (is_u ? a.u : a.h_hist);
+        const int len = is_dp ? R3 : (is_u ? a.n_x : a.C);
+        const int col = is_dp ? min(r, R3 - 4) : (is_u ? k : k - a.n_x);
+        const bool inside = is_dp ? r < R3 : k0 + x < n_in;
+        const float* p0 = base + (int64_t)b * len + col;
+        const int64_t step = (int64_t)a.B * len;   // floats from step t to t + 1
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int m = 0; m < kFillSeg; ++m) {
+            const int tt = (threadIdx.x >> 5) + m * (kThreads / 32);
+            const int t = t0 - min(tt, nst - 1) - 1;   // clamped into bounds
+            v[m] = *reinterpret_cast<const f32x4*>(p0 + t * step);
+            vok[m] = tt < nst && inside;
+        }
+    };
+    auto place = [&]() __attribute__((always_inline)) {
+        float* row0 = is_dp ? &dps[threadIdx.x >> 5][x] : &zs[threadIdx.x >> 5][x];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float sb = 0.0f;
+        for (int m = 0; m < kFillSeg; ++m)
+            *reinterpret_cast<f32x4*>(row0 + m * (kThreads / 32) * kFillPitch) =
+                vok[m] ? v[m] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
 
-    for (int t0 = a.K; t0 >= 1; t0 -= kFillSteps) {
+    const bool vec_out = (n_in % 4 == 0) && ((((uintptr_t)a.gW_s) & 15u) == 0);
+
+    f32x4 acc[2][2];
+    float sb = 0.0f;
+    if (vec) issue(0);
+    for (int it = 0; it < items; ++it) {
+        const int j = it / npass;
+        const int p = it - j * npass;
+        const int k0 = (kt0 + j) * kFillTile;
+        const int t0 = a.K - p * kFillSteps;
         const int nst = min(kFillSteps, t0);   // steps t0, t0 - 1, .., t0 - nst + 1
+        const bool do_bias = (kt0 + j == 0) && (threadIdx.x < kFillTile);
         if (vec) {
-            // 16 segments of 4 floats per staged row, dp and z rows
-            // interleaved; every load of the pass is in flight before the
-            // first LDS store.
-            constexpr int kSeg = kFillSteps * 32 / kThreads;
-            f32x4 v[kSeg];
-#pragma unroll
-            for (int m = 0; m < kSeg; ++m) {
-                const int i = threadIdx.x + m * kThreads;
-                const int tt = i / 32;
-                const int sgi = i - tt * 32;
-                const int x = 4 * (sgi & 15);
-                // clamped into bounds; zero outside the tile's rows, columns and steps
-                const int64_t tb = (int64_t)(t0 - min(tt, nst - 1) - 1) * a.B + b;
-                if (sgi < 16) {
-                    const int r = r0 + x;
-                    v[m] = load4_or_zero(a.dp + tb * R3 + min(r, R3 - 4), tt < nst && r < R3);
-                } else {
-                    const int k = min(k0 + x, n_in - 4);
-                    const float* src = (k < a.n_x) ? a.u + tb * a.n_x + k : a.h_hist + tb * a.C + (k - a.n_x);
-                    v[m] = load4_or_zero(src, tt < nst && k0 + x < n_in);
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < kSeg; ++m) {
-                const int i = threadIdx.x + m * kThreads;
-                const int tt = i / 32;
-                const int sgi = i - tt * 32;
-                const int x = 4 * (sgi & 15);
-                *reinterpret_cast<f32x4*>(sgi >= 16 ? &zs[tt][x] : &dps[tt][x]) = v[m];
-            }
+            place();
         } else {
             for (int i = threadIdx.x; i < kFillSteps * kFillTile; i += kThreads) {
                 const int tt = i / kFillTile;
@@ -1505,6 +1528,14 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
             }
         }
         __syncthreads();
+        if (vec && it + 1 < items) issue(it + 1);   // in flight during this pass's MFMAs
+        if (p == 0) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            sb = 0.0f;
+        }
         const int nst4 = nst & ~3;
         // operands of the next 4 steps read while the current MFMAs run
         // (two operand sets in turn, so that no copy waits for a read)
@@ -1547,47 +1578,51 @@ __global__ __launch_bounds__(kThreads) void scratch_fill_kernel(FillArgs a)
         }
         if (do_bias)
             for (int tt = 0; tt < nst; ++tt) sb = sb + dps[tt][threadIdx.x];
-        __syncthreads();
-    }
-
-    // The tile through LDS (dps reused as [64][kFillPitch]) for row-wise stores.
+        if (p == npass - 1) {
+            // The tile through LDS (zs reused as [64][kFillPitch]) for row-wise
+            // stores: 16 lanes write one 256-byte row segment, whole cache
+            // lines (stores from the accumulators' layout, 64 bytes per row,
+            // wrote 1.43 times the scratch's bytes to HBM).
+            __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dps[wr + 16 * mt + 4 * lk + e][wc + 16 * nt + li] = acc[mt][nt][e];
-    __syncthreads();
-    const bool vec_out = (n_in % 4 == 0) && ((((uintptr_t)a.gW_s) & 15u) == 0);
-    // every LDS read of the tile first, then the stores (one LDS wait, not one per store)
-    constexpr int kOut = kFillTile * (kFillTile / 4) / kThreads;
-    static_assert(kFillTile * (kFillTile / 4) % kThreads == 0, "whole output passes");
-    f32x4 ov[kOut];
+                    for (int e = 0; e < 4; ++e) zs[wr + 16 * mt + 4 * lk + e][wc + 16 * nt + li] = acc[mt][nt][e];
+            __syncthreads();
+            // every LDS read of the tile first, then the stores (one LDS wait, not one per store)
+            constexpr int kOut = kFillTile * (kFillTile / 4) / kThreads;
+            static_assert(kFillTile * (kFillTile / 4) % kThreads == 0, "whole output passes");
+            f32x4 ov[kOut];
 #pragma unroll
-    for (int m = 0; m < kOut; ++m) {
-        const int u = threadIdx.x + m * kThreads;
-        const int row = u / (kFillTile / 4);
-        ov[m] = *reinterpret_cast<const f32x4*>(&dps[row][4 * (u - row * (kFillTile / 4))]);
-    }
-#pragma unroll
-    for (int m = 0; m < kOut; ++m) {
-        const int u = threadIdx.x + m * kThreads;
-        const int row = u / (kFillTile / 4);
-        const int c4 = 4 * (u - row * (kFillTile / 4));
-        const int r = r0 + row;
-        const int k = k0 + c4;
-        if (r < R3 && k < n_in) {
-            float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in + k;
-            if (vec_out && k + 4 <= n_in) {
-                __builtin_nontemporal_store(ov[m], reinterpret_cast<f32x4*>(dst));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (k + e < n_in) dst[e] = ov[m][e];
+            for (int m = 0; m < kOut; ++m) {
+                const int u = threadIdx.x + m * kThreads;
+                const int row = u / (kFillTile / 4);
+                ov[m] = *reinterpret_cast<const f32x4*>(&zs[row][4 * (u - row * (kFillTile / 4))]);
             }
+#pragma unroll
+            for (int m = 0; m < kOut; ++m) {
+                const int u = threadIdx.x + m * kThreads;
+                const int row = u / (kFillTile / 4);
+                const int c4 = 4 * (u - row * (kFillTile / 4));
+                const int r = r0 + row;
+                const int k = k0 + c4;
+                if (r < R3 && k < n_in) {
+                    float* dst = a.gW_s + ((int64_t)b * R3 + r) * n_in + k;
+                    if (vec_out && k + 4 <= n_in) {
+                        __builtin_nontemporal_store(ov[m], reinterpret_cast<f32x4*>(dst));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (k + e < n_in) dst[e] = ov[m][e];
+                    }
+                }
+            }
+            if (do_bias && r0 + (int)threadIdx.x < R3) a.gb_s[(int64_t)b * R3 + r0 + threadIdx.x] = sb;
         }
+        __syncthreads();   // LDS free for the next item's operands
     }
-    if (do_bias && r0 + (int)threadIdx.x < R3) a.gb_s[(int64_t)b * R3 + r0 + threadIdx.x] = sb;
 }
 
 // [persistent kernel source: begin]
@@ -2598,10 +2633,19 @@ hipError_t launch_bwd(const BwdArgs& a, const StepPlan& p, hipStream_t s)
 
 hipError_t launch_fill(const FillArgs& a, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)a.B * a.n_rt * a.n_kt;
+    if (a.n_rt <= 0 || a.n_kt <= 0) return hipSuccess;
+    if (a.K < 1) return hipErrorInvalidValue;   // K = 0 has no steps to stage: callers zero the scratch
+    // A workgroup walks a whole row of column tiles when the row tiles alone
+    // fill the device (at least 4 per CU), so that its next tile loads while
+    // this one computes; below that the tiles spread one per workgroup.
+    // Measured at B = 256, C = 256, n_x = 128, K = 64: 1, 2, 3, 6 tiles per
+    // workgroup 134, 125, 122, 120 us.
+    FillArgs f = a;
+    f.kt_per = ((int64_t)a.B * a.n_rt >= 1024) ? a.n_kt : 1;
+    const int64_t blocks = (int64_t)a.B * a.n_rt * ((a.n_kt + f.kt_per - 1) / f.kt_per);
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(scratch_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(scratch_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, f);
     return hipGetLastError();
 }
 

@@ -474,14 +474,19 @@ def test_kloop_equals_its_phases(cfc, case, path):
 
 
 @pytest.mark.parametrize("B,C,n_x,K", [(256, 128, 64, 64), (420, 100, 20, 37), (1400, 64, 0, 4),
-                                        (32, 128, 64, 64), (30, 124, 64, 70), (30, 126, 62, 37)])
+                                        (32, 128, 64, 64), (30, 124, 64, 70), (30, 126, 62, 37),
+                                        (256, 128, 64, 70), (256, 256, 128, 64), (420, 126, 62, 37)])
 def test_scratch_fill_large_batch_equals_slices(cfc, B, C, n_x, K):
     """A sample's scratch depends on that sample alone: on large batches
     (thousands of tiles, ragged tiles, the fma tail, n_x = 0) the
     full-batch call equals calls on slices of 16 samples bit for bit, and
-    both match fp64 sums.  The last three shapes: the pages shape, then
-    ragged tiles near it on 16-byte staging with two staging passes
-    (K = 70), and on scalar staging (3C = 378) with the fma tail."""
+    both match fp64 sums.  Large batches give a workgroup several column
+    tiles of its row tile (2 of 3 at B = 256, C = 128; all 6 at the wide
+    shape; 3 on scalar staging at 3C = 378), slices one, so the two sides
+    also cover both tile walks.  Shapes 4-6: the pages shape, then ragged
+    tiles near it on 16-byte staging with two staging passes (K = 70), and
+    on scalar staging (3C = 378) with the fma tail; shape 7 has two
+    staging passes per tile with several tiles per workgroup."""
     say("scratch fill, large batch against slices", B, C, n_x, K)
     n_in = n_x + C
     dp = normal((K, B, 3 * C), 19, 1)
