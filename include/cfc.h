@@ -124,18 +124,24 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *   ws, ws_bytes         workspace of at least
  *                        cfc_train_kloop_workspace_bytes(B, C, n_x, K) bytes
  *                        (the pre-activation gradients of every step, the
- *                        input projection of every step, the BPTT carry and
- *                        the step kernels' re-laid copy of W); contents are
- *                        undefined afterwards
+ *                        input projection of every step, the BPTT carry,
+ *                        the step kernels' re-laid copy of W and the step
+ *                        flags of the resident and persistent launches);
+ *                        contents are undefined afterwards
  *   gW_scratch [B, 3, C, n_in], gb_scratch [B, 3, C]   out: per-sample sums
  *                        S[b,q,c,:] = sum_t dp_q[t,b,c] z_t[b,:] (t = K..1)
  *   gW [3, C, n_in], gb [3, C]   out, OVERWRITTEN; valid only once this
  *                        call's work on `stream` has completed
  * The paths give the same bits:
- *  - persistent (C <= 128): an input-projection launch for all steps, one
- *    workgroup per sample running every K step with the recurrent W in
- *    registers, the scratch fill and the reduction -- four launches,
- *    enqueued directly on `stream`;
+ *  - persistent (C <= 128): one workgroup per sample running every K step
+ *    with the recurrent W in registers, after the input projection of all
+ *    steps, then the scratch fill and the reduction, enqueued directly on
+ *    `stream`.  With B <= 128 the projection is formed by extra workgroups
+ *    of the same launch, which the sample workgroups wait for -- three
+ *    launches.  The wait is bounded: only other work holding the device's
+ *    CUs for about a second makes it give up, which marks an error word in
+ *    ws and leaves the results undefined.  Otherwise, and on a stream under
+ *    capture, the projection is a launch of its own -- four launches;
  *  - resident MFMA (B >= 64, C > 128, shapes of the MFMA step kernels whose
  *    grid fits the device at once): a W re-layout, one cooperative launch
  *    running all 2K steps, the fill and the reduction, enqueued directly (a

@@ -3,6 +3,7 @@
 // K-loop training step.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -132,9 +133,20 @@ int64_t kloop_ws_flags(int B, int C)
     return ((((int64_t)(B + 15) / 16) * ((C + 15) / 16) + 1) * cfc::kResFlagStride + 63) & ~(int64_t)63;
 }
 int64_t kloop_ws_resident(int B, int C) { return cfc::resident_exchange_floats(B, C) + kloop_ws_flags(B, C); }
-int64_t kloop_ws_floats(int B, int C, int n_x, int K)
+// Last: the flags of the persistent launch that also forms X (one per
+// projection workgroup, then its error word).
+int64_t kloop_ws_pofs(int B, int C, int n_x, int K)
 {
     return kloop_ws_wofs(B, C, K) + cfc::mfma_w_floats(C, n_x) + kloop_ws_resident(B, C);
+}
+int64_t kloop_ws_proj(int B, int C, int K)
+{
+    const int n = cfc::persist_proj_blocks(B, C, K);
+    return n < 0 ? 0 : ((int64_t)n + 1 + 63) & ~(int64_t)63;
+}
+int64_t kloop_ws_floats(int B, int C, int n_x, int K)
+{
+    return kloop_ws_pofs(B, C, n_x, K) + kloop_ws_proj(B, C, K);
 }
 
 struct KloopArgs {
@@ -159,6 +171,25 @@ constexpr int kMfmaMinB = 64;
 // one load of the counters and a short sleep, about a microsecond): far
 // beyond any step, so that it only ends a wait that cannot end.
 constexpr int kResidentSpinLimit = 1 << 20;
+// The persistent launch forms X itself (extra workgroups ahead of the sample
+// workgroups, which wait for them) when at most this many samples: the
+// sample workgroups, one per CU, then leave at least half the CUs to the
+// projection, whatever order the workgroups start in.
+constexpr int kPersistFuseMaxB = 128;
+constexpr int kPersistSpinLimit = 1 << 20;
+// Launch numbers for the projection flags: distinct for 2^32 launches, never 0.
+std::atomic<unsigned> g_persist_call{0x9e3779b9u};
+unsigned next_persist_call()
+{
+    unsigned c = g_persist_call.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (c == 0) c = g_persist_call.fetch_add(1, std::memory_order_relaxed) + 1;
+    return c;
+}
+bool stream_capturing(hipStream_t s)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return !(hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusNone);
+}
 
 // A cooperative launch cannot be captured into a graph: a stream under
 // capture takes the MFMA step kernels instead of the resident kernel.
@@ -212,10 +243,23 @@ int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipSt
     float* X = k.ws + (int64_t)k.K * 3 * BC;            // [K, B, 3C]
     float* dh_ws = k.ws + (int64_t)2 * k.K * 3 * BC;    // [2, B, C]
     if (path == Path::Persistent) {
+        cfc::PersistArgs a{X, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
+        const int n_proj = cfc::persist_proj_blocks(k.B, k.C, k.K);
+        // One launch that forms X and runs the recurrence; a stream under
+        // capture takes two (a replayed graph would repeat the launch number
+        // that the flags are matched against).
+        if (k.B <= kPersistFuseMaxB && n_proj > 0 && !stream_capturing(s)) {
+            a.u = k.u;
+            a.flags = reinterpret_cast<int*>(k.ws + kloop_ws_pofs(k.B, k.C, k.n_x, k.K));
+            a.n_proj = n_proj;
+            a.call = next_persist_call();
+            a.spin_limit = kPersistSpinLimit;
+            CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch (with the input projection)");
+            return CFC_OK;
+        }
         const cfc::XprojArgs x{k.u, k.W, k.bias, X, (int64_t)k.K * k.B, 3 * k.C, k.n_x, k.n_x + k.C,
                                (3 * k.C + 63) / 64};
         CFC_HIP(cfc::launch_xproj(x, s), "input projection launch");
-        const cfc::PersistArgs a{X, k.y, k.h0, k.W, k.bias, k.h_hist, k.act, dp, k.B, k.C, k.n_x, k.K};
         CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch");
         return CFC_OK;
     }

@@ -162,6 +162,17 @@ struct PersistArgs {
     float* act;           // [K, 3, B, C]
     float* dp;            // [K, B, 3C]
     int B, C, n_x, K;
+    // n_proj > 0: the launch also forms X.  Workgroups 0 .. n_proj - 1 each
+    // form 64 rows x 128 outputs of X from u (xproj_kernel's tiles and
+    // bits) and then set flags[their index] = call; the sample workgroups
+    // n_proj .. n_proj + B - 1 wait for every flag (at most spin_limit
+    // polls; flags[n_proj] = call marks a wait that gave up) before their
+    // first read of X.  n_proj == 0: X comes from an earlier launch.
+    const float* u;       // [K, B, n_x]
+    int* flags;           // [n_proj + 1]
+    int n_proj;
+    unsigned call;        // nonzero, distinct between launches that share flags
+    int spin_limit;
 };
 // [persistent kernel source: end]
 
@@ -225,6 +236,7 @@ int reduce_slices(int64_t B);
 // Persistent K-loop kernel: returns the LDS bytes it needs for C channels,
 // or 0 if no instantiation holds the recurrent W in registers (C > 128).
 size_t persist_smem(int C);
+int persist_proj_blocks(int B, int C, int K);   // -1 when too many
 
 hipError_t launch_fwd(const FwdArgs& a, const StepPlan& p, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, const StepPlan& p, hipStream_t s);

@@ -60,6 +60,13 @@ __device__ __forceinline__ f32x4 load4_or_zero(const float* clamped, bool valid)
     return valid ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// 4-byte store at device scope (sc1): written through to memory, so that a
+// workgroup on another XCD of the same launch reads it.
+__device__ __forceinline__ void st_agent(float* p, float v)
+{
+    __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // z_s = [u_t[b0+s] ; h_prev[b0+s]] for the tile's samples into LDS rows of
 // pitch ldz (zero padded past n_in and for absent samples).
 template <int BT>
@@ -208,15 +215,15 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a)
 // waves of 32 x 32 (2 x 2 MFMA tiles, 4 chains each).  The chains start
 // from +0 and zero padding past n_x leaves them unchanged.
 // ---------------------------------------------------------------------------
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
+// [persistent kernel source: begin]
+// (the tile code is also run by the persistent launch that forms X)
+// One 64 x 64 tile (mtile, ntile) of X; wave (0..3) forms its 32 x 32
+// block.  DEV: X stored at device scope (written through to memory), for
+// readers in the same launch.
+template <bool VEC, bool DEV = false>
+__device__ __forceinline__ void xproj_tile(const XprojArgs& a, int64_t mtile, int ntile, int wave)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    // the column tiles of a row tile share its u rows: keep them on one XCD
-    const int64_t blk = xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
-    const int ntile = (int)(blk % a.n_ntiles);
-    const int64_t mtile = blk / a.n_ntiles;
     const int64_t m0 = mtile * 64 + (wave >> 1) * 32;
     const int n0 = ntile * 64 + (wave & 1) * 32;
     const int li = lane & 15;
@@ -298,11 +305,26 @@ __global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t row = m0 + 16 * mt + 4 * lk + i;
-                if (r < N && row < M)
-                    a.X[row * N + r] = xproj_combine(bias[nt], acc[mt][nt][0][i], acc[mt][nt][1][i],
-                                                     acc[mt][nt][2][i], acc[mt][nt][3][i]);
+                if (r < N && row < M) {
+                    const float v = xproj_combine(bias[nt], acc[mt][nt][0][i], acc[mt][nt][1][i],
+                                                  acc[mt][nt][2][i], acc[mt][nt][3][i]);
+                    if (DEV)
+                        st_agent(a.X + row * N + r, v);
+                    else
+                        a.X[row * N + r] = v;
+                }
             }
     }
+}
+
+// [persistent kernel source: end]
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void xproj_kernel(XprojArgs a)
+{
+    // the column tiles of a row tile share its u rows: keep them on one XCD
+    const int64_t blk = xcd_local_order(blockIdx.x, (int64_t)gridDim.x);
+    xproj_tile<VEC>(a, blk / a.n_ntiles, (int)(blk % a.n_ntiles), threadIdx.x >> 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -504,11 +526,9 @@ __global__ __launch_bounds__(kThreads) void permute_w_kernel(PermuteArgs a)
 // they run, so those moves are made at device scope (sc1): write-through
 // stores, and loads that the vector L1 does not serve; the step kernels,
 // whose launches are ordered by the stream, and the resident kernel's moves
-// of a workgroup's own data use plain moves.
-__device__ __forceinline__ void st_agent(float* p, float v)
-{
-    __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// of a workgroup's own data use plain moves.  (st_agent, above, is the
+// 4-byte store.)
+//
 // 16-byte device-scope load through a raw buffer resource over [base, base
 // + bytes): one request per 16 bytes, where two 8-byte agent-scope atomic
 // loads make two.  Offsets at or past `bytes` read zero.
@@ -1761,6 +1781,78 @@ __device__ __forceinline__ BwdFactors bwd_factors(const float* st, int c)
     return f;
 }
 
+// The projection workgroups of a launch that also forms X (n_proj > 0):
+// workgroup p forms row tile p / ncol2 (64 rows (t, b)) of X and its column
+// tiles 2 (p % ncol2) and 2 (p % ncol2) + 1 (waves 0-3 and 4-7), with
+// xproj_kernel's code and device-scope stores, then, once every wave's
+// stores are performed, sets flags[p] = call.
+__device__ __forceinline__ void persist_projection(const PersistArgs& a)
+{
+    const int N = 3 * a.C;
+    const int n_nt = (N + 63) / 64;
+    const int ncol2 = (n_nt + 1) / 2;
+    const XprojArgs x{a.u, a.W, a.bias, const_cast<float*>(a.X), (int64_t)a.K * a.B, N, a.n_x, a.n_x + a.C, n_nt};
+    // the column tiles of a row tile share its u rows: keep them on one XCD
+    const int p = (int)xcd_local_order(blockIdx.x, (int64_t)a.n_proj);
+    const int ntile = 2 * (p % ncol2) + (int)(threadIdx.x >> 8);
+    const int wave = (threadIdx.x >> 6) & 3;
+    const bool vec = (a.n_x % 4 == 0) && ((a.n_x + a.C) % 4 == 0) &&
+                     ((((uintptr_t)a.u) | ((uintptr_t)a.W)) & 15u) == 0;
+    if (ntile < n_nt) {
+        if (vec)
+            xproj_tile<true, true>(x, p / ncol2, ntile, wave);
+        else
+            xproj_tile<false, true>(x, p / ncol2, ntile, wave);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(a.flags + blockIdx.x, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A sample workgroup of such a launch, before its first read of X: wave 0
+// polls the n_proj flags and the error word after them until every flag
+// holds this launch's call number, or a wait has given up (error word ==
+// call); after spin_limit polls it gives up itself and marks the error
+// word.  A poll is one round trip: its loads (64 words each, up to
+// kPollLoads of them) are all in flight together.  The other waves wait at
+// the barrier.  X is then read with plain loads: it was written through to
+// memory, and no cache on this workgroup's CU or XCD holds a line of it
+// (they start each launch empty of it, and nothing here reads X before
+// this wait).
+constexpr int kPollLoads = 4;
+__device__ __forceinline__ void persist_wait_projection(const PersistArgs& a)
+{
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int call = (int)a.call;
+        const int n = a.n_proj;   // words n_proj + 1: the flags, then the error word
+        for (int it = 0;; ++it) {
+            int ok = 1, gave_up = 0;
+            for (int base = 0; base <= n; base += 64 * kPollLoads) {
+                int v[kPollLoads];
+#pragma unroll
+                for (int m = 0; m < kPollLoads; ++m)
+                    v[m] = __hip_atomic_load(a.flags + min(base + 64 * m + lane, n), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int m = 0; m < kPollLoads; ++m) {
+                    const int i = base + 64 * m + lane;
+                    ok &= __all(i >= n || v[m] == call) ? 1 : 0;
+                    gave_up |= __any(i == n && v[m] == call) ? 1 : 0;
+                }
+            }
+            if (ok || gave_up) break;
+            if (it >= a.spin_limit) {
+                if (lane == 0) __hip_atomic_store(a.flags + n, call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+}
+
 template <int CPG, int NH>
 __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistArgs a)
 {
@@ -1774,7 +1866,11 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     __shared__ __attribute__((aligned(16))) float stage[L::STAGE];
     __shared__ __attribute__((aligned(16))) float dbuf[L::DBUF];
     float* obuf = &part[0][0][0];   // forward output buffer [kFwdChunk][4][C] (partials unused then)
-    const int b = blockIdx.x;
+    if ((int)blockIdx.x < a.n_proj) {
+        persist_projection(a);
+        return;
+    }
+    const int b = (int)blockIdx.x - a.n_proj;
     const int tid = threadIdx.x;
     const int g = tid >> 3;          // canonical dz group
     const int j = tid & 7;           // lane of the group: recurrent columns 32 i + 4 j + e
@@ -1984,6 +2080,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                    (int64_t)b * C;
         };
     };
+    if (a.n_proj > 0) persist_wait_projection(a);   // X is formed by this launch
     if (c_vec && K >= 1) load_x(1, min(kFwdChunk, K));
     int prev_t0 = 0, prev_nt = 0;
     // With K a whole number of chunks the backward's first chunk (steps K ..
@@ -2579,7 +2676,12 @@ bool persist_shape(int C, PersistShape& ps)
 template <int CPG, int NH>
 hipError_t launch_persist_t(const PersistArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL((kloop_persist_kernel<CPG, NH>), dim3((unsigned)a.B), dim3(kPersistThreads), 0, s, a);
+    const int64_t blocks = (int64_t)a.n_proj + a.B;
+    if (a.n_proj < 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.n_proj > 0 && (a.flags == nullptr || (a.u == nullptr && a.n_x > 0) || a.call == 0 ||
+                         a.n_proj != persist_proj_blocks(a.B, a.C, a.K)))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((kloop_persist_kernel<CPG, NH>), dim3((unsigned)blocks), dim3(kPersistThreads), 0, s, a);
     return hipGetLastError();
 }
 // [persistent kernel source: end]
@@ -2593,6 +2695,15 @@ int reduce_slices(int64_t B)
     int R = 1;
     while (R < 16 && (int64_t)R * 2 * 8 <= B) R *= 2;
     return R;
+}
+
+// Projection workgroups of a launch that also forms X: 64 rows x 128
+// outputs each.
+int persist_proj_blocks(int B, int C, int K)
+{
+    const int64_t rows = (int64_t)K * B;
+    const int64_t n = ((rows + 63) / 64) * ((((3 * C + 63) / 64) + 1) / 2);
+    return n > 0x3fffffffLL ? -1 : (int)n;
 }
 
 size_t persist_smem(int C)

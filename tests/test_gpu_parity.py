@@ -304,10 +304,24 @@ def test_input_projection_rows_do_not_depend_on_the_launch(cfc, case, rows):
     np.testing.assert_array_equal(bits(part), bits(full[:rows]))
 
 
+def persist_projection_flags(ws, B, C, K):
+    """The flags of a persistent launch that formed X itself: the last
+    region of the workspace, one per projection workgroup (64 rows x 128
+    outputs of X each), then the error word."""
+    n = -(-K * B // 64) * ((-(-3 * C // 64) + 1) // 2)
+    region = (n + 1 + 63) // 64 * 64
+    f = host(ws[ws.numel() - region:]).view(np.int32)
+    return f[:n], f[n]
+
+
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "three_blocks", "odd_channels"])
 def test_recurrence_composes_to_fwd_bwd(cfc, case):
-    """cfc_input_projection then cfc_kloop_recurrence gives the bits of
-    cfc_kloop_fwd_bwd (persistent path)."""
+    """cfc_input_projection then cfc_kloop_recurrence (two launches) gives
+    the bits of cfc_kloop_fwd_bwd on the persistent path, whose one launch
+    (B <= 128) also forms X: extra workgroups form it while the sample
+    workgroups load W, and those wait for them.  Its bookkeeping afterwards:
+    every projection workgroup's flag holds the launch's number and the
+    error word, which a wait that gave up would have set to it, does not."""
     d = CASES[case]
     say("projection + recurrence == fwd_bwd", case)
     x = cfc_inputs(**d, seed=9, bias_scale=0.3)
@@ -315,9 +329,18 @@ def test_recurrence_composes_to_fwd_bwd(cfc, case):
     cfc.cfc_set_kloop_mode(cfc.KLOOP_PERSISTENT)
     try:
         a = cfc.KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
+        a.ws.fill_(float("nan"))
+        # first on other inputs, so that the flags and X of an earlier
+        # launch are in place: X read before this launch formed it would
+        # show in the bits
+        cfc.cfc_kloop_fwd_bwd(dev(-0.5 * x.u), y, h0, W, bias, out=a)
         cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
     finally:
         cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
+    if d["B"] <= 128:
+        flags, err = persist_projection_flags(a.ws, d["B"], d["C"], d["K"])
+        assert flags[0] != 0 and err != flags[0], "a wait for the input projection gave up"
+        np.testing.assert_array_equal(flags, np.full(flags.size, flags[0], np.int32))
     b = cfc.KloopBuffers.allocate(d["B"], d["C"], d["n_x"], d["K"], "cuda")
     X = cfc.cfc_input_projection(u, W, bias)
     cfc.cfc_kloop_recurrence(X, y, h0, W, out=b)
