@@ -556,6 +556,51 @@ def test_scratch_fill_matches_its_definition(cfc, case):
     assert_ok(check_grad("Sb", host(Sb), refb, np.abs(dp.astype(np.float64)).sum(0).reshape(B, 3, C)))
 
 
+@pytest.mark.parametrize("entry", ["train_kloop", "noalloc"])
+def test_persistent_step_replays_under_graph_capture(cfc, entry):
+    """On a stream under capture the persistent path launches the input
+    projection on its own (a replayed graph would repeat the number that the
+    fused launch's projection flags are matched against).  One step captured
+    with torch's graph API, replayed on three input sets with eager copies
+    and synchronizations between the replays: every replay gives the bits of
+    an eager step on the same inputs."""
+    d = CASES["pages"]
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    say("persistent step under graph capture", entry)
+    keys = ("h_hist", "act", "gW_scratch", "gb_scratch", "gW", "gb")
+    xs = [cfc_inputs(**d, seed=40 + i, bias_scale=0.2) for i in range(3)]
+    ref = []
+    for x in xs:
+        out, _ = kloop_dev(cfc, x)
+        ref.append({k: host(getattr(out, k)).copy() for k in keys})
+    st = [dev(a) for a in (xs[0].u, xs[0].y, xs[0].h0, xs[0].W, xs[0].bias)]
+    buf = cfc.KloopBuffers.allocate(B, C, n_x, K, "cuda")
+
+    def step():
+        if entry == "noalloc":
+            cfc.cfc_train_kloop_noalloc(*st, out=buf)
+        else:
+            cfc.cfc_train_kloop(*st, out=buf)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in (1, 0, 2):
+        for a, v in zip(st, (xs[i].u, xs[i].y, xs[i].h0, xs[i].W, xs[i].bias)):
+            a.copy_(torch.from_numpy(np.ascontiguousarray(v)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            np.testing.assert_array_equal(bits(host(getattr(buf, k))), bits(ref[i][k]), err_msg="%s %d" % (k, i))
+
+
 def test_persistent_mode_refuses_shapes_it_cannot_hold(cfc):
     d = CASES["wide"]
     say("persistent refusal", d)
