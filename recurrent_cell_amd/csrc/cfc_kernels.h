@@ -163,8 +163,8 @@ struct PersistArgs {
     float* dp;            // [K, B, 3C]
     int B, C, n_x, K;
     // n_proj > 0: the launch also forms X.  Workgroups 0 .. n_proj - 1 each
-    // form 64 rows x 128 outputs of X from u (xproj_kernel's tiles and
-    // bits) and then set flags[their index] = call; the sample workgroups
+    // form one 64 x 64 tile of X from u (xproj_kernel's tiles and bits)
+    // and then set flags[their index] = call; the sample workgroups
     // n_proj .. n_proj + B - 1 wait for every flag (at most spin_limit
     // polls; flags[n_proj] = call marks a wait that gave up) before their
     // first read of X.  n_proj == 0: X comes from an earlier launch.

@@ -1782,27 +1782,25 @@ __device__ __forceinline__ BwdFactors bwd_factors(const float* st, int c)
 }
 
 // The projection workgroups of a launch that also forms X (n_proj > 0):
-// workgroup p forms row tile p / ncol2 (64 rows (t, b)) of X and its column
-// tiles 2 (p % ncol2) and 2 (p % ncol2) + 1 (waves 0-3 and 4-7), with
-// xproj_kernel's code and device-scope stores, then, once every wave's
-// stores are performed, sets flags[p] = call.
+// workgroup p forms tile (p / n_nt, p % n_nt) of X (64 rows (t, b) x 64
+// outputs) with xproj_kernel's code and device-scope stores, on waves 0-3
+// (one wave per SIMD, as in xproj_kernel: two would share each SIMD's
+// matrix core), then, once every wave's stores are performed, sets
+// flags[p] = call.
 __device__ __forceinline__ void persist_projection(const PersistArgs& a)
 {
     const int N = 3 * a.C;
     const int n_nt = (N + 63) / 64;
-    const int ncol2 = (n_nt + 1) / 2;
     const XprojArgs x{a.u, a.W, a.bias, const_cast<float*>(a.X), (int64_t)a.K * a.B, N, a.n_x, a.n_x + a.C, n_nt};
     // the column tiles of a row tile share its u rows: keep them on one XCD
     const int p = (int)xcd_local_order(blockIdx.x, (int64_t)a.n_proj);
-    const int ntile = 2 * (p % ncol2) + (int)(threadIdx.x >> 8);
-    const int wave = (threadIdx.x >> 6) & 3;
     const bool vec = (a.n_x % 4 == 0) && ((a.n_x + a.C) % 4 == 0) &&
                      ((((uintptr_t)a.u) | ((uintptr_t)a.W)) & 15u) == 0;
-    if (ntile < n_nt) {
+    if (threadIdx.x < 256) {
         if (vec)
-            xproj_tile<true, true>(x, p / ncol2, ntile, wave);
+            xproj_tile<true, true>(x, p / n_nt, p % n_nt, threadIdx.x >> 6);
         else
-            xproj_tile<false, true>(x, p / ncol2, ntile, wave);
+            xproj_tile<false, true>(x, p / n_nt, p % n_nt, threadIdx.x >> 6);
     }
     wait_vmem_all();
     __syncthreads();
@@ -1814,40 +1812,63 @@ __device__ __forceinline__ void persist_projection(const PersistArgs& a)
 // polls the n_proj flags and the error word after them until every flag
 // holds this launch's call number, or a wait has given up (error word ==
 // call); after spin_limit polls it gives up itself and marks the error
-// word.  A poll is one round trip: its loads (64 words each, up to
-// kPollLoads of them) are all in flight together.  The other waves wait at
-// the barrier.  X is then read with plain loads: it was written through to
+// word.  A poll's loads (64 words each, up to kPollLoads of them) are in
+// flight together, and two polls are in flight at once, the second issued
+// half a round trip after the first, so that flags set between two polls
+// are seen about half a round trip sooner.  The other waves wait at the
+// barrier.  X is then read with plain loads: it was written through to
 // memory, and no cache on this workgroup's CU or XCD holds a line of it
 // (they start each launch empty of it, and nothing here reads X before
 // this wait).
 constexpr int kPollLoads = 4;
+__device__ __forceinline__ void persist_poll(const PersistArgs& a, int base, int (&v)[kPollLoads])
+{
+#pragma unroll
+    for (int m = 0; m < kPollLoads; ++m)
+        v[m] = __hip_atomic_load(a.flags + min(base + 64 * m + (int)threadIdx.x, a.n_proj), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+// 1: every flag of the words [base, base + 64 kPollLoads) holds call; 2: the
+// error word among them does; 0: neither
+__device__ __forceinline__ int persist_poll_state(const PersistArgs& a, int base, const int (&v)[kPollLoads])
+{
+    const int call = (int)a.call;
+    int ok = 1, gave_up = 0;
+#pragma unroll
+    for (int m = 0; m < kPollLoads; ++m) {
+        const int i = base + 64 * m + (int)threadIdx.x;
+        ok &= __all(i >= a.n_proj || v[m] == call) ? 1 : 0;
+        gave_up |= __any(i == a.n_proj && v[m] == call) ? 1 : 0;
+    }
+    return gave_up ? 2 : ok;
+}
 __device__ __forceinline__ void persist_wait_projection(const PersistArgs& a)
 {
     if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const int call = (int)a.call;
-        const int n = a.n_proj;   // words n_proj + 1: the flags, then the error word
-        for (int it = 0;; ++it) {
-            int ok = 1, gave_up = 0;
-            for (int base = 0; base <= n; base += 64 * kPollLoads) {
-                int v[kPollLoads];
-#pragma unroll
-                for (int m = 0; m < kPollLoads; ++m)
-                    v[m] = __hip_atomic_load(a.flags + min(base + 64 * m + lane, n), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int m = 0; m < kPollLoads; ++m) {
-                    const int i = base + 64 * m + lane;
-                    ok &= __all(i >= n || v[m] == call) ? 1 : 0;
-                    gave_up |= __any(i == n && v[m] == call) ? 1 : 0;
+        // groups of 64 kPollLoads words, one after another; within a group
+        // two polls in flight (A, B)
+        for (int base = 0; base <= a.n_proj; base += 64 * kPollLoads) {
+            int va[kPollLoads], vb[kPollLoads];
+            persist_poll(a, base, va);
+            __builtin_amdgcn_s_sleep(16);   // about 1k cycles: half a round trip
+            int st = 0;
+            // one poll (A) in flight at the top of every pass, so that each
+            // check waits for its own poll only
+            for (int it = 0;; it += 2) {
+                persist_poll(a, base, vb);
+                st = persist_poll_state(a, base, va);
+                if (st) break;
+                persist_poll(a, base, va);
+                st = persist_poll_state(a, base, vb);
+                if (st) break;
+                if (it >= a.spin_limit) {
+                    if (threadIdx.x == 0)
+                        __hip_atomic_store(a.flags + a.n_proj, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    st = 2;
+                    break;
                 }
             }
-            if (ok || gave_up) break;
-            if (it >= a.spin_limit) {
-                if (lane == 0) __hip_atomic_store(a.flags + n, call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
+            if (st == 2) break;   // this wait or another gave up: no further group is waited for
         }
     }
     __syncthreads();
@@ -2697,12 +2718,12 @@ int reduce_slices(int64_t B)
     return R;
 }
 
-// Projection workgroups of a launch that also forms X: 64 rows x 128
-// outputs each.
+// Projection workgroups of a launch that also forms X: one 64 x 64 tile of
+// X each.
 int persist_proj_blocks(int B, int C, int K)
 {
     const int64_t rows = (int64_t)K * B;
-    const int64_t n = ((rows + 63) / 64) * ((((3 * C + 63) / 64) + 1) / 2);
+    const int64_t n = ((rows + 63) / 64) * ((3 * C + 63) / 64);
     return n > 0x3fffffffLL ? -1 : (int)n;
 }
 

@@ -137,9 +137,9 @@ def ws_bytes(B, C, n_x, K):
     nbt = (B + 15) // 16
     flags = (32 * (nbt * ((C + 15) // 16) + 1) + 63) // 64 * 64
     xch = 32 * nbt * ((C + 31) // 32 * 32 + 1024)
-    # flags of the persistent launch that also forms X: one per workgroup of
-    # 64 rows x 128 outputs of X, then the error word
-    proj = ((K * B + 63) // 64 * (((3 * C + 63) // 64 + 1) // 2) + 1 + 63) // 64 * 64
+    # flags of the persistent launch that also forms X: one per workgroup
+    # (one 64 x 64 tile of X each), then the error word
+    proj = ((K * B + 63) // 64 * ((3 * C + 63) // 64) + 1 + 63) // 64 * 64
     return 4 * (((6 * K * B * C + 2 * B * C + 63) // 64) * 64 + 3 * C * ldf + 1024 * C + xch + flags + proj)
 
 

@@ -306,9 +306,9 @@ def test_input_projection_rows_do_not_depend_on_the_launch(cfc, case, rows):
 
 def persist_projection_flags(ws, B, C, K):
     """The flags of a persistent launch that formed X itself: the last
-    region of the workspace, one per projection workgroup (64 rows x 128
-    outputs of X each), then the error word."""
-    n = -(-K * B // 64) * ((-(-3 * C // 64) + 1) // 2)
+    region of the workspace, one per projection workgroup (one 64 x 64 tile
+    of X each), then the error word."""
+    n = -(-K * B // 64) * -(-3 * C // 64)
     region = (n + 1 + 63) // 64 * 64
     f = host(ws[ws.numel() - region:]).view(np.int32)
     return f[:n], f[n]
