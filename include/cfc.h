@@ -305,6 +305,23 @@ int cfc_set_kloop_mode(int mode);
  * sizes or a forced path the sizes cannot take. */
 int cfc_kloop_path(int B, int C, int n_x, int K);
 
+/* Whether the bounded waits of the last K-loop call on `ws` ended normally.
+ * The resident launch's workgroups, and the persistent launch's sample
+ * workgroups (B <= 128, outside graph capture), wait for other workgroups
+ * of the same launch; a wait gives up only after about a second (other work
+ * holding the device's CUs), marks an error word in ws and lets the kernel
+ * finish, with undefined results.  Call once that call's work on `stream`
+ * has completed, with its sizes, on the thread that made it (the path is
+ * the one cfc_kloop_path reports there).  Reads at most two words of ws
+ * with a copy on `stream` and waits for it: unlike the compute calls, this
+ * one synchronises the host with the stream.  Returns CFC_EHIP if a wait
+ * gave up, CFC_OK otherwise (also for paths without waits and for K == 0 or
+ * B == 0), CFC_EINVAL for bad sizes, a null or short ws, or a kloop mode
+ * that forces a path these sizes cannot take.
+ */
+int cfc_kloop_status(const float* ws, size_t ws_bytes, int B, int C, int n_x,
+                     int K, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the
  * K-loop training step of cfc_train_kloop, same arguments without ws and

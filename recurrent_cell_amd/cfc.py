@@ -65,6 +65,8 @@ def lib():
         L.cfc_set_kloop_mode.argtypes = [_I]
         L.cfc_kloop_path.argtypes = [_I, _I, _I, _I]
         L.cfc_kloop_path.restype = _I
+        L.cfc_kloop_status.argtypes = [_P, ctypes.c_size_t, _I, _I, _I, _I, _P]
+        L.cfc_kloop_status.restype = _I
         L.cfc_last_error.argtypes = []
         L.cfc_last_error.restype = ctypes.c_char_p
         L.cfc_clear_graph_cache.argtypes = []
@@ -364,6 +366,16 @@ def cfc_kloop_path(B, C, n_x, K):
     the path cfc_train_kloop takes now on this thread (-1 if its mode cannot
     take these sizes)."""
     return int(lib().cfc_kloop_path(B, C, n_x, K))
+
+
+def cfc_kloop_status(out, B, C, n_x, K):
+    """Raises CfcError (code CFC_EHIP) if a bounded wait of the last K-loop
+    call on out.ws gave up (that call's results are then undefined).  Waits
+    for the current stream.  Call on the thread that made the call."""
+    if out.ws.dim() != 1 or not out.ws.is_contiguous():
+        raise ValueError("ws must be a contiguous 1-D tensor")
+    _check("cfc_kloop_status", lib().cfc_kloop_status(_dev(out.ws, "ws"), out.ws.numel() * 4, B, C, n_x, K,
+                                                      _stream(out.ws)))
 
 
 def clear_graph_cache():

@@ -564,6 +564,49 @@ int cfc_kloop_path(int B, int C, int n_x, int K)
          : path == Path::StepsMfma  ? CFC_KLOOP_STEPS_MFMA : CFC_KLOOP_STEPS_VALU;
 }
 
+int cfc_kloop_status(const float* ws, size_t ws_bytes, int B, int C, int n_x, int K, void* stream)
+{
+    cfc_host::last_error().clear();
+    const char* fn = "cfc_kloop_status";
+    if (int rc = check_dims(B, C, n_x)) return rc;
+    if (K < 0 || K > (1 << 20)) return fail(CFC_EINVAL, "%s: K=%d out of range", fn, K);
+    const int64_t ws_floats = kloop_ws_floats(B, C, n_x, K);
+    if (ws == nullptr || ws_bytes < (size_t)ws_floats * sizeof(float))
+        return fail(CFC_EINVAL, "%s: workspace of %zu bytes, %lld needed", fn, ws_bytes, (long long)(ws_floats * 4));
+    if (K == 0 || B == 0) return CFC_OK;   // nothing was launched
+    Path path;
+    if (!choose_path(g_kloop_mode, B, C, n_x, {}, &path))
+        return fail(CFC_EINVAL, "%s: the K-loop mode forces a path these sizes cannot take", fn);
+    hipStream_t s = (hipStream_t)stream;
+    int words[2] = {0, 0};
+    if (path == Path::Resident) {
+        // the error word after the step counters (zeroed before every launch)
+        const float* flags = ws + kloop_ws_wofs(B, C, K) + cfc::mfma_w_floats(C, n_x) + cfc::resident_exchange_floats(B, C);
+        const int64_t n = ((int64_t)(B + 15) / 16) * ((C + 15) / 16);
+        CFC_HIP(hipMemcpyAsync(&words[0], flags + n * cfc::kResFlagStride, sizeof(int), hipMemcpyDeviceToHost, s),
+                "status read");
+        CFC_HIP(hipStreamSynchronize(s), "status wait");
+        if (words[0] != 0)
+            return fail(CFC_EHIP, "%s: a bounded wait of the resident K-loop launch gave up; its results are undefined",
+                        fn);
+        return CFC_OK;
+    }
+    const int n_proj = cfc::persist_proj_blocks(B, C, K);
+    if (path == Path::Persistent && B <= kPersistFuseMaxB && n_proj > 0) {
+        // flags[0] holds the number of the last launch that formed X here;
+        // the error word holds it too if that launch's wait gave up
+        const float* f = ws + kloop_ws_pofs(B, C, n_x, K);
+        CFC_HIP(hipMemcpyAsync(&words[0], f, sizeof(int), hipMemcpyDeviceToHost, s), "status read");
+        CFC_HIP(hipMemcpyAsync(&words[1], f + n_proj, sizeof(int), hipMemcpyDeviceToHost, s), "status read");
+        CFC_HIP(hipStreamSynchronize(s), "status wait");
+        if (words[0] != 0 && words[1] == words[0])
+            return fail(CFC_EHIP,
+                        "%s: the persistent launch's wait for its input projection gave up; its results are undefined",
+                        fn);
+    }
+    return CFC_OK;
+}
+
 // Checks shared by cfc_train_kloop and cfc_kloop_fwd_bwd; sets *path.
 static int check_kloop(const char* fn, const float* u, const float* y, const float* h0, const float* W,
                 const float* bias, float* h_hist, float* act, float* ws, size_t ws_bytes, float* gW_scratch,

@@ -114,6 +114,20 @@ def test_kloop_argument_errors(L):
     assert b"workspace" in L.cfc_last_error()
 
 
+def test_kloop_status_argument_errors(L):
+    """cfc_kloop_status refuses bad sizes and a null or short workspace before
+    any HIP call; with K == 0 or B == 0 nothing was launched: CFC_OK."""
+    B, C, n_x, K = 4, 16, 8, 3
+    need = ws_bytes(B, C, n_x, K)
+    assert L.cfc_kloop_status(None, need, B, C, n_x, K, None) == -1
+    assert L.cfc_kloop_status(FAKE, need - 4, B, C, n_x, K, None) == -1
+    assert b"workspace" in L.cfc_last_error()
+    assert L.cfc_kloop_status(FAKE, need, B, 0, n_x, K, None) == -1
+    assert L.cfc_kloop_status(FAKE, need, B, C, n_x, -1, None) == -1
+    assert L.cfc_kloop_status(FAKE, ws_bytes(B, C, n_x, 0), B, C, n_x, 0, None) == 0
+    assert L.cfc_kloop_status(FAKE, ws_bytes(0, C, n_x, K), 0, C, n_x, K, None) == 0
+
+
 def test_projection_and_recurrence_argument_errors(L):
     # input projection: bad sizes, null pointers, output overlapping an input
     assert L.cfc_input_projection(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), -1, 8, 4, None) == -1

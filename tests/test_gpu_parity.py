@@ -314,6 +314,37 @@ def persist_projection_flags(ws, B, C, K):
     return f[:n], f[n]
 
 
+def test_persistent_wait_that_gives_up_is_reported(cfc):
+    """The host forces the persistent launch's wait for its input projection
+    to give up: it writes the next launch's number into the error word
+    first, so the sample workgroups stop waiting at their first poll and the
+    kernel finishes as usual.  cfc_kloop_status then reports CFC_EHIP; after
+    a normal call on the same workspace it reports nothing again."""
+    d = CASES["pages"]
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    say("persistent wait forced to give up", d)
+    x = cfc_inputs(**d, seed=5)
+    u, y, h0, W, bias = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    a = cfc.KloopBuffers.allocate(B, C, n_x, K, "cuda")
+    assert cfc.cfc_kloop_path(B, C, n_x, K) == cfc.KLOOP_PERSISTENT
+    cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
+    cfc.cfc_kloop_status(a, B, C, n_x, K)
+    flags, err = persist_projection_flags(a.ws, B, C, K)
+    n = flags.size
+    region = (n + 1 + 63) // 64 * 64
+    words = a.ws[a.ws.numel() - region:].view(torch.int32)
+    words[n] = int(flags[0]) + 1   # the next launch's number (launch numbers count up by one)
+    torch.cuda.synchronize()
+    cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
+    with pytest.raises(cfc.CfcError) as e:
+        cfc.cfc_kloop_status(a, B, C, n_x, K)
+    assert e.value.code == cfc.CFC_EHIP
+    flags, err = persist_projection_flags(a.ws, B, C, K)
+    assert err == flags[0]
+    cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
+    cfc.cfc_kloop_status(a, B, C, n_x, K)
+
+
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "three_blocks", "odd_channels"])
 def test_recurrence_composes_to_fwd_bwd(cfc, case):
     """cfc_input_projection then cfc_kloop_recurrence (two launches) gives
@@ -335,6 +366,7 @@ def test_recurrence_composes_to_fwd_bwd(cfc, case):
         # show in the bits
         cfc.cfc_kloop_fwd_bwd(dev(-0.5 * x.u), y, h0, W, bias, out=a)
         cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
+        cfc.cfc_kloop_status(a, d["B"], d["C"], d["n_x"], d["K"])   # raises if a wait gave up
     finally:
         cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
     if d["B"] <= 128:
@@ -466,6 +498,7 @@ def test_resident_kernel_equals_step_kernels_and_finishes_its_waits(cfc, case):
                 n = nbt * ((C + 15) // 16)
                 flags = host(out.ws[fofs:fofs + 32 * (n + 1)]).view(np.int32)[::32]   # one per 128-byte line
                 assert flags[n] == 0, "a wait of the resident kernel gave up"
+                cfc.cfc_kloop_status(out, B, C, n_x, K)   # reads the same word
                 np.testing.assert_array_equal(flags[:n], np.full(n, 2 * K - 1, np.int32))
         finally:
             cfc.cfc_set_kloop_mode(cfc.KLOOP_AUTO)
