@@ -66,6 +66,14 @@ __device__ __forceinline__ void st_agent(float* p, float v)
 {
     __hip_atomic_store(reinterpret_cast<int*>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte device-scope (write-through) store through a raw buffer resource
+// over [base, base + bytes); offsets at or past `bytes` write nothing.
+__device__ __forceinline__ void st4_dev(float* base, int bytes, int byte_off, f32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                           byte_off, 0, 16 /* sc1 */);
+}
 
 // z_s = [u_t[b0+s] ; h_prev[b0+s]] for the tile's samples into LDS rows of
 // pitch ldz (zero padded past n_in and for absent samples).
@@ -218,8 +226,11 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a)
 // [persistent kernel source: begin]
 // (the tile code is also run by the persistent launch that forms X)
 // One 64 x 64 tile (mtile, ntile) of X; wave (0..3) forms its 32 x 32
-// block.  DEV: X stored at device scope (written through to memory), for
-// readers in the same launch.
+// block.  The MFMAs take W as their first operand and u as their second,
+// so that a lane ends with 4 adjacent outputs of one row (16-byte stores);
+// each product and each chain's order are those of the layout above.
+// DEV: X stored at device scope (written through to memory), for readers
+// in the same launch.
 template <bool VEC, bool DEV = false>
 __device__ __forceinline__ void xproj_tile(const XprojArgs& a, int64_t mtile, int ntile, int wave)
 {
@@ -234,9 +245,11 @@ __device__ __forceinline__ void xproj_tile(const XprojArgs& a, int64_t mtile, in
 
     // the bias first: its load overlaps the operand loads instead of
     // following the MFMAs with a round trip of its own
-    float bias[2];
+    float bias[2][4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bias[nt] = a.bias[min(n0 + 16 * nt + li, N - 1)];
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias[nt][e] = a.bias[min(n0 + 16 * nt + 4 * lk + e, N - 1)];
 
     f32x4 acc[2][2][4];
 #pragma unroll
@@ -293,27 +306,46 @@ __device__ __forceinline__ void xproj_tile(const XprojArgs& a, int64_t mtile, in
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
                         acc[mt][nt][c] =
-                            __builtin_amdgcn_mfma_f32_16x16x4f32(av[kb][mt][c], bv[kb][nt][c], acc[mt][nt][c], 0, 0, 0);
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(bv[kb][nt][c], av[kb][mt][c], acc[mt][nt][c], 0, 0, 0);
     }
 
     wait_vmem_all();   // so that no store below waits behind another
+    // lane (li, lk): row m0 + 16 mt + li, outputs n0 + 16 nt + 4 lk .. + 3
+    const bool vec_out = (N % 4 == 0) && ((((uintptr_t)a.X) & 15u) == 0);
+    const bool dev16 = DEV && vec_out && M * N < (int64_t)(1 << 29);   // byte offsets fit the buffer store's
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const int r = n0 + 16 * nt + li;
+        const int r0 = n0 + 16 * nt + 4 * lk;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+            const int64_t row = m0 + 16 * mt + li;
+            if (row >= M) continue;
+            f32x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + 16 * mt + 4 * lk + i;
-                if (r < N && row < M) {
-                    const float v = xproj_combine(bias[nt], acc[mt][nt][0][i], acc[mt][nt][1][i],
-                                                  acc[mt][nt][2][i], acc[mt][nt][3][i]);
-                    if (DEV)
-                        st_agent(a.X + row * N + r, v);
-                    else
-                        a.X[row * N + r] = v;
+            for (int e = 0; e < 4; ++e)
+                v[e] = xproj_combine(bias[nt][e], acc[mt][nt][0][e], acc[mt][nt][1][e], acc[mt][nt][2][e],
+                                     acc[mt][nt][3][e]);
+            float* dst = a.X + row * N + r0;
+            if (vec_out && r0 + 4 <= N) {
+                if (dev16)
+                    st4_dev(a.X, (int)(4 * M * N), (int)(4 * (row * N + r0)), v);
+                else if (DEV) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st_agent(dst + e, v[e]);
+                } else {
+                    *reinterpret_cast<f32x4*>(dst) = v;
                 }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (r0 + e < N) {
+                        if (DEV)
+                            st_agent(dst + e, v[e]);
+                        else
+                            dst[e] = v[e];
+                    }
             }
+        }
     }
 }
 
@@ -537,14 +569,6 @@ __device__ __forceinline__ f32x4 ld4_dev(const float* base, int bytes, int byte_
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
-}
-// 16-byte device-scope (write-through) store through a raw buffer resource
-// over [base, base + bytes); offsets at or past `bytes` write nothing.
-__device__ __forceinline__ void st4_dev(float* base, int bytes, int byte_off, f32x4 v)
-{
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
-                                           byte_off, 0, 16 /* sc1 */);
 }
 // RES: a 16-byte device-scope load (two 8-byte agent-scope loads).
 template <bool RES>
@@ -1916,26 +1940,41 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     // CPG == 2, quad 1 holds them swapped (w[s] of channel g CPG + (s ^ jq))
     // so that the last level of sum8 can leave each quad its own channel.
     float w[CPG][3][NH][4];
+    if (wvec) {
+        // clamped addresses, zero selected: no branch between the loads,
+        // so all of them are in flight together (under a per-load branch
+        // each was waited for before the next was issued)
 #pragma unroll
-    for (int cl = 0; cl < CPG; ++cl)
+        for (int cl = 0; cl < CPG; ++cl)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int c = g * CPG + (CPG == 2 ? (cl ^ jq) : cl);
-            const bool ok = c < C;
-            const float* wrow = a.W + (int64_t)(q * C + min(c, C - 1)) * n_in + n_x;
+            for (int q = 0; q < 3; ++q) {
+                const int c = g * CPG + (CPG == 2 ? (cl ^ jq) : cl);
+                const float* wrow = a.W + (int64_t)(q * C + min(c, C - 1)) * n_in + n_x;
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const int m = 32 * i + 4 * j;
-                if (ok && wvec && m < C) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(wrow + m);
+                for (int i = 0; i < NH; ++i) {
+                    const int m = 32 * i + 4 * j;   // C % 4 == 0 here: m < C covers m + 3
+                    const f32x4 v = load4_or_zero(wrow + min(m, C - 4), c < C && m < C);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[cl][q][i][e] = v[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[cl][q][i][e] = (ok && m + e < C) ? wrow[m + e] : 0.0f;
                 }
             }
-        }
+    } else {
+#pragma unroll
+        for (int cl = 0; cl < CPG; ++cl)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const int c = g * CPG + (CPG == 2 ? (cl ^ jq) : cl);
+                const bool ok = c < C;
+                const float* wrow = a.W + (int64_t)(q * C + min(c, C - 1)) * n_in + n_x;
+#pragma unroll
+                for (int i = 0; i < NH; ++i) {
+                    const int m = 32 * i + 4 * j;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[cl][q][i][e] = (ok && m + e < C) ? wrow[min(m + e, C - 1)] : 0.0f;
+                }
+            }
+    }
     // Backward: staged rows per step tt of a chunk: 5 tt + v, v = gate, g, hh (act), h_t,
     // y_t, each C floats at row pitch HW (so that, in a whole chunk, every
     // step's LDS offsets are constants); register prefetch on the 16-byte path.
