@@ -138,10 +138,15 @@ int reduce_axis0(const float* per_batch, int64_t n_batch, int64_t n_tail,
  *    steps, then the scratch fill and the reduction, enqueued directly on
  *    `stream`.  With B <= 128 the projection is formed by extra workgroups
  *    of the same launch, which the sample workgroups wait for -- three
- *    launches.  The wait is bounded: only other work holding the device's
- *    CUs for about a second makes it give up, which marks an error word in
- *    ws and leaves the results undefined.  Otherwise, and on a stream under
- *    capture, the projection is a launch of its own -- four launches;
+ *    launches.  When, besides, every array is 16-byte aligned, C and n_x are
+ *    multiples of 4, n_in <= 256 and the launch's workgroups fit the device's
+ *    CUs one each, those workgroups then also form the scratch, following
+ *    the backward one chunk of 16 steps at a time (a flag per sample and
+ *    chunk in ws) -- two launches.  The waits are bounded: only other work
+ *    holding the device's CUs for about a second makes one give up, which
+ *    marks an error word in ws and leaves the results undefined.
+ *    Otherwise, and on a stream under capture, the projection is a launch of
+ *    its own -- four launches;
  *  - resident MFMA (B >= 64, C > 128, shapes of the MFMA step kernels whose
  *    grid fits the device at once): a W re-layout, one cooperative launch
  *    running all 2K steps, the fill and the reduction, enqueued directly (a

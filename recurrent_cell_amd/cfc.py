@@ -180,8 +180,8 @@ class KloopBuffers:
 
 def cfc_train_kloop(u, y, h0, W, bias, out=None):
     """One training step of the K-loop (forward, BPTT, scratch, reduce):
-    three direct launches on the persistent path (four for B > 128 or on a
-    stream under capture), one graph replay on the step path.  Returns the KloopBuffers holding h_hist, act, the per-sample
+    two to four direct launches on the persistent path (include/cfc.h
+    says which), one graph replay on the step path.  Returns the KloopBuffers holding h_hist, act, the per-sample
     scratch, gW and gb."""
     K, B, n_x = u.shape
     C = h0.shape[1]

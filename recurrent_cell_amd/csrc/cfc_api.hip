@@ -134,7 +134,8 @@ int64_t kloop_ws_flags(int B, int C)
 }
 int64_t kloop_ws_resident(int B, int C) { return cfc::resident_exchange_floats(B, C) + kloop_ws_flags(B, C); }
 // Last: the flags of the persistent launch that also forms X (one per
-// projection workgroup, then its error word).
+// projection workgroup, then its error word, then one per sample and
+// backward chunk of 16 steps for a launch that also forms the scratch).
 int64_t kloop_ws_pofs(int B, int C, int n_x, int K)
 {
     return kloop_ws_wofs(B, C, K) + cfc::mfma_w_floats(C, n_x) + kloop_ws_resident(B, C);
@@ -142,7 +143,7 @@ int64_t kloop_ws_pofs(int B, int C, int n_x, int K)
 int64_t kloop_ws_proj(int B, int C, int K)
 {
     const int n = cfc::persist_proj_blocks(B, C, K);
-    return n < 0 ? 0 : ((int64_t)n + 1 + 63) & ~(int64_t)63;
+    return n < 0 ? 0 : ((int64_t)n + 1 + (int64_t)B * ((K + 15) / 16) + 63) & ~(int64_t)63;
 }
 int64_t kloop_ws_floats(int B, int C, int n_x, int K)
 {
@@ -184,6 +185,17 @@ unsigned next_persist_call()
     unsigned c = g_persist_call.fetch_add(1, std::memory_order_relaxed) + 1;
     while (c == 0) c = g_persist_call.fetch_add(1, std::memory_order_relaxed) + 1;
     return c;
+}
+// CUs of the current device (read once per device); 0 if unknown.
+int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cus[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
 }
 bool stream_capturing(hipStream_t s)
 {
@@ -235,8 +247,11 @@ bool choose_path(int mode, int B, int C, int n_x, std::initializer_list<const vo
 //                   h_hist[0]) and K backward step launches; the MFMA ones
 //                   after one launch that re-lays W into their operand
 //                   layouts.
-int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipStream_t s)
+// filled (nullable): the scratch of gW_s / gb_s may be formed by the same
+// launch; *filled tells whether it was.
+int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipStream_t s, bool* filled = nullptr)
 {
+    if (filled) *filled = false;
     const int64_t BC = (int64_t)k.B * k.C;
     const int64_t BX = (int64_t)k.B * k.n_x;
     float* dp = k.ws;                                   // [K, B, 3C]
@@ -254,7 +269,18 @@ int enqueue_fwd_bwd(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipSt
             a.n_proj = n_proj;
             a.call = next_persist_call();
             a.spin_limit = kPersistSpinLimit;
-            CFC_HIP(cfc::launch_persist(a, s), "persistent K-loop launch (with the input projection)");
+            // the scratch too, by fill units that follow the backward chunk by chunk
+            // (16-byte rows on every array they or the samples move)
+            if (filled && k.gW_s && k.gb_s && cfc::persist_fill_fits(k.B, k.C, k.n_x, k.K, device_cus()) &&
+                aligned16(k.ws) && aligned16(k.h_hist) && aligned16(k.act) && aligned16(k.y) &&
+                aligned16(k.gW_s) && (k.n_x == 0 || aligned16(k.u))) {
+                a.gW_s = k.gW_s;
+                a.gb_s = k.gb_s;
+                a.n_fill = k.B * ((3 * k.C + 63) / 64);
+                *filled = true;
+            }
+            CFC_HIP(cfc::launch_persist(a, s), a.n_fill ? "persistent K-loop launch (with the projection and the scratch)"
+                                                        : "persistent K-loop launch (with the input projection)");
             return CFC_OK;
         }
         const cfc::XprojArgs x{k.u, k.W, k.bias, X, (int64_t)k.K * k.B, 3 * k.C, k.n_x, k.n_x + k.C,
@@ -372,8 +398,10 @@ int enqueue_fill(const float* dp, const float* u, const float* h_hist, float* gW
 int enqueue_kloop(const KloopArgs& k, Path path, const cfc::StepPlan& p, hipStream_t s)
 {
     const int n_in = k.n_x + k.C;
-    if (int rc = enqueue_fwd_bwd(k, path, p, s)) return rc;
-    if (int rc = enqueue_fill(k.ws, k.u, k.h_hist, k.gW_s, k.gb_s, k.B, k.C, k.n_x, k.K, s)) return rc;
+    bool filled = false;
+    if (int rc = enqueue_fwd_bwd(k, path, p, s, &filled)) return rc;
+    if (!filled)
+        if (int rc = enqueue_fill(k.ws, k.u, k.h_hist, k.gW_s, k.gb_s, k.B, k.C, k.n_x, k.K, s)) return rc;
     cfc::ReduceSeg segs[2] = {
         {k.gW_s, k.gW, (int64_t)3 * k.C * n_in, 0},
         {k.gb_s, k.gb, (int64_t)3 * k.C, 0},

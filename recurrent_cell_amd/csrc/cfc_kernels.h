@@ -169,11 +169,29 @@ struct PersistArgs {
     // polls; flags[n_proj] = call marks a wait that gave up) before their
     // first read of X.  n_proj == 0: X comes from an earlier launch.
     const float* u;       // [K, B, n_x]
-    int* flags;           // [n_proj + 1]
+    int* flags;           // [n_proj + 1 + B ceil(K / 16)]
     int n_proj;
     unsigned call;        // nonzero, distinct between launches that share flags
     int spin_limit;
+    // n_fill > 0 (with n_proj > 0 only): the launch also forms the per-sample
+    // scratch of scratch_fill_kernel, with its bits.  Workgroups 0 ..
+    // max(n_proj, n_fill) - 1 come ahead of the sample workgroups; after its
+    // projection tile (if any), such a workgroup takes fill unit f < n_fill:
+    // sample f / n_rt, dp rows 64 (f % n_rt) .. + 63, every column of z, one
+    // pass of 16 steps per backward chunk c (steps K - 16 c down to
+    // max(1, K - 16 c - 15)), each after flags[n_proj + 1 + b ceil(K / 16) + c]
+    // holds call: sample b sets it once its dp of that chunk (and every h_t
+    // before it) is performed at device scope.  Every workgroup of the launch
+    // must be resident at once (the host checks the CU count).
+    float* gW_s;          // [B, 3C, n_in]
+    float* gb_s;          // [B, 3C]
+    int n_fill;           // 0 or B ceil(3C / 64)
 };
+// Rows of the LDS (floats) that a fill unit stages per pass: dp [16][80] and
+// z [16][zp], zp = n_in rounded up to 64, plus 16 (a read's 4 k-slots hit
+// distinct banks); the partial buffers of the sample role hold them.
+__host__ __device__ inline int persist_fill_zpitch(int n_in) { return ((n_in + 63) / 64) * 64 + 16; }
+__host__ __device__ inline int persist_fill_lds_floats(int n_in) { return 16 * (80 + persist_fill_zpitch(n_in)); }
 // [persistent kernel source: end]
 
 constexpr int kMaxAdamwSegs = 4;
@@ -237,6 +255,11 @@ int reduce_slices(int64_t B);
 // or 0 if no instantiation holds the recurrent W in registers (C > 128).
 size_t persist_smem(int C);
 int persist_proj_blocks(int B, int C, int K);   // -1 when too many
+// Whether a launch with the projection can also form the scratch (n_fill =
+// B ceil(3C / 64) units) for these sizes: z rows of at most 256 floats in
+// whole float4, the unit's LDS within the partial buffers, and every
+// workgroup resident at once on a device of n_cus CUs (one per CU).
+bool persist_fill_fits(int B, int C, int n_x, int K, int n_cus);
 
 hipError_t launch_fwd(const FwdArgs& a, const StepPlan& p, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, const StepPlan& p, hipStream_t s);

@@ -1714,6 +1714,13 @@ constexpr int kBwdChunk = 16;
 typedef __attribute__((address_space(1))) f32x4 global_f32x4;
 __device__ __forceinline__ f32x4 gload4(uint64_t addr) { return *(const global_f32x4*)addr; }
 __device__ __forceinline__ void gstore4(uint64_t addr, f32x4 v) { *(global_f32x4*)addr = v; }
+// The same store at device scope (write-through, as st4_dev) at a byte
+// address inside [base, base + bytes), for rows that workgroups on other
+// XCDs of the same launch read.
+__device__ __forceinline__ void gstore4_dev(const float* base, int bytes, uint64_t addr, f32x4 v)
+{
+    st4_dev(const_cast<float*>(base), bytes, (int)(addr - (uint64_t)base), v);
+}
 
 template <int CPG, int NH>
 struct PersistLds {
@@ -1898,6 +1905,184 @@ __device__ __forceinline__ void persist_wait_projection(const PersistArgs& a)
     __syncthreads();
 }
 
+// A fill unit's wait for one chunk flag: wave 0 polls the flag (lane 0)
+// and the error word (lane 1) until either holds this launch's call number;
+// after spin_limit polls it gives up itself and marks the error word.  Two
+// polls in flight, the second issued about half a round trip after the
+// first, each check waiting for its own poll only (as in the projection
+// wait).  The other waves wait at the barrier.
+__device__ __forceinline__ int persist_fill_poll(const PersistArgs& a, int word)
+{
+    return __hip_atomic_load(a.flags + (threadIdx.x == 0 ? word : a.n_proj), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void persist_fill_wait(const PersistArgs& a, int word)
+{
+    if (threadIdx.x < 64) {
+        const int call = (int)a.call;
+        auto seen = [&](int v) __attribute__((always_inline)) {
+            return __builtin_amdgcn_readlane(v, 0) == call || __builtin_amdgcn_readlane(v, 1) == call;
+        };
+        int va = persist_fill_poll(a, word);
+        __builtin_amdgcn_s_sleep(16);
+        for (int it = 0;; it += 2) {
+            const int vb = persist_fill_poll(a, word);
+            if (seen(va)) break;
+            va = persist_fill_poll(a, word);
+            if (seen(vb)) break;
+            if (it >= a.spin_limit) {
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(a.flags + a.n_proj, call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Fill unit f of a launch that also forms the scratch: sample b = f / n_rt,
+// dp rows r0 = 64 (f % n_rt) .. r0 + 63 against every column of z, i.e.
+// the tiles (b, r0 / 64, *) of scratch_fill_kernel with its arithmetic:
+// per output an fma chain over t = K .. 1 from +0, the steps in k-slot
+// groups of 4 from t = K through v_mfma_f32_16x16x4f32 (slot kk of the
+// group at staged step tt is step t0 - tt - kk) and the last K mod 4 steps
+// through VALU fma, and the bias sums as an add chain over t descending.
+// A pass stages one backward chunk (16 steps): the groups and the order are
+// those of the fill's 64-step passes, hence the same bits.  Wave w holds
+// rows 32 (w & 1) .. + 31 and 16-column blocks npw (w >> 1) .. + npw - 1.
+// dp and h_hist come from the sample workgroups of this launch and are read
+// with device-scope loads after the chunk's flag; u is an input.
+__device__ __forceinline__ void persist_fill(const PersistArgs& a, int f, float* lds)
+{
+    const int C = a.C, n_x = a.n_x, n_in = n_x + C, R3 = 3 * C, B = a.B, K = a.K;
+    const bool vec = (C % 4 == 0) && (n_x % 4 == 0) && n_in <= 256 &&
+                     ((((uintptr_t)a.dp) | ((uintptr_t)a.h_hist) | ((uintptr_t)a.u) | ((uintptr_t)a.gW_s)) & 15u) == 0;
+    if (!vec) {   // the host does not fuse such shapes
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.flags + a.n_proj, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int n_rt = (R3 + 63) / 64;
+    const int b = f / n_rt;
+    const int r0 = (f - b * n_rt) * 64;
+    const int nc = (K + kBwdChunk - 1) / kBwdChunk;
+    const int zp = persist_fill_zpitch(n_in);
+    constexpr int DPP = 80;            // dp row pitch
+    float* dps = lds;                  // [16][DPP]
+    float* zs = lds + 16 * DPP;        // [16][zp]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int rw = 32 * (wave & 1);
+    const int npw = ((n_in + 15) / 16 + 3) / 4;
+    const int cb0 = 16 * npw * (wave >> 1);
+    const int nb = min(npw, max(0, (n_in - cb0 + 15) / 16));   // uniform per wave
+    const int w4 = n_in / 4;
+    const int dp_bytes = (int)((int64_t)K * B * R3 * 4);       // below 2^31 (host)
+    const int h_bytes = (int)((int64_t)(K + 1) * B * C * 4);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float sb = 0.0f;
+    for (int c = 0; c < nc; ++c) {
+        const int t0 = K - kBwdChunk * c;
+        const int nst = min(kBwdChunk, t0);   // steps t0, t0 - 1, .., t0 - nst + 1
+        persist_fill_wait(a, a.n_proj + 1 + b * nc + c);
+        // dp: threads < 256, one float4 each; z: two float4 per thread.
+        // Addresses clamped into bounds; LDS rows past nst are never read.
+        f32x4 dv;
+        {
+            const int t = t0 - min(tid >> 4, nst - 1);
+            const int r = min(r0 + 4 * (tid & 15), R3 - 4);
+            dv = ld4_dev(a.dp, dp_bytes, (int)((((int64_t)(t - 1) * B + b) * R3 + r) * 4));
+        }
+        f32x4 zv[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = tid + m * kPersistThreads;
+            const int tq = i / w4;
+            const int k = 4 * (i - tq * w4);
+            const int t = t0 - min(tq, nst - 1);
+            const int64_t row = (int64_t)(t - 1) * B + b;
+            const f32x4 hv = ld4_dev(a.h_hist, h_bytes, (int)((row * C + max(k - n_x, 0)) * 4));
+            f32x4 uv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (n_x > 0) uv = *reinterpret_cast<const f32x4*>(a.u + row * n_x + min(k, n_x - 4));
+            zv[m] = (k < n_x) ? uv : hv;
+        }
+        wait_vmem_all();
+        if (tid < 256) *reinterpret_cast<f32x4*>(dps + (tid >> 4) * DPP + 4 * (tid & 15)) = dv;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = tid + m * kPersistThreads;
+            if (i < 16 * w4) {
+                const int tq = i / w4;
+                *reinterpret_cast<f32x4*>(zs + tq * zp + 4 * (i - tq * w4)) = zv[m];
+            }
+        }
+        __syncthreads();
+        const int nst4 = nst & ~3;
+        for (int tt = 0; tt < nst4; tt += 4) {
+            float av[2], bv[4];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) av[mt] = dps[(tt + lk) * DPP + rw + 16 * mt + li];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) bv[nt] = zs[(tt + lk) * zp + min(cb0 + 16 * nt, zp - 16) + li];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    if (nt < nb) acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+        }
+        for (int tt = nst4; tt < nst; ++tt) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    if (nt < nb) {
+                        const float zval = zs[tt * zp + cb0 + 16 * nt + li];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[mt][nt][e] = fmaf(dps[tt * DPP + rw + 16 * mt + 4 * lk + e], zval, acc[mt][nt][e]);
+                    }
+        }
+        if (tid < 64)
+            for (int tt = 0; tt < nst; ++tt) sb = sb + dps[tt * DPP + tid];
+        __syncthreads();   // LDS free for the next pass
+    }
+    // The unit through LDS in four rounds of 16 rows, each stored row-wise
+    // (16 lanes per 256 bytes: whole cache lines).  Row pitch: the wave's
+    // whole 16-column blocks, plus 4 (a round's writes hit distinct banks).
+    const int op = ((n_in + 15) & ~15) + 4;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        if ((wave & 1) == (rb >> 1)) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                if (nt < nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lds[(4 * lk + e) * op + cb0 + 16 * nt + li] = acc[rb & 1][nt][e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int i = tid + m * kPersistThreads;
+            const int row = i / w4;
+            const int k = 4 * (i - row * w4);
+            const int r = r0 + 16 * rb + row;
+            if (i < 16 * w4 && r < R3) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(lds + row * op + k);
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(a.gW_s + ((int64_t)b * R3 + r) * n_in + k));
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < 64 && r0 + tid < R3) a.gb_s[(int64_t)b * R3 + r0 + tid] = sb;
+}
+
 template <int CPG, int NH>
 __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistArgs a)
 {
@@ -1911,11 +2096,15 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     __shared__ __attribute__((aligned(16))) float stage[L::STAGE];
     __shared__ __attribute__((aligned(16))) float dbuf[L::DBUF];
     float* obuf = &part[0][0][0];   // forward output buffer [kFwdChunk][4][C] (partials unused then)
-    if ((int)blockIdx.x < a.n_proj) {
-        persist_projection(a);
+    const int n_help = max(a.n_proj, a.n_fill);
+    if ((int)blockIdx.x < n_help) {
+        if ((int)blockIdx.x < a.n_proj) persist_projection(a);
+        // a sample's fill units on one XCD, where they share its u rows
+        const int f = (int)xcd_local_order(blockIdx.x, (int64_t)n_help);
+        if (f < a.n_fill) persist_fill(a, f, &part[0][0][0]);
         return;
     }
-    const int b = (int)blockIdx.x - a.n_proj;
+    const int b = (int)blockIdx.x - n_help;
     const int tid = threadIdx.x;
     const int g = tid >> 3;          // canonical dz group
     const int j = tid & 7;           // lane of the group: recurrent columns 32 i + 4 j + e
@@ -1935,6 +2124,13 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     // 16-byte moves need rows of a multiple of 4 floats on 16-byte aligned arrays
     const bool c_vec = (C % 4 == 0) && ((((uintptr_t)a.act) | ((uintptr_t)a.h_hist) | ((uintptr_t)a.y) |
                                           ((uintptr_t)a.dp) | ((uintptr_t)a.X)) & 15u) == 0;
+    // fill units in this launch read h_t and dp: device-scope stores, and a
+    // flag per backward chunk (the host fuses 16-byte shapes only)
+    const bool fuse = a.n_fill > 0 && c_vec;
+    const int h_bytes = (int)((int64_t)(K + 1) * BC * 4);   // below 2^31 when fused (host)
+    const int dp_bytes = (int)((int64_t)K * BC * 12);
+    if (a.n_fill > 0 && !c_vec && tid == 0)
+        __hip_atomic_store(a.flags + a.n_proj, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // w[s]: the recurrent columns of channel g CPG + s; in the forward, with
     // CPG == 2, quad 1 holds them swapped (w[s] of channel g CPG + (s ^ jq))
@@ -2045,7 +2241,7 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     for (int c = tid; c < C; c += THREADS) {
         const float h = a.h0[(int64_t)b * C + c];
         zs[0][c] = h;
-        a.h_hist[(int64_t)b * C + c] = h;
+        st_agent(a.h_hist + (int64_t)b * C + c, h);   // read by fill units of a fused launch
     }
     wait_vmem_all();   // W is in registers before any step loop reads it
 
@@ -2128,9 +2324,18 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         f32x4 v[OM];
 #pragma unroll
         for (int m = 0; m < OM; ++m) v[m] = *reinterpret_cast<const f32x4*>(obuf + o_lds[m]);
+        if (fuse) {   // h_t rows at device scope (fill units read them); act rows stay local
 #pragma unroll
-        for (int m = 0; m < OM; ++m)
-            if (o_rr[m] < 4 * nt) gstore4(o_addr[m] + (o_act[m] ? sa : sh), v[m]);
+            for (int m = 0; m < OM; ++m)
+                if (o_rr[m] < 4 * nt) {
+                    if (o_act[m]) gstore4(o_addr[m] + sa, v[m]);
+                    else gstore4_dev(a.h_hist, h_bytes, o_addr[m] + sh, v[m]);
+                }
+        } else {
+#pragma unroll
+            for (int m = 0; m < OM; ++m)
+                if (o_rr[m] < 4 * nt) gstore4(o_addr[m] + (o_act[m] ? sa : sh), v[m]);
+        }
     };
     auto out_row = [&](int t0) {
         return [=](int rr) {
@@ -2294,9 +2499,15 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         f32x4 v[DM];
 #pragma unroll
         for (int m = 0; m < DM; ++m) v[m] = *reinterpret_cast<const f32x4*>(dbuf + d_lds[m]);
+        if (fuse) {
 #pragma unroll
-        for (int m = 0; m < DM; ++m)
-            if (d_tt[m] < nt) gstore4(d_addr[m] + t1o, v[m]);
+            for (int m = 0; m < DM; ++m)
+                if (d_tt[m] < nt) gstore4_dev(a.dp, dp_bytes, d_addr[m] + t1o, v[m]);
+        } else {
+#pragma unroll
+            for (int m = 0; m < DM; ++m)
+                if (d_tt[m] < nt) gstore4(d_addr[m] + t1o, v[m]);
+        }
     };
     auto load_b = [&](int t1, int nt) {
         if (nt == kBwdChunk) {
@@ -2318,6 +2529,15 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
     float carry_mine = 0.0f;   // the carry of the quad's channel
     int prev_t1 = 0;
     prev_nt = 0;
+    // chunk flags (fused launch): the wait at the boundary of chunk ci covers
+    // the dp stores of chunk ci - 2, which are published after its barrier;
+    // in the last chunk, chunk ci - 1 after step kPub, once every wave has
+    // waited for its stores (issued kPub steps before: performed by then);
+    // chunks not yet published go after the last chunk's stores
+    constexpr int kPub = 10;
+    const int nchunks = (K + kBwdChunk - 1) / kBwdChunk;
+    int* const cflags = a.flags + a.n_proj + 1 + b * nchunks;
+    int ci = 0, published = 0;
     for (int t1 = K; t1 >= 1; t1 -= kBwdChunk) {
         const int nt = min(kBwdChunk, t1);   // steps t1, t1 - 1, .., t1 - nt + 1
         if (!first_from_lds || t1 != K) {
@@ -2339,6 +2559,11 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
         }
         if (c_vec && t1 - kBwdChunk >= 1) load_b(t1 - kBwdChunk, min(kBwdChunk, t1 - kBwdChunk));
         lds_barrier();
+        if (fuse && ci >= 2) {
+            if (tid == 0)
+                __hip_atomic_store(cflags + ci - 2, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            published = ci - 1;
+        }
         // One step.  The partial buffers alternate with tt (the barrier at
         // a chunk boundary orders the last reads of one chunk before the
         // first writes of the next).
@@ -2427,16 +2652,31 @@ __global__ __launch_bounds__(kPersistThreads) void kloop_persist_kernel(PersistA
                 carry_mine = quad_sum4(v);
             }
         };
+        const bool pub = fuse && prev_nt > 0 && nt > kPub && ci == nchunks - 1;
 #pragma unroll
         for (int tt = 0; tt < kBwdChunk; ++tt)
-            if (tt < nt) bstep(tt);
+            if (tt < nt) {
+                if (tt == kPub && pub) wait_vmem_all();
+                bstep(tt);   // its barrier orders every wave's wait before the flag
+                if (tt == kPub && pub && tid == 0)
+                    __hip_atomic_store(cflags + ci - 1, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        if (pub) published = ci;
         prev_t1 = t1;
         prev_nt = nt;
+        ++ci;
     }
     lds_barrier();
     if (prev_nt > 0) {
         if (c_vec) store_dp(prev_t1, prev_nt);
         else move_rows<THREADS, true>(dbuf, prev_nt, R3, R3, false, dp_row(prev_t1));
+    }
+    if (fuse) {
+        wait_vmem_all();
+        __syncthreads();
+        if (tid == 0)
+            for (int c = published; c < nchunks; ++c)
+                __hip_atomic_store(cflags + c, (int)a.call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 // [persistent kernel source: end]
@@ -2736,10 +2976,13 @@ bool persist_shape(int C, PersistShape& ps)
 template <int CPG, int NH>
 hipError_t launch_persist_t(const PersistArgs& a, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)a.n_proj + a.B;
+    const int64_t blocks = (int64_t)(a.n_proj > a.n_fill ? a.n_proj : a.n_fill) + a.B;
     if (a.n_proj < 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.n_proj > 0 && (a.flags == nullptr || (a.u == nullptr && a.n_x > 0) || a.call == 0 ||
                          a.n_proj != persist_proj_blocks(a.B, a.C, a.K)))
+        return hipErrorInvalidValue;
+    if (a.n_fill != 0 && (a.n_proj == 0 || a.gW_s == nullptr || a.gb_s == nullptr ||
+                          a.n_fill != a.B * ((3 * a.C + 63) / 64) || !persist_fill_fits(a.B, a.C, a.n_x, a.K, 1 << 30)))
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((kloop_persist_kernel<CPG, NH>), dim3((unsigned)blocks), dim3(kPersistThreads), 0, s, a);
     return hipGetLastError();
@@ -2764,6 +3007,22 @@ int persist_proj_blocks(int B, int C, int K)
     const int64_t rows = (int64_t)K * B;
     const int64_t n = ((rows + 63) / 64) * ((3 * C + 63) / 64);
     return n > 0x3fffffffLL ? -1 : (int)n;
+}
+
+bool persist_fill_fits(int B, int C, int n_x, int K, int n_cus)
+{
+    PersistShape ps;
+    if (!persist_shape(C, ps) || B < 1 || K < 1 || n_x < 0) return false;
+    const int n_in = n_x + C;
+    if (C % 4 != 0 || n_x % 4 != 0 || n_in > 256) return false;
+    // device-scope loads take 32-bit byte offsets into dp and h_hist
+    if ((int64_t)K * B * 3 * C * 4 >= (1LL << 31) || (int64_t)(K + 1) * B * C * 4 >= (1LL << 31)) return false;
+    const int part_floats = 2 * kDzGroups * (32 * ps.nh + 8);
+    if (persist_fill_lds_floats(n_in) > part_floats || 16 * (((n_in + 15) & ~15) + 4) > part_floats) return false;
+    const int n_proj = persist_proj_blocks(B, C, K);
+    if (n_proj < 1) return false;
+    const int n_fill = B * ((3 * C + 63) / 64);
+    return (int64_t)(n_proj > n_fill ? n_proj : n_fill) + B <= n_cus;
 }
 
 size_t persist_smem(int C)

@@ -153,7 +153,7 @@ def ws_bytes(B, C, n_x, K):
     xch = 32 * nbt * ((C + 31) // 32 * 32 + 1024)
     # flags of the persistent launch that also forms X: one per workgroup
     # (one 64 x 64 tile of X each), then the error word
-    proj = ((K * B + 63) // 64 * ((3 * C + 63) // 64) + 1 + 63) // 64 * 64
+    proj = ((K * B + 63) // 64 * ((3 * C + 63) // 64) + 1 + B * ((K + 15) // 16) + 63) // 64 * 64
     return 4 * (((6 * K * B * C + 2 * B * C + 63) // 64) * 64 + 3 * C * ldf + 1024 * C + xch + flags + proj)
 
 

@@ -304,14 +304,27 @@ def test_input_projection_rows_do_not_depend_on_the_launch(cfc, case, rows):
     np.testing.assert_array_equal(bits(part), bits(full[:rows]))
 
 
-def persist_projection_flags(ws, B, C, K):
-    """The flags of a persistent launch that formed X itself: the last
-    region of the workspace, one per projection workgroup (one 64 x 64 tile
-    of X each), then the error word."""
+def persist_flag_region(B, C, K):
+    """Words of the workspace's last region, the flags of a persistent launch
+    that formed X itself: one per projection workgroup (one 64 x 64 tile of
+    X each), the error word, then one per sample and backward chunk of 16
+    steps (set when the launch also forms the scratch)."""
     n = -(-K * B // 64) * -(-3 * C // 64)
-    region = (n + 1 + 63) // 64 * 64
+    return n, (n + 1 + B * -(-K // 16) + 63) // 64 * 64
+
+
+def persist_projection_flags(ws, B, C, K):
+    """(projection flags, error word) of that region."""
+    n, region = persist_flag_region(B, C, K)
     f = host(ws[ws.numel() - region:]).view(np.int32)
     return f[:n], f[n]
+
+
+def persist_chunk_flags(ws, B, C, K):
+    """The chunk flags of that region, [B, ceil(K / 16)]."""
+    n, region = persist_flag_region(B, C, K)
+    f = host(ws[ws.numel() - region:]).view(np.int32)
+    return f[n + 1:n + 1 + B * -(-K // 16)].reshape(B, -(-K // 16))
 
 
 def test_persistent_wait_that_gives_up_is_reported(cfc):
@@ -330,8 +343,7 @@ def test_persistent_wait_that_gives_up_is_reported(cfc):
     cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
     cfc.cfc_kloop_status(a, B, C, n_x, K)
     flags, err = persist_projection_flags(a.ws, B, C, K)
-    n = flags.size
-    region = (n + 1 + 63) // 64 * 64
+    n, region = persist_flag_region(B, C, K)
     words = a.ws[a.ws.numel() - region:].view(torch.int32)
     words[n] = int(flags[0]) + 1   # the next launch's number (launch numbers count up by one)
     torch.cuda.synchronize()
@@ -343,6 +355,35 @@ def test_persistent_wait_that_gives_up_is_reported(cfc):
     assert err == flags[0]
     cfc.cfc_kloop_fwd_bwd(u, y, h0, W, bias, out=a)
     cfc.cfc_kloop_status(a, B, C, n_x, K)
+
+
+@pytest.mark.parametrize("case", ["tiny", "pages", "long_input48", "long_ragged_k", "no_input", "single_step",
+                                  "two_channel_groups"])
+def test_persistent_step_forms_scratch_in_launch(cfc, case):
+    """For B <= 128 and rows of whole float4 the persistent step's one launch
+    also forms the per-sample scratch: fill units follow the backward one
+    chunk of 16 steps at a time, each after its sample's chunk flag.  After
+    the step every chunk flag holds the launch's number, no wait gave up, and
+    the scratch has the bits of cfc_scratch_fill (its own launch) over the
+    same dp, h_hist and u."""
+    d = CASES[case]
+    B, C, n_x, K = d["B"], d["C"], d["n_x"], d["K"]
+    say("scratch formed in the persistent launch", case)
+    x = cfc_inputs(**d, seed=21, bias_scale=0.2)
+    u, y, h0, W, bias = [dev(a) for a in (x.u, x.y, x.h0, x.W, x.bias)]
+    assert cfc.cfc_kloop_path(B, C, n_x, K) == cfc.KLOOP_PERSISTENT
+    g = cfc.cfc_train_kloop(u, y, h0, W, bias)
+    cfc.cfc_kloop_status(g, B, C, n_x, K)
+    flags, err = persist_projection_flags(g.ws, B, C, K)
+    chunks = persist_chunk_flags(g.ws, B, C, K)
+    assert err != flags[0]
+    np.testing.assert_array_equal(chunks, np.full_like(chunks, flags[0]))
+    dp = g.ws[:K * B * 3 * C].view(K, B, 3 * C)
+    S = torch.full_like(g.gW_scratch, float("nan"))
+    Sb = torch.full_like(g.gb_scratch, float("nan"))
+    cfc.cfc_scratch_fill(dp, u, g.h_hist, S, Sb)
+    np.testing.assert_array_equal(bits(host(S)), bits(host(g.gW_scratch)))
+    np.testing.assert_array_equal(bits(host(Sb)), bits(host(g.gb_scratch)))
 
 
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "three_blocks", "odd_channels"])
