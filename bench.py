@@ -2,9 +2,10 @@
 
 A step is one cfc_train_kloop call: forward t = 1..K, BPTT t = K..1, the
 per-sample scratch and reduce_axis0 of both scratch tensors (on the
-persistent path three launches -- the persistent K-loop, whose launch also
-forms the input projection (extra workgroups, for B <= 128), the scratch fill
-and the reduction; on the step path one graph replay of 2K + 2 launches), on
+persistent path two launches -- the persistent K-loop, whose launch also
+forms the input projection and the scratch (extra workgroups, for B <= 128
+and 16-byte shapes that fit the CUs; three or four launches otherwise), and
+the reduction; on the step path one graph replay of 2K + 2 launches), on
 the pages-shaped configuration B=32, C=128, n_x=64 (n_in=192), K=64, fp32,
 inputs seeded and already resident in HBM.  Prints ONE JSON line.
 
@@ -550,7 +551,7 @@ def cpu_baselines(configs, budget_s):
 PATH_NAMES = {2: "persistent", 3: "steps_valu", 4: "steps_mfma", 5: "resident_mfma"}
 
 
-def step_roofline(path, B, C, n_x, K, ms_per_step, t_node):
+def step_roofline(path, B, C, n_x, K, ms_per_step, t_node, persist_launches=None):
     """The step against its bounds.  The persistent path's headline ratio is
     the critical path at the non-packed fp32 rate: the 2K recurrence steps of
     a sample run in order on one CU, so they are bounded by one CU's rate, not
@@ -559,7 +560,8 @@ def step_roofline(path, B, C, n_x, K, ms_per_step, t_node):
     floor of the flops or bytes) is given beside it, over this path's launches
     and, as context only, over the pages' 2K + 3 dependent launches."""
     bytes_min, flops = step_bytes_flops(B, C, n_x, K)
-    nodes = {"persistent": 3 if B <= PERSIST_FUSE_MAX_B else 4, "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3,
+    nodes = {"persistent": persist_launches or (3 if B <= PERSIST_FUSE_MAX_B else 4),
+             "steps_valu": 2 * K + 2, "steps_mfma": 2 * K + 3,
              "resident_mfma": 5}[path]
     t_formula = nodes * t_node + max(flops / FP32_PEAK, bytes_min / HBM_PEAK)
     pages_nodes = 2 * K + 3
@@ -592,17 +594,34 @@ def step_roofline(path, B, C, n_x, K, ms_per_step, t_node):
     return r
 
 
+def persist_fill_fused(torch, out, B, C, K):
+    """Whether the persistent launch last made on out.ws also formed the
+    scratch: the workspace's last region holds one flag per projection
+    workgroup, the error word, then one per sample and chunk of 16 steps,
+    which such a launch sets to its number (that of the projection flags)."""
+    n = -(-K * B // 64) * -(-3 * C // 64)
+    nc = -(-K // 16)
+    region = (n + 1 + B * nc + 63) // 64 * 64
+    f = out.ws[out.ws.numel() - region:].view(torch.int32).cpu().numpy()
+    return bool(f[0] != 0 and f[n] != f[0] and (f[n + 1:n + 1 + B * nc] == f[0]).all())
+
+
 def kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload):
     """Roofline object of the K-loop's dominant kernel from live timings kt."""
     n_in = n_x + C
     if path == "persistent":
-        # the step's launch: with B <= PERSIST_FUSE_MAX_B it also forms X
-        # (its flops counted), timed through cfc_kloop_fwd_bwd, which is
-        # that one launch; the recurrence alone (X given) is reported beside
+        # the step's launch: with B <= PERSIST_FUSE_MAX_B it also forms X,
+        # and, when its workgroups fit the CUs, the per-sample scratch (their
+        # flops counted); timed through cfc_kloop_fwd_bwd_fill (or
+        # cfc_kloop_fwd_bwd), which is that one launch; the recurrence alone
+        # (X given) is reported beside
         fused = B <= PERSIST_FUSE_MAX_B
-        dur = kt["fwd_bwd"]["mean_s"] if fused else kt["recurrence"]["mean_s"]
+        filled = fused and kt.get("fill_fused", False)
+        dur = (kt["fwd_bwd_fill"]["mean_s"] if filled else kt["fwd_bwd"]["mean_s"]) if fused \
+            else kt["recurrence"]["mean_s"]
         rec_fl = recurrence_flops(B, C, K)
-        fl = rec_fl + (projection_flops(B, C, n_x, K) if fused else 0)
+        fl = rec_fl + (projection_flops(B, C, n_x, K) if fused else 0) + \
+            (2 * K * B * 3 * C * (n_x + C) if filled else 0)
         achieved = fl / dur
         rec_achieved = rec_fl / dur
         traffic = measured_traffic() if workload == "pages" else None
@@ -618,9 +637,11 @@ def kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload):
         return {"bound": "alu", "achieved": round(achieved / 1e12, 3), "peak": FP32_PEAK / 1e12,
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
-                "kernel": "kloop_persist_kernel" + (" (its launch also forms X)" if fused else ""),
+                "kernel": "kloop_persist_kernel" + (" (its launch also forms X and the scratch)" if filled
+                                                    else " (its launch also forms X)" if fused else ""),
                 "flops_per_launch": fl, "flops_note": "recurrence (W_h h forward, W_h^T dp backward)" +
-                                                      (" + input projection" if fused else ""),
+                                                      (" + input projection" if fused else "") +
+                                                      (" + scratch fill" if filled else ""),
                 "launch_us": round(dur * 1e6, 3),
                 "recurrence_alone_us": round(kt["recurrence"]["mean_s"] * 1e6, 3),
                 "recurrence_alone_note": "the same kernel given X (cfc_kloop_recurrence), one launch",
@@ -704,6 +725,8 @@ def bench_kloop(torch, cfc, workload, steps, warmup, trials, t_node, detail, tim
     n_rep = 20 if K * B * C * n_in < (1 << 26) else 5
     kt["fwd_bwd"] = timer(lambda: cfc.cfc_kloop_fwd_bwd(*t, out=out), n_rep)
     if path == "persistent":
+        kt["fwd_bwd_fill"] = timer(lambda: cfc.cfc_kloop_fwd_bwd_fill(*t, out=out), n_rep)
+        kt["fill_fused"] = persist_fill_fused(torch, out, B, C, K)
         X = torch.empty((K, B, 3 * C), device="cuda")
         kt["input_projection"] = timer(lambda: cfc.cfc_input_projection(t[0], t[3], t[4], X), 50)
         kt["recurrence"] = timer(lambda: cfc.cfc_kloop_recurrence(X, t[1], t[2], t[3], out=out), 20)
@@ -762,9 +785,12 @@ def bench_kloop(torch, cfc, workload, steps, warmup, trials, t_node, detail, tim
     cfc.cfc_train_kloop(*t, out=out)   # restore the step's own state
     torch.cuda.synchronize()
     res["kernels"] = {k: dict(mean_us=round(v["mean_s"] * 1e6, 3), pair_median_us=round(v["pair_median_s"] * 1e6, 3),
-                              n=v["n"]) for k, v in kt.items()}
+                              n=v["n"]) for k, v in kt.items() if isinstance(v, dict)}
+    if path == "persistent":
+        res["persist_launch_forms_scratch"] = kt["fill_fused"]
     res["roofline"] = kloop_roofline(torch, cfc, path, kt, B, C, n_x, K, workload)
-    res["step_roofline"] = step_roofline(path, B, C, n_x, K, ms_per_step, t_node)
+    res["step_roofline"] = step_roofline(path, B, C, n_x, K, ms_per_step, t_node,
+                                         2 if kt.get("fill_fused") else None)
     if detail:
         res["deterministic_3_runs"] = deterministic_runs(torch, cfc, t)
     del out

@@ -189,6 +189,21 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0,
                       float* h_hist, float* act, float* ws, size_t ws_bytes,
                       int B, int C, int n_x, int K, void* stream);
 
+/* cfc_train_kloop up to its reduction ("K-loop Parallelization", section
+ * Architecture Choice: the K-loop's per-sample scratch, before the
+ * reducer): the same launches and bits as cfc_train_kloop without the
+ * reduction, writing h_hist, act, the dp block of ws, gW_scratch and
+ * gb_scratch as it does (same arguments, layouts and errors; gW and gb are
+ * not touched).  On the persistent path with B <= 128 this is one launch
+ * whenever cfc_train_kloop's is (see there); otherwise cfc_kloop_fwd_bwd's
+ * launches followed by cfc_scratch_fill's.  K == 0 or B == 0 writes
+ * h_hist[0] = h0 and zero scratch. */
+int cfc_kloop_fwd_bwd_fill(const float* u, const float* y, const float* h0,
+                           const float* W, const float* bias,
+                           float* h_hist, float* act, float* ws, size_t ws_bytes,
+                           float* gW_scratch, float* gb_scratch,
+                           int B, int C, int n_x, int K, void* stream);
+
 /* AdamW after the reducer ("K-loop Parallelization", section Trainer Wiring:
  * the optimizer consumes the final gradient buffers and runs strictly after
  * every reducer -- on the same stream after cfc_train_kloop, stream order

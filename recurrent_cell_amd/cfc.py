@@ -48,6 +48,7 @@ def lib():
         L.reduce_axis0.argtypes = [_P, _I64, _I64, _P, _P]
         L.cfc_train_kloop.argtypes = [_P] * 8 + [ctypes.c_size_t] + [_P] * 4 + [_I, _I, _I, _I, _P]
         L.cfc_kloop_fwd_bwd.argtypes = [_P] * 8 + [ctypes.c_size_t, _I, _I, _I, _I, _P]
+        L.cfc_kloop_fwd_bwd_fill.argtypes = [_P] * 8 + [ctypes.c_size_t, _P, _P, _I, _I, _I, _I, _P]
         L.cfc_train_kloop_noalloc.argtypes = [_P] * 11 + [_I, _I, _I, _I, _P]
         L.cfc_scratch_fill.argtypes = [_P] * 5 + [_I, _I, _I, _I, _P]
         L.cfc_input_projection.argtypes = [_P] * 4 + [_I64, _I, _I, _P]
@@ -324,6 +325,21 @@ class KloopGemmBuffers:
         ws_floats = lib().cfc_train_kloop_gemm_workspace_bytes(B, C, n_x, K) // 4
         return KloopGemmBuffers(h_hist=e(K + 1, B, C), act=e(K, 3, B, C), ws=e(max(ws_floats, 1)),
                                 gW=e(3, C, n_x + C), gb=e(3, C))
+
+
+def cfc_kloop_fwd_bwd_fill(u, y, h0, W, bias, out):
+    """cfc_train_kloop up to its reduction: h_hist, act, dp in out.ws and the
+    per-sample scratch (out.gW_scratch, out.gb_scratch); gW and gb untouched."""
+    K, B, n_x = u.shape
+    C = h0.shape[1]
+    n_in = n_x + C
+    args = (_dev(u, "u", (K, B, n_x)), _dev(y, "y", (K, B, C)), _dev(h0, "h0", (B, C)),
+            _dev(W, "W", (3, C, n_in)), _dev(bias, "bias", (3, C)),
+            _dev(out.h_hist, "h_hist", (K + 1, B, C)), _dev(out.act, "act", (K, 3, B, C)),
+            _dev(out.ws, "ws"), out.ws.numel() * 4,
+            _dev(out.gW_scratch, "gW_scratch", (B, 3, C, n_in)), _dev(out.gb_scratch, "gb_scratch", (B, 3, C)))
+    _check("cfc_kloop_fwd_bwd_fill", lib().cfc_kloop_fwd_bwd_fill(*args, B, C, n_x, K, _stream(h0)))
+    return out
 
 
 def cfc_train_kloop_gemm(u, y, h0, W, bias, out=None):

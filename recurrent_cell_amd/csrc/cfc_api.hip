@@ -763,6 +763,32 @@ int cfc_kloop_fwd_bwd(const float* u, const float* y, const float* h0, const flo
     return enqueue_fwd_bwd(k, uncaptured(path, s), make_plan(B, C, n_x, W, nullptr), s);
 }
 
+int cfc_kloop_fwd_bwd_fill(const float* u, const float* y, const float* h0, const float* W, const float* bias,
+                           float* h_hist, float* act, float* ws, size_t ws_bytes, float* gW_scratch,
+                           float* gb_scratch, int B, int C, int n_x, int K, void* stream)
+{
+    cfc_host::last_error().clear();
+    const char* fn = "cfc_kloop_fwd_bwd_fill";
+    Path path = Path::Steps;
+    if (int rc = check_kloop(fn, u, y, h0, W, bias, h_hist, act, ws, ws_bytes, gW_scratch, gb_scratch, nullptr,
+                             nullptr, B, C, n_x, K, false, &path))
+        return rc;
+    const int64_t n_in = (int64_t)n_x + C, BC = (int64_t)B * C;
+    if ((BC * 3 * n_in > 0 && !gW_scratch) || (BC > 0 && !gb_scratch)) return fail(CFC_EINVAL, "%s: null pointer", fn);
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0 || B == 0) {
+        if (BC > 0) CFC_HIP(hipMemcpyAsync(h_hist, h0, BC * 4, hipMemcpyDeviceToDevice, s), "h0 copy");
+        CFC_HIP(cfc::launch_fill_zero(gW_scratch, BC * 3 * n_in, s), "zero fill");
+        CFC_HIP(cfc::launch_fill_zero(gb_scratch, 3 * BC, s), "zero fill");
+        return CFC_OK;
+    }
+    const KloopArgs k{u, y, h0, W, bias, h_hist, act, ws, gW_scratch, gb_scratch, nullptr, nullptr, B, C, n_x, K};
+    bool filled = false;
+    if (int rc = enqueue_fwd_bwd(k, uncaptured(path, s), make_plan(B, C, n_x, W, nullptr), s, &filled)) return rc;
+    if (!filled) return enqueue_fill(ws, u, h_hist, gW_scratch, gb_scratch, B, C, n_x, K, s);
+    return CFC_OK;
+}
+
 // ---------------------------------------------------------------------------
 // GEMM-form weight gradient: gW_q = sum over the K*B (t, b) rows of
 // dp_t[b, q C + c] z_t[b, k], one matrix-core contraction over the rows

@@ -114,6 +114,24 @@ def test_kloop_argument_errors(L):
     assert b"workspace" in L.cfc_last_error()
 
 
+def test_kloop_fwd_bwd_fill_argument_errors(L):
+    B, C, n_x, K = 4, 16, 8, 3
+    a = _kloop_args(B, C, n_x, K)[:11]   # through gb_scratch: no gW, gb
+    assert L.cfc_kloop_fwd_bwd_fill(*a, B, C, n_x, -1, None) == -1
+    bad = list(a)
+    bad[9] = None  # gW_scratch
+    assert L.cfc_kloop_fwd_bwd_fill(*bad, B, C, n_x, K, None) == -1
+    assert b"null" in L.cfc_last_error()
+    bad = list(a)
+    bad[10] = a[0]  # gb_scratch over u
+    assert L.cfc_kloop_fwd_bwd_fill(*bad, B, C, n_x, K, None) == -1
+    assert b"overlap" in L.cfc_last_error()
+    bad = list(a)
+    bad[8] = a[8] - 4  # workspace one float short
+    assert L.cfc_kloop_fwd_bwd_fill(*bad, B, C, n_x, K, None) == -1
+    assert b"workspace" in L.cfc_last_error()
+
+
 def test_kloop_status_argument_errors(L):
     """cfc_kloop_status refuses bad sizes and a null or short workspace before
     any HIP call; with K == 0 or B == 0 nothing was launched: CFC_OK."""

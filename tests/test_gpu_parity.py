@@ -384,6 +384,17 @@ def test_persistent_step_forms_scratch_in_launch(cfc, case):
     cfc.cfc_scratch_fill(dp, u, g.h_hist, S, Sb)
     np.testing.assert_array_equal(bits(host(S)), bits(host(g.gW_scratch)))
     np.testing.assert_array_equal(bits(host(Sb)), bits(host(g.gb_scratch)))
+    # cfc_kloop_fwd_bwd_fill: the same launch without the reduction, same bits
+    f = cfc.KloopBuffers.allocate(B, C, n_x, K, "cuda")
+    f.gW_scratch.fill_(float("nan"))
+    f.gb_scratch.fill_(float("nan"))
+    cfc.cfc_kloop_fwd_bwd_fill(u, y, h0, W, bias, out=f)
+    cfc.cfc_kloop_status(f, B, C, n_x, K)
+    chunks_f = persist_chunk_flags(f.ws, B, C, K)
+    np.testing.assert_array_equal(chunks_f, np.full_like(chunks_f, persist_projection_flags(f.ws, B, C, K)[0][0]))
+    for k in ("h_hist", "act", "gW_scratch", "gb_scratch"):
+        np.testing.assert_array_equal(bits(host(getattr(f, k))), bits(host(getattr(g, k))), err_msg=k)
+    np.testing.assert_array_equal(bits(host(f.ws[:K * B * 3 * C])), bits(host(dp.reshape(-1))))
 
 
 @pytest.mark.parametrize("case", ["pages", "ragged_scalar", "three_blocks", "odd_channels"])
