@@ -60,6 +60,7 @@ __device__ __forceinline__ f32x4 load4_or_zero(const float* clamped, bool valid)
     return valid ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// [persistent kernel source: begin]
 // 4-byte store at device scope (sc1): written through to memory, so that a
 // workgroup on another XCD of the same launch reads it.
 __device__ __forceinline__ void st_agent(float* p, float v)
@@ -74,6 +75,7 @@ __device__ __forceinline__ void st4_dev(float* base, int bytes, int byte_off, f3
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
                                            byte_off, 0, 16 /* sc1 */);
 }
+// [persistent kernel source: end]
 
 // z_s = [u_t[b0+s] ; h_prev[b0+s]] for the tile's samples into LDS rows of
 // pitch ldz (zero padded past n_in and for absent samples).
@@ -561,6 +563,7 @@ __global__ __launch_bounds__(kThreads) void permute_w_kernel(PermuteArgs a)
 // of a workgroup's own data use plain moves.  (st_agent, above, is the
 // 4-byte store.)
 //
+// [persistent kernel source: begin]
 // 16-byte device-scope load through a raw buffer resource over [base, base
 // + bytes): one request per 16 bytes, where two 8-byte agent-scope atomic
 // loads make two.  Offsets at or past `bytes` read zero.
@@ -570,6 +573,7 @@ __device__ __forceinline__ f32x4 ld4_dev(const float* base, int bytes, int byte_
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
 }
+// [persistent kernel source: end]
 // RES: a 16-byte device-scope load (two 8-byte agent-scope loads).
 template <bool RES>
 __device__ __forceinline__ f32x4 ld4(const float* p)
@@ -3009,6 +3013,7 @@ int persist_proj_blocks(int B, int C, int K)
     return n > 0x3fffffffLL ? -1 : (int)n;
 }
 
+// [persistent kernel source: begin]
 bool persist_fill_fits(int B, int C, int n_x, int K, int n_cus)
 {
     PersistShape ps;
@@ -3024,6 +3029,7 @@ bool persist_fill_fits(int B, int C, int n_x, int K, int n_cus)
     const int n_fill = B * ((3 * C + 63) / 64);
     return (int64_t)(n_proj > n_fill ? n_proj : n_fill) + B <= n_cus;
 }
+// [persistent kernel source: end]
 
 size_t persist_smem(int C)
 {
